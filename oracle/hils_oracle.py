@@ -1,0 +1,306 @@
+"""HiLS attention forward pass: CPU oracle.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or constants) and imports only
+NumPy.
+
+It is written for a reader to check against the pages by eye: one query row at
+a time, in the order the method states its steps, float64 arithmetic.
+
+What the method computes (sources are the pages' titles and sections):
+
+  [P1] "HiLS-Attention" model page, "Model Description": block-sparse attention
+       that ranks chunks by their exact attention mass would need the full QK
+       product; HiLS instead scores compressed per-chunk keys to get a surrogate
+       of that mass, selects the top-k chunks, and factorises attention into an
+       inter-chunk softmax and an intra-chunk softmax.
+  [P2] "HiLS Attention Extrapolates 64x at 90% Retrieval Accuracy": each query
+       attends to every retrieved chunk independently and the per-chunk outputs
+       are combined with the chunks' retrieval scores.
+  [P3] "HiLS Attention: Tencent ... Sparse Attention" explainer,
+       "Core idea: landmark tokens and hierarchical factorisation": one landmark
+       token per chunk; level 1 is the query's attention over the landmarks
+       (a distribution over chunks), level 2 is ordinary attention over the
+       tokens inside the selected chunks.
+       "Engineering details", Q-Cal item: a low-rank offset
+       delta_q = W_up W_down h, with h the token's hidden state, adapts the
+       query for chunk-level mass estimation.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  R1 one scale s (default 1/sqrt(d)) serves both softmax levels;
+  R2 candidates of query i are the causal chunks j <= floor(i/C), its own chunk
+     included and scored like the others (not forced in);
+  R3 ties in the landmark score go to the smaller chunk index;
+  R4 with fewer than k candidates every candidate is selected; idx is padded
+     with -1 and w with 0; idx is listed in ascending chunk order;
+  R5 W_down is [r, D], shared by the heads; W_up is [H*d, r]; rows
+     h*d..h*d+d-1 of W_up give head h's offset;
+  R6 the calibrated query q~ is used for chunk scoring only; the intra-chunk
+     attention uses the raw q;
+  R7 rounding points: delta_q and q + delta_q are formed and rounded to fp32,
+     then q~ is rounded once to the run dtype (round-to-nearest-even to bf16 for
+     bf16 runs); the landmark score sigma is rounded to fp32 before ranking and
+     before the inter-chunk softmax (the kernel's precision decides the integer
+     outcome, as both sides must take it in the same precision); everything else
+     is float64 here;
+  R8 the landmark token is not a key of the intra-chunk attention; the query's
+     own chunk is causally truncated at the query;
+  R9 decode: the new token's key/value are already in the cache; the query sits
+     at position kv_len-1 and a partial last chunk is allowed.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "round_to_bf16", "round_to_run_dtype", "qcal_offset", "calibrated_query", "landmark_scores",
+    "select_top_k", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
+    "prefill", "decode", "attend_given_selection",
+]
+
+
+# ------------------------------------------------------------------------------------------
+# Rounding (R7)
+# ------------------------------------------------------------------------------------------
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round fp32 values to the nearest bfloat16 (ties to even); returns fp32 holding the result.
+
+    bfloat16 keeps the top 16 bits of an fp32 word.  Round-to-nearest-even adds
+    0x7FFF plus the lowest kept bit to the word and truncates.  Finite inputs only."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = (u + np.uint64(0x7FFF) + keep_lsb) & np.uint64(0xFFFF0000)
+    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+
+
+def round_to_run_dtype(x, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "fp32":
+        return x32
+    if dtype == "bf16":
+        return round_to_bf16(x32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ------------------------------------------------------------------------------------------
+# Step 1: Q-Cal ([P3] Engineering details, Q-Cal)
+# ------------------------------------------------------------------------------------------
+
+def qcal_offset(h_row: np.ndarray, w_down: np.ndarray, w_up_head: np.ndarray) -> np.ndarray:
+    """delta_q = W_up[head rows] . (W_down . h), float64.  h_row [D], w_down [r,D], w_up_head [d,r]."""
+    t = np.zeros(w_down.shape[0], dtype=np.float64)
+    for a in range(w_down.shape[0]):
+        t[a] = np.dot(w_down[a].astype(np.float64), h_row.astype(np.float64))
+    dq = np.zeros(w_up_head.shape[0], dtype=np.float64)
+    for e in range(w_up_head.shape[0]):
+        dq[e] = np.dot(w_up_head[e].astype(np.float64), t)
+    return dq
+
+
+def calibrated_query(q_row: np.ndarray, h_row: Optional[np.ndarray], w_down: Optional[np.ndarray],
+                     w_up_head: Optional[np.ndarray], dtype: str) -> np.ndarray:
+    """q~ = round_dtype(fp32(q + fp32(delta_q)))  (R7).  Without Q-Cal (r = 0) q~ = q."""
+    q32 = np.asarray(q_row, dtype=np.float32)
+    if w_down is None or w_down.shape[0] == 0:
+        return round_to_run_dtype(q32, dtype)
+    dq32 = qcal_offset(h_row, w_down, w_up_head).astype(np.float32)
+    s32 = (q32.astype(np.float64) + dq32.astype(np.float64)).astype(np.float32)
+    return round_to_run_dtype(s32, dtype)
+
+
+# ------------------------------------------------------------------------------------------
+# Step 2: inter-chunk scores over the landmarks ([P1] Model Description; [P3] Core idea, level 1)
+# ------------------------------------------------------------------------------------------
+
+def landmark_scores(q_tilde: np.ndarray, lmk_rows: np.ndarray) -> np.ndarray:
+    """sigma_j = q~ . lmk_j for every given landmark row, float64 dot rounded to fp32 (R7)."""
+    qt = np.asarray(q_tilde, dtype=np.float64)
+    out = np.empty(lmk_rows.shape[0], dtype=np.float32)
+    for j in range(lmk_rows.shape[0]):
+        out[j] = np.float32(np.dot(lmk_rows[j].astype(np.float64), qt))
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# Step 3: top-k chunk selection ([P1] "selects top-k chunks"; R2-R4)
+# ------------------------------------------------------------------------------------------
+
+def select_top_k(sigma: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores (ties -> smaller index), ascending, padded with -1 to k.
+
+    Repeatedly takes the best remaining candidate; np.argmax returns the first
+    (smallest) index among equal maxima, which is the tie rule R3."""
+    s = np.asarray(sigma, dtype=np.float32).astype(np.float64)
+    n = s.shape[0]
+    taken = np.zeros(n, dtype=bool)
+    chosen = []
+    for _ in range(min(k, n)):
+        masked = np.where(taken, -np.inf, s)
+        j = int(np.argmax(masked))
+        if taken[j]:          # only -inf left (cannot happen for finite scores)
+            break
+        taken[j] = True
+        chosen.append(j)
+    out = np.full(k, -1, dtype=np.int64)
+    out[: len(chosen)] = sorted(chosen)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# Step 4: inter-chunk softmax over the selection ([P1] factorised inter-chunk softmax)
+# ------------------------------------------------------------------------------------------
+
+def inter_chunk_weights(sigma_selected: np.ndarray, scale: float) -> np.ndarray:
+    """w_j = exp(s*sigma_j - max) / sum over the selection; float64."""
+    z = scale * np.asarray(sigma_selected, dtype=np.float64)
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+# ------------------------------------------------------------------------------------------
+# Step 5: intra-chunk attention ([P3] Core idea, level 2; [P2] each chunk attended independently)
+# ------------------------------------------------------------------------------------------
+
+def intra_chunk_attention(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one (raw) query over one chunk's visible keys/values; float64 [d]."""
+    q = np.asarray(q_row, dtype=np.float64)
+    a = np.array([scale * np.dot(keys[t].astype(np.float64), q) for t in range(keys.shape[0])])
+    a = a - a.max()
+    p = np.exp(a)
+    p = p / p.sum()
+    o = np.zeros(values.shape[1], dtype=np.float64)
+    for t in range(values.shape[0]):
+        o += p[t] * values[t].astype(np.float64)
+    return o
+
+
+# ------------------------------------------------------------------------------------------
+# Step 6: fusion by the chunk weights ([P2] outputs fused by retrieval scores)
+# ------------------------------------------------------------------------------------------
+
+def fuse(weights: Sequence[float], chunk_outputs: Sequence[np.ndarray]) -> np.ndarray:
+    o = np.zeros_like(np.asarray(chunk_outputs[0], dtype=np.float64))
+    for w, oj in zip(weights, chunk_outputs):
+        o += w * np.asarray(oj, dtype=np.float64)
+    return o
+
+
+# ------------------------------------------------------------------------------------------
+# One query row end to end
+# ------------------------------------------------------------------------------------------
+
+def _visible_range(j: int, chunk: int, i: int):
+    """Keys of chunk j visible to query position i (R8): [jC, min(jC+C-1, i)]."""
+    lo = j * chunk
+    hi = min(lo + chunk, i + 1)
+    return lo, hi
+
+
+def attend_row(q_row, keys, values, idx, w, i, chunk, scale) -> np.ndarray:
+    """Steps 5-6 for one row, given its selection idx (ascending, -1 padded) and weights w."""
+    outs, ws = [], []
+    for j, wj in zip(idx, w):
+        if j < 0:
+            continue
+        lo, hi = _visible_range(int(j), chunk, i)
+        outs.append(intra_chunk_attention(q_row, keys[lo:hi], values[lo:hi], scale))
+        ws.append(wj)
+    return fuse(ws, outs)
+
+
+def hils_row(q_row, q_tilde, keys, values, lmk, i, chunk, topk, scale):
+    """All steps for query position i.  keys/values [>= i+1, d], lmk [>= i//C + 1, d].
+
+    Returns (o [d] float64, idx [k] int64, w [k] float64, sigma [c+1] fp32)."""
+    c = i // chunk
+    sigma = landmark_scores(q_tilde, lmk[: c + 1])
+    idx = select_top_k(sigma, topk)
+    sel = idx[idx >= 0]
+    w = np.zeros(topk, dtype=np.float64)
+    w[: len(sel)] = inter_chunk_weights(sigma[sel], scale)
+    o = attend_row(q_row, keys, values, idx, w, i, chunk, scale)
+    return o, idx, w, sigma
+
+
+# ------------------------------------------------------------------------------------------
+# Batched drivers (loops over batch, head and the requested rows)
+# ------------------------------------------------------------------------------------------
+
+def _w_up_head(w_up, head, d):
+    return None if w_up is None else w_up[head * d:(head + 1) * d]
+
+
+def prefill_rows(inp: Dict[str, np.ndarray], rows: Iterable[tuple], chunk: int, topk: int,
+                 dtype: str, scale: Optional[float] = None) -> Dict[tuple, dict]:
+    """Prefill for selected (b, h, i) rows.  inp holds q,k,v [B,H,L,d], lmk [B,H,N,d] and,
+    with Q-Cal, h [B,L,D], w_down [r,D], w_up [H*d,r] (fp32 arrays holding dtype-exact values).
+
+    Returns {(b,h,i): dict(o, idx, w, sigma, q_tilde)}."""
+    q, k, v, lmk = inp["q"], inp["k"], inp["v"], inp["lmk"]
+    d = q.shape[-1]
+    s = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    w_down = inp.get("w_down")
+    if w_down is not None and w_down.shape[0] == 0:
+        w_down = None
+    out = {}
+    for (b, h, i) in rows:
+        hid = None if w_down is None else inp["h"][b, i]
+        qt = calibrated_query(q[b, h, i], hid, w_down, _w_up_head(inp.get("w_up"), h, d), dtype)
+        o, idx, w, sigma = hils_row(q[b, h, i], qt, k[b, h], v[b, h], lmk[b, h], i, chunk, topk, s)
+        out[(b, h, i)] = dict(o=o, idx=idx, w=w, sigma=sigma, q_tilde=qt)
+    return out
+
+
+def prefill(inp: Dict[str, np.ndarray], chunk: int, topk: int, dtype: str,
+            scale: Optional[float] = None):
+    """Full prefill: returns o [B,H,L,d] float64, idx [B,H,L,k] int64, w [B,H,L,k] float64."""
+    B, H, L, d = inp["q"].shape
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(L)]
+    res = prefill_rows(inp, rows, chunk, topk, dtype, scale)
+    o = np.zeros((B, H, L, d))
+    idx = np.zeros((B, H, L, topk), dtype=np.int64)
+    w = np.zeros((B, H, L, topk))
+    for (b, h, i), r in res.items():
+        o[b, h, i], idx[b, h, i], w[b, h, i] = r["o"], r["idx"], r["w"]
+    return o, idx, w
+
+
+def decode(inp: Dict[str, np.ndarray], chunk: int, topk: int, dtype: str,
+           scale: Optional[float] = None, pairs: Optional[Iterable[tuple]] = None) -> Dict[tuple, dict]:
+    """Decode step (R9): q [B,H,d] at position kv_len[b]-1 over k_cache/v_cache [B,H,Lmax,d],
+    lmk [B,H,ceil(Lmax/C),d], h [B,D].  Returns {(b,h): dict(o, idx, w, sigma, q_tilde)}."""
+    q, kc, vc, lmk, kv_len = inp["q"], inp["k_cache"], inp["v_cache"], inp["lmk"], inp["kv_len"]
+    B, H, d = q.shape
+    s = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    w_down = inp.get("w_down")
+    if w_down is not None and w_down.shape[0] == 0:
+        w_down = None
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    out = {}
+    for (b, h) in pairs:
+        i = int(kv_len[b]) - 1
+        hid = None if w_down is None else inp["h"][b]
+        qt = calibrated_query(q[b, h], hid, w_down, _w_up_head(inp.get("w_up"), h, d), dtype)
+        o, idx, w, sigma = hils_row(q[b, h], qt, kc[b, h], vc[b, h], lmk[b, h], i, chunk, topk, s)
+        out[(b, h)] = dict(o=o, idx=idx, w=w, sigma=sigma, q_tilde=qt)
+    return out
+
+
+def attend_given_selection(q_row, keys, values, idx, sigma_selected, i, chunk, scale) -> np.ndarray:
+    """Steps 4-6 on a supplied selection: idx (ascending, -1 padded) and the fp32 scores of the
+    selected entries in the same order.  Used to check outputs where the selection differs from
+    the oracle's own only inside the tie band."""
+    idx = np.asarray(idx)
+    valid = idx >= 0
+    w = np.zeros(len(idx))
+    w[valid] = inter_chunk_weights(np.asarray(sigma_selected)[valid], scale)
+    return attend_row(q_row, keys, values, idx, w, i, chunk, scale)

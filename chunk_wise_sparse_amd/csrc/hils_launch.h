@@ -1,0 +1,68 @@
+// Internal launchers of the HiLS kernels (host side).  Shapes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+typedef __bf16 bf16;
+
+struct SelectArgs {
+  const void* q;        // [B,H,L,d]
+  const void* lmk;      // [B,H,N,d]
+  const float* tcode;   // [B*L, r] fp32 Q-Cal code (NULL if r == 0)
+  const void* w_up;     // [H*d, r]
+  int32_t* idx;         // [B,H,L,k]
+  float* w;             // [B,H,L,k]
+  int B, H, L, N, k, r;
+  float scale;
+};
+
+struct AttnArgs {
+  const void* q;        // [B,H,L,d]
+  const void* key;      // [B,H,L,d]
+  const void* val;      // [B,H,L,d]
+  const int32_t* idx;   // [B,H,L,k]
+  const float* w;       // [B,H,L,k]
+  void* o;              // [B,H,L,d]
+  int B, H, L, N, topk;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;        // [B,H,d] raw query
+  const void* q_tilde;  // [B,H,d] calibrated query (workspace)
+  const void* k_cache;  // [B,H,Lmax,d]
+  const void* v_cache;
+  const void* lmk;      // [B,H,Nmax,d]
+  const int32_t* kv_len;
+  float* scores;        // [B,H,Nmax] workspace
+  int32_t* idx;         // [B,H,k]
+  float* w;             // [B,H,k]
+  float* partial;       // [B,H,k,d] workspace
+  void* o;              // [B,H,d]
+  int B, H, Lmax, Nmax, k;
+  float scale;
+};
+
+template <typename T>
+hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,
+                                    int r, hipStream_t st);
+template <typename T>
+hipError_t launch_decode_qcal(const T* q, const T* hid, const T* w_down, const T* w_up,
+                              T* q_tilde, int B, int H, int d, int D, int r, hipStream_t st);
+
+template <typename T, int D>
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+template <typename T, int D>
+hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
+
+template <typename T, int D>
+hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st);
+template <typename T, int D>
+hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st);
+template <typename T, int D>
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace hils

@@ -1,0 +1,219 @@
+"""Thin Python binding of libhils.so (the HiLS C ABI, include/hils.h).
+
+Argument marshalling only: tensors are checked for device, dtype and contiguity, outputs and the
+workspace are allocated with torch on the tensors' device, and the call is enqueued on torch's
+current stream.  Every step of the computation runs in the library's HIP kernels; if the library
+is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhils.so")
+
+HILS_OK = 0
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", -3: "HILS_ERR_ALIGNMENT",
+          -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
+EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
+            "hils_prefill_fwd", "hils_decode_fwd", "hils_status_string", "hils_last_error"]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("q_tile", ctypes.c_int32), ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32)]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Open libhils.so and declare its signatures.  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m chunk_wise_sparse_amd.csrc.build` (there is no fallback)")
+    # One HIP runtime per process: torch ships its own libamdhip64, and the library must bind to
+    # that same runtime (it resolves libamdhip64.so.7 by soname to the copy already loaded).
+    # Opening the library first would load a second runtime that then finds no free device.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.hils_abi_version.restype = i32
+    lib.hils_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams), i32]
+    lib.hils_prefill_workspace_size.restype = sz
+    lib.hils_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), i32]
+    lib.hils_decode_workspace_size.restype = sz
+    lib.hils_prefill_fwd.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 10 + [vp, sz, vp]
+    lib.hils_prefill_fwd.restype = i32
+    lib.hils_decode_fwd.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 11 + [vp, sz, vp]
+    lib.hils_decode_fwd.restype = i32
+    lib.hils_status_string.argtypes = [i32]
+    lib.hils_status_string.restype = ctypes.c_char_p
+    lib.hils_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int, what: str):
+    if status != HILS_OK:
+        lib = load()
+        msg = lib.hils_status_string(status).decode()
+        detail = lib.hils_last_error().decode()
+        raise RuntimeError(f"{what} failed: {STATUS.get(status, status)} ({msg}): {detail}")
+
+
+# ----------------------------------------------------------------------------------------------
+# HIP events for per-stage timing (the library records them on the launch stream)
+# ----------------------------------------------------------------------------------------------
+class StageEvents:
+    """n hipEvent_t handles created through libamdhip64; elapsed_ms(i, j) after a sync."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.n = n
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.arr[i] = ev
+        self.ptr = ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p))
+
+    def synchronize(self):
+        rc = self.hip.hipEventSynchronize(ctypes.c_void_p(self.arr[self.n - 1]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventSynchronize failed ({rc})")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.arr[i]),
+                                          ctypes.c_void_p(self.arr[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            for i in range(self.n):
+                self.hip.hipEventDestroy(ctypes.c_void_p(self.arr[i]))
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------------------------
+# Calls
+# ----------------------------------------------------------------------------------------------
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(tensors: Sequence, device, dtype):
+    for name, t in tensors:
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
+            q_tile: int = 64, scale: Optional[float] = None, return_selection: bool = False,
+            out=None, workspace=None, events: Optional[StageEvents] = None):
+    """HiLS prefill.  q,k,v [B,H,L,d]; lmk [B,H,L/C,d]; h [B,L,D]; w_down [r,D]; w_up [H*d,r].
+
+    Returns o [B,H,L,d], or (o, idx [B,H,L,k] int32, w [B,H,L,k] float32)."""
+    import torch
+    lib = load()
+    B, H, L, d = q.shape
+    _require([("q", q), ("k", k), ("v", v), ("lmk", lmk), ("h", h), ("w_down", w_down), ("w_up", w_up)],
+             q.device, q.dtype)
+    r = 0 if w_down is None else w_down.shape[0]
+    D = 0 if h is None else h.shape[-1]
+    p = PrefillParams(B, H, L, d, chunk, topk, q_tile, D, r, 0.0 if scale is None else float(scale),
+                      _dtype_code(q), events.ptr if events else None, events.n if events else 0)
+    o = out if out is not None else torch.empty_like(q)
+    idx = w = None
+    if return_selection:
+        idx = torch.empty((B, H, L, topk), dtype=torch.int32, device=q.device)
+        w = torch.empty((B, H, L, topk), dtype=torch.float32, device=q.device)
+    need = lib.hils_prefill_workspace_size(ctypes.byref(p), 1 if return_selection else 0)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.hils_prefill_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk), _ptr(h), _ptr(w_down),
+                              _ptr(w_up), _ptr(o), _ptr(idx), _ptr(w), workspace.data_ptr(), need,
+                              _stream_handle(q.device))
+    check(st, "hils_prefill_fwd")
+    return (o, idx, w) if return_selection else o
+
+
+def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, topk: int,
+           chunk: int = 64, scale: Optional[float] = None, return_selection: bool = False,
+           out=None, workspace=None, events: Optional[StageEvents] = None):
+    """HiLS decode step.  q [B,H,d]; caches [B,H,Lmax,d]; lmk [B,H,ceil(Lmax/C),d]; kv_len [B] int32
+    (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k])."""
+    import torch
+    lib = load()
+    B, H, d = q.shape
+    Lmax = k_cache.shape[2]
+    _require([("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("lmk", lmk), ("h", h),
+              ("w_down", w_down), ("w_up", w_up)], q.device, q.dtype)
+    if kv_len.dtype != torch.int32 or kv_len.device != q.device or not kv_len.is_contiguous():
+        raise ValueError("kv_len must be a contiguous int32 tensor on the query's device")
+    r = 0 if w_down is None else w_down.shape[0]
+    D = 0 if h is None else h.shape[-1]
+    p = DecodeParams(B, H, Lmax, d, chunk, topk, D, r, 0.0 if scale is None else float(scale),
+                     _dtype_code(q), events.ptr if events else None, events.n if events else 0)
+    o = out if out is not None else torch.empty_like(q)
+    idx = w = None
+    if return_selection:
+        idx = torch.empty((B, H, topk), dtype=torch.int32, device=q.device)
+        w = torch.empty((B, H, topk), dtype=torch.float32, device=q.device)
+    need = lib.hils_decode_workspace_size(ctypes.byref(p), 1 if return_selection else 0)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.hils_decode_fwd(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lmk),
+                             kv_len.data_ptr(), _ptr(h), _ptr(w_down), _ptr(w_up), _ptr(o), _ptr(idx), _ptr(w),
+                             workspace.data_ptr(), need, _stream_handle(q.device))
+    check(st, "hils_decode_fwd")
+    return (o, idx, w) if return_selection else o
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,158 @@
+"""Prefill on the GPU through the C ABI, element by element against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from chunk_wise_sparse_amd import synth
+from oracle import hils_oracle as O
+from parity import assert_within, check_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+    return torch
+
+
+def _to_dev(inp, dtype):
+    torch = _torch()
+    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda", dt) for k, v in inp.items()}
+
+
+def _run(lib, dev, cfg, **kw):
+    from chunk_wise_sparse_amd import hils
+    return hils.prefill(dev["q"], dev["k"], dev["v"], dev["lmk"], dev.get("h"), dev.get("w_down"),
+                        dev.get("w_up"), topk=cfg.topk, return_selection=True, **kw)
+
+
+def _compare(inp, cfg, o, idx, w, rows, scale=None):
+    s = (1.0 / math.sqrt(cfg.head_dim)) if scale is None else scale
+    res = O.prefill_rows(inp, rows, cfg.chunk, cfg.topk, cfg.dtype, scale=scale)
+    rset = sorted(res)
+    bi = np.array([r[0] for r in rset]); hi = np.array([r[1] for r in rset]); ii = np.array([r[2] for r in rset])
+    import torch
+    o_np = o.float()[bi, hi, ii].cpu().numpy()
+    idx_np = idx[bi, hi, ii].cpu().numpy()
+    w_np = w[bi, hi, ii].cpu().numpy()
+    gpu_o = {key: o_np[t] for t, key in enumerate(rset)}
+    gpu_idx = {key: idx_np[t] for t, key in enumerate(rset)}
+    gpu_w = {key: w_np[t] for t, key in enumerate(rset)}
+    stats = check_rows(res, gpu_o, gpu_idx, gpu_w, cfg.dtype,
+                       lambda key: (inp["q"][key[0], key[1], key[2]], inp["k"][key[0], key[1]], inp["v"][key[0], key[1]]),
+                       cfg.chunk, s)
+    print(f"[parity] {cfg.name}: {stats['n_rows']} rows, max|do| {stats['max_abs']:.3g}, "
+          f"mean|do| {stats['mean_abs']:.3g}, max|dw| {stats['max_w']:.3g}, near-tie swaps {stats['n_diff_sel']}",
+          flush=True)
+    assert_within(stats, cfg.dtype)
+    return stats
+
+
+SMALL = [
+    synth.CONFIGS["tiny_fp32"],
+    synth.PrefillConfig("bf16_d128_k8", 2, 2, 1024, 128, 64, 8, "bf16", 16, 256),
+    synth.PrefillConfig("bf16_d64_allchunks", 1, 2, 2048, 64, 64, 64, "bf16", 4, 128),
+    synth.PrefillConfig("bf16_d128_noqcal", 1, 3, 640, 128, 64, 3, "bf16", 0, 0),
+    synth.PrefillConfig("fp32_d128_k1", 1, 1, 512, 128, 64, 1, "fp32", 64, 128),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_prefill_all_rows(lib, cfg):
+    print(f"[case] prefill all rows {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    dev = _to_dev(inp, cfg.dtype)
+    o, idx, w = _run(lib, dev, cfg)
+    _torch().cuda.synchronize()
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, o, idx, w, rows)
+
+
+def test_prefill_two_pass_selection(lib):
+    """More than 128 candidate chunks: the lower-bound pass and the buffered exact top-k."""
+    cfg = synth.PrefillConfig("bf16_16k_k32", 1, 2, 16384, 128, 64, 32, "bf16", 32, 512)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    _compare(inp, cfg, o, idx, w, sample_rows(1, 2, cfg.seq_len, 160, seed=1))
+
+
+def test_prefill_two_pass_k64(lib):
+    cfg = synth.PrefillConfig("bf16_16k_k64", 1, 1, 16384, 64, 64, 64, "bf16", 8, 128)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    _compare(inp, cfg, o, idx, w, sample_rows(1, 1, cfg.seq_len, 200, seed=2))
+
+
+def test_prefill_ties_overflow(lib):
+    """Every landmark identical: all scores tie, so every chunk passes the bound, the buffer
+    overflows and is cut, and the selection must be the k smallest chunk indices."""
+    cfg = synth.PrefillConfig("ties", 1, 2, 12288, 128, 64, 16, "bf16", 0, 0)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    inp["lmk"][:] = inp["lmk"][:, :, :1]
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    idx_np = idx.cpu().numpy()
+    for i in (0, 63, 64, 1023, 1024, 5000, 12287):
+        keff = min(16, i // 64 + 1)
+        assert list(idx_np[0, 0, i, :keff]) == list(range(keff)), (i, idx_np[0, 0, i])
+    _compare(inp, cfg, o, idx, w, sample_rows(1, 2, cfg.seq_len, 64, seed=3))
+
+
+def test_prefill_grouped_ties(lib):
+    """Landmarks drawn from three distinct rows: large groups of exactly equal scores."""
+    cfg = synth.PrefillConfig("group_ties", 1, 2, 10240, 64, 64, 24, "fp32", 8, 128)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    g = np.random.default_rng(5)
+    pick = g.integers(0, 3, size=inp["lmk"].shape[2])
+    inp["lmk"] = np.ascontiguousarray(inp["lmk"][:, :, pick])
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    _compare(inp, cfg, o, idx, w, sample_rows(1, 2, cfg.seq_len, 96, seed=4))
+
+
+def test_prefill_deterministic(lib):
+    cfg = SMALL[1]
+    inp = synth.make_prefill_inputs_np(cfg)
+    dev = _to_dev(inp, cfg.dtype)
+    a = _run(lib, dev, cfg)
+    b = _run(lib, dev, cfg)
+    torch = _torch()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_prefill_without_selection_output(lib):
+    """idx/w kept in the workspace gives the same o."""
+    from chunk_wise_sparse_amd import hils
+    cfg = SMALL[1]
+    dev = _to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)
+    o1, _, _ = _run(lib, dev, cfg)
+    o2 = hils.prefill(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["h"], dev["w_down"], dev["w_up"], topk=cfg.topk)
+    assert _torch().equal(o1, o2)
+
+
+@pytest.mark.parametrize("name,per_head", [("prefill_32k", 12), ("prefill_128k", 4)])
+def test_prefill_full_size_sampled(lib, name, per_head):
+    """Full-size workloads in the launch configuration the benchmark times; sampled rows."""
+    torch = _torch()
+    cfg = synth.CONFIGS[name]
+    print(f"[case] full size {cfg}", flush=True)
+    dev = synth.make_prefill_inputs_torch(cfg, "cuda")
+    o, idx, w = _run(lib, dev, cfg)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg.batch, cfg.heads, cfg.seq_len, per_head, seed=7)
+    inp = {key: dev[key].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
+    if cfg.qcal_rank:
+        pos = sorted({r[2] for r in rows})
+        h_full = np.zeros((cfg.batch, cfg.seq_len, cfg.hidden), dtype=np.float32)
+        h_full[:, pos] = dev["h"][:, pos].float().cpu().numpy()
+        inp["h"] = h_full
+        inp["w_down"] = dev["w_down"].float().cpu().numpy()
+        inp["w_up"] = dev["w_up"].float().cpu().numpy()
+    _compare(inp, cfg, o, idx, w, rows)

@@ -1,0 +1,205 @@
+"""Benchmark of the HiLS forward pass on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  prefill of the 7B-shape 128K workload (B=1, H=32, L=131072, d=128, C=64, k=32, Q-Cal r=32,
+  D=4096, bf16, random-walk queries and hidden states), then
+  one decode step of the 7B-shape 512K workload (8 sequences x 1 token, H=32, d=128, cache 524288,
+  C=64, k=64, r=32, 4 needles per (sequence, head)).
+Inputs are resident in HBM before timing starts.  `value` is the prefill's algorithmic TFLOP/s
+(the work the method must do, not the work the kernels execute); decode figures sit in "decode".
+
+Printed: one JSON line (rank 0).  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HiLS prefill TFLOP/s + decode µs/token & HBM GB/s at 128K–512K, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def prefill_work(cfg):
+    """Algorithmic FLOP per stage: Q-Cal code, selection (scores + Q-Cal offset), attention."""
+    B, H, L, d, C, k, r, D = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.chunk, cfg.topk, \
+        cfg.qcal_rank, cfg.hidden
+    N = L // C
+    scoring = B * H * 2 * d * C * N * (N + 1) // 2
+    pairs = B * H * C * sum(min(k, c + 1) for c in range(N))
+    attention = 4 * C * d * pairs
+    qcal_code = 2 * B * L * r * D
+    qcal_up = 2 * B * L * r * H * d
+    return dict(qcal_code=qcal_code, select=scoring + qcal_up, attention=attention,
+                total=scoring + attention + qcal_code + qcal_up,
+                qcal_code_bytes=B * L * D * 2 + r * D * 2 + B * L * r * 4)
+
+
+def decode_bytes(cfg):
+    """Algorithmic HBM bytes of one decode step (selection outputs not requested)."""
+    B, H, d, C, k, r, D = cfg.batch, cfg.heads, cfg.head_dim, cfg.chunk, cfg.topk, cfg.qcal_rank, cfg.hidden
+    e = 2
+    total = 0
+    for b in range(B):
+        kv = cfg.kv_len[b]
+        n = -(-kv // C)
+        total += H * n * d * e                       # landmarks
+        total += H * min(k, n) * 2 * C * d * e       # selected chunks' keys and values (full chunks)
+    total += 2 * B * H * d * e + B * D * e + r * (D + H * d) * e
+    return total
+
+
+def cpu_baseline(dev, cfg, budget_s=12.0):
+    """The oracle, as it stands, on rows of one head of the same workload, for about budget_s."""
+    import numpy as np
+    from oracle import hils_oracle as O
+    h = 5
+    inp = {key: dev[key][:, h:h + 1].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
+    rng = np.random.default_rng(11)
+    rows = [int(x) for x in rng.integers(0, cfg.seq_len, size=4096)]
+    inp["h"] = np.zeros((1, cfg.seq_len, cfg.hidden), np.float32)
+    sel = sorted(set(rows))
+    inp["h"][:, sel] = dev["h"][:, sel].float().cpu().numpy()
+    inp["w_down"] = dev["w_down"].float().cpu().numpy()
+    inp["w_up"] = np.zeros((cfg.heads * cfg.head_dim, cfg.qcal_rank), np.float32)
+    d = cfg.head_dim
+    inp["w_up"][:d] = dev["w_up"][h * d:(h + 1) * d].float().cpu().numpy()   # head slot 0 = head h
+    flops, done = 0, 0
+    t0 = time.perf_counter()
+    for i in rows:
+        O.prefill_rows(inp, [(0, 0, i)], cfg.chunk, cfg.topk, cfg.dtype)
+        c = i // cfg.chunk
+        flops += 2 * d * (c + 1) + 4 * cfg.chunk * d * min(cfg.topk, c + 1) + 2 * cfg.qcal_rank * (cfg.hidden + d)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{done} random query rows of head {h} of prefill_128k, timed end to end "
+                       f"({dt:.1f} s, single-threaded NumPy oracle)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+
+    hils.load()
+    dev = torch.device("cuda:0")
+    pcfg = synth.CONFIGS["prefill_128k"]
+    dcfg = synth.CONFIGS["decode_512k"]
+    print(f"[bench] generating {pcfg.name}", file=sys.stderr, flush=True)
+    P = synth.make_prefill_inputs_torch(pcfg, dev)
+    D = None
+    if not args.no_decode:
+        print(f"[bench] generating {dcfg.name}", file=sys.stderr, flush=True)
+        D = synth.make_decode_inputs_torch(dcfg, dev)
+    o = torch.empty_like(P["q"])
+    pev = [hils.StageEvents(4) for _ in range(args.steps)]       # one set per timed step, read after
+    dev_ev = [hils.StageEvents(5) for _ in range(args.steps)]
+    od = torch.empty_like(D["q"]) if D is not None else None
+    pws = torch.empty(1 << 31, dtype=torch.uint8, device=dev)     # >= the prefill workspace
+    dws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"], topk=pcfg.topk,
+                     out=o, workspace=pws, events=pev[i] if i >= 0 else None)
+        if D is not None:
+            hils.decode(D["q"], D["k_cache"], D["v_cache"], D["lmk"], D["kv_len"], D["h"], D["w_down"],
+                        D["w_up"], topk=dcfg.topk, out=od, workspace=dws, events=dev_ev[i] if i >= 0 else None)
+
+    for _ in range(args.warmup):
+        step(-1)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    stage_p = [0.0, 0.0, 0.0]
+    stage_d = [0.0, 0.0, 0.0, 0.0]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    for i in range(args.steps):
+        for s in range(3):
+            stage_p[s] += pev[i].elapsed_ms(s, s + 1)
+        if D is not None:
+            for s in range(4):
+                stage_d[s] += dev_ev[i].elapsed_ms(s, s + 1)
+    K = args.steps
+    stage_p = [x / K for x in stage_p]
+    stage_d = [x / K for x in stage_d]
+    work = prefill_work(pcfg)
+    prefill_ms = sum(stage_p)
+    value = work["total"] / (prefill_ms * 1e-3) / 1e12
+
+    stages = {
+        "qcal_code": dict(ms=stage_p[0], bound="hbm", achieved=work["qcal_code_bytes"] / stage_p[0] / 1e6,
+                          unit="GB/s", peak=PEAK_HBM_GBS),
+        "select": dict(ms=stage_p[1], bound="mfma", achieved=work["select"] / stage_p[1] / 1e9,
+                       unit="TFLOP/s", peak=PEAK_BF16_TFLOPS),
+        "attention": dict(ms=stage_p[2], bound="mfma", achieved=work["attention"] / stage_p[2] / 1e9,
+                          unit="TFLOP/s", peak=PEAK_BF16_TFLOPS),
+    }
+    for s in stages.values():
+        s["frac"] = s["achieved"] / s["peak"]
+    dom_name = max(stages, key=lambda n: stages[n]["ms"])
+    dom = stages[dom_name]
+    per_launch = {"qcal_code": work["qcal_code_bytes"], "select": work["select"],
+                  "attention": work["attention"]}[dom_name]
+    roofline = dict(kernel=dom_name, bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"],
+                    unit=dom["unit"], frac=dom["frac"], traffic=None, work_per_launch=per_launch,
+                    avg_launch_ms=dom["ms"])
+
+    decode = None
+    if D is not None:
+        dms = sum(stage_d)
+        dbytes = decode_bytes(dcfg)
+        decode = dict(workload=dcfg.name, us_per_step=dms * 1e3, us_per_token=dms * 1e3 / dcfg.batch,
+                      algorithmic_bytes=dbytes, GBps=dbytes / (dms * 1e-3) / 1e9,
+                      frac_hbm=dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      stages_us=dict(qcal=stage_d[0] * 1e3, scores=stage_d[1] * 1e3, select=stage_d[2] * 1e3,
+                                     attend_reduce=stage_d[3] * 1e3))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(P, pcfg)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_128k + decode_512k",
+                   "prefill": dict(batch=pcfg.batch, heads=pcfg.heads, seq_len=pcfg.seq_len,
+                                   head_dim=pcfg.head_dim, chunk=pcfg.chunk, topk=pcfg.topk,
+                                   q_tile=pcfg.q_tile, qcal_rank=pcfg.qcal_rank, hidden=pcfg.hidden,
+                                   queries="random walk", hidden_states="random walk"),
+                   "decode": dict(batch=dcfg.batch, heads=dcfg.heads, kv_len=dcfg.max_kv_len,
+                                  head_dim=dcfg.head_dim, chunk=dcfg.chunk, topk=dcfg.topk,
+                                  qcal_rank=dcfg.qcal_rank, hidden=dcfg.hidden, needles=dcfg.needles),
+                   "parallelism": "single GPU"},
+        "prefill_ms": prefill_ms, "prefill_algorithmic_flop": work["total"],
+        "stages": stages, "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

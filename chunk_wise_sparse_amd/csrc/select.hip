@@ -33,12 +33,16 @@ namespace hils {
 
 constexpr int kBufCap = 128;
 
+// Per-query candidate buffers use odd row strides so the 16 queries of a wave hit distinct banks.
+constexpr int kBsStride = kBufCap + 1;   // floats
+constexpr int kBjStride = kBufCap + 2;   // uint16
+
 template <typename T, int D>
 struct SelectSmem {
   static constexpr int LD = D + 16 / (int)sizeof(T);  // padded row stride (elements)
   T lmk[64 * LD];
-  float bs[64 * kBufCap];
-  uint16_t bj[64 * kBufCap];
+  float bs[64 * kBsStride];
+  uint16_t bj[64 * kBjStride];
 };
 
 // A fragment of a landmark row for MFMA step st.  Lane group g's k-slot z of step st holds
@@ -288,10 +292,12 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const SelectArgs a) {
 #pragma unroll
       for (int st = 0; st < NF; ++st) acc = Mfma<T>::mma(lmk_frag<T>(row, g, st), qf[st], acc);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int j = lt * 64 + blk * 16 + 4 * g + rr;
-        s[blk * 4 + rr] = j < n_cand ? acc[rr] : -INFINITY;
-      }
+      for (int rr = 0; rr < 4; ++rr) s[blk * 4 + rr] = acc[rr];
+    }
+    if (lt == n_lt - 1) {   // only the last landmark tile holds chunks after the query's own
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (lt * 64 + 16 * (i >> 2) + 4 * g + (i & 3) >= n_cand) s[i] = -INFINITY;
     }
   };
 
@@ -327,8 +333,8 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const SelectArgs a) {
   }
 
   // ---------------- pass 2: collect candidates ----------------------------------------------
-  float* bs = &sm.bs[(wave * 16 + m) * kBufCap];
-  uint16_t* bj = &sm.bj[(wave * 16 + m) * kBufCap];
+  float* bs = &sm.bs[(wave * 16 + m) * kBsStride];
+  uint16_t* bj = &sm.bj[(wave * 16 + m) * kBjStride];
   int cnt = 0;
   uint32_t key[kSeg];
   int jx[kSeg];

@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/hils.h"
+#include "hils.h"
 #include "hils_launch.h"
 
 namespace {
@@ -69,6 +69,8 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "seq_len %d is not a multiple of the chunk size", p->seq_len);
   if (p->seq_len / p->chunk > 65535)
     return fail(HILS_ERR_UNSUPPORTED, "more than 65535 chunks per sequence");
+  if (p->dtype == HILS_DTYPE_FP32 && p->head_dim == 128 && p->seq_len / p->chunk > 16384)
+    return fail(HILS_ERR_UNSUPPORTED, "fp32 with head_dim 128 supports at most 16384 chunks");
   if (p->q_tile != 0 && p->q_tile != 64)
     return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (64)", p->q_tile);
   if (p->qcal_rank < 0 || p->qcal_rank > 64)

@@ -29,12 +29,8 @@ constexpr int kChunk = 64;  // chunk size C (the only one this library builds)
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ bf16 bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return __builtin_bit_cast(bf16, static_cast<uint16_t>(u >> 16));
-}
+// fp32 -> bf16, round to nearest, ties to even (gfx950: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 bf16_rne(float x) { return static_cast<bf16>(x); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
@@ -93,14 +89,32 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Partner values across 16- and 32-lane halves without the LDS crossbar (gfx950
+// v_permlane16_swap / v_permlane32_swap with both operands holding v): the two results hold, at
+// every lane l, the values of lanes l and l^16 (resp. l^32) in some order.
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 // Reductions over the four lanes {l, l^16, l^32, l^48} that share column l % 16.
 __device__ __forceinline__ float col_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  return fmaxf(v, shfl_xor_f(v, 32));
+  float a, b;
+  swap16(v, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float col_sum(float v) {
-  v += shfl_xor_f(v, 16);
-  return v + shfl_xor_f(v, 32);
+  float a, b;
+  swap16(v, a, b);
+  swap32(a + b, a, b);
+  return a + b;
 }
 __device__ __forceinline__ int col_sum_i(int v) {
   v += shfl_xor_i(v, 16);

@@ -55,9 +55,9 @@ typedef enum {
 typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
 
 /* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk == 64;
- * 1 <= topk <= 64; seq_len a positive multiple of chunk with seq_len / chunk <= 65535;
- * q_tile == 64 (or 0 for the default); 0 <= qcal_rank <= 64; hidden a positive multiple of 32
- * when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
+ * 1 <= topk <= 64; seq_len a positive multiple of chunk with seq_len / chunk <= 65535
+ * (<= 16384 for fp32 with head_dim 128); q_tile == 64 (or 0 for the default);
+ * 0 <= qcal_rank <= 64; hidden a positive multiple of 128 when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
  * stage_events: optional array of n_stage_events hipEvent_t handles (NULL if unused); when it
  * holds at least 4 events, event 0 is recorded before the first kernel and events 1..3 after the
  * Q-Cal, chunk-selection and chunk-attention kernels, on `stream`. */
@@ -74,8 +74,8 @@ typedef struct hils_prefill_params {
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a
  * key/value cache of capacity max_kv_len (the new token's key and value are already stored).
  * Supported: head_dim in {64, 128}; chunk == 64; 1 <= topk <= 64;
- * 1 <= max_kv_len <= 65535 * chunk; 0 <= qcal_rank <= 64; hidden a positive multiple of 32 when
- * qcal_rank > 0.  A partial last chunk is allowed.  With at least 5 stage events, event 0 is
+ * 1 <= max_kv_len <= 65535 * chunk; 0 <= qcal_rank <= 64; hidden a positive multiple of 128
+ * when qcal_rank > 0.  A partial last chunk is allowed.  With at least 5 stage events, event 0 is
  * recorded first and events 1..4 after the Q-Cal, landmark-scoring, selection and
  * chunk-attention stages. */
 typedef struct hils_decode_params {

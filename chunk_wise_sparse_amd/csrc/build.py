@@ -12,8 +12,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "attention.hip", "decode.hip"]
+SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attention.hip", "decode.hip"]
 LIB = os.path.join(PKG, "libhils.so")
+# Per-file flags.  Selection compares finite scores only, so NaN handling is dropped there
+# (max/min then need no NaN quieting of their operands).
+FILE_FLAGS = {"select_fast.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -45,7 +48,8 @@ def build(verbose: bool = False, extra=()) -> str:
     objs = [os.path.join(out_dir, s.replace(".hip", ".o")) for s in SOURCES]
     jobs = min(len(SOURCES), os.cpu_count() or 1, 8)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(SOURCES, objs)))
+        list(ex.map(lambda so: _compile(so[0], so[1], FILE_FLAGS.get(so[0], []) + list(extra)),
+                    zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

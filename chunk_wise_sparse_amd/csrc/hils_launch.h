@@ -54,6 +54,8 @@ hipError_t launch_decode_qcal(const T* q, const T* hid, const T* w_down, const T
 
 template <typename T, int D>
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+template <int D>
+hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st);   // bf16, k <= 32
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
 

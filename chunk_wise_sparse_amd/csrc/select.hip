@@ -427,6 +427,9 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const SelectArgs a) {
 
 template <typename T, int D>
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.k <= 32) return launch_select_fast<D>(a, st);
+  }
   const uint32_t total = (uint32_t)a.B * a.H * a.N;
   if (a.k <= 32)
     hipLaunchKernelGGL((select_kernel<T, D, 1>), dim3(total), dim3(256), 0, st, a);

@@ -1,0 +1,410 @@
+// Chunk selection for prefill, bf16 with k <= 32: one wave per 64-query tile.
+//
+// Method: [HiLS-Attention model page, "Model Description"] every query scores all causal chunks
+// through their landmark keys, keeps the k best and weights them with a softmax over those
+// scores; [HiLS Attention explainer (molayo1419.me), "Engineering details", Q-Cal item] scoring
+// uses q~ = q + W_up W_down h.  Ties keep the smaller chunk index; the output is in ascending
+// chunk order with -1 / 0 padding when fewer than k chunks exist.
+//
+// With C = 64 the 64 queries of tile c share the candidate set {0..c}, so scoring is a GEMM
+// [64 queries x d] x [d x (c+1)] done with v_mfma_f32_32x32x16_bf16: A = 32 landmark rows loaded
+// straight from global memory (each landmark is used by this wave only, so no LDS staging),
+// B = q~ of 32 queries (registers, two column blocks).  The output of block jb holds, at lane
+// (col, half), query column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap
+// per element pair moves both halves of a query's 32 rows into one lane, so lane l owns query
+// 32*(l/32) + l%32 and all of its scores.
+//
+// Exact top-k in two passes over the landmarks:
+//   pass 1: per slot (landmark row within a 32-row block) the two largest scores; the kq-th
+//           largest of these 64 values is reached by at least kq distinct chunks, so it bounds
+//           the kq-th largest score from below (tau).  Skipped when all candidates fit LDS.
+//   pass 2: every score >= tau is appended, in ascending chunk order, to the query's LDS list
+//           ([position][query] so the 64 lanes write distinct banks).  A list that could
+//           overflow is cut to its exact top-kq first and tau is raised above the cut value
+//           (later chunks lose ties); with the tight tau of pass 1 this is rare.
+//   final:  the kq-th largest theta of the list; entries > theta and the first (kq - #>theta)
+//           entries == theta are kept in list order, then the inter-chunk softmax.
+// Scores are finite by contract: this file is compiled with -fno-honor-nans, so max/min skip
+// NaN quieting.
+#include <float.h>
+
+#include <type_traits>
+
+#include "hils_device.h"
+#include "hils_launch.h"
+
+namespace hils {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kCap = 48;   // list capacity per query (>= kq + 16 for kq <= 32)
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void cx_desc(float& a, float& b) {
+  const float hi = fmaxf(a, b), lo = fminf(a, b);
+  a = hi;
+  b = lo;
+}
+
+// Bitonic sort of N values, descending (static network, registers only).
+template <int N>
+__device__ __forceinline__ void sort_desc(float (&x)[N]) {
+#pragma unroll
+  for (int kk = 2; kk <= N; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ jj;
+        if (l > i) {
+          if ((i & kk) == 0) cx_desc(x[i], x[l]);
+          else cx_desc(x[l], x[i]);
+        }
+      }
+    }
+  }
+}
+
+// Sort a bitonic sequence of N values into descending order.
+template <int N>
+__device__ __forceinline__ void bitonic_merge_desc(float (&x)[N]) {
+#pragma unroll
+  for (int jj = N >> 1; jj > 0; jj >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & jj) == 0) cx_desc(x[i], x[i + jj]);
+  }
+}
+
+// x[kk - 1] for a runtime kk in [1, N].
+template <int N>
+__device__ __forceinline__ float pick(const float (&x)[N], int kk) {
+  float r = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = (i == kk - 1) ? x[i] : r;
+  return r;
+}
+
+template <int D>
+struct FastSmem {
+  static constexpr int QLD = D + 8;            // q~ staging row stride (elements)
+  union {
+    bf16 qt[64 * QLD];                         // q~ [query][d], before the passes
+    struct {
+      float s[kCap * 64];                      // [position][query] candidate scores
+      uint16_t j[kCap * 64];                   // [position][query] candidate chunks
+    } list;
+  };
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
+  constexpr int NS = D / 16;                   // MFMA k-steps over d
+  typedef FastSmem<D> Smem;
+  __shared__ Smem sm;
+
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  const uint32_t total = (uint32_t)a.B * a.H * a.N;
+  const uint32_t tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / a.N;
+  const int c = a.N - 1 - (int)(tile % a.N);   // longest tiles first
+  const int b = bh / a.H, hd = bh % a.H;
+  const int n_cand = c + 1;
+  const int nb = (n_cand + 31) >> 5;           // 32-landmark blocks
+  const int kq = min(a.k, n_cand);
+  const int q0 = c * 64;
+  const bf16* Q = static_cast<const bf16*>(a.q) + (size_t)bh * a.L * D;
+  const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)bh * a.N * D;
+  float* ls = &sm.list.s[lane];                // this lane's list, stride 64
+  uint16_t* lj = &sm.list.j[lane];
+
+  // ---------------- q~ as the B operand: query 32 cb + col, d = 16 s + 8 half + z -----------
+  bf16x8 qf[2][NS];
+  if (a.r > 0) {
+    // delta_q^T[d][query] = sum_r W_up[hd*D + d][r] t[query][r]; t (fp32) is split into three
+    // bf16 parts so that every product is exact and the sum is accumulated in fp32.
+    constexpr int NRS = 4;                     // r <= 64, 16 per step
+    const int nrs = (a.r + 15) >> 4;
+    bf16x8 tb[3][2][NRS];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float* tq = a.tcode + ((size_t)b * a.L + q0 + 32 * cb + col) * a.r;
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) {
+          const int ai = 16 * rs + 8 * half + z;
+          const float t = (rs < nrs && ai < a.r) ? tq[ai] : 0.f;
+          const bf16 t0 = bf16_rne(t);
+          const float r1 = t - to_f32(t0);
+          const bf16 t1 = bf16_rne(r1);
+          tb[0][cb][rs][z] = t0;
+          tb[1][cb][rs][z] = t1;
+          tb[2][cb][rs][z] = bf16_rne(r1 - to_f32(t1));
+        }
+      }
+    }
+    const bf16* WU = static_cast<const bf16*>(a.w_up) + (size_t)hd * D * a.r;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      f32x16 acc[2] = {};
+      const bf16* wrow = WU + (size_t)(32 * db + col) * a.r;
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) {
+        if (rs < nrs) {
+          bf16x8 wa;
+#pragma unroll
+          for (int z = 0; z < 8; ++z) {
+            const int ai = 16 * rs + 8 * half + z;
+            wa[z] = ai < a.r ? wrow[ai] : bf16_rne(0.f);
+          }
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) acc[cb] = mfma32(wa, tb[p][cb][rs], acc[cb]);
+        }
+      }
+      // acc[cb][e]: d = 32 db + 8 (e/4) + 4 half + e%4, query 32 cb + col.
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int qr = 32 * cb + col;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * db + 8 * a4 + 4 * half;
+          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(Q + (size_t)(q0 + qr) * D + d0);
+          bf16x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = bf16_rne(to_f32(qv[i]) + acc[cb][4 * a4 + i]);
+          *reinterpret_cast<bf16x4*>(&sm.qt[qr * Smem::QLD + d0]) = o;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qf[cb][s] = *reinterpret_cast<const bf16x8*>(&sm.qt[(32 * cb + col) * Smem::QLD + 16 * s + 8 * half]);
+    __syncthreads();                           // the candidate lists reuse this memory
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qf[cb][s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)(q0 + 32 * cb + col) * D + 16 * s + 8 * half);
+  }
+
+  // ---------------- scoring of one 32-landmark block ---------------------------------------
+  // A operand rows past the last candidate repeat the last landmark; their scores are masked.
+  auto load_a = [&](int jb, bf16x8 (&af)[NS]) {
+    const int row = min(32 * jb + col, n_cand - 1);
+    const bf16* p = LM + (size_t)row * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) af[s] = *reinterpret_cast<const bf16x8*>(p + 16 * s);
+  };
+  auto mma_block = [&](const bf16x8 (&af)[NS], f32x16& acc0, f32x16& acc1) {
+    acc0 = f32x16{};
+    acc1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      acc0 = mfma32(af[s], qf[0][s], acc0);
+      acc1 = mfma32(af[s], qf[1][s], acc1);
+    }
+  };
+  // The block's scores for this lane's query, handed to f(row, score) in ascending row order
+  // (rows past the last candidate read -inf).  acc0/acc1 hold column blocks 0/1 with rows
+  // 8(e/4) + 4 half + e%4; after the swap lanes 0-31 hold both row halves of column block 0
+  // and lanes 32-63 both row halves of column block 1.
+  auto for_scores = [&](auto last_block, int jb, const f32x16& acc0, const f32x16& acc1, auto&& f) {
+    constexpr bool last = decltype(last_block)::value;
+    const int lim = n_cand - 32 * jb;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      float x[4], y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = 4 * grp + t;
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[e]), __float_as_uint(acc1[e]),
+                                                        false, false);
+        x[t] = __uint_as_float(r[0]);          // row 8 grp + t
+        y[t] = __uint_as_float(r[1]);          // row 8 grp + 4 + t
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f(8 * grp + t, (last && 8 * grp + t >= lim) ? -INFINITY : x[t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f(8 * grp + 4 + t, (last && 8 * grp + 4 + t >= lim) ? -INFINITY : y[t]);
+    }
+  };
+
+  // ---------------- pass 1: lower bound tau of the kq-th largest score ---------------------
+  float tau = -FLT_MAX;                        // every finite score passes; masked ones do not
+  if (n_cand > kCap) {
+    float m1[32], m2[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m1[i] = m2[i] = -INFINITY;
+    auto top2 = [&](int i, float v) {
+      m2[i] = __builtin_amdgcn_fmed3f(m1[i], m2[i], v);
+      m1[i] = fmaxf(m1[i], v);
+    };
+    bf16x8 af[NS];
+    load_a(0, af);
+    f32x16 acc0, acc1;
+    for (int jb = 0; jb < nb - 1; ++jb) {
+      mma_block(af, acc0, acc1);
+      load_a(jb + 1, af);                      // in flight during this block's VALU work
+      for_scores(std::false_type{}, jb, acc0, acc1, top2);
+    }
+    mma_block(af, acc0, acc1);
+    for_scores(std::true_type{}, nb - 1, acc0, acc1, top2);
+    // Top 32 of the 64 slot values: merge the sorted halves, then pick the kq-th.
+    sort_desc<32>(m1);
+    sort_desc<32>(m2);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m1[i] = fmaxf(m1[i], m2[31 - i]);
+    bitonic_merge_desc<32>(m1);
+    tau = pick<32>(m1, kq);
+  }
+
+  // ---------------- pass 2: collect the candidates ------------------------------------------
+  int cnt = 0;
+  {
+    // Make room for the block's passing scores: a list that would overflow is cut to its exact
+    // top kq first (rare: lists end near kq + a few).  theta = kq-th largest key, bit by bit
+    // from the top, counting list entries in LDS; entries > theta and the first
+    // kq - #(> theta) entries == theta stay, in list order.
+    auto make_room = [&](const float (&sc)[32], int h0) {
+      if (__any(cnt + 16 > kCap)) {
+        int np = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) np += sc[h0 + i] >= tau ? 1 : 0;
+        if (cnt + np > kCap) {
+          uint32_t th = 0u;
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = th | (1u << bit);
+            int n = 0;
+            for (int i = 0; i < cnt; ++i) n += f32_key(ls[64 * i]) >= cand ? 1 : 0;
+            if (n >= kq) th = cand;
+          }
+          const float theta = key_f32(th);
+          int ngt = 0;
+          for (int i = 0; i < cnt; ++i) ngt += ls[64 * i] > theta ? 1 : 0;
+          const int m_eq = kq - ngt;
+          int w = 0, eq = 0;
+          for (int i = 0; i < cnt; ++i) {
+            const float sv = ls[64 * i];
+            const uint16_t jv = lj[64 * i];
+            bool keep = sv > theta;
+            if (sv == theta) {
+              keep = eq < m_eq;
+              ++eq;
+            }
+            if (keep) {
+              ls[64 * w] = sv;
+              lj[64 * w] = jv;
+              ++w;
+            }
+          }
+          cnt = w;
+          tau = key_f32(th + 1u);              // later chunks must beat theta strictly
+        }
+      }
+    };
+    auto collect = [&](int jb, const float (&sc)[32]) {
+#pragma unroll
+      for (int h0 = 0; h0 < 32; h0 += 16) {    // at most 16 appends after each check
+        make_room(sc, h0);
+#pragma unroll
+        for (int i = h0; i < h0 + 16; ++i) {
+          if (sc[i] >= tau) {
+            ls[64 * cnt] = sc[i];
+            lj[64 * cnt] = (uint16_t)(32 * jb + i);
+            ++cnt;
+          }
+        }
+      }
+    };
+    bf16x8 af[NS];
+    load_a(0, af);
+    f32x16 acc0, acc1;
+    float sc[32];
+    auto keep = [&](int i, float v) { sc[i] = v; };
+    for (int jb = 0; jb < nb - 1; ++jb) {
+      mma_block(af, acc0, acc1);
+      load_a(jb + 1, af);
+      for_scores(std::false_type{}, jb, acc0, acc1, keep);
+      collect(jb, sc);
+    }
+    mma_block(af, acc0, acc1);
+    for_scores(std::true_type{}, nb - 1, acc0, acc1, keep);
+    collect(nb - 1, sc);
+  }
+
+  // ---------------- final top-kq and inter-chunk softmax ------------------------------------
+  float theta, top;
+  {
+    float v[64];                               // kCap entries padded to the sort width
+    static_assert(kCap <= 64, "list longer than the sort");
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = (i < kCap && i < cnt) ? ls[64 * i] : -INFINITY;
+    sort_desc<64>(v);
+    top = v[0];
+    theta = pick<64>(v, kq);
+  }
+  int ngt = 0;
+  for (int i = 0; i < cnt; ++i) ngt += ls[64 * i] > theta ? 1 : 0;
+  const int m_eq = kq - ngt;
+  const float zs = a.scale * 1.4426950408889634f;   // scale * log2(e)
+  float esum = 0.f;
+  {
+    int eq = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const float sv = ls[64 * i];
+      bool keep = sv > theta;
+      if (sv == theta) {
+        keep = eq < m_eq;
+        ++eq;
+      }
+      if (keep) esum += exp2f((sv - top) * zs);
+    }
+  }
+  const float inv = 1.f / esum;
+  const int qpos = q0 + 32 * half + col;
+  const size_t orow = ((size_t)bh * a.L + qpos) * a.k;
+  int pos = 0, eq = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const float sv = ls[64 * i];
+    bool keep = sv > theta;
+    if (sv == theta) {
+      keep = eq < m_eq;
+      ++eq;
+    }
+    if (keep) {
+      a.idx[orow + pos] = (int32_t)lj[64 * i];
+      a.w[orow + pos] = exp2f((sv - top) * zs) * inv;
+      ++pos;
+    }
+  }
+  for (int p = kq; p < a.k; ++p) {
+    a.idx[orow + p] = -1;
+    a.w[orow + p] = 0.f;
+  }
+}
+
+template <int D>
+hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st) {
+  const uint32_t total = (uint32_t)a.B * a.H * a.N;
+  hipLaunchKernelGGL((select_fast_kernel<D>), dim3(total), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_select_fast<64>(const SelectArgs&, hipStream_t);
+template hipError_t launch_select_fast<128>(const SelectArgs&, hipStream_t);
+
+}  // namespace hils

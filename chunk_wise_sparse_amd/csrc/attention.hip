@@ -40,13 +40,13 @@ struct AttnLayout {
 };
 
 // Selection of the group's rows, staged once: chunk index (u16, 0xFFFF = padding) and weight.
-template <typename T, int D, int QG, int KMAX>
+template <typename T, int D, int QG, int KMAX, int STAGES>
 struct AttnSmem {
   // One bit per chunk of the sequence: 2048 words cover 65536 chunks; fp32 with d = 128 keeps
   // 512 words (1M tokens, enforced by the API) so that two 64 KiB stages still fit.
   static constexpr int BITMAP_WORDS = (sizeof(T) == 4 && D == 128) ? 512 : 2048;
-  alignas(16) char k[2][AttnLayout<T, D>::KBYTES];
-  alignas(16) char v[2][AttnLayout<T, D>::VBYTES];
+  alignas(16) char k[STAGES][AttnLayout<T, D>::KBYTES];
+  alignas(16) char v[STAGES][AttnLayout<T, D>::VBYTES];
   uint32_t bitmap[BITMAP_WORDS];
   int nunion;
   uint16_t sidx[QG * (KMAX + 1)];
@@ -76,10 +76,10 @@ __device__ __forceinline__ float v_frag_f32(const char* vbuf, int lane16, int g,
   return *reinterpret_cast<const float*>(vbuf + db * VDB + row * 64 + lane16 * 4);
 }
 
-template <typename T, int D, int NW, int KMAX>
-__global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnArgs a) {
+template <typename T, int D, int NW, int KMAX, int STAGES>
+__global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(const AttnArgs a) {
   constexpr int QG = 32 * NW;                // queries per workgroup
-  typedef AttnSmem<T, D, QG, KMAX> Smem;
+  typedef AttnSmem<T, D, QG, KMAX, STAGES> Smem;
   typedef AttnLayout<T, D> Lay;
   constexpr int KPL = Mfma<T>::KPL;
   constexpr int NF = D / 4 / KPL;            // QK^T steps over d
@@ -268,40 +268,65 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
     }
   };
 
-  // Pipeline over the union c_0 < c_1 < ... < c_{U-1}: iteration t computes c_t from stage t%2
-  // while c_{t+1} sits in register set (t+1)%2 and c_{t+2} is loaded into set t%2; after the
-  // compute the registers of c_{t+1} go to stage (t+1)%2 and one barrier publishes them.  Loads
-  // and stores are unconditional (past the end they repeat the last chunk) so that the
-  // compiler's wait counts stay exact across the loop.
   const int U = sm.nunion;
-  u32x4 kr[2][NV], vr[2][NV];
   int jl = -1;                               // last chunk returned by the iterator
   auto advance = [&]() -> int {
     const int j = next_chunk();
     if (j >= 0) jl = j;
     return j >= 0 ? j : jl;
   };
-  if (U > 0) {
-    const int c0 = advance();
-    load_kv(c0, kr[0], vr[0]);
-    store_kv(0, kr[0], vr[0]);
-    int ca = c0, cb = advance();             // chunks t and t+1
-    load_kv(cb, kr[1], vr[1]);
-    __syncthreads();
-    // Two chunks per trip (static register-set indexing); an odd U ends with an idle half.
-    for (int t = 0; t < U; t += 2) {
-      const int cc = advance();              // chunk t+2
-      load_kv(cc, kr[0], vr[0]);
-      compute(ca, 0, true);
-      store_kv(1, kr[1], vr[1]);
-      __syncthreads();
-      const int cd = advance();              // chunk t+3
-      load_kv(cd, kr[1], vr[1]);
-      compute(cb, 1, t + 1 < U);
+  // Loads and stores below are unconditional (past the end of the union they repeat its last
+  // chunk) so that the compiler's wait counts stay exact across the loop.
+  if constexpr (STAGES == 2) {
+    // Iteration t computes c_t from stage t%2 while c_{t+1} sits in register set (t+1)%2 and
+    // c_{t+2} is loaded into set t%2; after the compute the registers of c_{t+1} go to stage
+    // (t+1)%2 and one barrier publishes them.
+    u32x4 kr[2][NV], vr[2][NV];
+    if (U > 0) {
+      const int c0 = advance();
+      load_kv(c0, kr[0], vr[0]);
       store_kv(0, kr[0], vr[0]);
+      int ca = c0, cb = advance();           // chunks t and t+1
+      load_kv(cb, kr[1], vr[1]);
       __syncthreads();
-      ca = cc;
-      cb = cd;
+      // Two chunks per trip (static register-set indexing); an odd U ends with an idle half.
+      for (int t = 0; t < U; t += 2) {
+        const int cc = advance();            // chunk t+2
+        load_kv(cc, kr[0], vr[0]);
+        compute(ca, 0, true);
+        store_kv(1, kr[1], vr[1]);
+        __syncthreads();
+        const int cd = advance();            // chunk t+3
+        load_kv(cd, kr[1], vr[1]);
+        compute(cb, 1, t + 1 < U);
+        store_kv(0, kr[0], vr[0]);
+        __syncthreads();
+        ca = cc;
+        cb = cd;
+      }
+    }
+  } else {
+    // One LDS stage, so that two workgroups share a CU and their waves overlap on each SIMD:
+    // compute c_t; barrier; the registers holding c_{t+1} go to LDS and c_{t+2} is loaded into
+    // them; barrier.
+    u32x4 kr[NV], vr[NV];
+    if (U > 0) {
+      int cj = advance();
+      load_kv(cj, kr, vr);
+      store_kv(0, kr, vr);
+      int cn = advance();
+      load_kv(cn, kr, vr);
+      __syncthreads();
+      for (int t = 0; t < U; ++t) {
+        compute(cj, 0, true);
+        __syncthreads();
+        store_kv(0, kr, vr);
+        const int cn2 = advance();
+        load_kv(cn2, kr, vr);
+        __syncthreads();
+        cj = cn;
+        cn = cn2;
+      }
     }
   }
 
@@ -320,20 +345,23 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   }
 }
 
-// Queries per workgroup: 256 (8 waves) when k <= 32, else 128 (4 waves), so that the staged
-// selection fits LDS next to two chunk stages; 64 when the sequence does not split that way.
+// Queries per workgroup: bf16 with k <= 32 takes 128 (4 waves) with one LDS stage, two
+// workgroups per CU; otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with two stages, so that
+// the staged selection fits LDS; 64 when the sequence does not split that way.
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   const uint32_t bhs = (uint32_t)a.B * a.H;
   if constexpr (sizeof(T) == 4 && D == 128) {   // 32 KiB per tensor per chunk: 64-query groups
-    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
   } else {
-    if (a.topk <= 32 && a.L % 256 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32>), dim3(bhs * (a.L / 256)), dim3(512), 0, st, a);
+    if (sizeof(T) == 2 && a.topk <= 32 && a.L % 128 == 0) {
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 32, 1>), dim3(bhs * (a.L / 128)), dim3(256), 0, st, a);
+    } else if (a.topk <= 32 && a.L % 256 == 0) {
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), 0, st, a);
     } else if (a.L % 128 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 64>), dim3(bhs * (a.L / 128)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 64, 2>), dim3(bhs * (a.L / 128)), dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
     }
   }
   return hipGetLastError();

@@ -152,7 +152,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
 // Decode
 // ---------------------------------------------------------------------------------------------
 struct DecodeLayout {
-  size_t q_tilde, scores, idx, w, partial, total;
+  size_t tcode, scores, idx, w, partial, total;
 };
 
 int check_decode_params(const hils_decode_params* p) {
@@ -185,8 +185,8 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   const size_t B = p->batch, H = p->heads, d = p->head_dim, k = p->topk;
   const size_t N = (p->max_kv_len + 63) / 64;
   size_t off = 0;
-  L.q_tilde = off;
-  off += align_up(B * H * d * elem_bytes(p->dtype));
+  L.tcode = off;
+  off += align_up(B * (size_t)p->qcal_rank * sizeof(float));
   L.scores = off;
   off += align_up(B * H * N * sizeof(float));
   L.idx = off;
@@ -207,15 +207,15 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   hipError_t e;
   hipEvent_t* ev = p->n_stage_events >= 5 ? (hipEvent_t*)p->stage_events : nullptr;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  T* q_tilde = reinterpret_cast<T*>(ws + L.q_tilde);
-  e = hils::launch_decode_qcal<T>(static_cast<const T*>(q), static_cast<const T*>(h),
-                                  static_cast<const T*>(w_down), static_cast<const T*>(w_up),
-                                  q_tilde, p->batch, p->heads, D, p->hidden, p->qcal_rank, st);
+  float* tcode = reinterpret_cast<float*>(ws + L.tcode);
+  e = hils::launch_decode_tcode<T>(static_cast<const T*>(h), static_cast<const T*>(w_down), tcode,
+                                   p->batch, p->hidden, p->qcal_rank, st);
   if (e != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   hils::DecodeArgs a;
   a.q = q;
-  a.q_tilde = q_tilde;
+  a.w_up = w_up;
+  a.tcode = tcode;
   a.k_cache = kc;
   a.v_cache = vc;
   a.lmk = lmk;
@@ -230,13 +230,13 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.Lmax = p->max_kv_len;
   a.Nmax = (p->max_kv_len + 63) / 64;
   a.k = p->topk;
+  a.r = p->qcal_rank;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
   if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   if ((e = hils::launch_decode_select(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   if ((e = hils::launch_decode_attend<T, D>(a, st)) != hipSuccess) return e;
-  if ((e = hils::launch_decode_reduce<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
   return hipSuccess;
 }

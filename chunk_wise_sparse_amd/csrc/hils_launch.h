@@ -31,7 +31,8 @@ struct AttnArgs {
 
 struct DecodeArgs {
   const void* q;        // [B,H,d] raw query
-  const void* q_tilde;  // [B,H,d] calibrated query (workspace)
+  const void* w_up;     // [H*d, r] Q-Cal up-projection (unused when r == 0)
+  const float* tcode;   // [B, r] Q-Cal code W_down h (workspace)
   const void* k_cache;  // [B,H,Lmax,d]
   const void* v_cache;
   const void* lmk;      // [B,H,Nmax,d]
@@ -39,18 +40,15 @@ struct DecodeArgs {
   float* scores;        // [B,H,Nmax] workspace
   int32_t* idx;         // [B,H,k]
   float* w;             // [B,H,k]
-  float* partial;       // [B,H,k,d] workspace
+  float* partial;       // [B,H,k,d] workspace (split attend only)
   void* o;              // [B,H,d]
-  int B, H, Lmax, Nmax, k;
+  int B, H, Lmax, Nmax, k, r;
   float scale;
 };
 
 template <typename T>
 hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,
                                     int r, hipStream_t st);
-template <typename T>
-hipError_t launch_decode_qcal(const T* q, const T* hid, const T* w_down, const T* w_up,
-                              T* q_tilde, int B, int H, int d, int D, int r, hipStream_t st);
 
 template <typename T, int D>
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
@@ -59,12 +57,13 @@ hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st);   // bf16, k
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
 
+template <typename T>
+hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int B, int D, int r,
+                               hipStream_t st);
 template <typename T, int D>
 hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st);
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st);
-template <typename T, int D>
-hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace hils

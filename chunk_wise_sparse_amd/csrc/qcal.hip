@@ -72,37 +72,6 @@ __global__ __launch_bounds__(256) void prefill_qcal_code_kernel(const T* __restr
   }
 }
 
-// Decode: q~[b, h, :] = round_dtype(q + W_up[h rows] (W_down h_b)).  One workgroup per sequence.
-template <typename T>
-__global__ __launch_bounds__(256) void decode_qcal_kernel(const T* __restrict__ q,
-                                                          const T* __restrict__ hid,
-                                                          const T* __restrict__ w_down,
-                                                          const T* __restrict__ w_up,
-                                                          T* __restrict__ q_tilde, int H, int d,
-                                                          int D, int r) {
-  __shared__ float part[4][64];
-  __shared__ float tcode[64];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const T* hb = hid + (size_t)b * D;
-  // t[a] = sum over D, each thread a strided slice, fixed order -> deterministic.
-  for (int a = 0; a < r; ++a) {
-    float s = 0.f;
-    for (int x = tid; x < D; x += 256) s += to_f32(w_down[(size_t)a * D + x]) * to_f32(hb[x]);
-    s = wave_sum(s);
-    if (lane == 0) part[wave][a] = s;
-  }
-  __syncthreads();
-  if (tid < r) tcode[tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-  __syncthreads();
-  const int HD = H * d;
-  for (int e = tid; e < HD; e += 256) {
-    float dq = 0.f;
-    for (int a = 0; a < r; ++a) dq += to_f32(w_up[(size_t)e * r + a]) * tcode[a];
-    const float s = to_f32(q[(size_t)b * HD + e]) + dq;
-    q_tilde[(size_t)b * HD + e] = from_f32<T>(s);
-  }
-}
-
 template <typename T>
 hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,
                                     int r, hipStream_t st) {
@@ -111,17 +80,8 @@ hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, i
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_decode_qcal(const T* q, const T* hid, const T* w_down, const T* w_up,
-                              T* q_tilde, int B, int H, int d, int D, int r, hipStream_t st) {
-  hipLaunchKernelGGL(decode_qcal_kernel<T>, dim3(B), dim3(256), 0, st, q, hid, w_down, w_up,
-                     q_tilde, H, d, D, r);
-  return hipGetLastError();
-}
-
 template hipError_t launch_prefill_qcal_code<bf16>(const bf16*, const bf16*, float*, int, int, int, hipStream_t);
 template hipError_t launch_prefill_qcal_code<float>(const float*, const float*, float*, int, int, int, hipStream_t);
-template hipError_t launch_decode_qcal<bf16>(const bf16*, const bf16*, const bf16*, const bf16*, bf16*, int, int, int, int, int, hipStream_t);
-template hipError_t launch_decode_qcal<float>(const float*, const float*, const float*, const float*, float*, int, int, int, int, int, hipStream_t);
 
 }  // namespace hils
+

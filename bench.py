@@ -54,6 +54,89 @@ def decode_bytes(cfg):
     return total
 
 
+def source_digest(files):
+    """sha256 over the given library sources (relative to the package's csrc/), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "chunk_wise_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+# The dominant kernel's code: a change to any of these files makes stored counters stale.
+KERNEL_SOURCES = {"attention": ["attention.hip", "hils_device.h", "hils_launch.h"],
+                  "select": ["select_fast.hip", "select.hip", "hils_device.h", "hils_launch.h"],
+                  "qcal_code": ["qcal.hip", "hils_device.h", "hils_launch.h"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_128k.txt")
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or was taken from different kernel sources.  The file holds key = value
+    lines; FETCH_SIZE / WRITE_SIZE are KiB per dispatch, scaled by the copy-kernel factors."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get(f"{kernel}.source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        fetch = float(kv[f"{kernel}.FETCH_SIZE_KiB"]) * 1024 * float(kv["copy.fetch_factor"])
+        write = float(kv[f"{kernel}.WRITE_SIZE_KiB"]) * 1024 * float(kv["copy.write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def calib_copy(nbytes=1 << 30, reps=3):
+    """Plain device-to-device copies of a known size, for counter calibration under rocprofv3."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def union_stats(P, cfg, dev):
+    """Chunk-union statistics of one prefill's selection (idx written): mean fraction of a row's
+    chunks also chosen by the previous row, distinct chunks per 32-row wave block and per
+    128-row workgroup, and the attention FLOP the kernel executes (a wave computes every chunk
+    any of its 32 rows selected, for all 32 rows)."""
+    import torch
+    from chunk_wise_sparse_amd import hils
+    _, idx, _ = hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
+                             topk=cfg.topk, return_selection=True)
+    torch.cuda.synchronize()
+    B, H, L, k = idx.shape
+    overlap, u32, u128 = 0.0, 0.0, 0.0
+    for b in range(B):
+        for h in range(H):
+            x = idx[b, h].long()
+            a, pr = x[1:], x[:-1]
+            inter = ((a.unsqueeze(-1) == pr.unsqueeze(-2)) & (a.unsqueeze(-1) >= 0)).any(-1).sum(-1).float()
+            overlap += (inter / (a >= 0).sum(-1).float()).mean().item()
+            for m, acc in ((32, "u32"), (128, "u128")):
+                s, _ = torch.sort(x.reshape(L // m, m * k), dim=-1)
+                distinct = ((s[:, 1:] != s[:, :-1]) & (s[:, 1:] >= 0)).sum(-1) + (s[:, 0] >= 0).long()
+                if acc == "u32":
+                    u32 += distinct.float().sum().item()
+                else:
+                    u128 += distinct.float().sum().item()
+    n_bh = B * H
+    del idx
+    executed = u32 * 32 * 4 * cfg.chunk * cfg.head_dim      # FLOP: chunk-steps x rows x 4 C d
+    return dict(adjacent_overlap=overlap / n_bh,
+                union_per_32_rows=u32 / n_bh / (L // 32), union_per_128_rows=u128 / n_bh / (L // 128),
+                executed_attention_flop=executed)
+
+
 def cpu_baseline(dev, cfg, budget_s=12.0):
     """The oracle, as it stands, on rows of one head of the same workload, for about budget_s."""
     import numpy as np
@@ -91,11 +174,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-union-stats", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run plain 1 GiB device copies (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.calib_copy:
+        calib_copy()
+        return
 
     import torch
     from chunk_wise_sparse_amd import hils, synth
@@ -164,8 +254,8 @@ def main():
     per_launch = {"qcal_code": work["qcal_code_bytes"], "select": work["select"],
                   "attention": work["attention"]}[dom_name]
     roofline = dict(kernel=dom_name, bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"],
-                    unit=dom["unit"], frac=dom["frac"], traffic=None, work_per_launch=per_launch,
-                    avg_launch_ms=dom["ms"])
+                    unit=dom["unit"], frac=dom["frac"], traffic=stored_traffic(dom_name),
+                    work_per_launch=per_launch, avg_launch_ms=dom["ms"])
 
     decode = None
     if D is not None:
@@ -176,6 +266,12 @@ def main():
                       frac_hbm=dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       stages_us=dict(qcal=stage_d[0] * 1e3, scores=stage_d[1] * 1e3, select=stage_d[2] * 1e3,
                                      attend_reduce=stage_d[3] * 1e3))
+
+    ustats = None
+    if not args.no_union_stats:
+        print("[bench] union statistics of one selection", file=sys.stderr, flush=True)
+        ustats = union_stats(P, pcfg, dev)
+        ustats["executed_over_algorithmic"] = ustats["executed_attention_flop"] / work["attention"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -196,7 +292,7 @@ def main():
                                   qcal_rank=dcfg.qcal_rank, hidden=dcfg.hidden, needles=dcfg.needles),
                    "parallelism": "single GPU"},
         "prefill_ms": prefill_ms, "prefill_algorithmic_flop": work["total"],
-        "stages": stages, "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+        "stages": stages, "roofline": roofline, "decode": decode, "union": ustats, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

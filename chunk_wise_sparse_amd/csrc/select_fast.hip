@@ -81,12 +81,13 @@ __device__ __forceinline__ void bitonic_merge_desc(float (&x)[N]) {
   }
 }
 
-// x[kk - 1] for a runtime kk in [1, N].
+// x[kk - 1] of a descending array for a runtime kk in [1, N]: the minimum of its first kk
+// entries (a select-by-index chain would be lowered to a scratch-memory array).
 template <int N>
 __device__ __forceinline__ float pick(const float (&x)[N], int kk) {
   float r = x[0];
 #pragma unroll
-  for (int i = 1; i < N; ++i) r = (i == kk - 1) ? x[i] : r;
+  for (int i = 1; i < N; ++i) r = fminf(r, i < kk ? x[i] : INFINITY);
   return r;
 }
 

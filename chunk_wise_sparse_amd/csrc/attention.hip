@@ -189,6 +189,9 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
   const float zs = a.scale * 1.4426950408889634f;
 
   // One chunk: selection, S^T, per-chunk softmax, PV.  Both row blocks run when either does.
+  // The chunk that holds a block's own rows needs the causal mask; every other chunk takes a
+  // branch-free path, so that one block's softmax can be scheduled between the other block's
+  // MFMAs.
   auto compute = [&](int j, int stg, bool live) {
     bool sel[2];
     float wq[2];
@@ -204,67 +207,102 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
     if (!__any(sel[0] || sel[1])) return;
     const char* kbuf = sm.k[stg];
     const char* vbuf = sm.v[stg];
-    float s[2][16];
+    // S^T of block b: lane (m, g) holds query row m and keys 16 kb + 4 g + rr.
+    auto qk = [&](int b, float (&sv)[16]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4 acc0 = zero4(), acc1 = zero4();
-      const T* krow = reinterpret_cast<const T*>(kbuf + (kb * 16 + m) * Lay::KLD) + g * (D / 4);
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 acc = zero4();
+        const T* krow = reinterpret_cast<const T*>(kbuf + (kb * 16 + m) * Lay::KLD) + g * (D / 4);
 #pragma unroll
-      for (int st = 0; st < NF; ++st) {
-        const typename Mfma<T>::frag kf = load_frag<T>(krow + st * KPL);
-        acc0 = Mfma<T>::mma(kf, qf[0][st], acc0);
-        acc1 = Mfma<T>::mma(kf, qf[1][st], acc1);
+        for (int st = 0; st < NF; ++st) acc = Mfma<T>::mma(load_frag<T>(krow + st * KPL), qf[b][st], acc);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
       }
+    };
+    // Keys after the query in its own chunk are masked.
+    auto mask = [&](int b, float (&sv)[16]) {
+      const int ql = qpos[b] & 63;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        s[0][kb * 4 + rr] = acc0[rr];
-        s[1][kb * 4 + rr] = acc1[rr];
-      }
-    }
-    typename Mfma<T>::frag pf[2][NP];
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (j == crow[b]) {     // own chunk: keys after the query are masked
-        const int ql = qpos[b] & 63;
+        for (int rr = 0; rr < 4; ++rr)
+          if (kb * 16 + 4 * g + rr > ql) sv[kb * 4 + rr] = -INFINITY;
+    };
+    // Per-chunk softmax of block b scaled by w_j / l_j, as the PV B operand.
+    auto softmax = [&](int b, float (&sv)[16], typename Mfma<T>::frag (&pf)[NP]) {
+      float mx = sv[0];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (kb * 16 + 4 * g + rr > ql) s[b][kb * 4 + rr] = -INFINITY;
-      }
-      float mx = s[b][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
       mx = col_max(mx) * zs;
       float l = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
-        s[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], zs, -mx));
-        l += s[b][i];
+        sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], zs, -mx));
+        l += sv[i];
       }
       l = col_sum(l);                        // >= 1: the row maximum contributes exp2(0)
       const float f = wq[b] * __builtin_amdgcn_rcpf(l);
 #pragma unroll
       for (int st = 0; st < NP; ++st) {
         if constexpr (KPL == 1) {
-          pf[b][st] = s[b][st] * f;
+          pf[st] = sv[st] * f;
         } else {
 #pragma unroll
-          for (int z = 0; z < KPL; ++z) pf[b][st][z] = bf16_rne(s[b][st * KPL + z] * f);
+          for (int z = 0; z < KPL; ++z) pf[st][z] = bf16_rne(sv[st * KPL + z] * f);
         }
       }
-    }
+    };
+    auto pv = [&](const typename Mfma<T>::frag (&p0)[NP], const typename Mfma<T>::frag (&p1)[NP]) {
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
+      for (int db = 0; db < D / 16; ++db) {
 #pragma unroll
-      for (int st = 0; st < NP; ++st) {
-        typename Mfma<T>::frag va;
-        if constexpr (KPL == 1) va = v_frag_f32<Lay::VDB>(vbuf, m, g, db, st);
-        else va = v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st);
-        acc_o[0][db] = Mfma<T>::mma(va, pf[0][st], acc_o[0][db]);
-        acc_o[1][db] = Mfma<T>::mma(va, pf[1][st], acc_o[1][db]);
+        for (int st = 0; st < NP; ++st) {
+          typename Mfma<T>::frag va;
+          if constexpr (KPL == 1) va = v_frag_f32<Lay::VDB>(vbuf, m, g, db, st);
+          else va = v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st);
+          acc_o[0][db] = Mfma<T>::mma(va, p0[st], acc_o[0][db]);
+          acc_o[1][db] = Mfma<T>::mma(va, p1[st], acc_o[1][db]);
+        }
       }
+    };
+    float s0[16], s1[16];
+    typename Mfma<T>::frag pf0[NP], pf1[NP];
+    if (j == crow[0] || j == crow[1]) {      // wave-uniform: rows of a block share a chunk
+      qk(0, s0);
+      qk(1, s1);
+      if (j == crow[0]) mask(0, s0);
+      if (j == crow[1]) mask(1, s1);
+      softmax(0, s0, pf0);
+      softmax(1, s1, pf1);
+      pv(pf0, pf1);
+    } else if constexpr (KPL == 1) {
+      qk(0, s0);
+      qk(1, s1);
+      softmax(0, s0, pf0);
+      softmax(1, s1, pf1);
+      pv(pf0, pf1);
+    } else {
+      // One basic block, ordered so that independent MFMA and VALU work can overlap: block 1's
+      // S^T with block 0's softmax, block 0's PV with block 1's softmax (V fragments are read
+      // once and kept for both blocks).
+      qk(0, s0);
+      qk(1, s1);
+      softmax(0, s0, pf0);
+      typename Mfma<T>::frag va[D / 16][NP];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int st = 0; st < NP; ++st) va[db][st] = v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int st = 0; st < NP; ++st) acc_o[0][db] = Mfma<T>::mma(va[db][st], pf0[st], acc_o[0][db]);
+      softmax(1, s1, pf1);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int st = 0; st < NP; ++st) acc_o[1][db] = Mfma<T>::mma(va[db][st], pf1[st], acc_o[1][db]);
     }
   };
 

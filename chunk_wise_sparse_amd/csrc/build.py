@@ -14,9 +14,9 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attention.hip", "decode.hip"]
 LIB = os.path.join(PKG, "libhils.so")
-# Per-file flags.  Selection compares finite scores only, so NaN handling is dropped there
-# (max/min then need no NaN quieting of their operands).
-FILE_FLAGS = {"select_fast.hip": ["-fno-honor-nans"]}
+# Per-file flags.  Selection and attention take finite scores only, so NaN handling is dropped
+# there (max/min then need no NaN quieting of their operands).
+FILE_FLAGS = {"select_fast.hip": ["-fno-honor-nans"], "attention.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 CFLAGS = [

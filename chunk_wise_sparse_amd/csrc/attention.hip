@@ -40,17 +40,15 @@ struct AttnLayout {
 };
 
 // Selection of the group's rows, staged once: chunk index (u16, 0xFFFF = padding) and weight.
+// The union bitmap, one bit per chunk of the sequence, is the dynamic part of LDS.
 template <typename T, int D, int QG, int KMAX, int STAGES>
 struct AttnSmem {
-  // One bit per chunk of the sequence: 2048 words cover 65536 chunks; fp32 with d = 128 keeps
-  // 512 words (1M tokens, enforced by the API) so that two 64 KiB stages still fit.
-  static constexpr int BITMAP_WORDS = (sizeof(T) == 4 && D == 128) ? 512 : 2048;
+  typedef float WT;
   alignas(16) char k[STAGES][AttnLayout<T, D>::KBYTES];
   alignas(16) char v[STAGES][AttnLayout<T, D>::VBYTES];
-  uint32_t bitmap[BITMAP_WORDS];
   int nunion;
   uint16_t sidx[QG * (KMAX + 1)];
-  float sw[QG * (KMAX + 1)];
+  WT sw[QG * (KMAX + 1)];
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -77,18 +75,21 @@ __device__ __forceinline__ float v_frag_f32(const char* vbuf, int lane16, int g,
 }
 
 template <typename T, int D, int NW, int KMAX, int STAGES>
-__global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, STAGES == 1 ? 2 : 1) void chunk_attention_kernel(const AttnArgs a) {
   constexpr int QG = 32 * NW;                // queries per workgroup
   typedef AttnSmem<T, D, QG, KMAX, STAGES> Smem;
   typedef AttnLayout<T, D> Lay;
   constexpr int KPL = Mfma<T>::KPL;
   constexpr int NF = D / 4 / KPL;            // QK^T steps over d
+  // The chunk's V fragments stay in registers between the two blocks' PV (64 VGPRs at d = 128).
+  constexpr bool kSplitPV = true;
   constexpr int NP = 64 / Mfma<T>::K;        // PV steps over the 64 keys
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int NT = NW * 64;                // threads
   constexpr int NV = 64 * Lay::VPR / NT;     // 16-byte vectors per thread per tensor per chunk
   static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
   __shared__ Smem sm;
+  extern __shared__ uint32_t bitmap[];       // ceil(N / 32) words
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
   const int nwords = (c_last + 1 + 31) >> 5;
-  for (int x = tid; x < nwords; x += NT) sm.bitmap[x] = 0u;
+  for (int x = tid; x < nwords; x += NT) bitmap[x] = 0u;
   if (tid == 0) sm.nunion = 0;
   for (int r = tid; r < QG; r += NT) sm.sidx[r * ks + k] = (uint16_t)0xFFFF;   // end sentinel
   __syncthreads();
@@ -115,13 +116,13 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
     const int j = a.idx[(row0 + q0) * k + x];
     const bool ok = j >= 0 && j <= c_last;
     sm.sidx[r * ks + e] = ok ? (uint16_t)j : (uint16_t)0xFFFF;
-    sm.sw[r * ks + e] = a.w[(row0 + q0) * k + x];
-    if (ok) atomicOr(&sm.bitmap[j >> 5], 1u << (j & 31));
+    sm.sw[r * ks + e] = static_cast<typename Smem::WT>(a.w[(row0 + q0) * k + x]);
+    if (ok) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
   {
     int cnt = 0;
-    for (int x = tid; x < nwords; x += NT) cnt += __popc(sm.bitmap[x]);
+    for (int x = tid; x < nwords; x += NT) cnt += __popc(bitmap[x]);
     cnt = (int)wave_sum((float)cnt);   // exact: at most 65536
     if (lane == 0) atomicAdd(&sm.nunion, cnt);
   }
@@ -177,9 +178,9 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
   __syncthreads();
   // Union iterator, identical in every thread: ascending chunk order.
   int wi = 0;
-  uint32_t cur = sm.bitmap[0];
+  uint32_t cur = bitmap[0];
   auto next_chunk = [&]() -> int {
-    while (cur == 0u && wi + 1 < nwords) cur = sm.bitmap[++wi];
+    while (cur == 0u && wi + 1 < nwords) cur = bitmap[++wi];
     if (cur == 0u) return -1;
     const int j = wi * 32 + __builtin_ctz(cur);
     cur &= cur - 1u;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
       // The row's selection is ascending with a sentinel after entry k-1, so ptr stays <= k.
       const int e = rloc[b] * ks + ptr[b];
       sel[b] = live && sm.sidx[e] == (uint16_t)j;
-      const float wv = sm.sw[e];
+      const float wv = static_cast<float>(sm.sw[e]);
       wq[b] = sel[b] ? wv : 0.f;
       ptr[b] += sel[b] ? 1 : 0;
     }
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
       softmax(0, s0, pf0);
       softmax(1, s1, pf1);
       pv(pf0, pf1);
-    } else if constexpr (KPL == 1) {
+    } else if constexpr (KPL == 1 || !kSplitPV) {
       qk(0, s0);
       qk(1, s1);
       softmax(0, s0, pf0);
@@ -389,17 +390,18 @@ __global__ __launch_bounds__(NW * 64, 3 - STAGES) void chunk_attention_kernel(co
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   const uint32_t bhs = (uint32_t)a.B * a.H;
+  const size_t bm = (size_t)((a.N + 31) / 32) * 4;   // union bitmap (dynamic LDS)
   if constexpr (sizeof(T) == 4 && D == 128) {   // 32 KiB per tensor per chunk: 64-query groups
-    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
   } else {
     if (sizeof(T) == 2 && a.topk <= 32 && a.L % 128 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 32, 1>), dim3(bhs * (a.L / 128)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 32, 1>), dim3(bhs * (a.L / 128)), dim3(256), bm, st, a);
     } else if (a.topk <= 32 && a.L % 256 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), bm, st, a);
     } else if (a.L % 128 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 64, 2>), dim3(bhs * (a.L / 128)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 64, 2>), dim3(bhs * (a.L / 128)), dim3(256), bm, st, a);
     } else {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), 0, st, a);
+      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
     }
   }
   return hipGetLastError();

@@ -16,7 +16,11 @@ SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attenti
 LIB = os.path.join(PKG, "libhils.so")
 # Per-file flags.  Selection and attention take finite scores only, so NaN handling is dropped
 # there (max/min then need no NaN quieting of their operands).
-FILE_FLAGS = {"select_fast.hip": ["-fno-honor-nans"], "attention.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {
+    # MFMA results in ordinary VGPRs (no accumulation-register copies before the VALU work)
+    "select_fast.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attention.hip": ["-fno-honor-nans"],
+}
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -134,15 +134,33 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
     constexpr int NRS = 4;                     // r <= 64, 16 per step
     const int nrs = (a.r + 15) >> 4;
     bf16x8 tb[3][2][NRS];
+    // With r a multiple of 8 every 8-slot run is a whole, 16-byte aligned piece of a row.
+    const bool vec = (a.r & 7) == 0;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const float* tq = a.tcode + ((size_t)b * a.L + q0 + 32 * cb + col) * a.r;
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
+        float tv[8];
+        if (vec) {
+          const int a0 = 16 * rs + 8 * half;
+          const f32x4 lo = a0 < a.r ? *reinterpret_cast<const f32x4*>(tq + a0) : zero4();
+          const f32x4 hi = a0 < a.r ? *reinterpret_cast<const f32x4*>(tq + a0 + 4) : zero4();
+#pragma unroll
+          for (int z = 0; z < 4; ++z) {
+            tv[z] = lo[z];
+            tv[4 + z] = hi[z];
+          }
+        } else {
+#pragma unroll
+          for (int z = 0; z < 8; ++z) {
+            const int ai = 16 * rs + 8 * half + z;
+            tv[z] = (rs < nrs && ai < a.r) ? tq[ai] : 0.f;
+          }
+        }
 #pragma unroll
         for (int z = 0; z < 8; ++z) {
-          const int ai = 16 * rs + 8 * half + z;
-          const float t = (rs < nrs && ai < a.r) ? tq[ai] : 0.f;
+          const float t = tv[z];
           const bf16 t0 = bf16_rne(t);
           const float r1 = t - to_f32(t0);
           const bf16 t1 = bf16_rne(r1);
@@ -161,10 +179,15 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
       for (int rs = 0; rs < NRS; ++rs) {
         if (rs < nrs) {
           bf16x8 wa;
+          if (vec) {
+            const int a0 = 16 * rs + 8 * half;
+            wa = a0 < a.r ? *reinterpret_cast<const bf16x8*>(wrow + a0) : bf16x8{};
+          } else {
 #pragma unroll
-          for (int z = 0; z < 8; ++z) {
-            const int ai = 16 * rs + 8 * half + z;
-            wa[z] = ai < a.r ? wrow[ai] : bf16_rne(0.f);
+            for (int z = 0; z < 8; ++z) {
+              const int ai = 16 * rs + 8 * half + z;
+              wa[z] = ai < a.r ? wrow[ai] : bf16_rne(0.f);
+            }
           }
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
@@ -348,47 +371,58 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
   }
 
   // ---------------- final top-kq and inter-chunk softmax ------------------------------------
+  // The list (cnt <= kCap entries, chunk order) is read into registers once.
+  float ev[kCap];
+  int ej[kCap];
+#pragma unroll
+  for (int i = 0; i < kCap; ++i) {
+    ev[i] = i < cnt ? ls[64 * i] : -INFINITY;
+    ej[i] = i < cnt ? (int)lj[64 * i] : 0;
+  }
   float theta, top;
   {
     float v[64];                               // kCap entries padded to the sort width
     static_assert(kCap <= 64, "list longer than the sort");
 #pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = (i < kCap && i < cnt) ? ls[64 * i] : -INFINITY;
+    for (int i = 0; i < 64; ++i) v[i] = i < kCap ? ev[i] : -INFINITY;
     sort_desc<64>(v);
     top = v[0];
     theta = pick<64>(v, kq);
   }
+  // Entries > theta, then the first kq - #(> theta) entries == theta in chunk order.
   int ngt = 0;
-  for (int i = 0; i < cnt; ++i) ngt += ls[64 * i] > theta ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < kCap; ++i) ngt += ev[i] > theta ? 1 : 0;   // padding is -inf
   const int m_eq = kq - ngt;
-  const float zs = a.scale * 1.4426950408889634f;   // scale * log2(e)
-  float esum = 0.f;
+  bool kept[kCap];
   {
     int eq = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const float sv = ls[64 * i];
-      bool keep = sv > theta;
-      if (sv == theta) {
+#pragma unroll
+    for (int i = 0; i < kCap; ++i) {
+      bool keep = ev[i] > theta;
+      if (i < cnt && ev[i] == theta) {
         keep = eq < m_eq;
         ++eq;
       }
-      if (keep) esum += exp2f((sv - top) * zs);
+      kept[i] = keep;
     }
+  }
+  const float zs = a.scale * 1.4426950408889634f;   // scale * log2(e)
+  float esum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCap; ++i) {
+    ev[i] = kept[i] ? exp2f((ev[i] - top) * zs) : 0.f;
+    esum += ev[i];
   }
   const float inv = 1.f / esum;
   const int qpos = q0 + 32 * half + col;
   const size_t orow = ((size_t)bh * a.L + qpos) * a.k;
-  int pos = 0, eq = 0;
-  for (int i = 0; i < cnt; ++i) {
-    const float sv = ls[64 * i];
-    bool keep = sv > theta;
-    if (sv == theta) {
-      keep = eq < m_eq;
-      ++eq;
-    }
-    if (keep) {
-      a.idx[orow + pos] = (int32_t)lj[64 * i];
-      a.w[orow + pos] = exp2f((sv - top) * zs) * inv;
+  int pos = 0;
+#pragma unroll
+  for (int i = 0; i < kCap; ++i) {
+    if (kept[i]) {
+      a.idx[orow + pos] = ej[i];
+      a.w[orow + pos] = ev[i] * inv;
       ++pos;
     }
   }

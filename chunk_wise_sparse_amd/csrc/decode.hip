@@ -23,7 +23,8 @@
 
 namespace hils {
 
-constexpr int kScoreChunksPerBlock = 256;
+constexpr int kScoreRowsPerWave = 64;                       // landmarks scored by one wave
+constexpr int kScoreChunksPerBlock = 4 * kScoreRowsPerWave;   // 4 waves per workgroup
 
 // Lanes sharing one 16-byte-vector row: reduce over the LPR lanes of a row group.
 template <int LPR>
@@ -67,14 +68,14 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int LPR = D / VE;          // lanes per landmark row
   constexpr int RPI = 64 / LPR;        // rows per wave iteration
-  constexpr int NIT = 64 / RPI;        // iterations for a wave's 64 rows
+  constexpr int NIT = kScoreRowsPerWave / RPI;   // iterations for a wave's rows
   typedef T vecT __attribute__((ext_vector_type(VE)));
   __shared__ T qt[D];
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n_b = (kvl + kChunk - 1) / kChunk;
-  const int base = blockIdx.y * kScoreChunksPerBlock + wave * 64;
+  const int base = blockIdx.y * kScoreChunksPerBlock + wave * kScoreRowsPerWave;
   if (blockIdx.y * kScoreChunksPerBlock >= n_b) return;   // uniform: the whole workgroup
   const int seg = lane % LPR, sub = lane / LPR;
   const T* L = static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D;

@@ -18,24 +18,39 @@
 // "HiLS Attention Extrapolates 64x ...": per-chunk outputs fused by the retrieval scores].
 #include <float.h>
 
+#include <algorithm>
+
 #include "hils_device.h"
 #include "hils_launch.h"
 
 namespace hils {
 
-constexpr int kScoreRowsPerWave = 64;                       // landmarks scored by one wave
+constexpr int kScoreRowsPerWave = 64;                       // landmarks scored by one wave (one per lane)
 constexpr int kScoreChunksPerBlock = 4 * kScoreRowsPerWave;   // 4 waves per workgroup
+constexpr int kScoreWorkgroups = 2048;                       // landmark-scan grid size target
 
-// Lanes sharing one 16-byte-vector row: reduce over the LPR lanes of a row group.
+// Lanes sharing one 16-byte-vector row: sum over the LPR lanes of a row group (every lane of the
+// group gets it).  Within a 16-lane DPP row the partners come from DPP moves (quad_perm swaps
+// of 1 and 2 lanes, then the 8-lane and 16-lane mirrors), wider groups add lane shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int LPR>
 __device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int mk = LPR / 2; mk >= 1; mk >>= 1) v += shfl_xor_f(v, mk);
+  static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row group of 2^n lanes");
+  if constexpr (LPR >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (LPR >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (LPR >= 32) v += shfl_xor_f(v, 16);
+  if constexpr (LPR >= 64) v += shfl_xor_f(v, 32);
   return v;
 }
 
 // ------------------------------------------------------------------------------------------
-// Q-Cal code: t[b][a] = W_down[a] . h_b, one workgroup per (a, b), a fixed summation order.
+// Q-Cal code: t[b][a] = W_down[a] . h_b, one workgroup per (a, b), a fixed summation order; rows
+// padded with zeros to kTcodeStride entries.
 // ------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void decode_tcode_kernel(const T* __restrict__ hid,
@@ -45,6 +60,10 @@ __global__ __launch_bounds__(256) void decode_tcode_kernel(const T* __restrict__
   typedef T vecT __attribute__((ext_vector_type(VE)));
   __shared__ float part[4];
   const int a = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a >= r) {                                // padding entries of the row
+    if (tid == 0) tcode[(size_t)b * kTcodeStride + a] = 0.f;
+    return;
+  }
   const T* hb = hid + (size_t)b * D;
   const T* wr = w_down + (size_t)a * D;
   float s = 0.f;
@@ -57,71 +76,101 @@ __global__ __launch_bounds__(256) void decode_tcode_kernel(const T* __restrict__
   s = wave_sum(s);
   if (lane == 0) part[wave] = s;
   __syncthreads();
-  if (tid == 0) tcode[(size_t)b * r + a] = (part[0] + part[1]) + (part[2] + part[3]);
+  if (tid == 0) tcode[(size_t)b * kTcodeStride + a] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // ------------------------------------------------------------------------------------------
 // Landmark scan.
 // ------------------------------------------------------------------------------------------
-template <typename T, int D>
+// kVecW: W_up rows are read as 16-byte vectors (r a nonzero multiple of the vector width).
+// Grid (pairs, Y): workgroup y of a pair scores the pair's 256-landmark blocks y, y + Y, ...;
+// q~ is formed once per workgroup, while the first block's loads are in flight.
+template <typename T, int D, bool kVecW>
 __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) {
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int LPR = D / VE;          // lanes per landmark row
-  constexpr int RPI = 64 / LPR;        // rows per wave iteration
-  constexpr int NIT = kScoreRowsPerWave / RPI;   // iterations for a wave's rows
+  constexpr int RPI = 64 / LPR;        // rows per load instruction
+  constexpr int NIT = kScoreRowsPerWave / RPI;   // load instructions for a wave's rows
+  static_assert(D <= 256, "one q~ element per thread");
   typedef T vecT __attribute__((ext_vector_type(VE)));
-  __shared__ T qt[D];
+  __shared__ T qt[256];                        // q~ in entries 0..D-1 (threads >= D write copies)
+  __shared__ float tsh[kTcodeStride];          // the sequence's Q-Cal code
+  __shared__ float sws[4][kScoreRowsPerWave];  // each wave's scores of the current block
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n_b = (kvl + kChunk - 1) / kChunk;
-  const int base = blockIdx.y * kScoreChunksPerBlock + wave * kScoreRowsPerWave;
-  if (blockIdx.y * kScoreChunksPerBlock >= n_b) return;   // uniform: the whole workgroup
+  const int nblk = (n_b + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock;
+  int blk = blockIdx.y;
+  if (blk >= nblk) return;                     // uniform: the whole workgroup
   const int seg = lane % LPR, sub = lane / LPR;
-  const T* L = static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D;
-  // Landmark loads first; q~ is formed while they are in flight.
+  const T* L = static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D + seg * VE;
+  float* S = a.scores + (size_t)bh * a.Nmax;
   vecT rows[NIT];
+  auto load_rows = [&](int bk) {
+    const int base = bk * kScoreChunksPerBlock + wave * kScoreRowsPerWave + sub;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int r = base + it * RPI + sub;
-    rows[it] = r < n_b ? *reinterpret_cast<const vecT*>(L + (size_t)r * D + seg * VE) : vecT{};
+    for (int it = 0; it < NIT; ++it)           // row clamped: no branch per load
+      rows[it] = *reinterpret_cast<const vecT*>(L + (size_t)min(base + it * RPI, n_b - 1) * D);
+  };
+  // The loads q~ needs are issued first, then the landmark loads; memory counters retire in
+  // issue order, so q~ is formed while the landmarks are still in flight.
+  const int i = tid % D;                       // q~ element of this thread
+  const T* wr = static_cast<const T*>(a.w_up) + ((size_t)h * D + i) * a.r;
+  const float qi = to_f32(static_cast<const T*>(a.q)[(size_t)bh * D + i]);
+  // The code row is staged in LDS (one load per thread; the row holds kTcodeStride entries).
+  const float tv = kVecW ? a.tcode[(size_t)b * kTcodeStride + tid % kTcodeStride] : 0.f;
+  vecT wv[64 / VE];
+  if constexpr (kVecW) {                       // rows 16-byte aligned, r a multiple of VE
+#pragma unroll
+    for (int g = 0; g < 64 / VE; ++g)          // group clamped: no branch per load
+      wv[g] = *reinterpret_cast<const vecT*>(wr + min(g * VE, a.r - VE));
   }
+  asm volatile("" ::: "memory");               // keeps the landmark loads behind these
+  load_rows(blk);
   // q~[i] = round(q[i] + sum_a W_up[h*D + i][a] t[b][a]) (fp32 sum in order a = 0..r-1; r <= 64).
-  for (int i = tid; i < D; i += 256) {
+  {
     float dq = 0.f;
-    if (a.r > 0) {
-      const T* wr = static_cast<const T*>(a.w_up) + ((size_t)h * D + i) * a.r;
-      const float* tb = a.tcode + (size_t)b * a.r;
-      if (a.r % VE == 0) {                     // rows are 16-byte aligned: vector loads
-        vecT wv[64 / VE];
+    const float* tb = a.tcode + (size_t)b * kTcodeStride;
+    if constexpr (kVecW) {
+      static_assert(kTcodeStride == 64, "one W_up row group per 64 code entries");
+      if (tid < kTcodeStride) tsh[tid] = tv;
+      __syncthreads();
 #pragma unroll
-        for (int g = 0; g < 64 / VE; ++g)
-          if (g * VE < a.r) wv[g] = *reinterpret_cast<const vecT*>(wr + g * VE);
+      for (int g = 0; g < 64 / VE; ++g) {      // the zero code entries past r add exact zeros
 #pragma unroll
-        for (int g = 0; g < 64 / VE; ++g)
-          if (g * VE < a.r) {
-#pragma unroll
-            for (int e = 0; e < VE; ++e) dq = fmaf(to_f32(wv[g][e]), tb[g * VE + e], dq);
-          }
-      } else {
-        for (int x = 0; x < a.r; ++x) dq = fmaf(to_f32(wr[x]), tb[x], dq);
+        for (int e = 0; e < VE; ++e) dq = fmaf(to_f32(wv[g][e]), tsh[g * VE + e], dq);
       }
+    } else {
+      for (int x = 0; x < a.r; ++x) dq = fmaf(to_f32(wr[x]), tb[x], dq);
     }
-    qt[i] = from_f32<T>(to_f32(static_cast<const T*>(a.q)[(size_t)bh * D + i]) + dq);
+    qt[tid] = from_f32<T>(qi + dq);
   }
   __syncthreads();
   const vecT qv = *reinterpret_cast<const vecT*>(&qt[seg * VE]);
   float qf[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) qf[e] = to_f32(qv[e]);
+  // A wave's 64 scores are gathered in LDS and written with one 256-byte store (one store
+  // instruction per row group would cost as much as the loads).
+  float* sw = sws[wave];
+  while (true) {
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    float s = 0.f;
+    for (int it = 0; it < NIT; ++it) {
+      float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) s = fmaf(to_f32(rows[it][e]), qf[e], s);
-    s = row_sum<LPR>(s);
-    const int r = base + it * RPI + sub;
-    if (seg == 0 && r < n_b) a.scores[(size_t)bh * a.Nmax + r] = s;
+      for (int e = 0; e < VE; ++e) s = fmaf(to_f32(rows[it][e]), qf[e], s);
+      s = row_sum<LPR>(s);
+      if (seg == 0) sw[it * RPI + sub] = s;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): the wave's scores are in LDS
+    __builtin_amdgcn_wave_barrier();
+    const int r = blk * kScoreChunksPerBlock + wave * kScoreRowsPerWave + lane;
+    if (r < n_b) S[r] = sw[lane];
+    __builtin_amdgcn_wave_barrier();           // sw is rewritten by the next block
+    blk += gridDim.y;
+    if (blk >= nblk) break;
+    load_rows(blk);
   }
 }
 
@@ -151,51 +200,170 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
 // ------------------------------------------------------------------------------------------
 // Selection.
 // ------------------------------------------------------------------------------------------
-// Candidates that fit 32 per thread (n <= 8192): keys in registers, theta (the kk-th largest
-// key) by bisection over the key bits with counts from wave ballots, then the selected set as
-// bitmaps (chunk order), ties at theta to the smallest indices, and the inter-chunk softmax.
+// Candidates that fit 32 per thread (n <= 8192), keys in registers.  The kk-th largest key
+// theta is at least tau, the kk-th largest of the 256 per-thread maxima (kk threads each hold a
+// key >= tau), so every selected chunk is among the candidates with key >= tau.  On spread-out
+// scores these are a few dozen: they are compacted into LDS and one wave finds theta among them
+// by bisection over the key bits (counts from ballots, no block barriers), takes the keys above
+// theta and the smallest indices at theta, and writes the chunks in ascending order with the
+// inter-chunk softmax.  If the candidates overflow the compaction buffer (heavy ties or adversarial
+// scores), the whole block bisects over all keys instead.  Both paths select the same set.
 constexpr int kSelReg = 8192;
+constexpr int kCandCap = 512;                  // 8 candidates per lane of the finishing wave
+
+// Largest t with #(v >= t) >= kk over one wave's NV values per lane (kk >= 1 and at least kk
+// values nonzero).
+template <int NV>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&v)[NV], int kk) {
+  uint32_t th = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) c += __popcll(__ballot(v[i] >= cand));
+    if (c >= kk) th = cand;
+  }
+  return th;
+}
+
+// The selected chunks (one per lane < kk, any lane order) to ascending slots with their
+// weights; pads slots kk..k-1.  sx, ev: 64-entry LDS arrays of this wave.
+__device__ __forceinline__ void write_selection(const DecodeArgs& a, int bh, int kk, bool has, int x,
+                                                float sv, float smax, int* sx, float* ev) {
+  const int lane = threadIdx.x & 63;
+  sx[lane] = has ? x : INT32_MAX;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  int rank = 0;
+#pragma unroll 8
+  for (int m = 0; m < 64; ++m) rank += sx[m] < x ? 1 : 0;   // distinct indices: ranks 0..kk-1
+  const float zs = a.scale * 1.4426950408889634f;
+  int32_t* I = a.idx + (size_t)bh * a.k;
+  float* W = a.w + (size_t)bh * a.k;
+  if (has) {
+    I[rank] = x;
+    ev[rank] = exp2f((sv - smax) * zs);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const float e = lane < kk ? ev[lane] : 0.f;
+  const float sum = wave_sum(e);
+  if (lane < kk) W[lane] = e / sum;
+  else if (lane < a.k) { W[lane] = 0.f; I[lane] = -1; }
+}
 
 __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs a) {
-  __shared__ float sc[kSelReg];
-  __shared__ uint32_t gtw[kSelReg / 32], eqw[kSelReg / 32];
-  __shared__ int cnt_w[2][4];
+  __shared__ uint32_t tmax[256];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint16_t cidx[kCandCap];
   __shared__ int scratch[8];
   __shared__ uint32_t kmax_w[4];
-  __shared__ float evals[64];
+  __shared__ int sx[64];
+  __shared__ uint32_t skey[64];
+  __shared__ float ev[64];
+  __shared__ uint32_t gtw[kSelReg / 32], eqw[kSelReg / 32];   // overflow path
+  __shared__ int cnt_w[2][4];
   const int bh = blockIdx.x, b = bh / a.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n = (kvl + kChunk - 1) / kChunk;
   const int kk = min(a.k, n);
   const float* G = a.scores + (size_t)bh * a.Nmax;
   uint32_t key[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {               // all loads in flight at once (index clamped)
+    const int x = tid + 256 * i;
+    key[i] = f32_key(G[min(x, n - 1)]);
+  }
   uint32_t kmax = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const int x = tid + 256 * i;
-    const float v = x < n ? G[x] : 0.f;
-    if (x < n) sc[x] = v;
-    key[i] = x < n ? f32_key(v) : 0u;   // 0 is below the key of every finite score
+    if (tid + 256 * i >= n) key[i] = 0u;       // 0 is below the key of every finite score
     kmax = max(kmax, key[i]);
   }
+  tmax[tid] = kmax;
 #pragma unroll
   for (int mk = 32; mk >= 1; mk >>= 1) kmax = max(kmax, shfl_xor_u(kmax, mk));
   if (lane == 0) kmax_w[wave] = kmax;
-  // theta = largest key with #(key >= theta) >= kk, one bit at a time from the top; the wave's
-  // count is the popcount of ballots (scalar work), the block's a sum of four slots.
+  __syncthreads();
+  const float smax = key_f32(max(max(kmax_w[0], kmax_w[1]), max(kmax_w[2], kmax_w[3])));
+  uint32_t tm[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) tm[q] = tmax[lane + 64 * q];
+  const uint32_t tau = wave_kth_key(tm, kk);   // the same in every wave
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) c += key[i] >= tau ? 1 : 0;
+  int ncand;
+  int pos = block_exclusive_scan(c, scratch, ncand);
+  if (ncand <= kCandCap) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (key[i] >= tau) {
+        ckey[pos] = key[i];
+        cidx[pos] = (uint16_t)(tid + 256 * i);
+        ++pos;
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    uint32_t ck[kCandCap / 64];
+    int cx[kCandCap / 64];
+#pragma unroll
+    for (int q = 0; q < kCandCap / 64; ++q) {
+      const int p = lane + 64 * q;
+      ck[q] = p < ncand ? ckey[p] : 0u;
+      cx[q] = p < ncand ? (int)cidx[p] : INT32_MAX;
+    }
+    const uint32_t th = wave_kth_key(ck, kk);
+    int ngt = 0;
+#pragma unroll
+    for (int q = 0; q < kCandCap / 64; ++q) ngt += __popcll(__ballot(ck[q] > th));
+    bool sel[kCandCap / 64];
+#pragma unroll
+    for (int q = 0; q < kCandCap / 64; ++q) sel[q] = ck[q] > th;
+    for (int t = ngt; t < kk; ++t) {           // at theta: the smallest remaining index, kk - ngt times
+      int mn = INT32_MAX;
+#pragma unroll
+      for (int q = 0; q < kCandCap / 64; ++q) mn = min(mn, (ck[q] == th && !sel[q]) ? cx[q] : INT32_MAX);
+#pragma unroll
+      for (int mk = 32; mk >= 1; mk >>= 1) mn = min(mn, shfl_xor_i(mn, mk));
+#pragma unroll
+      for (int q = 0; q < kCandCap / 64; ++q) sel[q] = sel[q] || (ck[q] == th && cx[q] == mn);
+    }
+    // One selected chunk per lane: compact by ballot prefix.
+    int slot = 0;
+    bool has = false;
+    int x = 0;
+    uint32_t xk = 0u;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int q = 0; q < kCandCap / 64; ++q) {
+      const uint64_t bq = __ballot(sel[q]);
+      const int at = slot + __popcll(bq & below);
+      slot += __popcll(bq);
+      if (sel[q]) { sx[at] = cx[q]; skey[at] = ck[q]; }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    has = lane < kk;
+    if (has) { x = sx[lane]; xk = skey[lane]; }
+    __builtin_amdgcn_wave_barrier();
+    write_selection(a, bh, kk, has, has ? x : INT32_MAX, key_f32(xk), smax, sx, ev);
+    return;
+  }
+  // Overflow: theta over all keys (block-wide counts, one barrier per bit), then bitmaps of the
+  // keys > theta and == theta; the wave's 64 lanes cover 64 consecutive chunks.
   uint32_t th = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = th | (1u << bit);
-    int c = 0;
+    int cb = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) c += __popcll(__ballot(key[i] >= cand));
-    if (lane == 0) cnt_w[bit & 1][wave] = c;
+    for (int i = 0; i < 32; ++i) cb += __popcll(__ballot(key[i] >= cand));
+    if (lane == 0) cnt_w[bit & 1][wave] = cb;
     __syncthreads();                           // slots alternate, so one barrier per bit
     const int tot = (cnt_w[bit & 1][0] + cnt_w[bit & 1][1]) + (cnt_w[bit & 1][2] + cnt_w[bit & 1][3]);
     if (tot >= kk) th = cand;
   }
-  const float smax = key_f32(max(max(kmax_w[0], kmax_w[1]), max(kmax_w[2], kmax_w[3])));
-  // Bitmaps of keys > theta and == theta; the wave's 64 lanes cover 64 consecutive chunks.
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint64_t g = __ballot(key[i] > th);
@@ -223,7 +391,7 @@ __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs
     rest &= rest - 1u;
   }
   uint32_t sel = gw | ek;
-  int pos = block_exclusive_scan(__popc(sel), scratch, tot);
+  int p = block_exclusive_scan(__popc(sel), scratch, tot);
   const float zs = a.scale * 1.4426950408889634f;
   int32_t* I = a.idx + (size_t)bh * a.k;
   float* W = a.w + (size_t)bh * a.k;
@@ -231,13 +399,13 @@ __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs
     const int bt = __builtin_ctz(sel);
     sel &= sel - 1u;
     const int x = 32 * tid + bt;
-    I[pos] = x;
-    evals[pos] = exp2f((sc[x] - smax) * zs);
-    ++pos;
+    I[p] = x;
+    ev[p] = exp2f((G[x] - smax) * zs);
+    ++p;
   }
   __syncthreads();
   if (tid < 64) {
-    const float e = tid < kk ? evals[tid] : 0.f;
+    const float e = tid < kk ? ev[tid] : 0.f;
     const float sum = wave_sum(e);
     if (tid < kk) W[tid] = e / sum;
     else if (tid < a.k) { W[tid] = 0.f; I[tid] = -1; }
@@ -347,40 +515,52 @@ __global__ __launch_bounds__(256) void decode_select_kernel(const DecodeArgs a) 
 // ------------------------------------------------------------------------------------------
 // Chunk attention.
 // ------------------------------------------------------------------------------------------
-// One selected chunk for one wave: softmax of the raw query over the chunk's visible keys and
-// the weighted output w_j * o_j (lanes < LPR hold it, VE values each, in acc).
+// One selected chunk for one wave.  Rows are read with raw buffer loads through a descriptor
+// that covers only the chunk's visible rows: rows past the causal cut (and every row of an empty
+// slot) come back as zeros without touching memory, so the loads need no branches and all of a
+// chunk's loads are in flight together.
+constexpr int kBufDword3 = 0x00020000;         // gfx9 buffer descriptor word 3 (32-bit data format)
+
+struct Slot {
+  int j;        // chunk index, -1 for an empty slot
+  int n_vis;    // visible rows (0 for an empty slot)
+  float w;      // inter-chunk weight
+};
+
 template <typename T, int D>
 struct ChunkGather {
   static constexpr int VE = 16 / (int)sizeof(T);
-  static constexpr int LPR = D / VE;
-  static constexpr int RPI = 64 / LPR;
-  static constexpr int NIT = 64 / RPI;
+  static constexpr int LPR = D / VE;           // lanes per row
+  static constexpr int RPI = 64 / LPR;         // rows per load instruction
+  static constexpr int NIT = 64 / RPI;         // load instructions per chunk
   typedef T vecT __attribute__((ext_vector_type(VE)));
   vecT kr[NIT], vr[NIT];
-  int n_vis;
-  float wj;
 
-  __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int b, int u, int lane) {
-    const int j = u < a.k ? a.idx[(size_t)bh * a.k + u] : -1;
-    const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-    const bool live = j >= 0 && j * kChunk < kvl;
-    n_vis = live ? min(kChunk, kvl - j * kChunk) : 0;
-    wj = live ? a.w[(size_t)bh * a.k + u] : 0.f;
+  // Descriptor over the slot's visible rows of one (sequence, head) cache.
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(const void* cache, int bh, int Lmax,
+                                                                const Slot& s) {
+    // Every operand is wave-uniform; readfirstlane says so to the compiler (a descriptor must sit
+    // in scalar registers).
+    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const T*>(cache) +
+                                                     ((size_t)bh * Lmax + (size_t)max(s.j, 0) * kChunk) * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane(s.n_vis * D * (int)sizeof(T));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                             bytes, kBufDword3);
+  }
+  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, vecT (&dst)[NIT], int lane) {
     const int seg = lane % LPR, sub = lane / LPR;
-    const size_t row0 = (size_t)bh * a.Lmax + (size_t)(live ? j : 0) * kChunk;
-    const T* Kc = static_cast<const T*>(a.k_cache) + row0 * D;
-    const T* Vc = static_cast<const T*>(a.v_cache) + row0 * D;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + sub;
-      kr[it] = r < n_vis ? *reinterpret_cast<const vecT*>(Kc + (size_t)r * D + seg * VE) : vecT{};
-      vr[it] = r < n_vis ? *reinterpret_cast<const vecT*>(Vc + (size_t)r * D + seg * VE) : vecT{};
+      const int off = ((it * RPI + sub) * D + seg * VE) * (int)sizeof(T);
+      const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      dst[it] = __builtin_bit_cast(vecT, raw);
     }
   }
 
-  // sp: this wave's 64 floats of LDS.  Adds the chunk's weighted output to acc.
-  __device__ __forceinline__ void attend(const float (&qf)[VE], float scale, float* sp, int lane,
-                                         float (&acc)[VE]) {
+  // sigma_r = q . k_r for the chunk's rows into this wave's 64 floats of LDS (-inf past n_vis).
+  __device__ __forceinline__ void scores(const float (&qf)[VE], int n_vis, float* sp, int lane) const {
     const int seg = lane % LPR, sub = lane / LPR;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -391,15 +571,22 @@ struct ChunkGather {
       const int r = it * RPI + sub;
       if (seg == 0) sp[r] = r < n_vis ? s : -INFINITY;
     }
+  }
+
+  // Softmax over the chunk's scores and the weighted output w_j * o_j added to acc (lanes < LPR
+  // hold it, VE values each).
+  __device__ __forceinline__ void finish(float scale, const Slot& s, float* sp, int lane,
+                                         float (&acc)[VE]) const {
+    const int sub = lane / LPR;
     __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): this wave's scores are in LDS
     __builtin_amdgcn_wave_barrier();
-    const bool live = n_vis > 0;
+    const bool live = s.n_vis > 0;
     const float zs = scale * 1.4426950408889634f;
     const float sv = sp[lane];
     const float mx = live ? wave_max(sv) : 0.f;
     const float p = live ? exp2f((sv - mx) * zs) : 0.f;
     const float l = wave_sum(p);
-    const float f = live ? wj / l : 0.f;
+    const float f = live ? s.w / l : 0.f;
     __builtin_amdgcn_wave_barrier();
     sp[lane] = p * f;
     __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -409,8 +596,7 @@ struct ChunkGather {
     for (int e = 0; e < VE; ++e) part[e] = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + sub;
-      const float pr = sp[r];
+      const float pr = sp[it * RPI + sub];
 #pragma unroll
       for (int e = 0; e < VE; ++e) part[e] = fmaf(pr, to_f32(vr[it][e]), part[e]);
     }
@@ -425,6 +611,17 @@ struct ChunkGather {
   }
 };
 
+// Slot u of (sequence b, head): chunk, visible rows and weight.  jl / wl: lane u holds slot u's
+// index and weight (lanes >= k: -1 and 0); u is wave-uniform.
+__device__ __forceinline__ Slot slot_of(int jl, float wl, int u, int kvl) {
+  Slot s;
+  s.j = __builtin_amdgcn_readlane(jl, u);
+  const bool live = s.j >= 0 && s.j * kChunk < kvl;
+  s.n_vis = live ? min(kChunk, kvl - s.j * kChunk) : 0;
+  s.w = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u)) : 0.f;
+  return s;
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int bh, int lane,
                                            float (&qf)[ChunkGather<T, D>::VE]) {
@@ -437,7 +634,9 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int bh, int lane
 
 // Whole (sequence, head) per workgroup of 8 waves: wave w takes slots w, w + 8, ... in order; the
 // 8 wave sums are then added in wave order.  Each wave holds one chunk's keys and values in
-// registers (32 KiB for bf16, d = 128), so eight waves keep 256 KiB in flight per workgroup.
+// registers (32 KiB for bf16, d = 128) and keeps the next chunk's loads in flight while it
+// computes: the next keys are requested once this chunk's scores are formed, the next values once
+// its weighted sum is done.
 template <typename T, int D>
 __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeArgs a) {
   typedef ChunkGather<T, D> CG;
@@ -445,16 +644,32 @@ __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeAr
   __shared__ float sp[NWV][64];
   __shared__ float wsum[NWV][D];
   const int bh = blockIdx.x, b = bh / a.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  const int jl = lane < a.k ? a.idx[(size_t)bh * a.k + lane] : -1;
+  const float wl = lane < a.k ? a.w[(size_t)bh * a.k + lane] : 0.f;
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];
 #pragma unroll
   for (int e = 0; e < CG::VE; ++e) acc[e] = 0.f;
-  for (int u = wave; u < a.k; u += NWV) {
+  if (wave < a.k) {
     CG cg;
-    cg.load(a, bh, b, u, lane);
-    cg.attend(qf, a.scale, sp[wave], lane, acc);
+    int u = wave;
+    Slot s = slot_of(jl, wl, u, kvl);
+    CG::load(CG::rows(a.k_cache, bh, a.Lmax, s), cg.kr, lane);
+    CG::load(CG::rows(a.v_cache, bh, a.Lmax, s), cg.vr, lane);
+    for (; u + NWV < a.k; u += NWV) {
+      cg.scores(qf, s.n_vis, sp[wave], lane);
+      const Slot nx = slot_of(jl, wl, u + NWV, kvl);
+      CG::load(CG::rows(a.k_cache, bh, a.Lmax, nx), cg.kr, lane);
+      cg.finish(a.scale, s, sp[wave], lane, acc);
+      CG::load(CG::rows(a.v_cache, bh, a.Lmax, nx), cg.vr, lane);
+      s = nx;
+    }
+    cg.scores(qf, s.n_vis, sp[wave], lane);
+    cg.finish(a.scale, s, sp[wave], lane, acc);
   }
   if (lane < CG::LPR) {
 #pragma unroll
@@ -475,16 +690,25 @@ __global__ __launch_bounds__(256) void decode_attend_split_kernel(const DecodeAr
   typedef ChunkGather<T, D> CG;
   __shared__ float sp[4][64];
   const int bh = blockIdx.x, b = bh / a.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int u = blockIdx.y * 4 + wave;
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  Slot s;
+  s.j = u < a.k ? a.idx[(size_t)bh * a.k + u] : -1;
+  const bool live = s.j >= 0 && s.j * kChunk < kvl;
+  s.n_vis = live ? min(kChunk, kvl - s.j * kChunk) : 0;
+  s.w = live ? a.w[(size_t)bh * a.k + u] : 0.f;
+  CG cg;
+  CG::load(CG::rows(a.k_cache, bh, a.Lmax, s), cg.kr, lane);
+  CG::load(CG::rows(a.v_cache, bh, a.Lmax, s), cg.vr, lane);
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];
 #pragma unroll
   for (int e = 0; e < CG::VE; ++e) acc[e] = 0.f;
-  CG cg;
-  cg.load(a, bh, b, u, lane);
-  cg.attend(qf, a.scale, sp[wave], lane, acc);
+  cg.scores(qf, s.n_vis, sp[wave], lane);
+  cg.finish(a.scale, s, sp[wave], lane, acc);
   if (u < a.k && lane < CG::LPR) {
     float* part = a.partial + ((size_t)bh * a.k + u) * D;
 #pragma unroll
@@ -523,13 +747,19 @@ template <typename T>
 hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int B, int D, int r,
                                hipStream_t st) {
   if (r == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_tcode_kernel<T>, dim3(r, B), dim3(256), 0, st, hid, w_down, tcode, D, r);
+  hipLaunchKernelGGL(decode_tcode_kernel<T>, dim3(kTcodeStride, B), dim3(256), 0, st, hid, w_down, tcode, D, r);
   return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.B * a.H, (a.Nmax + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock);
-  hipLaunchKernelGGL((decode_scores_kernel<T, D>), grid, dim3(256), 0, st, a);
+  // About kScoreWorkgroups workgroups in all (each then scores several blocks of its pair).
+  const int nblk = (a.Nmax + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock;
+  const int pairs = a.B * a.H;
+  dim3 grid(pairs, std::min(nblk, std::max(1, (kScoreWorkgroups + pairs - 1) / pairs)));
+  if (a.r > 0 && a.r % (16 / (int)sizeof(T)) == 0)
+    hipLaunchKernelGGL((decode_scores_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_scores_kernel<T, D, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {

@@ -186,7 +186,7 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   const size_t N = (p->max_kv_len + 63) / 64;
   size_t off = 0;
   L.tcode = off;
-  off += align_up(B * (size_t)p->qcal_rank * sizeof(float));
+  off += align_up(B * (size_t)(p->qcal_rank > 0 ? hils::kTcodeStride : 0) * sizeof(float));
   L.scores = off;
   off += align_up(B * H * N * sizeof(float));
   L.idx = off;

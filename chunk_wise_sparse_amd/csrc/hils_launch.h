@@ -29,10 +29,13 @@ struct AttnArgs {
   float scale;
 };
 
+// Decode Q-Cal code rows are padded to this many entries (zeros past the rank).
+constexpr int kTcodeStride = 64;
+
 struct DecodeArgs {
   const void* q;        // [B,H,d] raw query
   const void* w_up;     // [H*d, r] Q-Cal up-projection (unused when r == 0)
-  const float* tcode;   // [B, r] Q-Cal code W_down h (workspace)
+  const float* tcode;   // [B, kTcodeStride] Q-Cal code W_down h, zero past r (workspace)
   const void* k_cache;  // [B,H,Lmax,d]
   const void* v_cache;
   const void* lmk;      // [B,H,Nmax,d]

@@ -122,3 +122,72 @@ def test_decode_full_size_sampled(lib):
         sub["k_cache"] = dev["k_cache"][b:b + 1, h:h + 1].float().cpu().numpy()
         sub["v_cache"] = dev["v_cache"][b:b + 1, h:h + 1].float().cpu().numpy()
         _compare(sub, cfg, o[b:b + 1, h:h + 1], idx[b:b + 1, h:h + 1], w[b:b + 1, h:h + 1], [(0, 0)])
+
+
+# Whole-pair attention (one workgroup per (sequence, head)) is taken for bf16 once there are at
+# least 256 pairs: ragged caches there exercise empty slots and partial last chunks in it.
+WHOLE = [
+    synth.DecodeConfig("bf16_whole_ragged_d128", 4, 64, 3000, 128, 64, 64, "bf16", 32, 512,
+                       kv_len=(3000, 1, 65, 2047)),
+    synth.DecodeConfig("bf16_whole_ragged_d64", 8, 32, 1500, 64, 64, 16, "bf16", 16, 256,
+                       kv_len=(1500, 64, 1, 777, 1024, 1100, 3, 1499)),
+]
+
+
+@pytest.mark.parametrize("cfg", WHOLE, ids=lambda c: c.name)
+def test_decode_whole_pair_ragged(lib, cfg):
+    print(f"[case] decode {cfg}", flush=True)
+    inp = synth.make_decode_inputs_np(cfg)
+    o, idx, w = _run(_to_dev(inp, cfg.dtype), cfg)
+    _torch().cuda.synchronize()
+    pairs = [(b, h) for b in range(cfg.batch) for h in range(0, cfg.heads, 5)]
+    _compare(inp, cfg, o, idx, w, pairs)
+
+
+def _tied_landmarks(inp, cfg, kind):
+    """Overwrite the landmarks so that many chunks carry bit-identical rows (hence bit-identical
+    scores on both sides).  Scores of q-aligned rows c*q are about c*|q|^2, far above those of
+    the N(0,1) rows.
+      all_equal  - every chunk the same row: n equal scores (more candidates than the compaction
+                   buffer holds: the block-wide path), expected selection 0..k-1;
+      top_heavy  - 70% of chunks carry q itself: hundreds of ties at the k-th score;
+      boundary   - 60 chunks carry q, 30 carry 0.8 q: the k-th score is tied among 30 chunks and
+                   the 4 smallest of them are taken."""
+    rng = np.random.default_rng(1234)
+    lmk = inp["lmk"]
+    B, H, N, d = lmk.shape
+    for b in range(B):
+        n = -(-int(cfg.kv_len[b]) // cfg.chunk)
+        for h in range(H):
+            q = inp["q"][b, h]
+            if kind == "all_equal":
+                lmk[b, h, :n] = synth.round_to_dtype_np(rng.standard_normal(d).astype(np.float32), cfg.dtype)
+            elif kind == "top_heavy":
+                sel = rng.random(n) < 0.7
+                lmk[b, h, :n][sel] = q
+            else:
+                perm = rng.permutation(n)
+                lmk[b, h, perm[:60]] = q
+                lmk[b, h, perm[60:90]] = synth.round_to_dtype_np(0.8 * q, cfg.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["all_equal", "top_heavy", "boundary"])
+def test_decode_tied_scores(lib, kind, dtype):
+    """Ties at the k-th score go to the smaller chunk index: the selection equals the oracle's
+    exactly (no tolerance band: tied scores are bit-identical on both sides)."""
+    cfg = synth.DecodeConfig(f"ties_{kind}_{dtype}", 2, 2, 64000, 128, 64, 64, dtype, 32, 512,
+                             kv_len=(64000, 40001))
+    print(f"[case] decode {cfg}", flush=True)
+    inp = synth.make_decode_inputs_np(cfg)
+    _tied_landmarks(inp, cfg, kind)
+    o, idx, w = _run(_to_dev(inp, cfg.dtype), cfg)
+    _torch().cuda.synchronize()
+    pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    res = O.decode(inp, cfg.chunk, cfg.topk, cfg.dtype, pairs=pairs)
+    got = idx.cpu().numpy()
+    for p in pairs:
+        np.testing.assert_array_equal(got[p], res[p]["idx"], err_msg=str(p))
+        if kind == "all_equal":
+            np.testing.assert_array_equal(got[p], np.arange(cfg.topk), err_msg=str(p))
+    _compare(inp, cfg, o, idx, w, pairs)

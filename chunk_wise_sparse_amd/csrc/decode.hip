@@ -27,7 +27,6 @@ namespace hils {
 
 constexpr int kScoreRowsPerWave = 64;                       // landmarks scored by one wave (one per lane)
 constexpr int kScoreChunksPerBlock = 4 * kScoreRowsPerWave;   // 4 waves per workgroup
-constexpr int kScoreWorkgroups = 2048;                       // landmark-scan grid size target
 
 // Lanes sharing one 16-byte-vector row: sum over the LPR lanes of a row group (every lane of the
 // group gets it).  Within a 16-lane DPP row the partners come from DPP moves (quad_perm swaps
@@ -79,6 +78,18 @@ __global__ __launch_bounds__(256) void decode_tcode_kernel(const T* __restrict__
   if (tid == 0) tcode[(size_t)b * kTcodeStride + a] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
+// Raw buffer descriptor over `bytes` bytes at p (gfx9 word 3: 32-bit data format).  Every
+// operand is wave-uniform; readfirstlane says so to the compiler, since a descriptor lives in
+// scalar registers.  Loads through it past `bytes` return zeros without touching memory.
+constexpr int kBufDword3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  const uint64_t base = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufDword3);
+}
+
 // ------------------------------------------------------------------------------------------
 // Landmark scan.
 // ------------------------------------------------------------------------------------------
@@ -95,23 +106,31 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   typedef T vecT __attribute__((ext_vector_type(VE)));
   __shared__ T qt[256];                        // q~ in entries 0..D-1 (threads >= D write copies)
   __shared__ float tsh[kTcodeStride];          // the sequence's Q-Cal code
-  __shared__ float sws[4][kScoreRowsPerWave];  // each wave's scores of the current block
+  __shared__ float sws[4][4][kScoreRowsPerWave];   // [block q][wave][lane] scores
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n_b = (kvl + kChunk - 1) / kChunk;
   const int nblk = (n_b + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock;
-  int blk = blockIdx.y;
-  if (blk >= nblk) return;                     // uniform: the whole workgroup
+  const int qb = a.score_qb;
+  const int blk0 = blockIdx.y * qb;            // this workgroup's blocks: blk0 .. blk0 + nq - 1
+  if (blk0 >= nblk) return;                    // uniform: the whole workgroup
+  const int nq = min(qb, nblk - blk0);
+  int blk = blk0;
   const int seg = lane % LPR, sub = lane / LPR;
-  const T* L = static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D + seg * VE;
-  float* S = a.scores + (size_t)bh * a.Nmax;
+  float* S = a.scores + (size_t)bh * a.score_stride;
+  // Raw buffer loads through a descriptor over the pair's n_b landmark rows: rows past n_b (and
+  // blocks past the last) read as zeros without a memory access, so no load needs a clamp or a
+  // branch.
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D,
+                                                n_b * D * (int)sizeof(T));
+  const int lane_off = (wave * kScoreRowsPerWave * D + sub * D + seg * VE) * (int)sizeof(T);
+  constexpr int kBlockBytes = kScoreChunksPerBlock * D * (int)sizeof(T);
+  constexpr int kStepBytes = RPI * D * (int)sizeof(T);
   vecT rows[NIT];
-  auto load_rows = [&](int bk) {
-    const int base = bk * kScoreChunksPerBlock + wave * kScoreRowsPerWave + sub;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it)           // row clamped: no branch per load
-      rows[it] = *reinterpret_cast<const vecT*>(L + (size_t)min(base + it * RPI, n_b - 1) * D);
+  auto load_row = [&](int bk, int it) {
+    return __builtin_bit_cast(vecT, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, bk * kBlockBytes + lane_off + it * kStepBytes, 0, 0));
   };
   // The loads q~ needs are issued first, then the landmark loads; memory counters retire in
   // issue order, so q~ is formed while the landmarks are still in flight.
@@ -127,7 +146,10 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
       wv[g] = *reinterpret_cast<const vecT*>(wr + min(g * VE, a.r - VE));
   }
   asm volatile("" ::: "memory");               // keeps the landmark loads behind these
-  load_rows(blk);
+  // Half of the first block's loads go out before q~ is formed, the rest once its W_up registers
+  // are free (fewer registers live at once).
+#pragma unroll
+  for (int it = 0; it < NIT / 2; ++it) rows[it] = load_row(blk, it);
   // q~[i] = round(q[i] + sum_a W_up[h*D + i][a] t[b][a]) (fp32 sum in order a = 0..r-1; r <= 64).
   {
     float dq = 0.f;
@@ -146,31 +168,46 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     }
     qt[tid] = from_f32<T>(qi + dq);
   }
+#pragma unroll
+  for (int it = NIT / 2; it < NIT; ++it) rows[it] = load_row(blk, it);
   __syncthreads();
   const vecT qv = *reinterpret_cast<const vecT*>(&qt[seg * VE]);
   float qf[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) qf[e] = to_f32(qv[e]);
-  // A wave's 64 scores are gathered in LDS and written with one 256-byte store (one store
-  // instruction per row group would cost as much as the loads).
-  float* sw = sws[wave];
+  // Rolling prefetch: once row group it of this block is consumed, its registers take the same
+  // row group of the workgroup's next block, so about NIT loads stay in flight per wave (after the
+  // last block they address the block past the pair's end: outside the descriptor, no memory
+  // traffic).  Scores wait in LDS and leave in one vector store per lane at the end: stores share
+  // the vector memory counter with the loads, and every store instruction between the loads
+  // holds up the waits on them.
+  int q = 0;
   while (true) {
+    const int nxt = q + 1 < nq ? blk + 1 : nblk;
+    float* sw = sws[q][wave];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < VE; ++e) s = fmaf(to_f32(rows[it][e]), qf[e], s);
+      rows[it] = load_row(nxt, it);
       s = row_sum<LPR>(s);
       if (seg == 0) sw[it * RPI + sub] = s;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): the wave's scores are in LDS
-    __builtin_amdgcn_wave_barrier();
-    const int r = blk * kScoreChunksPerBlock + wave * kScoreRowsPerWave + lane;
-    if (r < n_b) S[r] = sw[lane];
-    __builtin_amdgcn_wave_barrier();           // sw is rewritten by the next block
-    blk += gridDim.y;
-    if (blk >= nblk) break;
-    load_rows(blk);
+    blk = nxt;
+    if (++q >= nq) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's scores are in LDS
+  __builtin_amdgcn_wave_barrier();
+  // Thread tid's record: the scores of chunks (blk0 + q) * 256 + tid, q = 0..qb-1 (entries past
+  // the sequence's chunks hold values the selection never reads).
+  float* rec = S + ((size_t)blockIdx.y * kScoreChunksPerBlock + tid) * qb;
+  if (qb == 4) {
+    *reinterpret_cast<f32x4*>(rec) = f32x4{sws[0][wave][lane], sws[1][wave][lane], sws[2][wave][lane], sws[3][wave][lane]};
+  } else if (qb == 2) {
+    *reinterpret_cast<float2*>(rec) = float2{sws[0][wave][lane], sws[1][wave][lane]};
+  } else {
+    *rec = sws[0][wave][lane];
   }
 }
 
@@ -252,6 +289,8 @@ __device__ __forceinline__ void write_selection(const DecodeArgs& a, int bh, int
   else if (lane < a.k) { W[lane] = 0.f; I[lane] = -1; }
 }
 
+// QB: the score buffer's blocks per record (decode_score_pos).
+template <int QB>
 __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs a) {
   __shared__ uint32_t tmax[256];
   __shared__ uint32_t ckey[kCandCap];
@@ -267,12 +306,25 @@ __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n = (kvl + kChunk - 1) / kChunk;
   const int kk = min(a.k, n);
-  const float* G = a.scores + (size_t)bh * a.Nmax;
+  const float* G = a.scores + (size_t)bh * a.score_stride;
+  // Thread tid's keys: chunks x = tid + 256 i, i = 0..31; block i sits in record i / QB, slot
+  // i % QB.  All loads in flight at once (records clamped to the buffer; entries past n masked).
   uint32_t key[32];
+  const int ymax = (int)(a.score_stride / (QB * kScoreBlock)) - 1;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {               // all loads in flight at once (index clamped)
-    const int x = tid + 256 * i;
-    key[i] = f32_key(G[min(x, n - 1)]);
+  for (int y = 0; y < 32 / QB; ++y) {
+    const float* rec = G + ((size_t)min(y, ymax) * kScoreBlock + tid) * QB;
+    if constexpr (QB == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(rec);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[4 * y + q] = f32_key(v[q]);
+    } else if constexpr (QB == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(rec);
+      key[2 * y] = f32_key(v.x);
+      key[2 * y + 1] = f32_key(v.y);
+    } else {
+      key[y] = f32_key(*rec);
+    }
   }
   uint32_t kmax = 0u;
 #pragma unroll
@@ -400,7 +452,7 @@ __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs
     sel &= sel - 1u;
     const int x = 32 * tid + bt;
     I[p] = x;
-    ev[p] = exp2f((G[x] - smax) * zs);
+    ev[p] = exp2f((G[decode_score_pos(x, QB)] - smax) * zs);
     ++p;
   }
   __syncthreads();
@@ -423,8 +475,8 @@ __global__ __launch_bounds__(256) void decode_select_kernel(const DecodeArgs a) 
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   const int n = (kvl + kChunk - 1) / kChunk;
   const int kk = min(a.k, n);
-  const float* G = a.scores + (size_t)bh * a.Nmax;
-  auto S = [&](int x) -> float { return G[x]; };
+  const float* G = a.scores + (size_t)bh * a.score_stride;
+  auto S = [&](int x) -> float { return G[decode_score_pos(x, a.score_qb)]; };
 
   // Radix select of the kk-th largest key, 8 bits at a time from the top.
   uint32_t prefix = 0u, pmask = 0u;
@@ -519,8 +571,6 @@ __global__ __launch_bounds__(256) void decode_select_kernel(const DecodeArgs a) 
 // that covers only the chunk's visible rows: rows past the causal cut (and every row of an empty
 // slot) come back as zeros without touching memory, so the loads need no branches and all of a
 // chunk's loads are in flight together.
-constexpr int kBufDword3 = 0x00020000;         // gfx9 buffer descriptor word 3 (32-bit data format)
-
 struct Slot {
   int j;        // chunk index, -1 for an empty slot
   int n_vis;    // visible rows (0 for an empty slot)
@@ -539,15 +589,8 @@ struct ChunkGather {
   // Descriptor over the slot's visible rows of one (sequence, head) cache.
   static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(const void* cache, int bh, int Lmax,
                                                                 const Slot& s) {
-    // Every operand is wave-uniform; readfirstlane says so to the compiler (a descriptor must sit
-    // in scalar registers).
-    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const T*>(cache) +
-                                                     ((size_t)bh * Lmax + (size_t)max(s.j, 0) * kChunk) * D);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-    const int bytes = __builtin_amdgcn_readfirstlane(s.n_vis * D * (int)sizeof(T));
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
-                                             bytes, kBufDword3);
+    return buffer_rsrc(static_cast<const T*>(cache) + ((size_t)bh * Lmax + (size_t)max(s.j, 0) * kChunk) * D,
+                       s.n_vis * D * (int)sizeof(T));
   }
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, vecT (&dst)[NIT], int lane) {
     const int seg = lane % LPR, sub = lane / LPR;
@@ -752,10 +795,9 @@ hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int 
 }
 template <typename T, int D>
 hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st) {
-  // About kScoreWorkgroups workgroups in all (each then scores several blocks of its pair).
+  static_assert(kScoreChunksPerBlock == kScoreBlock, "one block = 4 waves x 64 landmarks");
   const int nblk = (a.Nmax + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock;
-  const int pairs = a.B * a.H;
-  dim3 grid(pairs, std::min(nblk, std::max(1, (kScoreWorkgroups + pairs - 1) / pairs)));
+  dim3 grid(a.B * a.H, (nblk + a.score_qb - 1) / a.score_qb);
   if (a.r > 0 && a.r % (16 / (int)sizeof(T)) == 0)
     hipLaunchKernelGGL((decode_scores_kernel<T, D, true>), grid, dim3(256), 0, st, a);
   else
@@ -763,9 +805,14 @@ hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {
-  if (a.Nmax <= kSelReg)
-    hipLaunchKernelGGL(decode_select_reg_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
-  else
+  if (a.Nmax <= kSelReg) {
+    if (a.score_qb == 4)
+      hipLaunchKernelGGL(decode_select_reg_kernel<4>, dim3(a.B * a.H), dim3(256), 0, st, a);
+    else if (a.score_qb == 2)
+      hipLaunchKernelGGL(decode_select_reg_kernel<2>, dim3(a.B * a.H), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(decode_select_reg_kernel<1>, dim3(a.B * a.H), dim3(256), 0, st, a);
+  } else
     hipLaunchKernelGGL(decode_select_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -188,7 +188,8 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   L.tcode = off;
   off += align_up(B * (size_t)(p->qcal_rank > 0 ? hils::kTcodeStride : 0) * sizeof(float));
   L.scores = off;
-  off += align_up(B * H * N * sizeof(float));
+  const int qb = hils::decode_score_qb((int)(B * H), (int)N);
+  off += align_up(B * H * hils::decode_score_stride((int)N, qb) * sizeof(float));
   L.idx = off;
   if (!with_sel) off += align_up(B * H * k * sizeof(int32_t));
   L.w = off;
@@ -231,6 +232,8 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.Nmax = (p->max_kv_len + 63) / 64;
   a.k = p->topk;
   a.r = p->qcal_rank;
+  a.score_qb = hils::decode_score_qb(a.B * a.H, a.Nmax);
+  a.score_stride = hils::decode_score_stride(a.Nmax, a.score_qb);
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
   if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;

@@ -32,6 +32,28 @@ struct AttnArgs {
 // Decode Q-Cal code rows are padded to this many entries (zeros past the rank).
 constexpr int kTcodeStride = 64;
 
+// Decode landmark scores are stored workgroup-major.  The scan workgroup (pair, y) scores the qb
+// consecutive 256-landmark blocks y*qb .. y*qb+qb-1, and its thread t keeps the qb scores of
+// chunks (y*qb+q)*256 + t, q = 0..qb-1, side by side: one vector store per wave writes them.
+// qb is 4, 2 or 1, the largest that still gives the scan about 1024 workgroups.
+constexpr int kScoreBlock = 256;               // landmarks per block (4 waves x 64)
+inline int decode_score_qb(int pairs, int nmax) {
+  const int nblk = (nmax + kScoreBlock - 1) / kScoreBlock;
+  for (int qb = 4; qb > 1; qb >>= 1)
+    if ((long long)pairs * ((nblk + qb - 1) / qb) >= 1024) return qb;
+  return 1;
+}
+// Floats per pair of the score buffer.
+inline size_t decode_score_stride(int nmax, int qb) {
+  const int nblk = (nmax + kScoreBlock - 1) / kScoreBlock;
+  return (size_t)((nblk + qb - 1) / qb) * qb * kScoreBlock;
+}
+// Position of chunk x's score in its pair's part of the buffer.
+__host__ __device__ inline int decode_score_pos(int x, int qb) {
+  const int b = x / kScoreBlock;
+  return ((b / qb) * kScoreBlock + x % kScoreBlock) * qb + b % qb;
+}
+
 struct DecodeArgs {
   const void* q;        // [B,H,d] raw query
   const void* w_up;     // [H*d, r] Q-Cal up-projection (unused when r == 0)
@@ -40,12 +62,14 @@ struct DecodeArgs {
   const void* v_cache;
   const void* lmk;      // [B,H,Nmax,d]
   const int32_t* kv_len;
-  float* scores;        // [B,H,Nmax] workspace
+  float* scores;        // [B*H][score_stride] workspace, workgroup-major (decode_score_pos)
   int32_t* idx;         // [B,H,k]
   float* w;             // [B,H,k]
   float* partial;       // [B,H,k,d] workspace (split attend only)
   void* o;              // [B,H,d]
   int B, H, Lmax, Nmax, k, r;
+  int score_qb;         // decode_score_qb(B*H, Nmax)
+  size_t score_stride;  // decode_score_stride(Nmax, score_qb)
   float scale;
 };
 

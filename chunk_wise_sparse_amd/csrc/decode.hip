@@ -27,6 +27,7 @@ namespace hils {
 
 constexpr int kScoreRowsPerWave = 64;                       // landmarks scored by one wave (one per lane)
 constexpr int kScoreChunksPerBlock = 4 * kScoreRowsPerWave;   // 4 waves per workgroup
+constexpr int kCandSlot = 64;                                // candidates per scan workgroup (k <= 64)
 
 // Lanes sharing one 16-byte-vector row: sum over the LPR lanes of a row group (every lane of the
 // group gets it).  Within a 16-lane DPP row the partners come from DPP moves (quad_perm swaps
@@ -45,6 +46,45 @@ __device__ __forceinline__ float row_sum(float v) {
   if constexpr (LPR >= 32) v += shfl_xor_f(v, 16);
   if constexpr (LPR >= 64) v += shfl_xor_f(v, 32);
   return v;
+}
+
+// Block-wide exclusive scan of one int per thread (NW waves of 64); also returns the total.
+template <int NW = 4>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// Largest t with #(v >= t) >= kk over one wave's NV values per lane (kk >= 1 and at least kk
+// values nonzero).
+template <int NV>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&v)[NV], int kk) {
+  uint32_t th = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) c += __popcll(__ballot(v[i] >= cand));
+    if (c >= kk) th = cand;
+  }
+  return th;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -107,6 +147,11 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   __shared__ T qt[256];                        // q~ in entries 0..D-1 (threads >= D write copies)
   __shared__ float tsh[kTcodeStride];          // the sequence's Q-Cal code
   __shared__ float sws[4][4][kScoreRowsPerWave];   // [block q][wave][lane] scores
+  __shared__ uint32_t tmx[256];                // candidates: per-thread maximum keys
+  __shared__ int wcnt[4][4];                   // candidates per (block, wave); bisection counts
+  __shared__ u32x2 clist[4 * kScoreChunksPerBlock];   // candidates in chunk order
+  __shared__ u32x2 slot[kCandSlot];            // the workgroup's top-kk
+  __shared__ int scratch[4];
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
@@ -199,6 +244,134 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's scores are in LDS
   __builtin_amdgcn_wave_barrier();
+  if (a.cand != nullptr) {
+    // Candidates: this workgroup's top-kk chunks under the selection order (score descending,
+    // then chunk ascending), kk = min(k, n).  Every chunk of the sequence's top-kk is in the
+    // top-kk of its own workgroup, so the workgroups' lists together hold the whole selection.
+    // Filter: tau = kk-th largest of the 256 per-thread maxima (at least kk keys reach it, so the
+    // local kk-th key does too); the keys >= tau are compacted into LDS in chunk order, and wave 0
+    // keeps the exact top-kk among them (all of them when there are too many to rank here).
+    const int kk = min(a.k, n_b);
+    uint32_t kq[4];
+    int xq[4];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xq[q] = (blk0 + q) * kScoreChunksPerBlock + tid;
+      kq[q] = (q < nq && xq[q] < n_b) ? f32_key(sws[q][wave][lane]) : 0u;   // 0: no chunk
+      m = max(m, kq[q]);
+    }
+    tmx[tid] = m;
+    __syncthreads();
+    uint32_t tm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tm[j] = tmx[lane + 64 * j];
+    const uint32_t tau = max(wave_kth_key(tm, kk), 1u);   // the same in every wave
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bq[q] = __ballot(kq[q] >= tau);
+      if (lane == 0) wcnt[q][wave] = __popcll(bq[q]);
+    }
+    __syncthreads();
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {              // chunk order: block q, then wave, then lane
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = wcnt[q][w];
+        pre += w < wave ? c : 0;
+        tot += c;
+      }
+      if (kq[q] >= tau) clist[run + pre + __popcll(bq[q] & below)] = u32x2{kq[q], (uint32_t)xq[q]};
+      run += tot;
+    }
+    const int m1 = run;                        // >= 1: the workgroup holds a chunk
+    __syncthreads();
+    const int kl = min(kk, m1);
+    // The exact top-kl of clist under the selection order goes to this workgroup's slot of
+    // kCandSlot entries, in chunk order, padded with (0, 0).
+    u32x2* out = static_cast<u32x2*>(a.cand) + ((size_t)bh * a.score_ymax + blockIdx.y) * kCandSlot;
+    if (m1 <= 256) {
+      if (wave != 0) return;
+      uint32_t ck[4], cx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = lane + 64 * j;
+        const u32x2 c = clist[min(p, m1 - 1)];
+        ck[j] = p < m1 ? c.x : 0u;
+        cx[j] = c.y;
+      }
+      const uint32_t th = wave_kth_key(ck, kl);
+      int ngt = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ngt += __popcll(__ballot(ck[j] > th));
+      const int krem = kl - ngt;               // entries at th to keep, earliest chunks first
+      int eqb = 0, nout = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool eq = ck[j] == th;
+        const uint64_t be = __ballot(eq);
+        const bool sel = ck[j] > th || (eq && eqb + __popcll(be & below) < krem);
+        eqb += __popcll(be);
+        const uint64_t bs = __ballot(sel);
+        if (sel) slot[nout + __popcll(bs & below)] = u32x2{ck[j], cx[j]};
+        nout += __popcll(bs);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot is in LDS
+      __builtin_amdgcn_wave_barrier();
+      out[lane] = lane < kl ? slot[lane] : u32x2{0u, 0u};
+      return;
+    }
+    // Many candidates (ties): block-wide.  Thread tid takes entries [tid * P, tid * P + P).
+    const int P = (m1 + 255) / 256;            // <= 4
+    uint32_t ck[4], cx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid * P + i;
+      const u32x2 c = clist[min(p, m1 - 1)];
+      ck[i] = (i < P && p < m1) ? c.x : 0u;
+      cx[i] = c.y;
+    }
+    uint32_t th = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = th | (1u << bit);
+      int cb = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cb += __popcll(__ballot(ck[i] >= cand));
+      if (lane == 0) wcnt[bit & 1][wave] = cb;
+      __syncthreads();                         // slots alternate, so one barrier per bit
+      const int tot = (wcnt[bit & 1][0] + wcnt[bit & 1][1]) + (wcnt[bit & 1][2] + wcnt[bit & 1][3]);
+      if (tot >= kl) th = cand;
+    }
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ngt += ck[i] > th ? 1 : 0;
+      neq += ck[i] == th ? 1 : 0;
+    }
+    int tot, ngt_all;
+    (void)block_exclusive_scan(ngt, scratch, ngt_all);
+    const int krem = kl - ngt_all;
+    int er = block_exclusive_scan(neq, scratch, tot);
+    bool sel[4];
+    int nsel = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sel[i] = ck[i] > th;
+      if (ck[i] == th) { sel[i] = er < krem; ++er; }
+      nsel += sel[i] ? 1 : 0;
+    }
+    int o = block_exclusive_scan(nsel, scratch, tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (sel[i]) slot[o++] = u32x2{ck[i], cx[i]};
+    __syncthreads();
+    if (wave == 0) out[lane] = lane < kl ? slot[lane] : u32x2{0u, 0u};
+    return;
+  }
   // Thread tid's record: the scores of chunks (blk0 + q) * 256 + tid, q = 0..qb-1 (entries past
   // the sequence's chunks hold values the selection never reads).
   float* rec = S + ((size_t)blockIdx.y * kScoreChunksPerBlock + tid) * qb;
@@ -209,29 +382,6 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   } else {
     *rec = sws[0][wave][lane];
   }
-}
-
-// Block-wide exclusive scan of one int per thread (256 threads); also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int t = scratch[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + x - v;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -247,21 +397,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
 // scores), the whole block bisects over all keys instead.  Both paths select the same set.
 constexpr int kSelReg = 8192;
 constexpr int kCandCap = 512;                  // 8 candidates per lane of the finishing wave
-
-// Largest t with #(v >= t) >= kk over one wave's NV values per lane (kk >= 1 and at least kk
-// values nonzero).
-template <int NV>
-__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&v)[NV], int kk) {
-  uint32_t th = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) c += __popcll(__ballot(v[i] >= cand));
-    if (c >= kk) th = cand;
-  }
-  return th;
-}
 
 // The selected chunks (one per lane < kk, any lane order) to ascending slots with their
 // weights; pads slots kk..k-1.  sx, ev: 64-entry LDS arrays of this wave.
@@ -462,6 +597,94 @@ __global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs
     if (tid < kk) W[tid] = e / sum;
     else if (tid < a.k) { W[tid] = 0.f; I[tid] = -1; }
   }
+}
+
+// Candidate lists (n <= 8192): the scan workgroups' top-kk lists, concatenated in workgroup
+// order, hold the selection's chunks in chunk order.  Up to kCandCap of them: one wave finds
+// theta, the kk-th largest key, by bisection over the key bits, keeps the keys above theta and the
+// earliest (smallest-chunk) entries at theta, and writes them in list order, which is ascending
+// chunk order, with the inter-chunk softmax.  Longer lists (heavy ties) go block-wide: each
+// thread takes a contiguous stretch of the list, theta by bisection with block counts, then the
+// same rule through block scans.
+struct CandSelSmem {
+  float ev[64];
+  int32_t sidx[64];                            // the selection, also left in LDS: chunk indices,
+  float sw[64];                                // weights (-1 / 0 past kk)
+};
+
+// The selection of pair bh by one wave from the scan workgroups' slots (NJ >= the number of
+// slots): entry l of slot y sits at list position 64 y + l, and list order is chunk order
+// (padding entries have key 0, below every score).  theta, the kk-th largest key, by bisection
+// over the key bits; the keys above theta and the earliest entries at theta are kept, in list
+// order, with the inter-chunk softmax.  idx / w go to memory and to sm.sidx / sm.sw.
+template <int NJ>
+__device__ void select_candidates_wave(const DecodeArgs& a, int bh, int kk, int yb, CandSelSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  const u32x2* L = static_cast<const u32x2*>(a.cand) + (size_t)bh * a.score_ymax * kCandSlot;
+  uint32_t ck[NJ], cx[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const u32x2 c = L[min(j, yb - 1) * kCandSlot + lane];
+    ck[j] = j < yb ? c.x : 0u;
+    cx[j] = c.y;
+  }
+  uint32_t km = 0u;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) km = max(km, ck[j]);
+#pragma unroll
+  for (int mk = 32; mk >= 1; mk >>= 1) km = max(km, shfl_xor_u(km, mk));
+  const float smax = key_f32(km);
+  const uint32_t th = wave_kth_key(ck, kk);
+  int ngt = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) ngt += __popcll(__ballot(ck[j] > th));
+  const int krem = kk - ngt;                   // entries at theta to take, earliest first
+  const float zs = a.scale * 1.4426950408889634f;
+  int32_t* I = a.idx + (size_t)bh * a.k;
+  float* W = a.w + (size_t)bh * a.k;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eqb = 0, nout = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bool eq = ck[j] == th;
+    const uint64_t be = __ballot(eq);
+    const bool sel = ck[j] > th || (eq && eqb + __popcll(be & below) < krem);
+    eqb += __popcll(be);
+    const uint64_t bs = __ballot(sel);
+    if (sel) {
+      const int o = nout + __popcll(bs & below);
+      I[o] = (int32_t)cx[j];
+      sm.sidx[o] = (int32_t)cx[j];
+      sm.ev[o] = exp2f((key_f32(ck[j]) - smax) * zs);
+    }
+    nout += __popcll(bs);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): ev is in LDS
+  __builtin_amdgcn_wave_barrier();
+  const float e = lane < kk ? sm.ev[lane] : 0.f;
+  const float sum = wave_sum(e);
+  const float wv = lane < kk ? e / sum : 0.f;
+  if (lane < kk) W[lane] = wv;
+  else if (lane < a.k) { W[lane] = 0.f; I[lane] = -1; }
+  sm.sw[lane] = wv;
+  if (lane >= kk) sm.sidx[lane] = -1;
+}
+
+// Wave 0 of the calling workgroup selects for pair bh (the caller synchronises before reading sm).
+__device__ __forceinline__ void select_candidates(const DecodeArgs& a, int bh, CandSelSmem& sm) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int b = bh / a.H;
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  const int n = (kvl + kChunk - 1) / kChunk;
+  const int kk = min(a.k, n);
+  const int yb = ((n + kScoreBlock - 1) / kScoreBlock + a.score_qb - 1) / a.score_qb;   // scan workgroups, <= 32
+  if (yb <= 8) select_candidates_wave<8>(a, bh, kk, yb, sm);
+  else select_candidates_wave<32>(a, bh, kk, yb, sm);
+}
+
+__global__ __launch_bounds__(64) void decode_select_cand_kernel(const DecodeArgs a) {
+  __shared__ CandSelSmem sm;
+  select_candidates(a, blockIdx.x, sm);
 }
 
 // Larger caches: radix select over the scores in global memory, 8 bits at a time.
@@ -690,8 +913,18 @@ __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeAr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  const int jl = lane < a.k ? a.idx[(size_t)bh * a.k + lane] : -1;
-  const float wl = lane < a.k ? a.w[(size_t)bh * a.k + lane] : 0.f;
+  int jl;
+  float wl;
+  if (a.cand != nullptr) {                     // the selection runs here, from the scan's lists
+    __shared__ CandSelSmem sel;
+    select_candidates(a, bh, sel);
+    __syncthreads();
+    jl = lane < a.k ? sel.sidx[lane] : -1;
+    wl = lane < a.k ? sel.sw[lane] : 0.f;
+  } else {
+    jl = lane < a.k ? a.idx[(size_t)bh * a.k + lane] : -1;
+    wl = lane < a.k ? a.w[(size_t)bh * a.k + lane] : 0.f;
+  }
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];
@@ -805,7 +1038,9 @@ hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {
-  if (a.Nmax <= kSelReg) {
+  if (a.cand != nullptr) {
+    hipLaunchKernelGGL(decode_select_cand_kernel, dim3(a.B * a.H), dim3(64), 0, st, a);
+  } else if (a.Nmax <= kSelReg) {
     if (a.score_qb == 4)
       hipLaunchKernelGGL(decode_select_reg_kernel<4>, dim3(a.B * a.H), dim3(256), 0, st, a);
     else if (a.score_qb == 2)
@@ -816,11 +1051,17 @@ hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(decode_select_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
-// bf16: whole-pair workgroups once there are at least as many pairs as compute units.
+// bf16: whole-pair workgroups once there are at least as many pairs as compute units; they
+// also run the selection when the scan left candidate lists.
+template <typename T>
+bool decode_attend_whole(const DecodeArgs& a) { return sizeof(T) == 2 && a.B * a.H >= 256; }
+template <typename T>
+bool decode_select_fused(const DecodeArgs& a) { return a.cand != nullptr && decode_attend_whole<T>(a); }
+
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    if (a.B * a.H >= 256) {
+    if (decode_attend_whole<T>(a)) {
       hipLaunchKernelGGL((decode_attend_whole_kernel<T, D>), dim3(a.B * a.H), dim3(512), 0, st, a);
       return hipGetLastError();
     }
@@ -831,6 +1072,8 @@ hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template bool decode_select_fused<bf16>(const DecodeArgs&);
+template bool decode_select_fused<float>(const DecodeArgs&);
 template hipError_t launch_decode_tcode<bf16>(const bf16*, const bf16*, float*, int, int, int, hipStream_t);
 template hipError_t launch_decode_tcode<float>(const float*, const float*, float*, int, int, int, hipStream_t);
 #define HILS_DECODE_INST(T, D)                                                      \

@@ -152,8 +152,12 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
 // Decode
 // ---------------------------------------------------------------------------------------------
 struct DecodeLayout {
-  size_t tcode, scores, idx, w, partial, total;
+  size_t tcode, scores, cand, idx, w, partial, total;
 };
+
+// Caches of up to this many chunks select from the scan's per-workgroup candidate lists; longer
+// ones from dense scores.
+constexpr int kDecodeCandMaxChunks = 8192;
 
 int check_decode_params(const hils_decode_params* p) {
   if (!p) return fail(HILS_ERR_INVALID_ARG, "params is NULL");
@@ -187,9 +191,16 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   size_t off = 0;
   L.tcode = off;
   off += align_up(B * (size_t)(p->qcal_rank > 0 ? hils::kTcodeStride : 0) * sizeof(float));
-  L.scores = off;
   const int qb = hils::decode_score_qb((int)(B * H), (int)N);
-  off += align_up(B * H * hils::decode_score_stride((int)N, qb) * sizeof(float));
+  const size_t stride = hils::decode_score_stride((int)N, qb);   // landmarks per pair, padded
+  L.scores = L.cand = off;
+  if (N <= (size_t)kDecodeCandMaxChunks) {
+    L.cand = off;                              // 64 (key, chunk) entries per scan workgroup
+    off += align_up(B * H * (stride / (qb * hils::kScoreBlock)) * 64 * 2 * sizeof(uint32_t));
+  } else {
+    L.scores = off;
+    off += align_up(B * H * stride * sizeof(float));
+  }
   L.idx = off;
   if (!with_sel) off += align_up(B * H * k * sizeof(int32_t));
   L.w = off;
@@ -234,10 +245,13 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.r = p->qcal_rank;
   a.score_qb = hils::decode_score_qb(a.B * a.H, a.Nmax);
   a.score_stride = hils::decode_score_stride(a.Nmax, a.score_qb);
+  a.score_ymax = (int)(a.score_stride / (a.score_qb * hils::kScoreBlock));
+  const bool cand = a.Nmax <= kDecodeCandMaxChunks;
+  a.cand = cand ? static_cast<void*>(ws + L.cand) : nullptr;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
   if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  if ((e = hils::launch_decode_select(a, st)) != hipSuccess) return e;
+  if (!hils::decode_select_fused<T>(a) && (e = hils::launch_decode_select(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   if ((e = hils::launch_decode_attend<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;

@@ -70,6 +70,11 @@ struct DecodeArgs {
   int B, H, Lmax, Nmax, k, r;
   int score_qb;         // decode_score_qb(B*H, Nmax)
   size_t score_stride;  // decode_score_stride(Nmax, score_qb)
+  // Candidate mode (Nmax <= 8192; NULL otherwise): scan workgroup (pair, y) writes its top-k
+  // (key, chunk) pairs in chunk order to the 64-entry slot cand[(pair * score_ymax + y) * 64],
+  // padded with (0, 0); no dense scores are written.
+  void* cand;           // uint32 pairs (key, chunk)
+  int score_ymax;       // scan workgroups per pair: ceil(ceil(Nmax / 256) / score_qb)
   float scale;
 };
 
@@ -90,6 +95,10 @@ hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int 
 template <typename T, int D>
 hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st);
+// True when launch_decode_attend<T, D> performs the selection itself (launch_decode_select is
+// then skipped).
+template <typename T>
+bool decode_select_fused(const DecodeArgs& a);
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st);
 

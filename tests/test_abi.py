@@ -111,8 +111,8 @@ def test_decode_rejects_bad_arguments():
     assert call(_dp(), o=FAKE + (1 << 32) + 64) == -1
     need = lib.hils_decode_workspace_size(ctypes.byref(_dp()), 0)
     a256 = lambda x: (x + 255) // 256 * 256
-    # scores: one 256-landmark block per (sequence, head), workgroup-major
-    assert need == a256(2 * 64 * 4) + a256(2 * 2 * 256 * 4) + 2 * a256(2 * 2 * 4 * 4) + a256(2 * 2 * 4 * 64 * 4)
+    # selection candidates: one scan workgroup per (sequence, head), 64 entries of 8 bytes
+    assert need == a256(2 * 64 * 4) + a256(2 * 2 * 64 * 8) + 2 * a256(2 * 2 * 4 * 4) + a256(2 * 2 * 4 * 64 * 4)
 
 
 def test_status_strings():

@@ -191,3 +191,23 @@ def test_decode_tied_scores(lib, kind, dtype):
         if kind == "all_equal":
             np.testing.assert_array_equal(got[p], np.arange(cfg.topk), err_msg=str(p))
     _compare(inp, cfg, o, idx, w, pairs)
+
+
+def test_decode_tied_scores_whole_pair(lib):
+    """All landmarks of every (sequence, head) equal, 516 chunks, 256 pairs: the whole-pair
+    attention path runs the selection itself, here over more tied candidates than one wave
+    ranks.  The selection is the first k chunks with equal weights 1/k."""
+    torch = _torch()
+    cfg = synth.DecodeConfig("ties_whole_pair", 2, 128, 33000, 64, 64, 64, "bf16", 16, 256,
+                             kv_len=(33000, 32000))
+    print(f"[case] decode {cfg}", flush=True)
+    inp = synth.make_decode_inputs_np(cfg)
+    _tied_landmarks(inp, cfg, "all_equal")
+    o, idx, w = _run(_to_dev(inp, cfg.dtype), cfg)
+    torch.cuda.synchronize()
+    got, gw = idx.cpu().numpy(), w.cpu().numpy()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            np.testing.assert_array_equal(got[b, h], np.arange(cfg.topk), err_msg=str((b, h)))
+            np.testing.assert_allclose(gw[b, h], 1.0 / cfg.topk, rtol=1e-6, err_msg=str((b, h)))
+    _compare(inp, cfg, o, idx, w, [(0, 0), (1, 77), (1, 127)])

@@ -898,33 +898,17 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int bh, int lane
   for (int e = 0; e < CG::VE; ++e) qf[e] = to_f32(qv[e]);
 }
 
-// Whole (sequence, head) per workgroup of 8 waves: wave w takes slots w, w + 8, ... in order; the
-// 8 wave sums are then added in wave order.  Each wave holds one chunk's keys and values in
+// Whole (sequence, head) by a workgroup of NWV waves: wave w takes slots w, w + NWV, ... in order;
+// the wave sums are then added in wave order.  Each wave holds one chunk's keys and values in
 // registers (32 KiB for bf16, d = 128) and keeps the next chunk's loads in flight while it
 // computes: the next keys are requested once this chunk's scores are formed, the next values once
-// its weighted sum is done.
-template <typename T, int D>
-__global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeArgs a) {
+// its weighted sum is done.  jl / wl: lane u holds slot u's chunk and weight.
+template <typename T, int D, int NWV>
+__device__ __forceinline__ void gather_pair(const DecodeArgs& a, int bh, int kvl, int jl, float wl,
+                                            float (*sp)[64], float (*wsum)[D]) {
   typedef ChunkGather<T, D> CG;
-  constexpr int NWV = 8;
-  __shared__ float sp[NWV][64];
-  __shared__ float wsum[NWV][D];
-  const int bh = blockIdx.x, b = bh / a.H;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  int jl;
-  float wl;
-  if (a.cand != nullptr) {                     // the selection runs here, from the scan's lists
-    __shared__ CandSelSmem sel;
-    select_candidates(a, bh, sel);
-    __syncthreads();
-    jl = lane < a.k ? sel.sidx[lane] : -1;
-    wl = lane < a.k ? sel.sw[lane] : 0.f;
-  } else {
-    jl = lane < a.k ? a.idx[(size_t)bh * a.k + lane] : -1;
-    wl = lane < a.k ? a.w[(size_t)bh * a.k + lane] : 0.f;
-  }
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];
@@ -958,6 +942,297 @@ __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeAr
     for (int w = 0; w < NWV; ++w) s += wsum[w][threadIdx.x];
     static_cast<T*>(a.o)[(size_t)bh * D + threadIdx.x] = from_f32<T>(s);
   }
+}
+
+// The attention stage alone, one workgroup per (sequence, head).
+template <typename T, int D>
+__global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeArgs a) {
+  typedef ChunkGather<T, D> CG;
+  constexpr int NWV = 8;
+  __shared__ float sp[NWV][64];
+  __shared__ float wsum[NWV][D];
+  const int bh = blockIdx.x, b = bh / a.H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  int jl;
+  float wl;
+  if (a.cand != nullptr) {                     // the selection runs here, from the scan's lists
+    __shared__ CandSelSmem sel;
+    select_candidates(a, bh, sel);
+    __syncthreads();
+    jl = lane < a.k ? sel.sidx[lane] : -1;
+    wl = lane < a.k ? sel.sw[lane] : 0.f;
+  } else {
+    jl = lane < a.k ? a.idx[(size_t)bh * a.k + lane] : -1;
+    wl = lane < a.k ? a.w[(size_t)bh * a.k + lane] : 0.f;
+  }
+  gather_pair<T, D, NWV>(a, bh, kvl, jl, wl, sp, wsum);
+}
+
+// ------------------------------------------------------------------------------------------
+// Fused decode step: one workgroup of 8 waves per (sequence, head) scores the pair's landmarks,
+// selects and gathers, with the scores kept in LDS (n <= kFusedMaxChunks).  Used when there are
+// at least as many pairs as compute units, so that every compute unit streams its pairs' data
+// without a kernel boundary between the stages.
+// ------------------------------------------------------------------------------------------
+constexpr int kFusedMaxChunks = 8192;
+constexpr int kFusedWaves = 4;                 // one wave per SIMD: up to 512 registers each
+constexpr int kFusedRowsPerWave = 128;         // landmarks per wave and scan iteration
+constexpr int kFusedRows = kFusedWaves * kFusedRowsPerWave;   // per scan iteration (512)
+
+template <typename T, int D, bool kVecW>
+__global__ __launch_bounds__(kFusedWaves * 64) void decode_fused_kernel(const DecodeArgs a) {
+  constexpr int NWV = kFusedWaves;
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int LPR = D / VE;          // lanes per landmark row
+  constexpr int RPI = 64 / LPR;        // rows per load instruction
+  constexpr int NIT = kFusedRowsPerWave / RPI;   // load instructions per wave and iteration
+  constexpr int NK = kFusedMaxChunks / (NWV * 64);   // keys per thread in the selection (32)
+  typedef T vecT __attribute__((ext_vector_type(VE)));
+  __shared__ float sc[kFusedMaxChunks];        // the pair's landmark scores
+  __shared__ T qt[NWV * 64];                   // q~ in entries 0..D-1 (other threads write copies)
+  __shared__ float tsh[kTcodeStride];          // the sequence's Q-Cal code
+  __shared__ uint32_t tmx[NWV * 64];           // per-thread maximum keys
+  __shared__ int wcnt[2][NK][NWV];             // per (key slot, wave) counts, two uses
+  __shared__ int cnt_w[2][NWV];
+  __shared__ u32x2 clist[kCandCap];            // candidates in chunk order
+  __shared__ CandSelSmem sel;
+  __shared__ float sp[NWV][64];
+  __shared__ float wsum[NWV][D];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  const int n = (kvl + kChunk - 1) / kChunk;   // 1 <= n <= kFusedMaxChunks
+  const int kk = min(a.k, n);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // ---- landmark scan: iteration it covers rows [512 it, 512 it + 512), wave w 128 of them ----
+  const int seg = lane % LPR, sub = lane / LPR;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D,
+                                                n * D * (int)sizeof(T));
+  const int lane_off = (wave * kFusedRowsPerWave * D + sub * D + seg * VE) * (int)sizeof(T);
+  constexpr int kIterBytes = kFusedRows * D * (int)sizeof(T);
+  constexpr int kStepBytes = RPI * D * (int)sizeof(T);
+  auto load_row = [&](int it, int j) {
+    return __builtin_bit_cast(vecT, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, it * kIterBytes + lane_off + j * kStepBytes, 0, 0));
+  };
+  const int n_iter = (n + kFusedRows - 1) / kFusedRows;
+  // q~ = round(q + W_up[h] t_b): its loads go out first, then half of the first rows; q~ is
+  // formed while they are in flight (memory counters retire in issue order).
+  const int i = tid % D;
+  const T* wr = static_cast<const T*>(a.w_up) + ((size_t)h * D + i) * a.r;
+  const float qi = to_f32(static_cast<const T*>(a.q)[(size_t)bh * D + i]);
+  const float tv = kVecW ? a.tcode[(size_t)b * kTcodeStride + tid % kTcodeStride] : 0.f;
+  vecT wv[64 / VE];
+  if constexpr (kVecW) {
+#pragma unroll
+    for (int g = 0; g < 64 / VE; ++g)          // group clamped: no branch per load
+      wv[g] = *reinterpret_cast<const vecT*>(wr + min(g * VE, a.r - VE));
+  }
+  asm volatile("" ::: "memory");               // keeps the landmark loads behind these
+  vecT rows[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT / 2; ++j) rows[j] = load_row(0, j);
+  {
+    float dq = 0.f;
+    if constexpr (kVecW) {
+      if (tid < kTcodeStride) tsh[tid] = tv;
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < 64 / VE; ++g)        // the zero code entries past r add exact zeros
+#pragma unroll
+        for (int e = 0; e < VE; ++e) dq = fmaf(to_f32(wv[g][e]), tsh[g * VE + e], dq);
+    } else {
+      const float* tb = a.tcode + (size_t)b * kTcodeStride;
+      for (int x = 0; x < a.r; ++x) dq = fmaf(to_f32(wr[x]), tb[x], dq);
+    }
+    qt[tid] = from_f32<T>(qi + dq);
+  }
+#pragma unroll
+  for (int j = NIT / 2; j < NIT; ++j) rows[j] = load_row(0, j);
+  __syncthreads();
+  float qf[VE];
+  {
+    const vecT qv = *reinterpret_cast<const vecT*>(&qt[seg * VE]);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) qf[e] = to_f32(qv[e]);
+  }
+  // Rolling prefetch: a consumed row group's registers take the same row group of the next
+  // iteration (after the last one, rows past n: zeros, no memory traffic).
+  for (int it = 0; it < n_iter; ++it) {
+    const int nxt = it + 1 < n_iter ? it + 1 : n_iter;
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s = fmaf(to_f32(rows[j][e]), qf[e], s);
+      rows[j] = load_row(nxt, j);
+      s = row_sum<LPR>(s);
+      if (seg == 0) sc[it * kFusedRows + wave * kFusedRowsPerWave + j * RPI + sub] = s;
+    }
+  }
+  __syncthreads();
+
+  // ---- selection: top-kk under (score descending, chunk ascending) ----
+  // Thread tid holds the keys of chunks x = tid + 256 q, q < NK; list order (q, wave, lane) is
+  // chunk order.  tau = kk-th largest of the 256 per-thread maxima (every selected key reaches it).
+  uint32_t key[NK];
+  uint32_t m = 0u;
+#pragma unroll
+  for (int q = 0; q < NK; ++q) {
+    const int x = tid + NWV * 64 * q;
+    key[q] = x < n ? f32_key(sc[x]) : 0u;      // 0: no chunk
+    m = max(m, key[q]);
+  }
+  tmx[tid] = m;
+  __syncthreads();
+  uint32_t tm[NWV];                            // the NWV * 64 maxima, NWV per lane
+#pragma unroll
+  for (int j = 0; j < NWV; ++j) tm[j] = tmx[lane + 64 * j];
+  const uint32_t tau = max(wave_kth_key(tm, kk), 1u);   // the same in every wave
+  // Chunk-order positions of the keys >= tau (ballot prefixes and per-(q, wave) counts).
+  auto ordered_pos = [&](int use, const bool (&flag)[NK], int (&pos)[NK]) -> int {
+    uint64_t bq[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      bq[q] = __ballot(flag[q]);
+      if (lane == 0) wcnt[use][q][wave] = __popcll(bq[q]);
+    }
+    __syncthreads();
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        const int c = wcnt[use][q][w];
+        pre += w < wave ? c : 0;
+        tot += c;
+      }
+      pos[q] = run + pre + __popcll(bq[q] & below);
+      run += tot;
+    }
+    return run;
+  };
+  bool fl[NK];
+  int pos[NK];
+#pragma unroll
+  for (int q = 0; q < NK; ++q) fl[q] = key[q] >= tau;
+  const int M = ordered_pos(0, fl, pos);       // >= kk
+  const float zs = a.scale * 1.4426950408889634f;
+  int32_t* I = a.idx + (size_t)bh * a.k;
+  float* W = a.w + (size_t)bh * a.k;
+  if (M <= kCandCap) {
+#pragma unroll
+    for (int q = 0; q < NK; ++q)
+      if (fl[q]) clist[pos[q]] = u32x2{key[q], (uint32_t)(tid + NWV * 64 * q)};
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int NJ = kCandCap / 64;
+      uint32_t ck[NJ], cx[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int p = lane + 64 * j;
+        const u32x2 c = clist[min(p, M - 1)];
+        ck[j] = p < M ? c.x : 0u;
+        cx[j] = c.y;
+      }
+      uint32_t km = 0u;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) km = max(km, ck[j]);
+#pragma unroll
+      for (int mk = 32; mk >= 1; mk >>= 1) km = max(km, shfl_xor_u(km, mk));
+      const float smax = key_f32(km);
+      const uint32_t th = wave_kth_key(ck, kk);
+      int ngt = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) ngt += __popcll(__ballot(ck[j] > th));
+      const int krem = kk - ngt;               // entries at theta to take, earliest first
+      int eqb = 0, nout = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool eq = ck[j] == th;
+        const uint64_t be = __ballot(eq);
+        const bool s = ck[j] > th || (eq && eqb + __popcll(be & below) < krem);
+        eqb += __popcll(be);
+        const uint64_t bs = __ballot(s);
+        if (s) {
+          const int o = nout + __popcll(bs & below);
+          sel.sidx[o] = (int32_t)cx[j];
+          sel.ev[o] = exp2f((key_f32(ck[j]) - smax) * zs);
+        }
+        nout += __popcll(bs);
+      }
+    }
+  } else {
+    // Many candidates (ties): theta by bisection with block counts, then the keys above theta
+    // and the earliest entries at theta, positions in chunk order.
+    uint32_t km = 0u;
+#pragma unroll
+    for (int q = 0; q < NK; ++q) km = max(km, key[q]);
+#pragma unroll
+    for (int mk = 32; mk >= 1; mk >>= 1) km = max(km, shfl_xor_u(km, mk));
+    if (lane == 0) tmx[wave] = km;             // tmx is free again
+    uint32_t th = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = th | (1u << bit);
+      int cb = 0;
+#pragma unroll
+      for (int q = 0; q < NK; ++q) cb += __popcll(__ballot(key[q] >= cand));
+      if (lane == 0) cnt_w[bit & 1][wave] = cb;
+      __syncthreads();                         // slots alternate, so one barrier per bit
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) tot += cnt_w[bit & 1][w];
+      if (tot >= kk) th = cand;
+    }
+    uint32_t kmx = 0u;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) kmx = max(kmx, tmx[w]);
+    const float smax = key_f32(kmx);
+    bool gt[NK], eq[NK];
+    int epos[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      gt[q] = key[q] > th;
+      eq[q] = key[q] == th;
+    }
+    const int ngt_all = ordered_pos(1, gt, epos);
+    const int krem = kk - ngt_all;
+    __syncthreads();                           // wcnt[1] is reused
+    (void)ordered_pos(1, eq, epos);            // rank of each entry at theta in chunk order
+    bool sl[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) sl[q] = gt[q] || (eq[q] && epos[q] < krem);
+    __syncthreads();
+    (void)ordered_pos(1, sl, epos);            // output positions in chunk order
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      if (sl[q]) {
+        sel.sidx[epos[q]] = tid + NWV * 64 * q;
+        sel.ev[epos[q]] = exp2f((key_f32(key[q]) - smax) * zs);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {                             // weights; idx / w to memory
+    const float e = lane < kk ? sel.ev[lane] : 0.f;
+    const float sum = wave_sum(e);
+    const float wv2 = lane < kk ? e / sum : 0.f;
+    const int32_t xi = lane < kk ? sel.sidx[lane] : -1;
+    if (lane < a.k) { W[lane] = wv2; I[lane] = xi; }
+    sel.sw[lane] = wv2;
+    sel.sidx[lane] = xi;
+  }
+  __syncthreads();
+
+  // ---- chunk attention ----
+  const int jl = lane < a.k ? sel.sidx[lane] : -1;
+  const float wl = lane < a.k ? sel.sw[lane] : 0.f;
+  gather_pair<T, D, NWV>(a, bh, kvl, jl, wl, sp, wsum);
 }
 
 // Split over workgroups (few (sequence, head) pairs): one wave per slot, partials to memory.
@@ -1058,6 +1333,21 @@ bool decode_attend_whole(const DecodeArgs& a) { return sizeof(T) == 2 && a.B * a
 template <typename T>
 bool decode_select_fused(const DecodeArgs& a) { return a.cand != nullptr && decode_attend_whole<T>(a); }
 
+// The fused step: bf16, at least as many pairs as compute units, scores that fit in LDS.
+template <typename T>
+bool decode_fused_ok(const DecodeArgs& a) {
+  return sizeof(T) == 2 && a.B * a.H >= 256 && a.Nmax <= kFusedMaxChunks;
+}
+template <typename T, int D>
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t st) {
+  if (!decode_fused_ok<T>(a)) return hipErrorInvalidValue;
+  if (a.r > 0 && a.r % (16 / (int)sizeof(T)) == 0)
+    hipLaunchKernelGGL((decode_fused_kernel<T, D, true>), dim3(a.B * a.H), dim3(kFusedWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_fused_kernel<T, D, false>), dim3(a.B * a.H), dim3(kFusedWaves * 64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
@@ -1072,12 +1362,15 @@ hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template bool decode_fused_ok<bf16>(const DecodeArgs&);
+template bool decode_fused_ok<float>(const DecodeArgs&);
 template bool decode_select_fused<bf16>(const DecodeArgs&);
 template bool decode_select_fused<float>(const DecodeArgs&);
 template hipError_t launch_decode_tcode<bf16>(const bf16*, const bf16*, float*, int, int, int, hipStream_t);
 template hipError_t launch_decode_tcode<float>(const float*, const float*, float*, int, int, int, hipStream_t);
 #define HILS_DECODE_INST(T, D)                                                      \
   template hipError_t launch_decode_scores<T, D>(const DecodeArgs&, hipStream_t); \
+  template hipError_t launch_decode_fused<T, D>(const DecodeArgs&, hipStream_t); \
   template hipError_t launch_decode_attend<T, D>(const DecodeArgs&, hipStream_t);
 HILS_DECODE_INST(bf16, 64)
 HILS_DECODE_INST(bf16, 128)

@@ -249,6 +249,12 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   const bool cand = a.Nmax <= kDecodeCandMaxChunks;
   a.cand = cand ? static_cast<void*>(ws + L.cand) : nullptr;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
+  if (hils::decode_fused_ok<T>(a)) {           // scan, selection and attention in one kernel
+    if ((e = hils::launch_decode_fused<T, D>(a, st)) != hipSuccess) return e;
+    for (int s = 2; s <= 4; ++s)
+      if (ev && (e = hipEventRecord(ev[s], st)) != hipSuccess) return e;
+    return hipSuccess;
+  }
   if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   if (!hils::decode_select_fused<T>(a) && (e = hils::launch_decode_select(a, st)) != hipSuccess) return e;

@@ -94,6 +94,12 @@ hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int 
                                hipStream_t st);
 template <typename T, int D>
 hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st);
+// The whole step after the Q-Cal code in one kernel (one workgroup per (sequence, head)); only
+// when decode_fused_ok<T>(a).
+template <typename T>
+bool decode_fused_ok(const DecodeArgs& a);
+template <typename T, int D>
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st);
 // True when launch_decode_attend<T, D> performs the selection itself (launch_decode_select is
 // then skipped).

@@ -124,13 +124,16 @@ def test_decode_full_size_sampled(lib):
         _compare(sub, cfg, o[b:b + 1, h:h + 1], idx[b:b + 1, h:h + 1], w[b:b + 1, h:h + 1], [(0, 0)])
 
 
-# Whole-pair attention (one workgroup per (sequence, head)) is taken for bf16 once there are at
-# least 256 pairs: ragged caches there exercise empty slots and partial last chunks in it.
+# With bf16 and at least 256 (sequence, head) pairs the step runs as one fused kernel (one workgroup
+# per pair): ragged caches there exercise empty slots and partial last chunks in it.
 WHOLE = [
     synth.DecodeConfig("bf16_whole_ragged_d128", 4, 64, 3000, 128, 64, 64, "bf16", 32, 512,
                        kv_len=(3000, 1, 65, 2047)),
     synth.DecodeConfig("bf16_whole_ragged_d64", 8, 32, 1500, 64, 64, 16, "bf16", 16, 256,
                        kv_len=(1500, 64, 1, 777, 1024, 1100, 3, 1499)),
+    # Q-Cal rank not a multiple of the 8-element vectors (element-wise W_up reads), and no Q-Cal
+    synth.DecodeConfig("bf16_whole_rank12", 2, 128, 2000, 128, 64, 16, "bf16", 12, 256, kv_len=(2000, 700)),
+    synth.DecodeConfig("bf16_whole_noqcal", 4, 64, 1000, 64, 64, 8, "bf16", 0, 0, kv_len=(1000, 1, 64, 999)),
 ]
 
 

@@ -5,10 +5,13 @@
 // memory-bound: the step streams every landmark of every (sequence, head) once, then gathers the
 // k selected chunks' keys and values once.  Launches on the caller's stream:
 //   tcode   - Q-Cal code t_b = W_down h_b per sequence (skipped without Q-Cal);
-//   scores  - q~ = round(q + W_up t_b) per workgroup, then the landmark scan, coalesced 16-byte
-//             loads, sigma_j = q~ . lmk_j in fp32;
-//   select  - exact top-k per (sequence, head) (ties to the smaller chunk index), inter-chunk
-//             softmax, ascending output;
+//   fused   - bf16, at least 256 (sequence, head) pairs, up to 8192 chunks: one workgroup per
+//             pair forms q~ = round(q + W_up t_b), scores every landmark into LDS, selects the
+//             top-k (ties to the smaller chunk index) with the inter-chunk softmax, and gathers
+//             the selected chunks.  Otherwise three stages:
+//   scores  - q~ per workgroup, then the landmark scan, sigma_j = q~ . lmk_j in fp32; each
+//             workgroup keeps its own top-k (up to 8192 chunks) or writes its scores;
+//   select  - the exact top-k per (sequence, head), inter-chunk softmax, ascending output;
 //   attend  - per selected chunk: softmax of the raw query over the chunk's visible keys, the
 //             weighted partial w_j * o_j in fp32, summed in a fixed order (deterministic): in
 //             one workgroup per (sequence, head) when there are enough of them to fill the GPU,

@@ -77,7 +77,8 @@ typedef struct hils_prefill_params {
  * 1 <= max_kv_len <= 65535 * chunk; 0 <= qcal_rank <= 64; hidden a positive multiple of 128
  * when qcal_rank > 0.  A partial last chunk is allowed.  With at least 5 stage events, event 0 is
  * recorded first and events 1..4 after the Q-Cal, landmark-scoring, selection and
- * chunk-attention stages. */
+ * chunk-attention stages; for bf16 with batch*heads >= 256 and at most 8192 chunks these three
+ * stages run as one kernel, and events 2..4 are recorded together after it. */
 typedef struct hils_decode_params {
   int32_t batch, heads, max_kv_len, head_dim;
   int32_t chunk, topk;

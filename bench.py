@@ -243,6 +243,7 @@ def main():
             stage_p[s] += pev[i].elapsed_ms(s, s + 1)
         if D is not None:
             dec_ms += dec_ev[i][0].elapsed_time(dec_ev[i][1])
+    cold_ms = 0.0
     if D is not None:                          # stage breakdown (informational)
         for i in range(args.steps):
             run_decode(dev_ev[i])
@@ -250,6 +251,18 @@ def main():
         for i in range(args.steps):
             for s in range(4):
                 stage_d[s] += dev_ev[i].elapsed_ms(s, s + 1)
+        # Cold caches: a read sweep over 1 GiB evicts L2 and the 256 MB MALL before each step
+        # (a read leaves no dirty lines behind to be written back during the step).
+        sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        for i in range(args.steps):
+            torch.sum(sweep, dim=0, keepdim=True, out=sink)
+            dec_ev[i][0].record()
+            run_decode()
+            dec_ev[i][1].record()
+        torch.cuda.synchronize()
+        cold_ms = sum(dec_ev[i][0].elapsed_time(dec_ev[i][1]) for i in range(args.steps)) / args.steps
+        del sweep
     K = args.steps
     stage_p = [x / K for x in stage_p]
     stage_d = [x / K for x in stage_d]
@@ -282,6 +295,9 @@ def main():
         decode = dict(workload=dcfg.name, us_per_step=dms * 1e3, us_per_token=dms * 1e3 / dcfg.batch,
                       algorithmic_bytes=dbytes, GBps=dbytes / (dms * 1e-3) / 1e9,
                       frac_hbm=dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      cold_cache=dict(us_per_step=cold_ms * 1e3, GBps=dbytes / (cold_ms * 1e-3) / 1e9,
+                                      frac_hbm=dbytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                      note="after a read sweep of 1 GiB before each step"),
                       stages_us=dict(qcal=stage_d[0] * 1e3, scores=stage_d[1] * 1e3, select=stage_d[2] * 1e3,
                                      attend=stage_d[3] * 1e3,
                                      note="separate steps with an event between stages (the events "

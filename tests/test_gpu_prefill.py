@@ -156,3 +156,28 @@ def test_prefill_full_size_sampled(lib, name, per_head):
         inp["w_down"] = dev["w_down"].float().cpu().numpy()
         inp["w_up"] = dev["w_up"].float().cpu().numpy()
     _compare(inp, cfg, o, idx, w, rows)
+
+
+@pytest.mark.parametrize("name", ["prefill_512k_walk", "prefill_512k_iid"])
+def test_prefill_512k_sampled(lib, name):
+    """The 512K-token prefill (k = 64) in the benchmark's launch configuration: rows of three
+    heads against the oracle (only those heads are copied back)."""
+    torch = _torch()
+    cfg = synth.CONFIGS[name]
+    print(f"[case] full size {cfg}", flush=True)
+    dev = synth.make_prefill_inputs_torch(cfg, "cuda")
+    o, idx, w = _run(lib, dev, cfg)
+    torch.cuda.synchronize()
+    heads = [0, 13, cfg.heads - 1]
+    d = cfg.head_dim
+    rows = sample_rows(1, len(heads), cfg.seq_len, 10, seed=11)
+    sub = {key: dev[key][:, heads].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
+    pos = sorted({r[2] for r in rows})
+    h_sub = np.zeros((1, cfg.seq_len, cfg.hidden), dtype=np.float32)
+    h_sub[:, pos] = dev["h"][:, pos].float().cpu().numpy()
+    sub["h"] = h_sub
+    sub["w_down"] = dev["w_down"].float().cpu().numpy()
+    sub["w_up"] = np.concatenate([dev["w_up"][hh * d:(hh + 1) * d].float().cpu().numpy() for hh in heads])
+    sub_cfg = synth.PrefillConfig(cfg.name, 1, len(heads), cfg.seq_len, d, cfg.chunk, cfg.topk, cfg.dtype,
+                                  cfg.qcal_rank, cfg.hidden)
+    _compare(sub, sub_cfg, o[:, heads], idx[:, heads], w[:, heads], rows)

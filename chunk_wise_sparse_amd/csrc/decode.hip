@@ -390,225 +390,10 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
 // ------------------------------------------------------------------------------------------
 // Selection.
 // ------------------------------------------------------------------------------------------
-// Candidates that fit 32 per thread (n <= 8192), keys in registers.  The kk-th largest key
-// theta is at least tau, the kk-th largest of the 256 per-thread maxima (kk threads each hold a
-// key >= tau), so every selected chunk is among the candidates with key >= tau.  On spread-out
-// scores these are a few dozen: they are compacted into LDS and one wave finds theta among them
-// by bisection over the key bits (counts from ballots, no block barriers), takes the keys above
-// theta and the smallest indices at theta, and writes the chunks in ascending order with the
-// inter-chunk softmax.  If the candidates overflow the compaction buffer (heavy ties or adversarial
-// scores), the whole block bisects over all keys instead.  Both paths select the same set.
-constexpr int kSelReg = 8192;
-constexpr int kCandCap = 512;                  // 8 candidates per lane of the finishing wave
+constexpr int kCandCap = 512;                  // candidates the one-wave exact pass takes (8 per lane)
 
-// The selected chunks (one per lane < kk, any lane order) to ascending slots with their
-// weights; pads slots kk..k-1.  sx, ev: 64-entry LDS arrays of this wave.
-__device__ __forceinline__ void write_selection(const DecodeArgs& a, int bh, int kk, bool has, int x,
-                                                float sv, float smax, int* sx, float* ev) {
-  const int lane = threadIdx.x & 63;
-  sx[lane] = has ? x : INT32_MAX;
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  int rank = 0;
-#pragma unroll 8
-  for (int m = 0; m < 64; ++m) rank += sx[m] < x ? 1 : 0;   // distinct indices: ranks 0..kk-1
-  const float zs = a.scale * 1.4426950408889634f;
-  int32_t* I = a.idx + (size_t)bh * a.k;
-  float* W = a.w + (size_t)bh * a.k;
-  if (has) {
-    I[rank] = x;
-    ev[rank] = exp2f((sv - smax) * zs);
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  const float e = lane < kk ? ev[lane] : 0.f;
-  const float sum = wave_sum(e);
-  if (lane < kk) W[lane] = e / sum;
-  else if (lane < a.k) { W[lane] = 0.f; I[lane] = -1; }
-}
-
-// QB: the score buffer's blocks per record (decode_score_pos).
-template <int QB>
-__global__ __launch_bounds__(256) void decode_select_reg_kernel(const DecodeArgs a) {
-  __shared__ uint32_t tmax[256];
-  __shared__ uint32_t ckey[kCandCap];
-  __shared__ uint16_t cidx[kCandCap];
-  __shared__ int scratch[8];
-  __shared__ uint32_t kmax_w[4];
-  __shared__ int sx[64];
-  __shared__ uint32_t skey[64];
-  __shared__ float ev[64];
-  __shared__ uint32_t gtw[kSelReg / 32], eqw[kSelReg / 32];   // overflow path
-  __shared__ int cnt_w[2][4];
-  const int bh = blockIdx.x, b = bh / a.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  const int n = (kvl + kChunk - 1) / kChunk;
-  const int kk = min(a.k, n);
-  const float* G = a.scores + (size_t)bh * a.score_stride;
-  // Thread tid's keys: chunks x = tid + 256 i, i = 0..31; block i sits in record i / QB, slot
-  // i % QB.  All loads in flight at once (records clamped to the buffer; entries past n masked).
-  uint32_t key[32];
-  const int ymax = (int)(a.score_stride / (QB * kScoreBlock)) - 1;
-#pragma unroll
-  for (int y = 0; y < 32 / QB; ++y) {
-    const float* rec = G + ((size_t)min(y, ymax) * kScoreBlock + tid) * QB;
-    if constexpr (QB == 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(rec);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) key[4 * y + q] = f32_key(v[q]);
-    } else if constexpr (QB == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(rec);
-      key[2 * y] = f32_key(v.x);
-      key[2 * y + 1] = f32_key(v.y);
-    } else {
-      key[y] = f32_key(*rec);
-    }
-  }
-  uint32_t kmax = 0u;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (tid + 256 * i >= n) key[i] = 0u;       // 0 is below the key of every finite score
-    kmax = max(kmax, key[i]);
-  }
-  tmax[tid] = kmax;
-#pragma unroll
-  for (int mk = 32; mk >= 1; mk >>= 1) kmax = max(kmax, shfl_xor_u(kmax, mk));
-  if (lane == 0) kmax_w[wave] = kmax;
-  __syncthreads();
-  const float smax = key_f32(max(max(kmax_w[0], kmax_w[1]), max(kmax_w[2], kmax_w[3])));
-  uint32_t tm[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) tm[q] = tmax[lane + 64 * q];
-  const uint32_t tau = wave_kth_key(tm, kk);   // the same in every wave
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) c += key[i] >= tau ? 1 : 0;
-  int ncand;
-  int pos = block_exclusive_scan(c, scratch, ncand);
-  if (ncand <= kCandCap) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (key[i] >= tau) {
-        ckey[pos] = key[i];
-        cidx[pos] = (uint16_t)(tid + 256 * i);
-        ++pos;
-      }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    uint32_t ck[kCandCap / 64];
-    int cx[kCandCap / 64];
-#pragma unroll
-    for (int q = 0; q < kCandCap / 64; ++q) {
-      const int p = lane + 64 * q;
-      ck[q] = p < ncand ? ckey[p] : 0u;
-      cx[q] = p < ncand ? (int)cidx[p] : INT32_MAX;
-    }
-    const uint32_t th = wave_kth_key(ck, kk);
-    int ngt = 0;
-#pragma unroll
-    for (int q = 0; q < kCandCap / 64; ++q) ngt += __popcll(__ballot(ck[q] > th));
-    bool sel[kCandCap / 64];
-#pragma unroll
-    for (int q = 0; q < kCandCap / 64; ++q) sel[q] = ck[q] > th;
-    for (int t = ngt; t < kk; ++t) {           // at theta: the smallest remaining index, kk - ngt times
-      int mn = INT32_MAX;
-#pragma unroll
-      for (int q = 0; q < kCandCap / 64; ++q) mn = min(mn, (ck[q] == th && !sel[q]) ? cx[q] : INT32_MAX);
-#pragma unroll
-      for (int mk = 32; mk >= 1; mk >>= 1) mn = min(mn, shfl_xor_i(mn, mk));
-#pragma unroll
-      for (int q = 0; q < kCandCap / 64; ++q) sel[q] = sel[q] || (ck[q] == th && cx[q] == mn);
-    }
-    // One selected chunk per lane: compact by ballot prefix.
-    int slot = 0;
-    bool has = false;
-    int x = 0;
-    uint32_t xk = 0u;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int q = 0; q < kCandCap / 64; ++q) {
-      const uint64_t bq = __ballot(sel[q]);
-      const int at = slot + __popcll(bq & below);
-      slot += __popcll(bq);
-      if (sel[q]) { sx[at] = cx[q]; skey[at] = ck[q]; }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    has = lane < kk;
-    if (has) { x = sx[lane]; xk = skey[lane]; }
-    __builtin_amdgcn_wave_barrier();
-    write_selection(a, bh, kk, has, has ? x : INT32_MAX, key_f32(xk), smax, sx, ev);
-    return;
-  }
-  // Overflow: theta over all keys (block-wide counts, one barrier per bit), then bitmaps of the
-  // keys > theta and == theta; the wave's 64 lanes cover 64 consecutive chunks.
-  uint32_t th = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
-    int cb = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cb += __popcll(__ballot(key[i] >= cand));
-    if (lane == 0) cnt_w[bit & 1][wave] = cb;
-    __syncthreads();                           // slots alternate, so one barrier per bit
-    const int tot = (cnt_w[bit & 1][0] + cnt_w[bit & 1][1]) + (cnt_w[bit & 1][2] + cnt_w[bit & 1][3]);
-    if (tot >= kk) th = cand;
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint64_t g = __ballot(key[i] > th);
-    const uint64_t e = __ballot(key[i] == th);
-    if (lane == 0) {
-      const int w0 = (256 * i + 64 * wave) >> 5;
-      gtw[w0] = (uint32_t)g;
-      gtw[w0 + 1] = (uint32_t)(g >> 32);
-      eqw[w0] = (uint32_t)e;
-      eqw[w0 + 1] = (uint32_t)(e >> 32);
-    }
-  }
-  __syncthreads();
-  // Thread t owns chunks 32t .. 32t+31 (ascending).
-  const uint32_t gw = gtw[tid], ew = eqw[tid];
-  int ngt_total;
-  (void)block_exclusive_scan(__popc(gw), scratch, ngt_total);
-  const int krem = kk - ngt_total;             // entries == theta to take, smallest first
-  int tot;
-  const int eq_before = block_exclusive_scan(__popc(ew), scratch, tot);
-  const int take = max(0, min(__popc(ew), krem - eq_before));
-  uint32_t ek = 0u, rest = ew;
-  for (int t = 0; t < take; ++t) {
-    ek |= rest & (~rest + 1u);                 // lowest remaining set bit
-    rest &= rest - 1u;
-  }
-  uint32_t sel = gw | ek;
-  int p = block_exclusive_scan(__popc(sel), scratch, tot);
-  const float zs = a.scale * 1.4426950408889634f;
-  int32_t* I = a.idx + (size_t)bh * a.k;
-  float* W = a.w + (size_t)bh * a.k;
-  while (sel) {
-    const int bt = __builtin_ctz(sel);
-    sel &= sel - 1u;
-    const int x = 32 * tid + bt;
-    I[p] = x;
-    ev[p] = exp2f((G[decode_score_pos(x, QB)] - smax) * zs);
-    ++p;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const float e = tid < kk ? ev[tid] : 0.f;
-    const float sum = wave_sum(e);
-    if (tid < kk) W[tid] = e / sum;
-    else if (tid < a.k) { W[tid] = 0.f; I[tid] = -1; }
-  }
-}
-
-// Candidate lists (n <= 8192): the scan workgroups' top-kk lists, concatenated in workgroup
-// order, hold the selection's chunks in chunk order.  Up to kCandCap of them: one wave finds
-// theta, the kk-th largest key, by bisection over the key bits, keeps the keys above theta and the
-// earliest (smallest-chunk) entries at theta, and writes them in list order, which is ascending
-// chunk order, with the inter-chunk softmax.  Longer lists (heavy ties) go block-wide: each
-// thread takes a contiguous stretch of the list, theta by bisection with block counts, then the
-// same rule through block scans.
+// Candidate slots (n <= 8192): the scan workgroups' top-kk lists, one 64-entry slot each in
+// workgroup order, hold the selection's chunks in chunk order; one wave merges them.
 struct CandSelSmem {
   float ev[64];
   int32_t sidx[64];                            // the selection, also left in LDS: chunk indices,
@@ -1318,15 +1103,9 @@ hipError_t launch_decode_scores(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {
   if (a.cand != nullptr) {
     hipLaunchKernelGGL(decode_select_cand_kernel, dim3(a.B * a.H), dim3(64), 0, st, a);
-  } else if (a.Nmax <= kSelReg) {
-    if (a.score_qb == 4)
-      hipLaunchKernelGGL(decode_select_reg_kernel<4>, dim3(a.B * a.H), dim3(256), 0, st, a);
-    else if (a.score_qb == 2)
-      hipLaunchKernelGGL(decode_select_reg_kernel<2>, dim3(a.B * a.H), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(decode_select_reg_kernel<1>, dim3(a.B * a.H), dim3(256), 0, st, a);
-  } else
+  } else {                                     // dense scores (caches of more than 8192 chunks)
     hipLaunchKernelGGL(decode_select_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 // bf16: whole-pair workgroups once there are at least as many pairs as compute units; they

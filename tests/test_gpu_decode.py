@@ -214,3 +214,19 @@ def test_decode_tied_scores_whole_pair(lib):
             np.testing.assert_array_equal(got[b, h], np.arange(cfg.topk), err_msg=str((b, h)))
             np.testing.assert_allclose(gw[b, h], 1.0 / cfg.topk, rtol=1e-6, err_msg=str((b, h)))
     _compare(inp, cfg, o, idx, w, [(0, 0), (1, 77), (1, 127)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_long_cache_dense_scores(lib, dtype):
+    """Caches of more than 8192 chunks: dense landmark scores and the radix selection."""
+    cfg = synth.DecodeConfig(f"long_cache_{dtype}", 1, 2, 600000, 64, 64, 64, dtype, 8, 128,
+                             kv_len=(599937,), needles=4)
+    print(f"[case] decode {cfg}", flush=True)
+    inp = synth.make_decode_inputs_np(cfg)
+    o, idx, w = _run(_to_dev(inp, cfg.dtype), cfg)
+    _torch().cuda.synchronize()
+    pairs = [(0, h) for h in range(cfg.heads)]
+    _compare(inp, cfg, o, idx, w, pairs)
+    got = idx.cpu().numpy()
+    for b, h in pairs:
+        assert set(inp["needle_ids"][b, h]) <= set(got[b, h]), (b, h)

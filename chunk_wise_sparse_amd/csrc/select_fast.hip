@@ -1,4 +1,5 @@
-// Chunk selection for prefill, bf16 with k <= 32: one wave per 64-query tile.
+// Chunk selection for prefill, bf16 with k <= 32: one wave per 64-query tile, eight tiles per
+// workgroup.
 //
 // Method: [HiLS-Attention model page, "Model Description"] every query scores all causal chunks
 // through their landmark keys, keeps the k best and weights them with a softmax over those
@@ -7,21 +8,25 @@
 // chunk order with -1 / 0 padding when fewer than k chunks exist.
 //
 // With C = 64 the 64 queries of tile c share the candidate set {0..c}, so scoring is a GEMM
-// [64 queries x d] x [d x (c+1)] done with v_mfma_f32_32x32x16_bf16: A = 32 landmark rows loaded
-// straight from global memory (each landmark is used by this wave only, so no LDS staging),
-// B = q~ of 32 queries (registers, two column blocks).  The output of block jb holds, at lane
-// (col, half), query column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap
-// per element pair moves both halves of a query's 32 rows into one lane, so lane l owns query
+// [64 queries x d] x [d x (c+1)] done with v_mfma_f32_32x32x16_bf16: A = 32 landmark rows,
+// B = q~ of 32 queries (registers, two column blocks).  The eight tiles of a workgroup are
+// consecutive chunks of one (batch, head), so they need the same landmark blocks: each block is
+// loaded once, straight from global memory into an LDS ring (global_load_lds_dwordx4, no
+// registers), and read by all eight waves.  The output of block jb holds, at lane (col, half),
+// query column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap per element
+// pair moves both halves of a query's 32 rows into one lane, so lane l owns query
 // 32*(l/32) + l%32 and all of its scores.
 //
 // Exact top-k in two passes over the landmarks:
 //   pass 1: per slot (landmark row within a 32-row block) the two largest scores; the kq-th
 //           largest of these 64 values is reached by at least kq distinct chunks, so it bounds
-//           the kq-th largest score from below (tau).  Skipped when all candidates fit LDS.
+//           the kq-th largest score from below (tau).  Skipped when all candidates fit the
+//           list.
 //   pass 2: every score >= tau is appended, in ascending chunk order, to the query's LDS list
 //           ([position][query] so the 64 lanes write distinct banks).  A list that could
-//           overflow is cut to its exact top-kq first and tau is raised above the cut value
-//           (later chunks lose ties); with the tight tau of pass 1 this is rare.
+//           overflow is cut to its exact top-kq first (from a register copy of its keys) and
+//           tau is raised above the cut value (later chunks lose ties); with the tight tau of
+//           pass 1 this is rare.
 //   final:  the kq-th largest theta of the list; entries > theta and the first (kq - #>theta)
 //           entries == theta are kept in list order, then the inter-chunk softmax.
 // Scores are finite by contract: this file is compiled with -fno-honor-nans, so max/min skip
@@ -39,7 +44,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kCap = 48;   // list capacity per query (>= kq + 16 for kq <= 32)
+constexpr int kCap = 47;   // list capacity per query (>= kq + 8 for kq <= 32)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -91,40 +96,60 @@ __device__ __forceinline__ float pick(const float (&x)[N], int kk) {
   return r;
 }
 
+// Tiles per workgroup: wave w takes the 64-query tile of chunk c_top - w, so the eight tiles of a
+// workgroup are consecutive chunks of one (batch, head) and need the same landmark blocks.
+constexpr int kTiles = 8;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Landmark rows in the ring are stored with their 16-byte vectors permuted (vector v of row r at
+// position v ^ ring_swz(r)), so that the 16 rows of one MFMA operand read fall on distinct banks.
 template <int D>
-struct FastSmem {
+__device__ __forceinline__ int ring_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int D>
+struct GroupSmem {
+  static constexpr int RB = 2 * D;             // landmark row bytes
   static constexpr int QLD = D + 8;            // q~ staging row stride (elements)
+  alignas(16) char ring[2][32 * RB];           // 32-landmark blocks, even / odd block index
   union {
-    bf16 qt[64 * QLD];                         // q~ [query][d], before the passes
+    bf16 qt[64 * QLD];                         // q~ [query][d], before the sweeps
     struct {
       float s[kCap * 64];                      // [position][query] candidate scores
       uint16_t j[kCap * 64];                   // [position][query] candidate chunks
     } list;
-  };
+  } w[kTiles];
 };
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
+__global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectArgs a) {
   constexpr int NS = D / 16;                   // MFMA k-steps over d
-  typedef FastSmem<D> Smem;
+  typedef GroupSmem<D> Smem;
   __shared__ Smem sm;
 
-  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
-  const uint32_t total = (uint32_t)a.B * a.H * a.N;
-  const uint32_t tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / a.N;
-  const int c = a.N - 1 - (int)(tile % a.N);   // longest tiles first
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int G = (a.N + kTiles - 1) / kTiles;   // tile groups per (batch, head)
+  const uint32_t total = (uint32_t)a.B * a.H * G;
+  const uint32_t grp = xcd_remap(blockIdx.x, total);
+  const int bh = grp / G;
+  const int c_top = a.N - 1 - kTiles * (int)(grp % G);   // longest groups first
+  // A wave past chunk 0 (N not a multiple of kTiles) runs tile 0 again and writes nothing.
+  const bool active = c_top - wave >= 0;
+  const int c = max(c_top - wave, 0);
   const int b = bh / a.H, hd = bh % a.H;
   const int n_cand = c + 1;
-  const int nb = (n_cand + 31) >> 5;           // 32-landmark blocks
+  const int nb = (n_cand + 31) >> 5;           // this tile's 32-landmark blocks
+  const int nbg = (c_top + 1 + 31) >> 5;       // blocks the group sweeps
   const int kq = min(a.k, n_cand);
   const int q0 = c * 64;
   const bf16* Q = static_cast<const bf16*>(a.q) + (size_t)bh * a.L * D;
   const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)bh * a.N * D;
-  float* ls = &sm.list.s[lane];                // this lane's list, stride 64
-  uint16_t* lj = &sm.list.j[lane];
+  float* ls = &sm.w[wave].list.s[lane];        // this lane's list, stride 64
+  uint16_t* lj = &sm.w[wave].list.j[lane];
 
   // ---------------- q~ as the B operand: query 32 cb + col, d = 16 s + 8 half + z -----------
   bf16x8 qf[2][NS];
@@ -171,6 +196,7 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
       }
     }
     const bf16* WU = static_cast<const bf16*>(a.w_up) + (size_t)hd * D * a.r;
+    bf16* qt = sm.w[wave].qt;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       f32x16 acc[2] = {};
@@ -206,7 +232,7 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
           bf16x4 o;
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[i] = bf16_rne(to_f32(qv[i]) + acc[cb][4 * a4 + i]);
-          *reinterpret_cast<bf16x4*>(&sm.qt[qr * Smem::QLD + d0]) = o;
+          *reinterpret_cast<bf16x4*>(&qt[qr * Smem::QLD + d0]) = o;
         }
       }
     }
@@ -215,8 +241,7 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        qf[cb][s] = *reinterpret_cast<const bf16x8*>(&sm.qt[(32 * cb + col) * Smem::QLD + 16 * s + 8 * half]);
-    __syncthreads();                           // the candidate lists reuse this memory
+        qf[cb][s] = *reinterpret_cast<const bf16x8*>(&qt[(32 * cb + col) * Smem::QLD + 16 * s + 8 * half]);
   } else {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -225,13 +250,40 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
         qf[cb][s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)(q0 + 32 * cb + col) * D + 16 * s + 8 * half);
   }
 
+  // ---------------- landmark ring ------------------------------------------------------------
+  // Block jb (landmark rows 32 jb .. 32 jb + 31, clamped to the group's last candidate) is
+  // loaded straight into ring slot jb & 1, one 16-byte vector per thread (D = 128) or per thread
+  // of waves 0-3 (D = 64); lane l of a wave lands at the wave's 1 KiB piece + 16 l.
+  auto issue = [&](int jb, int slot) {
+    constexpr int VPR = D / 8;                 // vectors per row
+    if (D == 128 || wave < 4) {
+      const int r = tid / VPR, p = tid % VPR;
+      const int row = min(32 * jb + r, c_top);
+      const bf16* src = LM + (size_t)row * D + 8 * (p ^ ring_swz<D>(r));
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(sm.ring[slot] + 1024 * wave), 16, 0, 0);
+    }
+  };
+  // The group walks its blocks in order; f(jb, block) runs once the block is in LDS, while the
+  // next block is in flight.  Every wave takes every barrier; f skips blocks past its tile.
+  auto sweep = [&](auto&& f) {
+    __syncthreads();                           // no wave still reads the ring
+    issue(0, 0);
+    for (int jb = 0; jb < nbg; ++jb) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();                         // block jb is in LDS; slot (jb + 1) & 1 is free
+      if (jb + 1 < nbg) issue(jb + 1, (jb + 1) & 1);
+      f(jb, sm.ring[jb & 1]);
+    }
+  };
+
   // ---------------- scoring of one 32-landmark block ---------------------------------------
-  // A operand rows past the last candidate repeat the last landmark; their scores are masked.
-  auto load_a = [&](int jb, bf16x8 (&af)[NS]) {
-    const int row = min(32 * jb + col, n_cand - 1);
-    const bf16* p = LM + (size_t)row * D + 8 * half;
+  // A operand: lane (col, half) takes row col, d = 16 s + 8 half .. + 7.  Rows past the last
+  // candidate hold later landmarks or repeat the group's last one; their scores are masked.
+  auto read_a = [&](const char* blk, bf16x8 (&af)[NS]) {
+    const char* rp = blk + col * Smem::RB;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) af[s] = *reinterpret_cast<const bf16x8*>(p + 16 * s);
+    for (int s = 0; s < NS; ++s)
+      af[s] = *reinterpret_cast<const bf16x8*>(rp + 16 * ((2 * s + half) ^ ring_swz<D>(col)));
   };
   auto mma_block = [&](const bf16x8 (&af)[NS], f32x16& acc0, f32x16& acc1) {
     acc0 = f32x16{};
@@ -250,26 +302,27 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
     constexpr bool last = decltype(last_block)::value;
     const int lim = n_cand - 32 * jb;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
+    for (int grp4 = 0; grp4 < 4; ++grp4) {
       float x[4], y[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int e = 4 * grp + t;
+        const int e = 4 * grp4 + t;
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[e]), __float_as_uint(acc1[e]),
                                                         false, false);
-        x[t] = __uint_as_float(r[0]);          // row 8 grp + t
-        y[t] = __uint_as_float(r[1]);          // row 8 grp + 4 + t
+        x[t] = __uint_as_float(r[0]);          // row 8 grp4 + t
+        y[t] = __uint_as_float(r[1]);          // row 8 grp4 + 4 + t
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) f(8 * grp + t, (last && 8 * grp + t >= lim) ? -INFINITY : x[t]);
+      for (int t = 0; t < 4; ++t) f(8 * grp4 + t, (last && 8 * grp4 + t >= lim) ? -INFINITY : x[t]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) f(8 * grp + 4 + t, (last && 8 * grp + 4 + t >= lim) ? -INFINITY : y[t]);
+      for (int t = 0; t < 4; ++t) f(8 * grp4 + 4 + t, (last && 8 * grp4 + 4 + t >= lim) ? -INFINITY : y[t]);
     }
   };
 
   // ---------------- pass 1: lower bound tau of the kq-th largest score ---------------------
   float tau = -FLT_MAX;                        // every finite score passes; masked ones do not
-  if (n_cand > kCap) {
+  if (c_top + 1 > kCap) {                      // group-uniform: some tile has more than kCap
+    const bool mine = n_cand > kCap;
     float m1[32], m2[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) m1[i] = m2[i] = -INFINITY;
@@ -277,60 +330,66 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
       m2[i] = __builtin_amdgcn_fmed3f(m1[i], m2[i], v);
       m1[i] = fmaxf(m1[i], v);
     };
-    bf16x8 af[NS];
-    load_a(0, af);
-    f32x16 acc0, acc1;
-    for (int jb = 0; jb < nb - 1; ++jb) {
+    sweep([&](int jb, const char* blk) {
+      if (!mine || jb >= nb) return;
+      bf16x8 af[NS];
+      read_a(blk, af);
+      f32x16 acc0, acc1;
       mma_block(af, acc0, acc1);
-      load_a(jb + 1, af);                      // in flight during this block's VALU work
-      for_scores(std::false_type{}, jb, acc0, acc1, top2);
-    }
-    mma_block(af, acc0, acc1);
-    for_scores(std::true_type{}, nb - 1, acc0, acc1, top2);
-    // Top 32 of the 64 slot values: merge the sorted halves, then pick the kq-th.
-    sort_desc<32>(m1);
-    sort_desc<32>(m2);
+      if (jb == nb - 1) for_scores(std::true_type{}, jb, acc0, acc1, top2);
+      else for_scores(std::false_type{}, jb, acc0, acc1, top2);
+    });
+    if (mine) {
+      // Top 32 of the 64 slot values: merge the sorted halves, then pick the kq-th.
+      sort_desc<32>(m1);
+      sort_desc<32>(m2);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) m1[i] = fmaxf(m1[i], m2[31 - i]);
-    bitonic_merge_desc<32>(m1);
-    tau = pick<32>(m1, kq);
+      for (int i = 0; i < 32; ++i) m1[i] = fmaxf(m1[i], m2[31 - i]);
+      bitonic_merge_desc<32>(m1);
+      tau = pick<32>(m1, kq);
+    }
   }
 
   // ---------------- pass 2: collect the candidates ------------------------------------------
   int cnt = 0;
   {
-    // Make room for the block's passing scores: a list that would overflow is cut to its exact
-    // top kq first (rare: lists end near kq + a few).  theta = kq-th largest key, bit by bit
-    // from the top, counting list entries in LDS; entries > theta and the first
-    // kq - #(> theta) entries == theta stay, in list order.
+    // Make room for the next 8 scores: a list that would overflow is cut to its exact top kq
+    // first (rare: lists end near kq + a few).  theta = kq-th largest key, bit by bit from the
+    // top, counting list entries in LDS; entries > theta and the first kq - #(> theta)
+    // entries == theta stay, in list order.
     auto make_room = [&](const float (&sc)[32], int h0) {
-      if (__any(cnt + 16 > kCap)) {
+      if (__any(cnt + 8 > kCap)) {
         int np = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) np += sc[h0 + i] >= tau ? 1 : 0;
+        for (int i = 0; i < 8; ++i) np += sc[h0 + i] >= tau ? 1 : 0;
         if (cnt + np > kCap) {
+          // The list's keys in registers (-inf past its end), then theta bit by bit.
+          uint32_t key[kCap];
+#pragma unroll
+          for (int i = 0; i < kCap; ++i) key[i] = f32_key(i < cnt ? ls[64 * i] : -INFINITY);
           uint32_t th = 0u;
           for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = th | (1u << bit);
             int n = 0;
-            for (int i = 0; i < cnt; ++i) n += f32_key(ls[64 * i]) >= cand ? 1 : 0;
+#pragma unroll
+            for (int i = 0; i < kCap; ++i) n += key[i] >= cand ? 1 : 0;
             if (n >= kq) th = cand;
           }
-          const float theta = key_f32(th);
           int ngt = 0;
-          for (int i = 0; i < cnt; ++i) ngt += ls[64 * i] > theta ? 1 : 0;
+#pragma unroll
+          for (int i = 0; i < kCap; ++i) ngt += key[i] > th ? 1 : 0;
           const int m_eq = kq - ngt;
           int w = 0, eq = 0;
-          for (int i = 0; i < cnt; ++i) {
-            const float sv = ls[64 * i];
-            const uint16_t jv = lj[64 * i];
-            bool keep = sv > theta;
-            if (sv == theta) {
+#pragma unroll
+          for (int i = 0; i < kCap; ++i) {
+            bool keep = key[i] > th;
+            if (i < cnt && key[i] == th) {
               keep = eq < m_eq;
               ++eq;
             }
-            if (keep) {
-              ls[64 * w] = sv;
+            if (keep) {                        // w <= i: entries move towards the front
+              const uint16_t jv = lj[64 * i];
+              ls[64 * w] = key_f32(key[i]);
               lj[64 * w] = jv;
               ++w;
             }
@@ -342,10 +401,10 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
     };
     auto collect = [&](int jb, const float (&sc)[32]) {
 #pragma unroll
-      for (int h0 = 0; h0 < 32; h0 += 16) {    // at most 16 appends after each check
+      for (int h0 = 0; h0 < 32; h0 += 8) {     // at most 8 appends after each check
         make_room(sc, h0);
 #pragma unroll
-        for (int i = h0; i < h0 + 16; ++i) {
+        for (int i = h0; i < h0 + 8; ++i) {
           if (sc[i] >= tau) {
             ls[64 * cnt] = sc[i];
             lj[64 * cnt] = (uint16_t)(32 * jb + i);
@@ -354,20 +413,18 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
         }
       }
     };
-    bf16x8 af[NS];
-    load_a(0, af);
-    f32x16 acc0, acc1;
     float sc[32];
     auto keep = [&](int i, float v) { sc[i] = v; };
-    for (int jb = 0; jb < nb - 1; ++jb) {
+    sweep([&](int jb, const char* blk) {
+      if (jb >= nb) return;
+      bf16x8 af[NS];
+      read_a(blk, af);
+      f32x16 acc0, acc1;
       mma_block(af, acc0, acc1);
-      load_a(jb + 1, af);
-      for_scores(std::false_type{}, jb, acc0, acc1, keep);
+      if (jb == nb - 1) for_scores(std::true_type{}, jb, acc0, acc1, keep);
+      else for_scores(std::false_type{}, jb, acc0, acc1, keep);
       collect(jb, sc);
-    }
-    mma_block(af, acc0, acc1);
-    for_scores(std::true_type{}, nb - 1, acc0, acc1, keep);
-    collect(nb - 1, sc);
+    });
   }
 
   // ---------------- final top-kq and inter-chunk softmax ------------------------------------
@@ -407,6 +464,7 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
       kept[i] = keep;
     }
   }
+  if (!active) return;
   const float zs = a.scale * 1.4426950408889634f;   // scale * log2(e)
   float esum = 0.f;
 #pragma unroll
@@ -434,8 +492,8 @@ __global__ __launch_bounds__(64) void select_fast_kernel(const SelectArgs a) {
 
 template <int D>
 hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st) {
-  const uint32_t total = (uint32_t)a.B * a.H * a.N;
-  hipLaunchKernelGGL((select_fast_kernel<D>), dim3(total), dim3(64), 0, st, a);
+  const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + kTiles - 1) / kTiles);
+  hipLaunchKernelGGL((select_fast_kernel<D>), dim3(groups), dim3(64 * kTiles), 0, st, a);
   return hipGetLastError();
 }
 

@@ -81,6 +81,19 @@ def test_prefill_two_pass_selection(lib):
     _compare(inp, cfg, o, idx, w, sample_rows(1, 2, cfg.seq_len, 160, seed=1))
 
 
+def test_prefill_ragged_tile_groups(lib):
+    """203 chunks: the last group of eight 64-query tiles has five idle waves, and the long
+    tiles take the lower-bound pass; rows of the first three chunks (the short group) are all
+    checked."""
+    cfg = synth.PrefillConfig("bf16_203chunks_k32", 1, 2, 64 * 203, 128, 64, 32, "bf16", 16, 256)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    rows = sample_rows(1, 2, cfg.seq_len, 96, seed=6)
+    rows = sorted(set(rows) | {(0, h, i) for h in range(2) for i in range(0, 3 * 64, 5)})
+    _compare(inp, cfg, o, idx, w, rows)
+
+
 def test_prefill_two_pass_k64(lib):
     cfg = synth.PrefillConfig("bf16_16k_k64", 1, 1, 16384, 64, 64, 64, "bf16", 8, 128)
     print(f"[case] {cfg}", flush=True)

@@ -106,34 +106,34 @@ def calib_copy(nbytes=1 << 30, reps=3):
 
 def union_stats(P, cfg, dev):
     """Chunk-union statistics of one prefill's selection (idx written): mean fraction of a row's
-    chunks also chosen by the previous row, distinct chunks per 32-row wave block and per
+    chunks also chosen by the previous row, distinct chunks per 16-row wave block and per
     128-row workgroup, and the attention FLOP the kernel executes (a wave computes every chunk
-    any of its 32 rows selected, for all 32 rows)."""
+    any of its 16 rows selected, for all 16 rows)."""
     import torch
     from chunk_wise_sparse_amd import hils
     _, idx, _ = hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
                              topk=cfg.topk, return_selection=True)
     torch.cuda.synchronize()
     B, H, L, k = idx.shape
-    overlap, u32, u128 = 0.0, 0.0, 0.0
+    overlap, u16, u128 = 0.0, 0.0, 0.0
     for b in range(B):
         for h in range(H):
             x = idx[b, h].long()
             a, pr = x[1:], x[:-1]
             inter = ((a.unsqueeze(-1) == pr.unsqueeze(-2)) & (a.unsqueeze(-1) >= 0)).any(-1).sum(-1).float()
             overlap += (inter / (a >= 0).sum(-1).float()).mean().item()
-            for m, acc in ((32, "u32"), (128, "u128")):
+            for m, acc in ((16, "u16"), (128, "u128")):
                 s, _ = torch.sort(x.reshape(L // m, m * k), dim=-1)
                 distinct = ((s[:, 1:] != s[:, :-1]) & (s[:, 1:] >= 0)).sum(-1) + (s[:, 0] >= 0).long()
-                if acc == "u32":
-                    u32 += distinct.float().sum().item()
+                if acc == "u16":
+                    u16 += distinct.float().sum().item()
                 else:
                     u128 += distinct.float().sum().item()
     n_bh = B * H
     del idx
-    executed = u32 * 32 * 4 * cfg.chunk * cfg.head_dim      # FLOP: chunk-steps x rows x 4 C d
+    executed = u16 * 16 * 4 * cfg.chunk * cfg.head_dim      # FLOP: chunk-steps x rows x 4 C d
     return dict(adjacent_overlap=overlap / n_bh,
-                union_per_32_rows=u32 / n_bh / (L // 32), union_per_128_rows=u128 / n_bh / (L // 128),
+                union_per_16_rows=u16 / n_bh / (L // 16), union_per_128_rows=u128 / n_bh / (L // 128),
                 executed_attention_flop=executed)
 
 
@@ -309,6 +309,23 @@ def main():
         print("[bench] union statistics of one selection", file=sys.stderr, flush=True)
         ustats = union_stats(P, pcfg, dev)
         ustats["executed_over_algorithmic"] = ustats["executed_attention_flop"] / work["attention"]
+        # The same workload with i.i.d. N(0, 1) queries: adjacent rows share few chunks, so the
+        # union of a query group (and the attention kernel's executed work) grows towards k per
+        # row.  Informational: two timed prefills and the same union statistics.
+        print("[bench] i.i.d. queries: union statistics and two timed prefills", file=sys.stderr, flush=True)
+        gq = torch.Generator(device=dev).manual_seed(2024)
+        Pi = dict(P, q=torch.randn(P["q"].shape, generator=gq, device=dev).to(P["q"].dtype))
+        istats = union_stats(Pi, pcfg, dev)
+        istats["executed_over_algorithmic"] = istats["executed_attention_flop"] / work["attention"]
+        iev = [hils.StageEvents(4) for _ in range(2)]
+        for e in iev:
+            hils.prefill(Pi["q"], Pi["k"], Pi["v"], Pi["lmk"], Pi["h"], Pi["w_down"], Pi["w_up"],
+                         topk=pcfg.topk, out=o, workspace=pws, events=e)
+        torch.cuda.synchronize()
+        ist = [sum(e.elapsed_ms(s, s + 1) for e in iev) / len(iev) for s in range(3)]
+        istats.update(prefill_ms=sum(ist), qcal_code_ms=ist[0], select_ms=ist[1], attention_ms=ist[2])
+        ustats["iid_queries"] = istats
+        del Pi
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -6,13 +6,16 @@
 // with the inter-chunk weights.  Because every chunk's softmax is normalised on its own, the
 // fused output is sum_j (w_j / l_j) * sum_t exp(a_t - m_j) v_t: no rescaling across chunks.
 //
-// Kernel (the pages' "load the union once" idea, designed afresh for wave64/MFMA): a workgroup
-// takes 32*NW consecutive queries of one (batch, head) - several 64-query chunks - and walks the
-// union of their selected chunks in ascending order.  Each union chunk's K and V are staged once
-// in LDS and shared by all waves.  Wave w owns rows 32w..32w+31 as two 16-row blocks and skips a
-// chunk that none of its 32 rows selected; otherwise both blocks run (branch-free, so the two
-// blocks' MFMA and softmax work interleave), a block's rows that did not select the chunk get
-// weight 0.
+// Kernels (the pages' "load the union once" idea, designed afresh for wave64/MFMA): a workgroup
+// takes consecutive queries of one (batch, head) - several 64-query chunks - and walks the union
+// of their selected chunks in ascending order.  Each union chunk's K and V are staged once in
+// LDS and shared by all waves.
+//   chunk_attention_block_kernel (bf16, k <= 32): 128 queries, eight waves of one 16-row MFMA
+//     block each; a wave computes the chunks its 16 rows selected.
+//   chunk_attention_kernel (fp32, k > 32): wave w owns rows 32w..32w+31 as two 16-row blocks
+//     and skips a chunk that none of its 32 rows selected; otherwise both blocks run
+//     (branch-free, so the two blocks' MFMA and softmax work interleave).
+// Rows of a block that did not select the chunk get weight 0.
 //   S^T[key][q] = K . Q^T  : A = K rows (LDS), B = raw q (registers);
 //                            lane (m, g) holds query m and keys 16*kb + 4g + rr;
 //   O^T[d][q] += V^T . P'^T: A = V^T via LDS transpose reads, B = P' = p * (w_j / l_j).
@@ -75,7 +78,8 @@ __device__ __forceinline__ float v_frag_f32(const char* vbuf, int lane16, int g,
 }
 
 template <typename T, int D, int NW, int KMAX, int STAGES>
-__global__ __launch_bounds__(NW * 64, STAGES == 1 ? 2 : 1) void chunk_attention_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnArgs a) {
+  static_assert(STAGES == 2, "two LDS stages");
   constexpr int QG = 32 * NW;                // queries per workgroup
   typedef AttnSmem<T, D, QG, KMAX, STAGES> Smem;
   typedef AttnLayout<T, D> Lay;
@@ -316,56 +320,31 @@ __global__ __launch_bounds__(NW * 64, STAGES == 1 ? 2 : 1) void chunk_attention_
   };
   // Loads and stores below are unconditional (past the end of the union they repeat its last
   // chunk) so that the compiler's wait counts stay exact across the loop.
-  if constexpr (STAGES == 2) {
-    // Iteration t computes c_t from stage t%2 while c_{t+1} sits in register set (t+1)%2 and
-    // c_{t+2} is loaded into set t%2; after the compute the registers of c_{t+1} go to stage
-    // (t+1)%2 and one barrier publishes them.
-    u32x4 kr[2][NV], vr[2][NV];
-    if (U > 0) {
-      const int c0 = advance();
-      load_kv(c0, kr[0], vr[0]);
+  // Iteration t computes c_t from stage t%2 while c_{t+1} sits in register set (t+1)%2 and
+  // c_{t+2} is loaded into set t%2; after the compute the registers of c_{t+1} go to stage
+  // (t+1)%2 and one barrier publishes them.
+  u32x4 kr[2][NV], vr[2][NV];
+  if (U > 0) {
+    const int c0 = advance();
+    load_kv(c0, kr[0], vr[0]);
+    store_kv(0, kr[0], vr[0]);
+    int ca = c0, cb = advance();           // chunks t and t+1
+    load_kv(cb, kr[1], vr[1]);
+    __syncthreads();
+    // Two chunks per trip (static register-set indexing); an odd U ends with an idle half.
+    for (int t = 0; t < U; t += 2) {
+      const int cc = advance();            // chunk t+2
+      load_kv(cc, kr[0], vr[0]);
+      compute(ca, 0, true);
+      store_kv(1, kr[1], vr[1]);
+      __syncthreads();
+      const int cd = advance();            // chunk t+3
+      load_kv(cd, kr[1], vr[1]);
+      compute(cb, 1, t + 1 < U);
       store_kv(0, kr[0], vr[0]);
-      int ca = c0, cb = advance();           // chunks t and t+1
-      load_kv(cb, kr[1], vr[1]);
       __syncthreads();
-      // Two chunks per trip (static register-set indexing); an odd U ends with an idle half.
-      for (int t = 0; t < U; t += 2) {
-        const int cc = advance();            // chunk t+2
-        load_kv(cc, kr[0], vr[0]);
-        compute(ca, 0, true);
-        store_kv(1, kr[1], vr[1]);
-        __syncthreads();
-        const int cd = advance();            // chunk t+3
-        load_kv(cd, kr[1], vr[1]);
-        compute(cb, 1, t + 1 < U);
-        store_kv(0, kr[0], vr[0]);
-        __syncthreads();
-        ca = cc;
-        cb = cd;
-      }
-    }
-  } else {
-    // One LDS stage, so that two workgroups share a CU and their waves overlap on each SIMD:
-    // compute c_t; barrier; the registers holding c_{t+1} go to LDS and c_{t+2} is loaded into
-    // them; barrier.
-    u32x4 kr[NV], vr[NV];
-    if (U > 0) {
-      int cj = advance();
-      load_kv(cj, kr, vr);
-      store_kv(0, kr, vr);
-      int cn = advance();
-      load_kv(cn, kr, vr);
-      __syncthreads();
-      for (int t = 0; t < U; ++t) {
-        compute(cj, 0, true);
-        __syncthreads();
-        store_kv(0, kr, vr);
-        const int cn2 = advance();
-        load_kv(cn2, kr, vr);
-        __syncthreads();
-        cj = cn;
-        cn = cn2;
-      }
+      ca = cc;
+      cb = cd;
     }
   }
 
@@ -384,9 +363,207 @@ __global__ __launch_bounds__(NW * 64, STAGES == 1 ? 2 : 1) void chunk_attention_
   }
 }
 
-// Queries per workgroup: bf16 with k <= 32 takes 128 (4 waves) with one LDS stage, two
-// workgroups per CU; otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with two stages, so that
-// the staged selection fits LDS; 64 when the sequence does not split that way.
+// ------------------------------------------------------------------------------------------
+// bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
+// computes only the chunks its own 16 rows selected (no second block riding along), and a wave
+// needs about half the registers of the two-block kernel above, so two workgroups (four waves
+// per SIMD) share a CU.  Same staging and union walk as above: one LDS stage, the next chunk in
+// registers, two barriers per chunk.
+template <int D>
+__global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const AttnArgs a) {
+  constexpr int NW = 8, QG = 16 * NW, KMAX = 32;
+  typedef AttnSmem<bf16, D, QG, KMAX, 1> Smem;
+  typedef AttnLayout<bf16, D> Lay;
+  constexpr int NF = D / 32;                 // QK^T steps over d
+  constexpr int NP = 2;                      // PV steps over the 64 keys
+  constexpr int VE = 8;                      // elements per 16-byte vector
+  constexpr int NT = NW * 64;                // threads
+  constexpr int NV = 64 * Lay::VPR / NT;     // 16-byte vectors per thread per tensor per chunk
+  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
+  __shared__ Smem sm;
+  extern __shared__ uint32_t bitmap[];       // ceil(N / 32) words
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int groups = a.L / QG;
+  const uint32_t total = (uint32_t)a.B * a.H * groups;
+  const uint32_t gid = xcd_remap(blockIdx.x, total);
+  const int bh = gid / groups;
+  const int q0 = (int)(gid % groups) * QG;   // first query position of the group
+  const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
+  const int k = a.topk;
+  const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
+  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)bh * a.L * D;
+  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)bh * a.L * D;
+  const size_t row0 = (size_t)bh * a.L;
+
+  // Stage the group's selections and build the union bitmap (causal chunks only).
+  const int nwords = (c_last + 1 + 31) >> 5;
+  for (int x = tid; x < nwords; x += NT) bitmap[x] = 0u;
+  if (tid == 0) sm.nunion = 0;
+  for (int r = tid; r < QG; r += NT) sm.sidx[r * ks + k] = (uint16_t)0xFFFF;   // end sentinel
+  __syncthreads();
+  for (int x = tid; x < QG * k; x += NT) {
+    const int r = x / k, e = x - r * k;
+    const int j = a.idx[(row0 + q0) * k + x];
+    const bool ok = j >= 0 && j <= c_last;
+    sm.sidx[r * ks + e] = ok ? (uint16_t)j : (uint16_t)0xFFFF;
+    sm.sw[r * ks + e] = a.w[(row0 + q0) * k + x];
+    if (ok) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  {
+    int cnt = 0;
+    for (int x = tid; x < nwords; x += NT) cnt += __popc(bitmap[x]);
+    cnt = (int)wave_sum((float)cnt);   // exact: at most 65536
+    if (lane == 0) atomicAdd(&sm.nunion, cnt);
+  }
+
+  // This lane's row: 16 * wave + m of the group.
+  const int rloc = 16 * wave + m, qpos = q0 + rloc, crow = qpos >> 6;
+  int ptr = 0;
+  bf16x8 qf[NF];
+  {
+    const bf16* qp = static_cast<const bf16*>(a.q) + (row0 + qpos) * D + g * (D / 4);
+#pragma unroll
+    for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
+  }
+#pragma unroll
+  for (int st = 0; st < NF; ++st) asm volatile("" ::"v"(qf[st]));
+  f32x4 acc_o[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
+
+  auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
+    const bf16* kc = Kb + (size_t)j * 64 * D;
+    const bf16* vc = Vb + (size_t)j * 64 * D;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+    }
+  };
+  auto store_kv = [&](const u32x4 (&kr)[NV], const u32x4 (&vr)[NV]) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      const int row = v / Lay::VPR, p = v % Lay::VPR;
+      *reinterpret_cast<u32x4*>(sm.k[0] + row * Lay::KLD + p * 16) = kr[u];
+      const int e = p * VE;                  // first element of the vector
+      *reinterpret_cast<u32x4*>(sm.v[0] + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
+    }
+  };
+
+  __syncthreads();
+  int wi = 0;
+  uint32_t cur = bitmap[0];
+  auto next_chunk = [&]() -> int {
+    while (cur == 0u && wi + 1 < nwords) cur = bitmap[++wi];
+    if (cur == 0u) return -1;
+    const int j = wi * 32 + __builtin_ctz(cur);
+    cur &= cur - 1u;
+    return j;
+  };
+
+  const float zs = a.scale * 1.4426950408889634f;
+  auto compute = [&](int j) {
+    // The row's selection is ascending with a sentinel after entry k-1, so ptr stays <= k.
+    const int e = rloc * ks + ptr;
+    const bool sel = sm.sidx[e] == (uint16_t)j;
+    const float wq = sel ? sm.sw[e] : 0.f;
+    ptr += sel ? 1 : 0;
+    if (!__any(sel)) return;
+    const char* kbuf = sm.k[0];
+    const char* vbuf = sm.v[0];
+    // S^T: lane (m, g) holds query row m and keys 16 kb + 4 g + rr.
+    float sv[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 acc = zero4();
+      const bf16* krow = reinterpret_cast<const bf16*>(kbuf + (kb * 16 + m) * Lay::KLD) + g * (D / 4);
+#pragma unroll
+      for (int st = 0; st < NF; ++st) acc = Mfma<bf16>::mma(load_frag<bf16>(krow + st * 8), qf[st], acc);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
+    }
+    if (j == crow) {                         // wave-uniform: the block's rows share a chunk
+      const int ql = qpos & 63;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (kb * 16 + 4 * g + rr > ql) sv[kb * 4 + rr] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+    mx = col_max(mx) * zs;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
+      sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], zs, -mx));
+      l += sv[i];
+    }
+    l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
+    const float f = wq * __builtin_amdgcn_rcpf(l);
+    bf16x8 pf[NP];
+#pragma unroll
+    for (int st = 0; st < NP; ++st)
+#pragma unroll
+      for (int z = 0; z < 8; ++z) pf[st][z] = bf16_rne(sv[st * 8 + z] * f);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int st = 0; st < NP; ++st)
+        acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st), pf[st], acc_o[db]);
+  };
+
+  const int U = sm.nunion;
+  int jl = -1;                               // last chunk returned by the iterator
+  auto advance = [&]() -> int {
+    const int j = next_chunk();
+    if (j >= 0) jl = j;
+    return j >= 0 ? j : jl;
+  };
+  // compute c_t; barrier; the registers holding c_{t+1} go to LDS and c_{t+2} is loaded into
+  // them; barrier.  Loads and stores are unconditional (past the end of the union they repeat
+  // its last chunk) so that the compiler's wait counts stay exact across the loop.
+  u32x4 kr[NV], vr[NV];
+  if (U > 0) {
+    int cj = advance();
+    load_kv(cj, kr, vr);
+    store_kv(kr, vr);
+    int cn = advance();
+    load_kv(cn, kr, vr);
+    __syncthreads();
+    for (int t = 0; t < U; ++t) {
+      compute(cj);
+      __syncthreads();
+      store_kv(kr, vr);
+      const int cn2 = advance();
+      load_kv(cn2, kr, vr);
+      __syncthreads();
+      cj = cn;
+      cn = cn2;
+    }
+  }
+
+  // O^T fragments: lane holds its row's d = 16*db + 4g + rr.
+  bf16* op = static_cast<bf16*>(a.o) + (row0 + qpos) * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    bf16x4 out;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
+    *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
+  }
+}
+
+// Queries per workgroup: bf16 with k <= 32 takes 128 (eight one-block waves, one LDS stage, two
+// workgroups per CU); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with two stages, so
+// that the staged selection fits LDS; 64 when the sequence does not split that way.
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   const uint32_t bhs = (uint32_t)a.B * a.H;
@@ -394,9 +571,13 @@ hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 4 && D == 128) {   // 32 KiB per tensor per chunk: 64-query groups
     hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
   } else {
-    if (sizeof(T) == 2 && a.topk <= 32 && a.L % 128 == 0) {
-      hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 32, 1>), dim3(bhs * (a.L / 128)), dim3(256), bm, st, a);
-    } else if (a.topk <= 32 && a.L % 256 == 0) {
+    if constexpr (sizeof(T) == 2) {
+      if (a.topk <= 32 && a.L % 128 == 0) {
+        hipLaunchKernelGGL((chunk_attention_block_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
+        return hipGetLastError();
+      }
+    }
+    if (a.topk <= 32 && a.L % 256 == 0) {
       hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), bm, st, a);
     } else if (a.L % 128 == 0) {
       hipLaunchKernelGGL((chunk_attention_kernel<T, D, 4, 64, 2>), dim3(bhs * (a.L / 128)), dim3(256), bm, st, a);

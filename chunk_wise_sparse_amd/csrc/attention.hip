@@ -12,15 +12,17 @@
 // LDS and shared by all waves.
 //   chunk_attention_block_kernel (bf16, k <= 32): 128 queries, eight waves of one 16-row MFMA
 //     block each; a wave computes the chunks its 16 rows selected.
-//   chunk_attention_kernel (fp32, k > 32): wave w owns rows 32w..32w+31 as two 16-row blocks
+//   chunk_attention_kernel (fp32; bf16 with k > 32): wave w owns rows 32w..32w+31 as two 16-row blocks
 //     and skips a chunk that none of its 32 rows selected; otherwise both blocks run
 //     (branch-free, so the two blocks' MFMA and softmax work interleave).
 // Rows of a block that did not select the chunk get weight 0.
 //   S^T[key][q] = K . Q^T  : A = K rows (LDS), B = raw q (registers);
 //                            lane (m, g) holds query m and keys 16*kb + 4g + rr;
 //   O^T[d][q] += V^T . P'^T: A = V^T via LDS transpose reads, B = P' = p * (w_j / l_j).
-// Loads are staged through registers two chunks ahead: chunk t is computed from one LDS stage
-// while chunk t+1 is written to the other and chunk t+2 is in flight.
+// K and V are loaded into registers and then written to LDS.  The one-block kernel keeps one LDS
+// stage and the next chunk in registers (two barriers per chunk); the two-block kernel computes
+// chunk t from one of two stages while chunk t+1 is written to the other and chunk t+2 is in
+// flight.
 #include <float.h>
 
 #include "hils_device.h"

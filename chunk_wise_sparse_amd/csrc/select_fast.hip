@@ -20,8 +20,9 @@
 // Exact top-k in two passes over the landmarks:
 //   pass 1: per slot (landmark row within a 32-row block) the two largest scores; the kq-th
 //           largest of these 64 values is reached by at least kq distinct chunks, so it bounds
-//           the kq-th largest score from below (tau).  Skipped when all candidates fit the
-//           list.
+//           the kq-th largest score from below (tau).  They are kept in the MFMA output layout
+//           and swapped into the query's lane once, at the end.  Skipped when all candidates
+//           fit the list.
 //   pass 2: every score >= tau is appended, in ascending chunk order, to the query's LDS list
 //           ([position][query] so the 64 lanes write distinct banks).  A list that could
 //           overflow is cut to its exact top-kq first (from a register copy of its keys) and
@@ -336,10 +337,36 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
       read_a(blk, af);
       f32x16 acc0, acc1;
       mma_block(af, acc0, acc1);
-      if (jb == nb - 1) for_scores(std::true_type{}, jb, acc0, acc1, top2);
-      else for_scores(std::false_type{}, jb, acc0, acc1, top2);
+      // Slot maxima kept in the MFMA output layout: m[e] for query col (rows 8(e/4) + 4 half +
+      // e%4), m[16 + e] for query col + 32; the lanes' halves are swapped once at the end.
+      if (jb == nb - 1) {
+        const int lim = n_cand - 32 * jb;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool out = 8 * (e / 4) + 4 * half + e % 4 >= lim;
+          top2(e, out ? -INFINITY : acc0[e]);
+          top2(16 + e, out ? -INFINITY : acc1[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          top2(e, acc0[e]);
+          top2(16 + e, acc1[e]);
+        }
+      }
     });
     if (mine) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1[e]), __float_as_uint(m1[16 + e]),
+                                                         false, false);
+        m1[e] = __uint_as_float(r1[0]);
+        m1[16 + e] = __uint_as_float(r1[1]);
+        const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2[e]), __float_as_uint(m2[16 + e]),
+                                                         false, false);
+        m2[e] = __uint_as_float(r2[0]);
+        m2[16 + e] = __uint_as_float(r2[1]);
+      }
       // Top 32 of the 64 slot values: merge the sorted halves, then pick the kq-th.
       sort_desc<32>(m1);
       sort_desc<32>(m2);

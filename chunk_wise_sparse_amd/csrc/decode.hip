@@ -23,6 +23,8 @@
 
 #include <algorithm>
 
+#include <type_traits>
+
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -918,8 +920,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void decode_fused_kernel(const De
     for (int q = 0; q < NK; ++q)
       if (fl[q]) clist[pos[q]] = u32x2{key[q], (uint32_t)(tid + NWV * 64 * q)};
     __syncthreads();
-    if (wave == 0) {
-      constexpr int NJ = kCandCap / 64;
+    // Wave 0 takes the candidates in chunk order, NJ per lane (NJ = 2 covers the usual case of
+    // at most 128; the bisection below costs NJ ballots per bit).
+    auto exact = [&](auto nj) {
+      constexpr int NJ = decltype(nj)::value;
       uint32_t ck[NJ], cx[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -954,6 +958,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void decode_fused_kernel(const De
         }
         nout += __popcll(bs);
       }
+    };
+    if (wave == 0) {
+      if (M <= 128) exact(std::integral_constant<int, 2>{});
+      else exact(std::integral_constant<int, kCandCap / 64>{});
     }
   } else {
     // Many candidates (ties): theta by bisection with block counts, then the keys above theta

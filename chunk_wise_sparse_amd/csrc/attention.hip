@@ -10,9 +10,10 @@
 // takes consecutive queries of one (batch, head) - several 64-query chunks - and walks the union
 // of their selected chunks in ascending order.  Each union chunk's K and V are staged once in
 // LDS and shared by all waves.
-//   chunk_attention_block_kernel (bf16, k <= 32): 128 queries, eight waves of one 16-row MFMA
-//     block each; a wave computes the chunks its 16 rows selected.
-//   chunk_attention_kernel (fp32; bf16 with k > 32): wave w owns rows 32w..32w+31 as two 16-row blocks
+//   chunk_attention_block_kernel (bf16): 128 queries, eight waves of one 16-row MFMA block
+//     each; a wave computes the chunks its 16 rows selected.
+//   chunk_attention_kernel (fp32, or sequences not a multiple of 128): wave w owns rows
+//     32w..32w+31 as two 16-row blocks
 //     and skips a chunk that none of its 32 rows selected; otherwise both blocks run
 //     (branch-free, so the two blocks' MFMA and softmax work interleave).
 // Rows of a block that did not select the chunk get weight 0.
@@ -366,14 +367,15 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
-// computes only the chunks its own 16 rows selected (no second block riding along), and a wave
-// needs about half the registers of the two-block kernel above, so two workgroups (four waves
-// per SIMD) share a CU.  Same staging and union walk as above: one LDS stage, the next chunk in
-// registers, two barriers per chunk.
-template <int D>
-__global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const AttnArgs a) {
-  constexpr int NW = 8, QG = 16 * NW, KMAX = 32;
+// bf16: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave computes
+// only the chunks its own 16 rows selected (no second block riding along), and a wave needs
+// about half the registers of the two-block kernel above: with k <= 32 two workgroups (four
+// waves per SIMD) share a CU; with k <= 64 the staged selection takes one CU's LDS.  Same
+// staging and union walk as above: one LDS stage, the next chunk in registers, two barriers per
+// chunk.
+template <int D, int KMAX>
+__global__ __launch_bounds__(512, KMAX <= 32 ? 2 : 1) void chunk_attention_block_kernel(const AttnArgs a) {
+  constexpr int NW = 8, QG = 16 * NW;
   typedef AttnSmem<bf16, D, QG, KMAX, 1> Smem;
   typedef AttnLayout<bf16, D> Lay;
   constexpr int NF = D / 32;                 // QK^T steps over d
@@ -563,9 +565,10 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const Att
   }
 }
 
-// Queries per workgroup: bf16 with k <= 32 takes 128 (eight one-block waves, one LDS stage, two
-// workgroups per CU); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with two stages, so
-// that the staged selection fits LDS; 64 when the sequence does not split that way.
+// Queries per workgroup: bf16 takes 128 (eight one-block waves, one LDS stage; two workgroups
+// per CU for k <= 32, one for k <= 64); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with
+// two stages, so that the staged selection fits LDS; 64 when the sequence does not split that
+// way.
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   const uint32_t bhs = (uint32_t)a.B * a.H;
@@ -574,8 +577,11 @@ hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
   } else {
     if constexpr (sizeof(T) == 2) {
-      if (a.topk <= 32 && a.L % 128 == 0) {
-        hipLaunchKernelGGL((chunk_attention_block_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
+      if (a.L % 128 == 0) {
+        if (a.topk <= 32)
+          hipLaunchKernelGGL((chunk_attention_block_kernel<D, 32>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
+        else
+          hipLaunchKernelGGL((chunk_attention_block_kernel<D, 64>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
         return hipGetLastError();
       }
     }

@@ -85,7 +85,7 @@ hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, i
 template <typename T, int D>
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 template <int D>
-hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st);   // bf16, k <= 32
+hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st);   // bf16, k <= 64
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
 

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const SelectArgs a) {
 template <typename T, int D>
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    if (a.k <= 32) return launch_select_fast<D>(a, st);
+    return launch_select_fast<D>(a, st);   // k <= 64
   }
   const uint32_t total = (uint32_t)a.B * a.H * a.N;
   if (a.k <= 32)

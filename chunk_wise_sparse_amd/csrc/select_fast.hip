@@ -1,5 +1,5 @@
-// Chunk selection for prefill, bf16 with k <= 32: one wave per 64-query tile, eight tiles per
-// workgroup.
+// Chunk selection for prefill, bf16 with k <= 64: one wave per 64-query tile, eight tiles per
+// workgroup for k <= 32, four for 32 < k <= 64.
 //
 // Method: [HiLS-Attention model page, "Model Description"] every query scores all causal chunks
 // through their landmark keys, keeps the k best and weights them with a softmax over those
@@ -9,18 +9,19 @@
 //
 // With C = 64 the 64 queries of tile c share the candidate set {0..c}, so scoring is a GEMM
 // [64 queries x d] x [d x (c+1)] done with v_mfma_f32_32x32x16_bf16: A = 32 landmark rows,
-// B = q~ of 32 queries (registers, two column blocks).  The eight tiles of a workgroup are
+// B = q~ of 32 queries (registers, two column blocks).  The tiles of a workgroup are
 // consecutive chunks of one (batch, head), so they need the same landmark blocks: each block is
 // loaded once, straight from global memory into an LDS ring (global_load_lds_dwordx4, no
-// registers), and read by all eight waves.  The output of block jb holds, at lane (col, half),
+// registers), and read by all the workgroup's waves.  The output of block jb holds, at lane (col, half),
 // query column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap per element
 // pair moves both halves of a query's 32 rows into one lane, so lane l owns query
 // 32*(l/32) + l%32 and all of its scores.
 //
 // Exact top-k in two passes over the landmarks:
-//   pass 1: per slot (landmark row within a 32-row block) the two largest scores; the kq-th
-//           largest of these 64 values is reached by at least kq distinct chunks, so it bounds
-//           the kq-th largest score from below (tau).  They are kept in the MFMA output layout
+//   pass 1: per slot the two largest scores, a slot being a landmark row within a 32-row block
+//           (k <= 32: 32 slots) or a row and the block's parity (k <= 64: 64 slots); the kq-th
+//           largest of these 2 x slots values is reached by at least kq distinct chunks, so it
+//           bounds the kq-th largest score from below (tau).  They are kept in the MFMA output layout
 //           and swapped into the query's lane once, at the end.  Skipped when all candidates
 //           fit the list.
 //   pass 2: every score >= tau is appended, in ascending chunk order, to the query's LDS list
@@ -28,8 +29,10 @@
 //           overflow is cut to its exact top-kq first (from a register copy of its keys) and
 //           tau is raised above the cut value (later chunks lose ties); with the tight tau of
 //           pass 1 this is rare.
-//   final:  the kq-th largest theta of the list; entries > theta and the first (kq - #>theta)
-//           entries == theta are kept in list order, then the inter-chunk softmax.
+//   final:  the kq-th largest theta of the list (a sorting network for lists of up to 64
+//           entries, else a bisection over the order-preserving 32-bit keys); entries > theta
+//           and the first (kq - #>theta) entries == theta are kept in list order, then the
+//           inter-chunk softmax.
 // Scores are finite by contract: this file is compiled with -fno-honor-nans, so max/min skip
 // NaN quieting.
 #include <float.h>
@@ -45,7 +48,12 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kCap = 47;   // list capacity per query (>= kq + 8 for kq <= 32)
+// Per k range: tiles per workgroup, list capacity per query (>= kq + 8) and the number of
+// pass-1 slots per query (rows of a 32-landmark block, times the block parity for k > 32).
+// k <= 64 takes one workgroup per CU (LDS), so one wave per SIMD, with room for 512 registers.
+template <int KQ> struct SelCfg;
+template <> struct SelCfg<32> { static constexpr int kTiles = 8, kCap = 47, kPar = 1; };
+template <> struct SelCfg<64> { static constexpr int kTiles = 4, kCap = 88, kPar = 2; };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -97,9 +105,8 @@ __device__ __forceinline__ float pick(const float (&x)[N], int kk) {
   return r;
 }
 
-// Tiles per workgroup: wave w takes the 64-query tile of chunk c_top - w, so the eight tiles of a
-// workgroup are consecutive chunks of one (batch, head) and need the same landmark blocks.
-constexpr int kTiles = 8;
+// Wave w takes the 64-query tile of chunk c_top - w, so the tiles of a workgroup are consecutive
+// chunks of one (batch, head) and need the same landmark blocks.
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -110,8 +117,9 @@ __device__ __forceinline__ int ring_swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
-template <int D>
+template <int D, int KQ>
 struct GroupSmem {
+  static constexpr int kCap = SelCfg<KQ>::kCap;
   static constexpr int RB = 2 * D;             // landmark row bytes
   static constexpr int QLD = D + 8;            // q~ staging row stride (elements)
   alignas(16) char ring[2][32 * RB];           // 32-landmark blocks, even / odd block index
@@ -121,15 +129,16 @@ struct GroupSmem {
       float s[kCap * 64];                      // [position][query] candidate scores
       uint16_t j[kCap * 64];                   // [position][query] candidate chunks
     } list;
-  } w[kTiles];
+  } w[SelCfg<KQ>::kTiles];
 };
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectArgs a) {
+template <int D, int KQ>
+__global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(const SelectArgs a) {
+  constexpr int kTiles = SelCfg<KQ>::kTiles, kCap = SelCfg<KQ>::kCap, kPar = SelCfg<KQ>::kPar;
   constexpr int NS = D / 16;                   // MFMA k-steps over d
-  typedef GroupSmem<D> Smem;
+  typedef GroupSmem<D, KQ> Smem;
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
@@ -253,15 +262,21 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
 
   // ---------------- landmark ring ------------------------------------------------------------
   // Block jb (landmark rows 32 jb .. 32 jb + 31, clamped to the group's last candidate) is
-  // loaded straight into ring slot jb & 1, one 16-byte vector per thread (D = 128) or per thread
-  // of waves 0-3 (D = 64); lane l of a wave lands at the wave's 1 KiB piece + 16 l.
+  // loaded straight into ring slot jb & 1 as NL = 32 * 2D / 1024 loads of 1 KiB, load li by wave
+  // li % kTiles; lane l of a load lands at its 1 KiB piece + 16 l.
   auto issue = [&](int jb, int slot) {
-    constexpr int VPR = D / 8;                 // vectors per row
-    if (D == 128 || wave < 4) {
-      const int r = tid / VPR, p = tid % VPR;
-      const int row = min(32 * jb + r, c_top);
-      const bf16* src = LM + (size_t)row * D + 8 * (p ^ ring_swz<D>(r));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(sm.ring[slot] + 1024 * wave), 16, 0, 0);
+    constexpr int VPR = D / 8;                 // 16-byte vectors per row
+    constexpr int NL = D / 16;                 // loads per block
+    static_assert(NL * 1024 == 32 * Smem::RB, "block size");
+#pragma unroll
+    for (int li0 = 0; li0 < NL; li0 += kTiles) {
+      const int li = li0 + wave;
+      if (li < NL) {
+        const int r = li * (8 * 64 / D) + lane / VPR, p = lane % VPR;
+        const int row = min(32 * jb + r, c_top);
+        const bf16* src = LM + (size_t)row * D + 8 * (p ^ ring_swz<D>(r));
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(sm.ring[slot] + 1024 * li), 16, 0, 0);
+      }
     }
   };
   // The group walks its blocks in order; f(jb, block) runs once the block is in LDS, while the
@@ -321,24 +336,24 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
   };
 
   // ---------------- pass 1: lower bound tau of the kq-th largest score ---------------------
+  // Slots: the 32 rows of a block (k <= 32), or rows times block parity (k <= 64).  The two
+  // largest scores per slot are kept in the MFMA output layout: m[p][e] for query col (rows
+  // 8(e/4) + 4 half + e%4), m[p][16 + e] for query col + 32; the lanes' halves are swapped once
+  // at the end, giving each lane 64 kPar values of its query.
   float tau = -FLT_MAX;                        // every finite score passes; masked ones do not
   if (c_top + 1 > kCap) {                      // group-uniform: some tile has more than kCap
     const bool mine = n_cand > kCap;
-    float m1[32], m2[32];
+    float m1[kPar][32], m2[kPar][32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) m1[i] = m2[i] = -INFINITY;
-    auto top2 = [&](int i, float v) {
-      m2[i] = __builtin_amdgcn_fmed3f(m1[i], m2[i], v);
-      m1[i] = fmaxf(m1[i], v);
-    };
-    sweep([&](int jb, const char* blk) {
-      if (!mine || jb >= nb) return;
-      bf16x8 af[NS];
-      read_a(blk, af);
-      f32x16 acc0, acc1;
-      mma_block(af, acc0, acc1);
-      // Slot maxima kept in the MFMA output layout: m[e] for query col (rows 8(e/4) + 4 half +
-      // e%4), m[16 + e] for query col + 32; the lanes' halves are swapped once at the end.
+    for (int p = 0; p < kPar; ++p)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m1[p][i] = m2[p][i] = -INFINITY;
+    auto slots = [&](auto par, int jb, const f32x16& acc0, const f32x16& acc1) {
+      constexpr int P = decltype(par)::value;
+      auto top2 = [&](int i, float v) {
+        m2[P][i] = __builtin_amdgcn_fmed3f(m1[P][i], m2[P][i], v);
+        m1[P][i] = fmaxf(m1[P][i], v);
+      };
       if (jb == nb - 1) {
         const int lim = n_cand - 32 * jb;
 #pragma unroll
@@ -354,26 +369,46 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
           top2(16 + e, acc1[e]);
         }
       }
+    };
+    sweep([&](int jb, const char* blk) {
+      if (!mine || jb >= nb) return;
+      bf16x8 af[NS];
+      read_a(blk, af);
+      f32x16 acc0, acc1;
+      mma_block(af, acc0, acc1);
+      if (kPar == 2 && (jb & 1)) slots(std::integral_constant<int, kPar - 1>{}, jb, acc0, acc1);
+      else slots(std::integral_constant<int, 0>{}, jb, acc0, acc1);
     });
     if (mine) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1[e]), __float_as_uint(m1[16 + e]),
-                                                         false, false);
-        m1[e] = __uint_as_float(r1[0]);
-        m1[16 + e] = __uint_as_float(r1[1]);
-        const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2[e]), __float_as_uint(m2[16 + e]),
-                                                         false, false);
-        m2[e] = __uint_as_float(r2[0]);
-        m2[16 + e] = __uint_as_float(r2[1]);
-      }
-      // Top 32 of the 64 slot values: merge the sorted halves, then pick the kq-th.
-      sort_desc<32>(m1);
-      sort_desc<32>(m2);
+      for (int p = 0; p < kPar; ++p)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) m1[i] = fmaxf(m1[i], m2[31 - i]);
-      bitonic_merge_desc<32>(m1);
-      tau = pick<32>(m1, kq);
+        for (int e = 0; e < 16; ++e) {
+          const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1[p][e]),
+                                                           __float_as_uint(m1[p][16 + e]), false, false);
+          m1[p][e] = __uint_as_float(r1[0]);
+          m1[p][16 + e] = __uint_as_float(r1[1]);
+          const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2[p][e]),
+                                                           __float_as_uint(m2[p][16 + e]), false, false);
+          m2[p][e] = __uint_as_float(r2[0]);
+          m2[p][16 + e] = __uint_as_float(r2[1]);
+        }
+      // Top 32 kPar of the 64 kPar values: sort the first and second maxima, merge, pick kq-th.
+      constexpr int NM = 32 * kPar;
+      float u1[NM], u2[NM];
+#pragma unroll
+      for (int p = 0; p < kPar; ++p)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          u1[32 * p + i] = m1[p][i];
+          u2[32 * p + i] = m2[p][i];
+        }
+      sort_desc<NM>(u1);
+      sort_desc<NM>(u2);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) u1[i] = fmaxf(u1[i], u2[NM - 1 - i]);
+      bitonic_merge_desc<NM>(u1);
+      tau = pick<NM>(u1, kq);
     }
   }
 
@@ -464,14 +499,27 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
     ej[i] = i < cnt ? (int)lj[64 * i] : 0;
   }
   float theta, top;
-  {
+  if constexpr (kCap <= 64) {
     float v[64];                               // kCap entries padded to the sort width
-    static_assert(kCap <= 64, "list longer than the sort");
 #pragma unroll
     for (int i = 0; i < 64; ++i) v[i] = i < kCap ? ev[i] : -INFINITY;
     sort_desc<64>(v);
     top = v[0];
     theta = pick<64>(v, kq);
+  } else {
+    // theta = kq-th largest key, bit by bit over the list in registers (padding is -inf).
+    top = ev[0];
+#pragma unroll
+    for (int i = 1; i < kCap; ++i) top = fmaxf(top, ev[i]);
+    uint32_t th = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = th | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kCap; ++i) n += f32_key(ev[i]) >= cand ? 1 : 0;
+      if (n >= kq) th = cand;
+    }
+    theta = key_f32(th);
   }
   // Entries > theta, then the first kq - #(> theta) entries == theta in chunk order.
   int ngt = 0;
@@ -519,8 +567,15 @@ __global__ __launch_bounds__(64 * kTiles) void select_fast_kernel(const SelectAr
 
 template <int D>
 hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st) {
-  const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + kTiles - 1) / kTiles);
-  hipLaunchKernelGGL((select_fast_kernel<D>), dim3(groups), dim3(64 * kTiles), 0, st, a);
+  if (a.k <= 32) {
+    constexpr int T = SelCfg<32>::kTiles;
+    const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
+    hipLaunchKernelGGL((select_fast_kernel<D, 32>), dim3(groups), dim3(64 * T), 0, st, a);
+  } else {
+    constexpr int T = SelCfg<64>::kTiles;
+    const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
+    hipLaunchKernelGGL((select_fast_kernel<D, 64>), dim3(groups), dim3(64 * T), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -46,6 +46,22 @@ struct AttnLayout {
   static constexpr int VBYTES = (D / 16) * VDB;
 };
 
+// K tile of the bf16 one-block kernels.  At d = 128: 256-byte rows whose 16-byte vectors are
+// XOR-permuted by the row, so that a 16x16x32 A-fragment read (lane (m, g): row 16 kb + m,
+// vector 4 g + st) touches every LDS bank once; rows padded by 16 bytes instead conflict two
+// ways on gfx950 (measured: 127 against 243 bytes per clock per CU).  Other d keep padded rows.
+template <int D>
+struct BlockKLayout {
+  static constexpr int RB = D * 2;
+  static constexpr bool kSwz = D == 128;
+  static constexpr int LD = kSwz ? RB : RB + 16;
+  __device__ static __forceinline__ int off(int row, int vec) {
+    if constexpr (kSwz) return row * RB + ((vec ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
+    else return row * LD + vec * 16;
+  }
+};
+static_assert(64 * BlockKLayout<128>::LD <= AttnLayout<bf16, 128>::KBYTES, "K tile fits its stage");
+
 // Selection of the group's rows, staged once: chunk index (u16, 0xFFFF = padding) and weight.
 // The union bitmap, one bit per chunk of the sequence, is the dynamic part of LDS.
 template <typename T, int D, int QG, int KMAX, int STAGES>
@@ -453,7 +469,7 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const Att
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
       const int row = v / Lay::VPR, p = v % Lay::VPR;
-      *reinterpret_cast<u32x4*>(sm.k[0] + row * Lay::KLD + p * 16) = kr[u];
+      *reinterpret_cast<u32x4*>(sm.k[0] + BlockKLayout<D>::off(row, p)) = kr[u];
       const int e = p * VE;                  // first element of the vector
       *reinterpret_cast<u32x4*>(sm.v[0] + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
     }
@@ -485,9 +501,9 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const Att
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x4 acc = zero4();
-      const bf16* krow = reinterpret_cast<const bf16*>(kbuf + (kb * 16 + m) * Lay::KLD) + g * (D / 4);
 #pragma unroll
-      for (int st = 0; st < NF; ++st) acc = Mfma<bf16>::mma(load_frag<bf16>(krow + st * 8), qf[st], acc);
+      for (int st = 0; st < NF; ++st)
+        acc = Mfma<bf16>::mma(load_frag<bf16>(reinterpret_cast<const bf16*>(kbuf + BlockKLayout<D>::off(kb * 16 + m, g * NF + st))), qf[st], acc);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
     }
@@ -661,7 +677,7 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block2_kernel(const At
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
       const int row = v / Lay::VPR, p = v % Lay::VPR;
-      *reinterpret_cast<u32x4*>(sm.k[s] + row * Lay::KLD + p * 16) = kr[u];
+      *reinterpret_cast<u32x4*>(sm.k[s] + BlockKLayout<D>::off(row, p)) = kr[u];
       const int e = p * VE;                  // first element of the vector
       *reinterpret_cast<u32x4*>(sm.v[s] + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
     }
@@ -697,9 +713,9 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block2_kernel(const At
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x4 acc = zero4();
-      const bf16* krow = reinterpret_cast<const bf16*>(kbuf + (kb * 16 + m) * Lay::KLD) + g * (D / 4);
 #pragma unroll
-      for (int st = 0; st < NF; ++st) acc = Mfma<bf16>::mma(load_frag<bf16>(krow + st * 8), qf[st], acc);
+      for (int st = 0; st < NF; ++st)
+        acc = Mfma<bf16>::mma(load_frag<bf16>(reinterpret_cast<const bf16*>(kbuf + BlockKLayout<D>::off(kb * 16 + m, g * NF + st))), qf[st], acc);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
     }

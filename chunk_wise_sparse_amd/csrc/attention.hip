@@ -793,6 +793,325 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block2_kernel(const At
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Chunk-major mode (bf16), for selections whose rows share few chunks: the union walk above
+// stages every chunk any row of a 128-row group chose and computes whole 16-row blocks, which on
+// such inputs re-reads each chunk's K/V once per group and computes mostly discarded rows.  Here
+// one (batch, head) pair at a time: the pair's selections are inverted into per-chunk lists
+// (count, prefix, fill); each work item stages one chunk's K/V once and runs up to 128 of the
+// rows that chose it, 16 per wave, writing w_j * o_j of that (row, slot) to a partial buffer;
+// finally every row sums its partials in slot order.  The result of a (row, slot) does not
+// depend on which rows share its tile, so the output is deterministic although the lists are
+// filled in arrival order.
+
+__global__ __launch_bounds__(256) void cm_zero_kernel(uint32_t* cnt, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0u;
+}
+
+// Selections per chunk.  Each workgroup takes a contiguous slice of the pair's (row, slot)
+// entries and counts it into an LDS histogram first (nchunks <= kCmLdsChunks), so that a chunk
+// costs one global atomic per workgroup instead of one per selection.
+constexpr int kCmLdsChunks = 16384;
+__global__ __launch_bounds__(256) void cm_count_kernel(const int32_t* idx, int n, int nchunks, uint32_t* cnt) {
+  extern __shared__ uint32_t hist[];
+  const int per = (n + gridDim.x - 1) / gridDim.x;
+  const int b = min(n, (int)blockIdx.x * per), e = min(n, b + per);
+  if (nchunks > kCmLdsChunks) {
+    for (int i = b + threadIdx.x; i < e; i += 256) {
+      const int j = idx[i];
+      if (j >= 0 && j < nchunks) atomicAdd(&cnt[j], 1u);
+    }
+    return;
+  }
+  for (int j = threadIdx.x; j < nchunks; j += 256) hist[j] = 0u;
+  __syncthreads();
+  for (int i = b + threadIdx.x; i < e; i += 256) {
+    const int j = idx[i];
+    if (j >= 0 && j < nchunks) atomicAdd(&hist[j], 1u);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nchunks; j += 256)
+    if (hist[j]) atomicAdd(&cnt[j], hist[j]);
+}
+
+// One workgroup: off = exclusive prefix of cnt, cur = off, toff = exclusive prefix of
+// ceil(cnt / kCmItem); off[N] and toff[N] are the totals.
+__global__ __launch_bounds__(1024) void cm_scan_kernel(const uint32_t* cnt, int N, uint32_t* off, uint32_t* cur,
+                                                       uint32_t* toff) {
+  __shared__ uint32_t s_e[1024], s_t[1024];
+  const int t = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int b = min(N, t * per), e = min(N, b + per);
+  uint32_t se = 0, st = 0;
+  for (int i = b; i < e; ++i) {
+    se += cnt[i];
+    st += (cnt[i] + kCmItem - 1) / kCmItem;
+  }
+  s_e[t] = se;
+  s_t[t] = st;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {         // inclusive Hillis-Steele scan
+    const uint32_t ae = t >= d ? s_e[t - d] : 0u, at = t >= d ? s_t[t - d] : 0u;
+    __syncthreads();
+    s_e[t] += ae;
+    s_t[t] += at;
+    __syncthreads();
+  }
+  uint32_t pe = s_e[t] - se, pt = s_t[t] - st;
+  for (int i = b; i < e; ++i) {
+    off[i] = pe;
+    cur[i] = pe;
+    toff[i] = pt;
+    pe += cnt[i];
+    pt += (cnt[i] + kCmItem - 1) / kCmItem;
+  }
+  if (t == 1023) {
+    off[N] = s_e[1023];
+    toff[N] = s_t[1023];
+  }
+}
+
+// List entries (row << 6 | slot), grouped by chunk.  A workgroup reserves its share of each
+// chunk's list with one global atomic (LDS histogram, then LDS cursors), over the same slices
+// as cm_count_kernel.  The order inside a chunk's list is arrival order; results do not depend
+// on it.
+__global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t* idx, int n, int k, int nchunks, uint32_t* cur,
+                                                      uint32_t* ent) {
+  extern __shared__ uint32_t sh[];             // hist[nchunks], base[nchunks]
+  const int per = (n + gridDim.x - 1) / gridDim.x;
+  const int b = min(n, (int)blockIdx.x * per), e = min(n, b + per);
+  if (nchunks > kCmLdsChunks) {
+    for (int i = b + threadIdx.x; i < e; i += 256) {
+      const int j = idx[i];
+      if (j >= 0 && j < nchunks) {
+        const int r = i / k, s = i - r * k;
+        ent[atomicAdd(&cur[j], 1u)] = ((uint32_t)r << 6) | (uint32_t)s;
+      }
+    }
+    return;
+  }
+  uint32_t* hist = sh;
+  uint32_t* base = sh + nchunks;
+  for (int j = threadIdx.x; j < nchunks; j += 256) hist[j] = 0u;
+  __syncthreads();
+  for (int i = b + threadIdx.x; i < e; i += 256) {
+    const int j = idx[i];
+    if (j >= 0 && j < nchunks) atomicAdd(&hist[j], 1u);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nchunks; j += 256) {
+    const uint32_t c = hist[j];
+    if (c) base[j] = atomicAdd(&cur[j], c);
+    hist[j] = 0u;                              // now this workgroup's cursor into its share
+  }
+  __syncthreads();
+  for (int i = b + threadIdx.x; i < e; i += 256) {
+    const int j = idx[i];
+    if (j >= 0 && j < nchunks) {
+      const int r = i / k, s = i - r * k;
+      ent[base[j] + atomicAdd(&hist[j], 1u)] = ((uint32_t)r << 6) | (uint32_t)s;
+    }
+  }
+}
+
+// Persistent: workgroup b takes work items b, b + gridDim.x, ...; item i belongs to the chunk j
+// with toff[j] <= i < toff[j + 1] and covers list entries off[j] + 128 (i - toff[j]) onward.
+template <int D>
+__global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
+  constexpr int NT = 512;
+  typedef AttnLayout<bf16, D> Lay;
+  constexpr int NF = D / 32, NP = 2, VE = 8;
+  constexpr int NV = 64 * Lay::VPR / NT;
+  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
+  __shared__ __attribute__((aligned(16))) char sk[AttnLayout<bf16, D>::KBYTES];
+  __shared__ __attribute__((aligned(16))) char sv_[AttnLayout<bf16, D>::VBYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int N = a.N, k = a.k;
+  const uint32_t items = a.toff[N];
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* Kb = static_cast<const bf16*>(a.key);
+  const bf16* Vb = static_cast<const bf16*>(a.val);
+  bf16* P = static_cast<bf16*>(a.partial);
+  const float zs = a.scale * 1.4426950408889634f;
+  // The next item's K/V are loaded into registers while the current item is computed.
+  auto locate = [&](uint32_t item, int& j, uint32_t& e0, uint32_t& e1) {
+    int lo = 0, hi = N;                        // toff[lo] <= item < toff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.toff[mid] <= item) lo = mid;
+      else hi = mid;
+    }
+    j = lo;
+    e0 = a.off[j] + kCmItem * (item - a.toff[j]);
+    e1 = min(e0 + (uint32_t)kCmItem, a.off[j + 1]);
+  };
+  u32x4 kr[NV], vr[NV];
+  auto load_kv = [&](int j) {
+    const bf16* kc = Kb + (size_t)j * 64 * D;
+    const bf16* vc = Vb + (size_t)j * 64 * D;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+    }
+  };
+  uint32_t item = blockIdx.x;
+  if (item >= items) return;                   // workgroup-uniform
+  int j;
+  uint32_t e0, e1;
+  locate(item, j, e0, e1);
+  load_kv(j);
+  for (;;) {
+    __syncthreads();                           // the previous item's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      const int row = v / Lay::VPR, p = v % Lay::VPR;
+      *reinterpret_cast<u32x4*>(sk + BlockKLayout<D>::off(row, p)) = kr[u];
+      const int e = p * VE;
+      *reinterpret_cast<u32x4*>(sv_ + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
+    }
+    __syncthreads();
+    const uint32_t next = item + gridDim.x;
+    const bool has_next = next < items;        // workgroup-uniform
+    // This tile's rows and queries are read before the next item's K/V (the memory counter
+    // drains in issue order).
+    const uint32_t t0 = e0 + 16 * wave;
+    const bool act = t0 < e1;                  // wave-uniform
+    const bool valid = act && t0 + m < e1;
+    uint32_t pe = 0;
+    bf16x8 qf[NF];
+    if (act) {
+      pe = a.ent[valid ? t0 + m : t0];
+      const bf16* qp = Q + (size_t)(pe >> 6) * D + g * (D / 4);
+#pragma unroll
+      for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
+    }
+    int jn = 0;
+    uint32_t e0n = 0, e1n = 0;
+    if (has_next) {
+      locate(next, jn, e0n, e1n);
+      load_kv(jn);
+    }
+    if (act) {
+      const int r = (int)(pe >> 6), es = (int)(pe & 63u);
+      float sc[16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int st = 0; st < NF; ++st)
+          acc = Mfma<bf16>::mma(load_frag<bf16>(reinterpret_cast<const bf16*>(sk + BlockKLayout<D>::off(kb * 16 + m, g * NF + st))), qf[st], acc);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sc[kb * 4 + rr] = acc[rr];
+      }
+      if ((r >> 6) == j) {                     // the row's own chunk: keys after it are masked
+        const int ql = r & 63;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (kb * 16 + 4 * g + rr > ql) sc[kb * 4 + rr] = -INFINITY;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = col_max(mx) * zs;
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
+        sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], zs, -mx));
+        l += sc[i];
+      }
+      l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
+      const float f = a.w[(size_t)r * k + es] * __builtin_amdgcn_rcpf(l);
+      bf16x8 pf[NP];
+#pragma unroll
+      for (int st = 0; st < NP; ++st)
+#pragma unroll
+        for (int z = 0; z < 8; ++z) pf[st][z] = bf16_rne(sc[st * 8 + z] * f);
+      f32x4 acc_o[D / 16];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int st = 0; st < NP; ++st)
+          acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(sv_, m, g, db, st), pf[st], acc_o[db]);
+      if (valid) {
+        bf16* op = P + ((size_t)r * k + es) * D;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          bf16x4 out;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
+          *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
+        }
+      }
+    }
+    if (!has_next) break;
+    item = next;
+    j = jn;
+    e0 = e0n;
+    e1 = e1n;
+  }
+}
+
+// o[r] = sum over the row's slots, in slot order, of its partials (fp32), rounded once.  The
+// selection holds min(k, c + 1) chunks at the front of row r's list (c = r / 64, the row's
+// chunk), so those are the valid slots.  Eight elements per thread, D / 8 threads per row.
+template <int D>
+__global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
+  constexpr int TPR = D / 8;                   // threads per row
+  const int r = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int t = threadIdx.x % TPR;
+  if (r >= a.L) return;
+  const int nv = min(a.k, (r >> 6) + 1);
+  const bf16* P = static_cast<const bf16*>(a.partial) + (size_t)r * a.k * D + t * 8;
+  float acc[8] = {};
+  int e = 0;
+  for (; e + 4 <= nv; e += 4) {                // four independent loads in flight
+    bf16x8 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const bf16x8*>(P + (size_t)(e + u) * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int z = 0; z < 8; ++z) acc[z] += to_f32(x[u][z]);
+  }
+  for (; e < nv; ++e) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(P + (size_t)e * D);
+#pragma unroll
+    for (int z = 0; z < 8; ++z) acc[z] += to_f32(x[z]);
+  }
+  bf16x8 out;
+#pragma unroll
+  for (int z = 0; z < 8; ++z) out[z] = bf16_rne(acc[z]);
+  *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.o) + (size_t)r * D + t * 8) = out;
+}
+
+template <int D>
+hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st) {
+  const int n = a.L * a.k;
+  const int gb = min((n + 8191) / 8192, 1024);   // workgroups over the entries, 8192+ each
+  const bool lds = a.N <= kCmLdsChunks;
+  hipLaunchKernelGGL(cm_zero_kernel, dim3(min((a.N + 255) / 256, 1024)), dim3(256), 0, st, a.cnt, a.N);
+  hipLaunchKernelGGL(cm_count_kernel, dim3(gb), dim3(256), lds ? (size_t)a.N * 4 : 0, st, a.idx, n, a.N, a.cnt);
+  hipLaunchKernelGGL(cm_scan_kernel, dim3(1), dim3(1024), 0, st, a.cnt, a.N, a.off, a.cur, a.toff);
+  hipLaunchKernelGGL(cm_fill_kernel, dim3(gb), dim3(256), lds ? (size_t)a.N * 8 : 0, st, a.idx, n, a.k, a.N, a.cur,
+                     a.ent);
+  hipLaunchKernelGGL((cm_attn_kernel<D>), dim3(512), dim3(512), 0, st, a);
+  constexpr int RPB = 256 / (D / 8);           // rows per reduce workgroup
+  hipLaunchKernelGGL((cm_reduce_kernel<D>), dim3((a.L + RPB - 1) / RPB), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_chunk_attention_cm<64>(const CmArgs&, hipStream_t);
+template hipError_t launch_chunk_attention_cm<128>(const CmArgs&, hipStream_t);
+
 // Queries per workgroup: bf16 takes 128 (eight one-block waves, two workgroups per CU; the
 // selection staged in LDS for k <= 32, read from memory for k <= 64); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with
 // two stages, so that the staged selection fits LDS; 64 when the sequence does not split that

@@ -51,7 +51,7 @@ size_t elem_bytes(int dtype) { return dtype == HILS_DTYPE_BF16 ? 2 : 4; }
 // Prefill
 // ---------------------------------------------------------------------------------------------
 struct PrefillLayout {
-  size_t tcode, idx, w, total;
+  size_t tcode, idx, w, cm_cnt, cm_off, cm_cur, cm_toff, cm_ent, cm_partial, total;
 };
 
 int check_prefill_params(const hils_prefill_params* p) {
@@ -80,6 +80,10 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (!(isfinite(p->scale))) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events))
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+  if (p->attn_mode != HILS_ATTN_UNION && p->attn_mode != HILS_ATTN_CHUNK_MAJOR)
+    return fail(HILS_ERR_UNSUPPORTED, "attn_mode %d is not supported", p->attn_mode);
+  if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR && p->dtype != HILS_DTYPE_BF16)
+    return fail(HILS_ERR_UNSUPPORTED, "the chunk-major attention mode is bf16 only");
   const double bhld = (double)p->batch * p->heads * p->seq_len * p->head_dim;
   if (bhld > 4e18 / 8 || (double)p->batch * p->heads * (p->seq_len / 64) > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
@@ -96,6 +100,21 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   if (!with_sel) off += align_up(B * H * S * k * sizeof(int32_t));
   L.w = off;
   if (!with_sel) off += align_up(B * H * S * k * sizeof(float));
+  if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR) {  // one (batch, head) pair at a time
+    const size_t N = S / 64, d = p->head_dim;
+    L.cm_cnt = off;
+    off += align_up(N * 4);
+    L.cm_off = off;
+    off += align_up((N + 1) * 4);
+    L.cm_cur = off;
+    off += align_up(N * 4);
+    L.cm_toff = off;
+    off += align_up((N + 1) * 4);
+    L.cm_ent = off;
+    off += align_up(S * k * 4);
+    L.cm_partial = off;
+    off += align_up(S * k * d * 2);
+  }
   L.total = off;
   return L;
 }
@@ -103,7 +122,8 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
 template <typename T, int D>
 hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* k, const void* v,
                        const void* lmk, const void* h, const void* w_down, const void* w_up,
-                       void* o, int32_t* idx, float* w, float* tcode, hipStream_t st) {
+                       void* o, int32_t* idx, float* w, float* tcode, char* ws,
+                       const PrefillLayout& L, hipStream_t st) {
   hipError_t e;
   hipEvent_t* ev = p->n_stage_events >= 4 ? (hipEvent_t*)p->stage_events : nullptr;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
@@ -143,6 +163,33 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   aa.N = p->seq_len / 64;
   aa.topk = p->topk;
   aa.scale = scale;
+  if constexpr (sizeof(T) == 2) {
+    if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR) {
+      hils::CmArgs ca;
+      ca.cnt = reinterpret_cast<uint32_t*>(ws + L.cm_cnt);
+      ca.off = reinterpret_cast<uint32_t*>(ws + L.cm_off);
+      ca.cur = reinterpret_cast<uint32_t*>(ws + L.cm_cur);
+      ca.toff = reinterpret_cast<uint32_t*>(ws + L.cm_toff);
+      ca.ent = reinterpret_cast<uint32_t*>(ws + L.cm_ent);
+      ca.partial = ws + L.cm_partial;
+      ca.L = p->seq_len;
+      ca.N = p->seq_len / 64;
+      ca.k = p->topk;
+      ca.scale = scale;
+      const size_t ld = (size_t)p->seq_len * D, lk = (size_t)p->seq_len * p->topk;
+      for (size_t bh = 0; bh < (size_t)p->batch * p->heads; ++bh) {
+        ca.q = static_cast<const T*>(q) + bh * ld;
+        ca.key = static_cast<const T*>(k) + bh * ld;
+        ca.val = static_cast<const T*>(v) + bh * ld;
+        ca.o = static_cast<T*>(o) + bh * ld;
+        ca.idx = idx + bh * lk;
+        ca.w = w + bh * lk;
+        if ((e = hils::launch_chunk_attention_cm<D>(ca, st)) != hipSuccess) return e;
+      }
+      if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+      return hipSuccess;
+    }
+  }
   if ((e = hils::launch_chunk_attention<T, D>(aa, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
@@ -330,12 +377,12 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   hipError_t err;
   if (p->dtype == HILS_DTYPE_BF16) {
     err = p->head_dim == 64
-              ? run_prefill<hils::bf16, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, s)
-              : run_prefill<hils::bf16, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, s);
+              ? run_prefill<hils::bf16, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s)
+              : run_prefill<hils::bf16, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s);
   } else {
     err = p->head_dim == 64
-              ? run_prefill<float, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, s)
-              : run_prefill<float, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, s);
+              ? run_prefill<float, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s)
+              : run_prefill<float, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s);
   }
   if (err != hipSuccess) return hip_fail(err, "hils_prefill_fwd");
   return HILS_OK;

@@ -29,6 +29,28 @@ struct AttnArgs {
   float scale;
 };
 
+// Chunk-major attention of one (batch, head) pair, bf16: the pair's selections inverted into
+// per-chunk lists, each chunk attended only by the rows that selected it (one partial output
+// per (row, slot)), then every row's partials summed in slot order.  Pointers are the pair's
+// slices; cnt / cur hold N words, off / toff N + 1, ent L * k, partial L * k * d bf16.
+struct CmArgs {
+  const void* q;        // [L,d]
+  const void* key;      // [L,d]
+  const void* val;      // [L,d]
+  const int32_t* idx;   // [L,k]
+  const float* w;       // [L,k]
+  void* o;              // [L,d]
+  uint32_t* cnt;        // selections per chunk
+  uint32_t* off;        // first list entry of each chunk (exclusive prefix of cnt)
+  uint32_t* cur;        // fill cursors
+  uint32_t* toff;       // first work item of each chunk (prefix of ceil(cnt / kCmItem))
+  uint32_t* ent;        // list entries (row << 6 | slot), grouped by chunk
+  void* partial;        // [L,k,d] bf16: w_j * o_j of slot j of each row
+  int L, N, k;
+  float scale;
+};
+constexpr int kCmItem = 128;                   // list entries per work item (8 waves x 16 rows)
+
 // Decode Q-Cal code rows are padded to this many entries (zeros past the rank).
 constexpr int kTcodeStride = 64;
 
@@ -88,6 +110,8 @@ template <int D>
 hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st);   // bf16, k <= 64
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
+template <int D>
+hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st);
 
 template <typename T>
 hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int B, int D, int r,

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "libhils.so")
 HILS_OK = 0
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
+ATTN_UNION = 0
+ATTN_CHUNK_MAJOR = 1
 STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", -3: "HILS_ERR_ALIGNMENT",
           -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
@@ -29,7 +31,8 @@ class PrefillParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("q_tile", ctypes.c_int32), ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32)]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
+                ("attn_mode", ctypes.c_int32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -155,8 +158,10 @@ def _stream_handle(device):
 
 def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
             q_tile: int = 64, scale: Optional[float] = None, return_selection: bool = False,
-            out=None, workspace=None, events: Optional[StageEvents] = None):
+            out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0):
     """HiLS prefill.  q,k,v [B,H,L,d]; lmk [B,H,L/C,d]; h [B,L,D]; w_down [r,D]; w_up [H*d,r].
+    attn_mode: ATTN_UNION (0) or ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
+    between neighbouring rows).
 
     Returns o [B,H,L,d], or (o, idx [B,H,L,k] int32, w [B,H,L,k] float32)."""
     import torch
@@ -167,7 +172,8 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
     r = 0 if w_down is None else w_down.shape[0]
     D = 0 if h is None else h.shape[-1]
     p = PrefillParams(B, H, L, d, chunk, topk, q_tile, D, r, 0.0 if scale is None else float(scale),
-                      _dtype_code(q), events.ptr if events else None, events.n if events else 0)
+                      _dtype_code(q), events.ptr if events else None, events.n if events else 0,
+                      int(attn_mode))
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:

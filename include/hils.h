@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 1
+#define HILS_ABI_VERSION 2
 
 typedef enum {
   HILS_OK = 0,
@@ -60,7 +60,17 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  * 0 <= qcal_rank <= 64; hidden a positive multiple of 128 when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
  * stage_events: optional array of n_stage_events hipEvent_t handles (NULL if unused); when it
  * holds at least 4 events, event 0 is recorded before the first kernel and events 1..3 after the
- * Q-Cal, chunk-selection and chunk-attention kernels, on `stream`. */
+ * Q-Cal, chunk-selection and chunk-attention kernels, on `stream`.
+ * attn_mode selects how the chunk attention is organised; both compute the same result:
+ *   HILS_ATTN_UNION (0): each group of 128 consecutive queries stages the union of the chunks
+ *     its rows selected, once per group; best when neighbouring rows share most chunks (the
+ *     pages report high overlap between adjacent tokens for trained models).
+ *   HILS_ATTN_CHUNK_MAJOR (1, bf16 only): per (batch, head) pair the selections are inverted
+ *     into per-chunk row lists and each chunk is attended only by the rows that chose it; one
+ *     bf16 partial output per (row, slot) in the workspace, summed in slot order.  For
+ *     selections with little overlap between neighbouring rows.  The workspace grows by about
+ *     seq_len * topk * (2 * head_dim + 4) bytes. */
+typedef enum { HILS_ATTN_UNION = 0, HILS_ATTN_CHUNK_MAJOR = 1 } hils_attn_mode;
 typedef struct hils_prefill_params {
   int32_t batch, heads, seq_len, head_dim;
   int32_t chunk, topk, q_tile;
@@ -69,6 +79,7 @@ typedef struct hils_prefill_params {
   int32_t dtype;               /* hils_dtype */
   void* const* stage_events;
   int32_t n_stage_events;
+  int32_t attn_mode;           /* hils_attn_mode */
 } hils_prefill_params;
 
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a

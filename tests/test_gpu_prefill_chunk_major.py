@@ -1,0 +1,77 @@
+"""The chunk-major attention mode (attn_mode = 1) through the C ABI: against the CPU oracle, against
+the union-walk mode on the same selection, and run to run."""
+import numpy as np
+import pytest
+
+from chunk_wise_sparse_amd import hils, synth
+from parity import sample_rows
+from test_gpu_prefill import SMALL, _compare, _run, _to_dev, _torch
+
+pytestmark = pytest.mark.gpu
+
+CM = hils.ATTN_CHUNK_MAJOR
+SMALL_BF16 = [c for c in SMALL if c.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("cfg", SMALL_BF16, ids=lambda c: c.name)
+def test_chunk_major_all_rows(lib, cfg):
+    print(f"[case] chunk-major all rows {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg, attn_mode=CM)
+    _torch().cuda.synchronize()
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, o, idx, w, rows)
+
+
+def test_chunk_major_long_lists(lib):
+    """256 chunks, k = 32, i.i.d. queries: early chunks are chosen by thousands of rows (many
+    128-row work items per chunk), late ones by few (ragged last items)."""
+    cfg = synth.PrefillConfig("bf16_16k_k32_cm", 1, 2, 16384, 128, 64, 32, "bf16", 32, 512)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg, attn_mode=CM)
+    rows = sample_rows(1, 2, cfg.seq_len, 160, seed=21)
+    rows = sorted(set(rows) | {(0, h, i) for h in range(2) for i in range(0, 128, 3)})
+    _compare(inp, cfg, o, idx, w, rows)
+
+
+def test_chunk_major_deterministic(lib):
+    cfg = SMALL_BF16[0]
+    dev = _to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)
+    a = _run(lib, dev, cfg, attn_mode=CM)
+    b = _run(lib, dev, cfg, attn_mode=CM)
+    torch = _torch()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["prefill_128k", "prefill_512k_iid"])
+def test_chunk_major_matches_union_full_size(lib, name):
+    """Full-size workloads: the same selection (bitwise), and outputs of the two modes within the
+    bf16 tolerance on every row; rows of one head against the oracle."""
+    torch = _torch()
+    cfg = synth.CONFIGS[name]
+    print(f"[case] full size {cfg}", flush=True)
+    dev = synth.make_prefill_inputs_torch(cfg, "cuda")
+    o_u, idx_u, w_u = _run(lib, dev, cfg)
+    o_c, idx_c, w_c = _run(lib, dev, cfg, attn_mode=CM)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_u, idx_c) and torch.equal(w_u, w_c)
+    diff = (o_u.float() - o_c.float()).abs()
+    print(f"[parity] {name} chunk-major vs union: max {diff.max().item():.3g} mean {diff.mean().item():.3g}",
+          flush=True)
+    assert diff.max().item() <= 2e-2 and diff.mean().item() <= 1e-3
+    del diff, o_u, idx_u, w_u
+    heads = [cfg.heads - 1]
+    d = cfg.head_dim
+    rows = sample_rows(1, 1, cfg.seq_len, 12, seed=23)
+    sub = {key: dev[key][:, heads].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
+    pos = sorted({r[2] for r in rows})
+    h_sub = np.zeros((1, cfg.seq_len, cfg.hidden), dtype=np.float32)
+    h_sub[:, pos] = dev["h"][:, pos].float().cpu().numpy()
+    sub["h"] = h_sub
+    sub["w_down"] = dev["w_down"].float().cpu().numpy()
+    sub["w_up"] = np.concatenate([dev["w_up"][hh * d:(hh + 1) * d].float().cpu().numpy() for hh in heads])
+    sub_cfg = synth.PrefillConfig(cfg.name, 1, 1, cfg.seq_len, d, cfg.chunk, cfg.topk, cfg.dtype,
+                                  cfg.qcal_rank, cfg.hidden)
+    _compare(sub, sub_cfg, o_c[:, heads], idx_c[:, heads], w_c[:, heads], rows)

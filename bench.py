@@ -324,6 +324,14 @@ def main():
         torch.cuda.synchronize()
         ist = [sum(e.elapsed_ms(s, s + 1) for e in iev) / len(iev) for s in range(3)]
         istats.update(prefill_ms=sum(ist), qcal_code_ms=ist[0], select_ms=ist[1], attention_ms=ist[2])
+        # The same i.i.d. workload with the chunk-major attention mode (two timed prefills).
+        cev = [hils.StageEvents(4) for _ in range(2)]
+        for e in cev:
+            hils.prefill(Pi["q"], Pi["k"], Pi["v"], Pi["lmk"], Pi["h"], Pi["w_down"], Pi["w_up"],
+                         topk=pcfg.topk, out=o, events=e, attn_mode=hils.ATTN_CHUNK_MAJOR)
+        torch.cuda.synchronize()
+        cst = [sum(e.elapsed_ms(s, s + 1) for e in cev) / len(cev) for s in range(3)]
+        istats["chunk_major"] = dict(prefill_ms=sum(cst), select_ms=cst[1], attention_ms=cst[2])
         ustats["iid_queries"] = istats
         del Pi
 

@@ -957,11 +957,23 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
       vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
     }
   };
+  // A wave's tile of an item: list entry (row << 6 | slot) and the row's q fragments.
+  auto load_tile = [&](uint32_t e0_, uint32_t e1_, uint32_t& pe_, bf16x8 (&qf_)[NF]) {
+    const uint32_t t0_ = e0_ + 16 * wave;
+    if (t0_ < e1_) {
+      pe_ = a.ent[t0_ + m < e1_ ? t0_ + m : t0_];
+      const bf16* qp = Q + (size_t)(pe_ >> 6) * D + g * (D / 4);
+#pragma unroll
+      for (int st = 0; st < NF; ++st) qf_[st] = load_frag<bf16>(qp + st * 8);
+    }
+  };
   uint32_t item = blockIdx.x;
   if (item >= items) return;                   // workgroup-uniform
   int j;
-  uint32_t e0, e1;
+  uint32_t e0, e1, pe = 0;
+  bf16x8 qf[NF];
   locate(item, j, e0, e1);
+  load_tile(e0, e1, pe, qf);
   load_kv(j);
   for (;;) {
     __syncthreads();                           // the previous item's LDS reads are done
@@ -974,27 +986,21 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
       *reinterpret_cast<u32x4*>(sv_ + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
     }
     __syncthreads();
+    // The next item: its list entries and K/V are requested now, its q rows after this item's
+    // work (the memory counter drains in issue order, and this item's q are already here).
     const uint32_t next = item + gridDim.x;
     const bool has_next = next < items;        // workgroup-uniform
-    // This tile's rows and queries are read before the next item's K/V (the memory counter
-    // drains in issue order).
+    int jn = 0;
+    uint32_t e0n = 0, e1n = 0, pen = 0;
+    if (has_next) {
+      locate(next, jn, e0n, e1n);
+      const uint32_t t0n = e0n + 16 * wave;
+      if (t0n < e1n) pen = a.ent[t0n + m < e1n ? t0n + m : t0n];
+      load_kv(jn);
+    }
     const uint32_t t0 = e0 + 16 * wave;
     const bool act = t0 < e1;                  // wave-uniform
     const bool valid = act && t0 + m < e1;
-    uint32_t pe = 0;
-    bf16x8 qf[NF];
-    if (act) {
-      pe = a.ent[valid ? t0 + m : t0];
-      const bf16* qp = Q + (size_t)(pe >> 6) * D + g * (D / 4);
-#pragma unroll
-      for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
-    }
-    int jn = 0;
-    uint32_t e0n = 0, e1n = 0;
-    if (has_next) {
-      locate(next, jn, e0n, e1n);
-      load_kv(jn);
-    }
     if (act) {
       const int r = (int)(pe >> 6), es = (int)(pe & 63u);
       float sc[16];
@@ -1053,6 +1059,12 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
       }
     }
     if (!has_next) break;
+    if (e0n + 16 * wave < e1n) {
+      pe = pen;
+      const bf16* qp = Q + (size_t)(pe >> 6) * D + g * (D / 4);
+#pragma unroll
+      for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
+    }
     item = next;
     j = jn;
     e0 = e0n;

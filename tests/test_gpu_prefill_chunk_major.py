@@ -75,3 +75,22 @@ def test_chunk_major_matches_union_full_size(lib, name):
     sub_cfg = synth.PrefillConfig(cfg.name, 1, 1, cfg.seq_len, d, cfg.chunk, cfg.topk, cfg.dtype,
                                   cfg.qcal_rank, cfg.hidden)
     _compare(sub, sub_cfg, o_c[:, heads], idx_c[:, heads], w_c[:, heads], rows)
+
+
+EDGE = [
+    synth.PrefillConfig("cm_one_chunk", 1, 2, 64, 128, 64, 4, "bf16", 0, 0),
+    synth.PrefillConfig("cm_three_chunks_k1", 2, 1, 192, 64, 64, 1, "bf16", 8, 128),
+    synth.PrefillConfig("cm_five_chunks_k64", 1, 3, 320, 128, 64, 64, "bf16", 4, 128),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_chunk_major_edge_sizes(lib, cfg):
+    """One chunk (a single list), a length that is not a multiple of 128 rows with k = 1, and k
+    larger than the number of chunks (padded selections: fewer valid slots than k)."""
+    print(f"[case] chunk-major {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg, attn_mode=CM)
+    _torch().cuda.synchronize()
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, o, idx, w, rows)

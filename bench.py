@@ -167,6 +167,39 @@ def cpu_baseline(dev, cfg, budget_s=12.0):
                        f"({dt:.1f} s, single-threaded NumPy oracle)")
 
 
+def length_sweep(lengths=(32768, 65536, 131072, 262144, 524288), reps=3):
+    """Prefill time against sequence length on the 128K workload's shape (H = 32, d = 128, k = 32,
+    Q-Cal r = 32, random-walk queries): stage times and algorithmic TFLOP/s per length.  The
+    scoring work grows as L^2 / C and the attention work as L * k * C."""
+    import dataclasses
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+    hils.load()
+    dev = torch.device("cuda:0")
+    base = synth.CONFIGS["prefill_128k"]
+    for L in lengths:
+        cfg = dataclasses.replace(base, name=f"prefill_{L // 1024}k_k32", seq_len=L)
+        P = synth.make_prefill_inputs_torch(cfg, dev)
+        o = torch.empty_like(P["q"])
+        ws = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        run = lambda e=None: hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
+                                          topk=cfg.topk, out=o, workspace=ws, events=e)
+        run()
+        ev = [hils.StageEvents(4) for _ in range(reps)]
+        for e in ev:
+            run(e)
+        torch.cuda.synchronize()
+        st = [sum(e.elapsed_ms(s, s + 1) for e in ev) / reps for s in range(3)]
+        w = prefill_work(cfg)
+        ms = sum(st)
+        print(json.dumps(dict(seq_len=L, prefill_ms=ms, qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
+                              tflops=w["total"] / (ms * 1e-3) / 1e12,
+                              select_tflops=w["select"] / (st[1] * 1e-3) / 1e12,
+                              attention_tflops=w["attention"] / (st[2] * 1e-3) / 1e12)), flush=True)
+        del P, o, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +210,9 @@ def main():
     ap.add_argument("--no-union-stats", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the prefill of the 128K workload's shape at 32K..512K tokens "
+                         "(one JSON line per length) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -185,6 +221,9 @@ def main():
 
     if args.calib_copy:
         calib_copy()
+        return
+    if args.sweep:
+        length_sweep()
         return
 
     import torch

@@ -25,6 +25,11 @@
 // keeps one LDS stage and the next chunk in registers (two barriers per chunk); the other two
 // compute chunk t from one of two stages while chunk t+1 is written to the other and chunk t+2
 // is in flight.
+//
+// Chunk-major mode (cm_* kernels, bf16, chosen by the caller): for selections whose rows share
+// few chunks, one (batch, head) pair at a time is turned into per-chunk row lists, each chunk's
+// K/V is staged once per 128 rows that chose it, and every row sums its per-slot partial outputs
+// in slot order.
 #include <float.h>
 
 #include "hils_device.h"

@@ -192,10 +192,26 @@ def length_sweep(lengths=(32768, 65536, 131072, 262144, 524288), reps=3):
         st = [sum(e.elapsed_ms(s, s + 1) for e in ev) / reps for s in range(3)]
         w = prefill_work(cfg)
         ms = sum(st)
+        # Context only: dense causal attention of the same shape through PyTorch's own
+        # scaled_dot_product_attention (not this library), timed with events on its stream.
+        dense_ms = None
+        try:
+            f = torch.nn.functional.scaled_dot_product_attention
+            f(P["q"], P["k"], P["v"], is_causal=True)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(reps):
+                f(P["q"], P["k"], P["v"], is_causal=True)
+            a1.record()
+            torch.cuda.synchronize()
+            dense_ms = a0.elapsed_time(a1) / reps
+        except RuntimeError as ex:
+            print(f"[bench] dense attention at {L}: {ex}", file=sys.stderr, flush=True)
         print(json.dumps(dict(seq_len=L, prefill_ms=ms, qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
                               tflops=w["total"] / (ms * 1e-3) / 1e12,
                               select_tflops=w["select"] / (st[1] * 1e-3) / 1e12,
-                              attention_tflops=w["attention"] / (st[2] * 1e-3) / 1e12)), flush=True)
+                              attention_tflops=w["attention"] / (st[2] * 1e-3) / 1e12,
+                              dense_causal_sdpa_ms=dense_ms)), flush=True)
         del P, o, ws
         torch.cuda.empty_cache()
 
@@ -212,7 +228,8 @@ def main():
                     help="only run plain 1 GiB device copies (counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the prefill of the 128K workload's shape at 32K..512K tokens "
-                         "(one JSON line per length) and exit")
+                         "(one JSON line per length, with PyTorch's dense causal attention of the "
+                         "same shape for context) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

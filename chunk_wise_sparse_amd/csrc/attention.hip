@@ -130,8 +130,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
   const int k = a.topk;
   const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
-  const T* Kb = static_cast<const T*>(a.key) + (size_t)bh * a.L * D;
-  const T* Vb = static_cast<const T*>(a.val) + (size_t)bh * a.L * D;
+  const T* Kb = static_cast<const T*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const T* Vb = static_cast<const T*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const size_t row0 = (size_t)bh * a.L;
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
@@ -418,8 +418,8 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const Att
   const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
   const int k = a.topk;
   const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
-  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)bh * a.L * D;
-  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)bh * a.L * D;
+  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const size_t row0 = (size_t)bh * a.L;
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
@@ -623,8 +623,8 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block2_kernel(const At
   const int q0 = (int)(gid % groups) * QG;   // first query position of the group
   const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
   const int k = a.topk;
-  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)bh * a.L * D;
-  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)bh * a.L * D;
+  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const size_t row0 = (size_t)bh * a.L;
 
   // Union bitmap of the group's selections (causal chunks only).

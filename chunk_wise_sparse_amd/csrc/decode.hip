@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   // Raw buffer loads through a descriptor over the pair's n_b landmark rows: rows past n_b (and
   // blocks past the last) read as zeros without a memory access, so no load needs a clamp or a
   // branch.
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D,
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.Nmax * D,
                                                 n_b * D * (int)sizeof(T));
   const int lane_off = (wave * kScoreRowsPerWave * D + sub * D + seg * VE) * (int)sizeof(T);
   constexpr int kBlockBytes = kScoreChunksPerBlock * D * (int)sizeof(T);
@@ -708,14 +708,14 @@ __device__ __forceinline__ void gather_pair(const DecodeArgs& a, int bh, int kvl
     CG cg;
     int u = wave;
     Slot s = slot_of(jl, wl, u, kvl);
-    CG::load(CG::rows(a.k_cache, bh, a.Lmax, s), cg.kr, lane);
-    CG::load(CG::rows(a.v_cache, bh, a.Lmax, s), cg.vr, lane);
+    CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.kr, lane);
+    CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.vr, lane);
     for (; u + NWV < a.k; u += NWV) {
       cg.scores(qf, s.n_vis, sp[wave], lane);
       const Slot nx = slot_of(jl, wl, u + NWV, kvl);
-      CG::load(CG::rows(a.k_cache, bh, a.Lmax, nx), cg.kr, lane);
+      CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, nx), cg.kr, lane);
       cg.finish(a.scale, s, sp[wave], lane, acc);
-      CG::load(CG::rows(a.v_cache, bh, a.Lmax, nx), cg.vr, lane);
+      CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, nx), cg.vr, lane);
       s = nx;
     }
     cg.scores(qf, s.n_vis, sp[wave], lane);
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void decode_fused_kernel(const De
 
   // ---- landmark scan: iteration it covers rows [512 it, 512 it + 512), wave w 128 of them ----
   const int seg = lane % LPR, sub = lane / LPR;
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)bh * a.Nmax * D,
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(static_cast<const T*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.Nmax * D,
                                                 n * D * (int)sizeof(T));
   const int lane_off = (wave * kFusedRowsPerWave * D + sub * D + seg * VE) * (int)sizeof(T);
   constexpr int kIterBytes = kFusedRows * D * (int)sizeof(T);
@@ -1047,8 +1047,8 @@ __global__ __launch_bounds__(256) void decode_attend_split_kernel(const DecodeAr
   s.n_vis = live ? min(kChunk, kvl - s.j * kChunk) : 0;
   s.w = live ? a.w[(size_t)bh * a.k + u] : 0.f;
   CG cg;
-  CG::load(CG::rows(a.k_cache, bh, a.Lmax, s), cg.kr, lane);
-  CG::load(CG::rows(a.v_cache, bh, a.Lmax, s), cg.vr, lane);
+  CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.kr, lane);
+  CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.vr, lane);
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];

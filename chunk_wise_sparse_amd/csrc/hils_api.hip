@@ -80,6 +80,8 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (!(isfinite(p->scale))) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events))
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+  if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
+    return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
   if (p->attn_mode != HILS_ATTN_UNION && p->attn_mode != HILS_ATTN_CHUNK_MAJOR)
     return fail(HILS_ERR_UNSUPPORTED, "attn_mode %d is not supported", p->attn_mode);
   if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR && p->dtype != HILS_DTYPE_BF16)
@@ -142,6 +144,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   sa.idx = idx;
   sa.w = w;
   sa.B = p->batch;
+  sa.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
   sa.H = p->heads;
   sa.L = p->seq_len;
   sa.N = p->seq_len / 64;
@@ -158,6 +161,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   aa.w = w;
   aa.o = o;
   aa.B = p->batch;
+  aa.G = sa.G;
   aa.H = p->heads;
   aa.L = p->seq_len;
   aa.N = p->seq_len / 64;
@@ -179,8 +183,9 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
       const size_t ld = (size_t)p->seq_len * D, lk = (size_t)p->seq_len * p->topk;
       for (size_t bh = 0; bh < (size_t)p->batch * p->heads; ++bh) {
         ca.q = static_cast<const T*>(q) + bh * ld;
-        ca.key = static_cast<const T*>(k) + bh * ld;
-        ca.val = static_cast<const T*>(v) + bh * ld;
+        const size_t kvbh = (bh / p->heads) * (p->heads / aa.G) + (bh % p->heads) / aa.G;
+        ca.key = static_cast<const T*>(k) + kvbh * ld;
+        ca.val = static_cast<const T*>(v) + kvbh * ld;
         ca.o = static_cast<T*>(o) + bh * ld;
         ca.idx = idx + bh * lk;
         ca.w = w + bh * lk;
@@ -226,6 +231,8 @@ int check_decode_params(const hils_decode_params* p) {
   if (!(isfinite(p->scale))) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events))
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+  if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
+    return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
   if ((double)p->batch * p->heads > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
   return HILS_OK;
@@ -285,6 +292,7 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.partial = reinterpret_cast<float*>(ws + L.partial);
   a.o = o;
   a.B = p->batch;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
   a.H = p->heads;
   a.Lmax = p->max_kv_len;
   a.Nmax = (p->max_kv_len + 63) / 64;
@@ -355,8 +363,9 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   const size_t e = elem_bytes(p->dtype);
   const size_t B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim, kk = p->topk;
   const size_t r = p->qcal_rank, D = p->hidden;
-  const Range in[] = {{q, B * H * S * d * e, "q"},   {k, B * H * S * d * e, "k"},
-                      {v, B * H * S * d * e, "v"},   {lmk, B * H * (S / 64) * d * e, "lmk"},
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
+  const Range in[] = {{q, B * H * S * d * e, "q"},   {k, B * Hk * S * d * e, "k"},
+                      {v, B * Hk * S * d * e, "v"},  {lmk, B * Hk * (S / 64) * d * e, "lmk"},
                       {h, qcal ? B * S * D * e : 0, "h"}, {w_down, qcal ? r * D * e : 0, "w_down"},
                       {w_up, qcal ? H * d * r * e : 0, "w_up"}};
   const Range out[] = {{o, B * H * S * d * e, "o"},
@@ -416,8 +425,9 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
   const size_t e = elem_bytes(p->dtype);
   const size_t B = p->batch, H = p->heads, Lm = p->max_kv_len, d = p->head_dim, kk = p->topk;
   const size_t N = (Lm + 63) / 64, r = p->qcal_rank, D = p->hidden;
-  const Range in[] = {{q, B * H * d * e, "q"},           {k_cache, B * H * Lm * d * e, "k_cache"},
-                      {v_cache, B * H * Lm * d * e, "v_cache"}, {lmk, B * H * N * d * e, "lmk"},
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
+  const Range in[] = {{q, B * H * d * e, "q"},           {k_cache, B * Hk * Lm * d * e, "k_cache"},
+                      {v_cache, B * Hk * Lm * d * e, "v_cache"}, {lmk, B * Hk * N * d * e, "lmk"},
                       {kv_len, B * 4, "kv_len"},          {h, qcal ? B * D * e : 0, "h"},
                       {w_down, qcal ? r * D * e : 0, "w_down"}, {w_up, qcal ? H * d * r * e : 0, "w_up"}};
   const Range out[] = {{o, B * H * d * e, "o"},

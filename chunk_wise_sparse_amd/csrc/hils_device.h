@@ -152,6 +152,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Remap a workgroup id so that consecutive logical tiles run on the same XCD.  Workgroups are
 // dispatched round-robin over the 8 XCDs; this is a bijection on [0, total).
+// Key/value (and landmark) pair of query pair bh = b * H + h when G consecutive query heads
+// share one key/value head (grouped-query attention; G = 1 is one head each).
+__device__ __forceinline__ int kv_pair(int bh, int H, int G) {
+  return G == 1 ? bh : (bh / H) * (H / G) + (bh % H) / G;
+}
+
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   const uint32_t nx = 8;
   uint32_t x = bid % nx, slot = bid / nx;

@@ -9,23 +9,25 @@ typedef __bf16 bf16;
 
 struct SelectArgs {
   const void* q;        // [B,H,L,d]
-  const void* lmk;      // [B,H,N,d]
+  const void* lmk;      // [B,H/G,N,d]
   const float* tcode;   // [B*L, r] fp32 Q-Cal code (NULL if r == 0)
   const void* w_up;     // [H*d, r]
   int32_t* idx;         // [B,H,L,k]
   float* w;             // [B,H,L,k]
   int B, H, L, N, k, r;
+  int G;                // query heads per key/value (and landmark) head
   float scale;
 };
 
 struct AttnArgs {
   const void* q;        // [B,H,L,d]
-  const void* key;      // [B,H,L,d]
-  const void* val;      // [B,H,L,d]
+  const void* key;      // [B,H/G,L,d]
+  const void* val;      // [B,H/G,L,d]
   const int32_t* idx;   // [B,H,L,k]
   const float* w;       // [B,H,L,k]
   void* o;              // [B,H,L,d]
   int B, H, L, N, topk;
+  int G;                // query heads per key/value head
   float scale;
 };
 
@@ -80,9 +82,9 @@ struct DecodeArgs {
   const void* q;        // [B,H,d] raw query
   const void* w_up;     // [H*d, r] Q-Cal up-projection (unused when r == 0)
   const float* tcode;   // [B, kTcodeStride] Q-Cal code W_down h, zero past r (workspace)
-  const void* k_cache;  // [B,H,Lmax,d]
+  const void* k_cache;  // [B,H/G,Lmax,d]
   const void* v_cache;
-  const void* lmk;      // [B,H,Nmax,d]
+  const void* lmk;      // [B,H/G,Nmax,d]
   const int32_t* kv_len;
   float* scores;        // [B*H][score_stride] workspace, workgroup-major (decode_score_pos)
   int32_t* idx;         // [B,H,k]
@@ -90,6 +92,7 @@ struct DecodeArgs {
   float* partial;       // [B,H,k,d] workspace (split attend only)
   void* o;              // [B,H,d]
   int B, H, Lmax, Nmax, k, r;
+  int G;                // query heads per key/value (and landmark) head
   int score_qb;         // decode_score_qb(B*H, Nmax)
   size_t score_stride;  // decode_score_stride(Nmax, score_qb)
   // Candidate mode (Nmax <= 8192; NULL otherwise): scan workgroup (pair, y) writes its top-k

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const SelectArgs a) {
   const int n_lt = (n_cand + 63) >> 6;
   const int kk = min(a.k, n_cand);
   const T* Q = static_cast<const T*>(a.q) + (size_t)bh * a.L * D;
-  const T* LM = static_cast<const T*>(a.lmk) + (size_t)bh * a.N * D;
+  const T* LM = static_cast<const T*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.N * D;
 
   // ---------------- Q-Cal: q~ in the landmark-fragment layout -------------------------------
   typename Mfma<T>::frag qf[NF];

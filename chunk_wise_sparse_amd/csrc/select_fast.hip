@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   const int kq = min(a.k, n_cand);
   const int q0 = c * 64;
   const bf16* Q = static_cast<const bf16*>(a.q) + (size_t)bh * a.L * D;
-  const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)bh * a.N * D;
+  const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.N * D;
   float* ls = &sm.w[wave].list.s[lane];        // this lane's list, stride 64
   uint16_t* lj = &sm.w[wave].list.j[lane];
 

@@ -32,7 +32,7 @@ class PrefillParams(ctypes.Structure):
                 ("q_tile", ctypes.c_int32), ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
-                ("attn_mode", ctypes.c_int32)]
+                ("attn_mode", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -40,7 +40,8 @@ class DecodeParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32)]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32)]
 
 
 _lib = None
@@ -159,7 +160,8 @@ def _stream_handle(device):
 def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
             q_tile: int = 64, scale: Optional[float] = None, return_selection: bool = False,
             out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0):
-    """HiLS prefill.  q,k,v [B,H,L,d]; lmk [B,H,L/C,d]; h [B,L,D]; w_down [r,D]; w_up [H*d,r].
+    """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
+    w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
     attn_mode: ATTN_UNION (0) or ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
     between neighbouring rows).
 
@@ -173,7 +175,7 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
     D = 0 if h is None else h.shape[-1]
     p = PrefillParams(B, H, L, d, chunk, topk, q_tile, D, r, 0.0 if scale is None else float(scale),
                       _dtype_code(q), events.ptr if events else None, events.n if events else 0,
-                      int(attn_mode))
+                      int(attn_mode), int(k.shape[1]))
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:
@@ -192,8 +194,8 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
 def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, topk: int,
            chunk: int = 64, scale: Optional[float] = None, return_selection: bool = False,
            out=None, workspace=None, events: Optional[StageEvents] = None):
-    """HiLS decode step.  q [B,H,d]; caches [B,H,Lmax,d]; lmk [B,H,ceil(Lmax/C),d]; kv_len [B] int32
-    (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k])."""
+    """HiLS decode step.  q [B,H,d]; caches [B,Hkv,Lmax,d]; lmk [B,Hkv,ceil(Lmax/C),d] (Hkv divides
+    H); kv_len [B] int32 (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k])."""
     import torch
     lib = load()
     B, H, d = q.shape
@@ -205,7 +207,8 @@ def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, 
     r = 0 if w_down is None else w_down.shape[0]
     D = 0 if h is None else h.shape[-1]
     p = DecodeParams(B, H, Lmax, d, chunk, topk, D, r, 0.0 if scale is None else float(scale),
-                     _dtype_code(q), events.ptr if events else None, events.n if events else 0)
+                     _dtype_code(q), events.ptr if events else None, events.n if events else 0,
+                     int(k_cache.shape[1]))
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 2
+#define HILS_ABI_VERSION 3
 
 typedef enum {
   HILS_OK = 0,
@@ -71,6 +71,11 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  *     selections with little overlap between neighbouring rows.  The workspace grows by about
  *     seq_len * topk * (2 * head_dim + 4) bytes. */
 typedef enum { HILS_ATTN_UNION = 0, HILS_ATTN_CHUNK_MAJOR = 1 } hils_attn_mode;
+/* Grouped-query attention (both calls): kv_heads > 0 must divide heads; query head h then uses
+ * key/value head h / (heads / kv_heads), and k, v, lmk (prefill) or k_cache, v_cache, lmk
+ * (decode) hold kv_heads heads instead of heads.  Landmarks belong to the key/value head.
+ * Selection, weights and outputs stay per query head.  kv_heads = 0 or heads: one key/value
+ * head per query head. */
 typedef struct hils_prefill_params {
   int32_t batch, heads, seq_len, head_dim;
   int32_t chunk, topk, q_tile;
@@ -80,6 +85,7 @@ typedef struct hils_prefill_params {
   void* const* stage_events;
   int32_t n_stage_events;
   int32_t attn_mode;           /* hils_attn_mode */
+  int32_t kv_heads;            /* key/value (and landmark) heads; 0 = heads (see below) */
 } hils_prefill_params;
 
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a
@@ -98,6 +104,7 @@ typedef struct hils_decode_params {
   int32_t dtype;
   void* const* stage_events;
   int32_t n_stage_events;
+  int32_t kv_heads;            /* key/value (and landmark) heads; 0 = heads (see below) */
 } hils_decode_params;
 
 /* ABI version this library was built with (HILS_ABI_VERSION). */

@@ -23,20 +23,21 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 2
+    assert lib.hils_abi_version() == 3
 
 
 def _pp(**kw):
     base = dict(batch=1, heads=2, seq_len=2048, head_dim=64, chunk=64, topk=4, q_tile=64, hidden=128,
                 qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
-                attn_mode=0)
+                attn_mode=0, kv_heads=0)
     base.update(kw)
     return hils.PrefillParams(**base)
 
 
 def _dp(**kw):
     base = dict(batch=2, heads=2, max_kv_len=1000, head_dim=64, chunk=64, topk=4, hidden=128,
-                qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0)
+                qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
+                kv_heads=0)
     base.update(kw)
     return hils.DecodeParams(**base)
 
@@ -55,6 +56,7 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
     (dict(seq_len=2000), -2), (dict(q_tile=32), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
     (dict(dtype=7), -2), (dict(batch=0), -1), (dict(heads=-1), -1), (dict(scale=float("nan")), -1),
     (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=2), -2),
+    (dict(kv_heads=3), -1), (dict(kv_heads=-1), -1), (dict(kv_heads=4), -1),   # must divide heads = 2
     (dict(attn_mode=1), -2),                                   # chunk-major is bf16 only
 ])
 def test_prefill_rejects_bad_params(kw, status):
@@ -111,6 +113,9 @@ def test_decode_rejects_bad_arguments():
     assert call(_dp(head_dim=80)) == -2
     assert call(_dp(topk=100)) == -2
     assert call(_dp(max_kv_len=64 * 65536)) == -2
+    assert call(_dp(kv_heads=3)) == -1                          # must divide heads = 2
+    assert lib.hils_decode_workspace_size(ctypes.byref(_dp(kv_heads=1)), 0) > 0   # divides: accepted
+    assert lib.hils_decode_workspace_size(ctypes.byref(_dp(kv_heads=3)), 0) == 0
     assert call(_dp(), kv=None) == -1
     assert call(_dp(), kv=FAKE + (4 << 32) + 2) == -3
     assert call(_dp(), ws=None) == -4

@@ -588,7 +588,14 @@ struct Slot {
   int j;        // chunk index, -1 for an empty slot
   int n_vis;    // visible rows (0 for an empty slot)
   float w;      // inter-chunk weight
+  int page;     // page of the chunk in a paged cache (0 otherwise)
 };
+
+// Page of chunk j of sequence b in a paged cache, clamped to the pool; 0 without a block table.
+__device__ __forceinline__ int page_of(const DecodeArgs& a, int b, int j) {
+  if (!a.block_table) return 0;
+  return min(max(a.block_table[(size_t)b * a.bt_stride + max(j, 0)], 0), a.num_pages - 1);
+}
 
 template <typename T, int D>
 struct ChunkGather {
@@ -599,11 +606,19 @@ struct ChunkGather {
   typedef T vecT __attribute__((ext_vector_type(VE)));
   vecT kr[NIT], vr[NIT];
 
-  // Descriptor over the slot's visible rows of one (sequence, head) cache.
-  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(const void* cache, int bh, int Lmax,
+  // Descriptor over the slot's visible rows: in the (sequence, key/value head) cache, or in the
+  // slot's page of a paged pool [pages, H/G, 64, d].
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(const DecodeArgs& a, const void* cache, int bh,
                                                                 const Slot& s) {
-    return buffer_rsrc(static_cast<const T*>(cache) + ((size_t)bh * Lmax + (size_t)max(s.j, 0) * kChunk) * D,
-                       s.n_vis * D * (int)sizeof(T));
+    const int kvp = kv_pair(bh, a.H, a.G);
+    size_t row0;
+    if (a.block_table) {
+      const int hk = a.H / a.G;
+      row0 = ((size_t)s.page * hk + kvp % hk) * kChunk;
+    } else {
+      row0 = (size_t)kvp * a.Lmax + (size_t)max(s.j, 0) * kChunk;
+    }
+    return buffer_rsrc(static_cast<const T*>(cache) + row0 * D, s.n_vis * D * (int)sizeof(T));
   }
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, vecT (&dst)[NIT], int lane) {
     const int seg = lane % LPR, sub = lane / LPR;
@@ -669,9 +684,10 @@ struct ChunkGather {
 
 // Slot u of (sequence b, head): chunk, visible rows and weight.  jl / wl: lane u holds slot u's
 // index and weight (lanes >= k: -1 and 0); u is wave-uniform.
-__device__ __forceinline__ Slot slot_of(int jl, float wl, int u, int kvl) {
+__device__ __forceinline__ Slot slot_of(int jl, float wl, int pl, int u, int kvl) {
   Slot s;
   s.j = __builtin_amdgcn_readlane(jl, u);
+  s.page = __builtin_amdgcn_readlane(pl, u);
   const bool live = s.j >= 0 && s.j * kChunk < kvl;
   s.n_vis = live ? min(kChunk, kvl - s.j * kChunk) : 0;
   s.w = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u)) : 0.f;
@@ -699,6 +715,7 @@ __device__ __forceinline__ void gather_pair(const DecodeArgs& a, int bh, int kvl
   typedef ChunkGather<T, D> CG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pl = page_of(a, bh / a.H, jl);     // lane u: page of slot u's chunk (paged caches)
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];
@@ -707,15 +724,15 @@ __device__ __forceinline__ void gather_pair(const DecodeArgs& a, int bh, int kvl
   if (wave < a.k) {
     CG cg;
     int u = wave;
-    Slot s = slot_of(jl, wl, u, kvl);
-    CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.kr, lane);
-    CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.vr, lane);
+    Slot s = slot_of(jl, wl, pl, u, kvl);
+    CG::load(CG::rows(a, a.k_cache, bh, s), cg.kr, lane);
+    CG::load(CG::rows(a, a.v_cache, bh, s), cg.vr, lane);
     for (; u + NWV < a.k; u += NWV) {
       cg.scores(qf, s.n_vis, sp[wave], lane);
-      const Slot nx = slot_of(jl, wl, u + NWV, kvl);
-      CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, nx), cg.kr, lane);
+      const Slot nx = slot_of(jl, wl, pl, u + NWV, kvl);
+      CG::load(CG::rows(a, a.k_cache, bh, nx), cg.kr, lane);
       cg.finish(a.scale, s, sp[wave], lane, acc);
-      CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, nx), cg.vr, lane);
+      CG::load(CG::rows(a, a.v_cache, bh, nx), cg.vr, lane);
       s = nx;
     }
     cg.scores(qf, s.n_vis, sp[wave], lane);
@@ -1046,9 +1063,10 @@ __global__ __launch_bounds__(256) void decode_attend_split_kernel(const DecodeAr
   const bool live = s.j >= 0 && s.j * kChunk < kvl;
   s.n_vis = live ? min(kChunk, kvl - s.j * kChunk) : 0;
   s.w = live ? a.w[(size_t)bh * a.k + u] : 0.f;
+  s.page = page_of(a, b, s.j);
   CG cg;
-  CG::load(CG::rows(a.k_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.kr, lane);
-  CG::load(CG::rows(a.v_cache, kv_pair(bh, a.H, a.G), a.Lmax, s), cg.vr, lane);
+  CG::load(CG::rows(a, a.k_cache, bh, s), cg.kr, lane);
+  CG::load(CG::rows(a, a.v_cache, bh, s), cg.vr, lane);
   float qf[CG::VE];
   load_query<T, D>(a, bh, lane, qf);
   float acc[CG::VE];

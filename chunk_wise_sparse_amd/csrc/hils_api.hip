@@ -233,6 +233,9 @@ int check_decode_params(const hils_decode_params* p) {
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
   if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
     return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
+  if (p->block_table && (p->num_pages < 1 || p->block_table_stride < (p->max_kv_len + 63) / 64))
+    return fail(HILS_ERR_INVALID_ARG, "paged cache: num_pages >= 1 and block_table_stride >= %d needed",
+                (p->max_kv_len + 63) / 64);
   if ((double)p->batch * p->heads > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
   return HILS_OK;
@@ -293,6 +296,9 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.o = o;
   a.B = p->batch;
   a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.block_table = p->block_table;
+  a.bt_stride = p->block_table_stride;
+  a.num_pages = p->num_pages;
   a.H = p->heads;
   a.Lmax = p->max_kv_len;
   a.Nmax = (p->max_kv_len + 63) / 64;
@@ -426,8 +432,12 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
   const size_t B = p->batch, H = p->heads, Lm = p->max_kv_len, d = p->head_dim, kk = p->topk;
   const size_t N = (Lm + 63) / 64, r = p->qcal_rank, D = p->hidden;
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
-  const Range in[] = {{q, B * H * d * e, "q"},           {k_cache, B * Hk * Lm * d * e, "k_cache"},
-                      {v_cache, B * Hk * Lm * d * e, "v_cache"}, {lmk, B * Hk * N * d * e, "lmk"},
+  const size_t cache = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * Lm * d * e;
+  if (p->block_table && ((uintptr_t)p->block_table & 3))
+    return fail(HILS_ERR_ALIGNMENT, "block_table is not 4-byte aligned");
+  const Range in[] = {{q, B * H * d * e, "q"},           {k_cache, cache, "k_cache"},
+                      {v_cache, cache, "v_cache"},       {lmk, B * Hk * N * d * e, "lmk"},
+                      {p->block_table, p->block_table ? B * (size_t)p->block_table_stride * 4 : 0, "block_table"},
                       {kv_len, B * 4, "kv_len"},          {h, qcal ? B * D * e : 0, "h"},
                       {w_down, qcal ? r * D * e : 0, "w_down"}, {w_up, qcal ? H * d * r * e : 0, "w_up"}};
   const Range out[] = {{o, B * H * d * e, "o"},

@@ -93,6 +93,11 @@ struct DecodeArgs {
   void* o;              // [B,H,d]
   int B, H, Lmax, Nmax, k, r;
   int G;                // query heads per key/value (and landmark) head
+  // Paged caches (NULL: k_cache / v_cache are [B,H/G,Lmax,d]): k_cache / v_cache are pools of
+  // num_pages pages [num_pages, H/G, 64, d], and chunk j of sequence b is page
+  // block_table[b * bt_stride + j] (clamped to the pool).
+  const int32_t* block_table;
+  int bt_stride, num_pages;
   int score_qb;         // decode_score_qb(B*H, Nmax)
   size_t score_stride;  // decode_score_stride(Nmax, score_qb)
   // Candidate mode (Nmax <= 8192; NULL otherwise): scan workgroup (pair, y) writes its top-k

@@ -41,7 +41,8 @@ class DecodeParams(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
-                ("kv_heads", ctypes.c_int32)]
+                ("kv_heads", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("block_table_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -193,13 +194,22 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
 
 def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, topk: int,
            chunk: int = 64, scale: Optional[float] = None, return_selection: bool = False,
-           out=None, workspace=None, events: Optional[StageEvents] = None):
+           out=None, workspace=None, events: Optional[StageEvents] = None, block_table=None,
+           max_kv_len: Optional[int] = None):
     """HiLS decode step.  q [B,H,d]; caches [B,Hkv,Lmax,d]; lmk [B,Hkv,ceil(Lmax/C),d] (Hkv divides
-    H); kv_len [B] int32 (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k])."""
+    H); kv_len [B] int32 (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k]).
+    Paged caches: block_table [B, S] int32 (device) and caches [pages, Hkv, C, d]; chunk j of
+    sequence b is page block_table[b, j]; max_kv_len (<= S * C) is then required."""
     import torch
     lib = load()
     B, H, d = q.shape
-    Lmax = k_cache.shape[2]
+    paged = block_table is not None
+    if paged:
+        if (max_kv_len is None or block_table.dtype != torch.int32 or block_table.device != q.device
+                or not block_table.is_contiguous() or block_table.dim() != 2 or block_table.shape[0] != B):
+            raise ValueError("block_table must be a contiguous [B, S] int32 tensor on the query's device, "
+                             "with max_kv_len given")
+    Lmax = int(max_kv_len) if paged else k_cache.shape[2]
     _require([("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("lmk", lmk), ("h", h),
               ("w_down", w_down), ("w_up", w_up)], q.device, q.dtype)
     if kv_len.dtype != torch.int32 or kv_len.device != q.device or not kv_len.is_contiguous():
@@ -208,7 +218,8 @@ def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, 
     D = 0 if h is None else h.shape[-1]
     p = DecodeParams(B, H, Lmax, d, chunk, topk, D, r, 0.0 if scale is None else float(scale),
                      _dtype_code(q), events.ptr if events else None, events.n if events else 0,
-                     int(k_cache.shape[1]))
+                     int(k_cache.shape[1]), block_table.data_ptr() if paged else None,
+                     int(block_table.shape[1]) if paged else 0, int(k_cache.shape[0]) if paged else 0)
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:

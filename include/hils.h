@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 3
+#define HILS_ABI_VERSION 4
 
 typedef enum {
   HILS_OK = 0,
@@ -105,7 +105,14 @@ typedef struct hils_decode_params {
   void* const* stage_events;
   int32_t n_stage_events;
   int32_t kv_heads;            /* key/value (and landmark) heads; 0 = heads (see below) */
+  const int32_t* block_table;  /* device, int32; NULL for contiguous caches (see below) */
+  int32_t block_table_stride;  /* block_table entries per sequence, >= ceil(max_kv_len / chunk) */
+  int32_t num_pages;           /* pages in the k_cache / v_cache pools when paged */
 } hils_decode_params;
+/* Paged caches (decode): with block_table non-NULL, k_cache and v_cache are pools of num_pages
+ * pages of one chunk each, [num_pages, kv heads, chunk, head_dim], and chunk j of sequence b is
+ * page block_table[b * block_table_stride + j] (entries outside [0, num_pages) are clamped).
+ * lmk stays [batch, kv heads, ceil(max_kv_len / chunk), head_dim]. */
 
 /* ABI version this library was built with (HILS_ABI_VERSION). */
 int hils_abi_version(void);

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 3
+    assert lib.hils_abi_version() == 4
 
 
 def _pp(**kw):
@@ -37,7 +37,7 @@ def _pp(**kw):
 def _dp(**kw):
     base = dict(batch=2, heads=2, max_kv_len=1000, head_dim=64, chunk=64, topk=4, hidden=128,
                 qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
-                kv_heads=0)
+                kv_heads=0, block_table=None, block_table_stride=0, num_pages=0)
     base.update(kw)
     return hils.DecodeParams(**base)
 
@@ -116,6 +116,10 @@ def test_decode_rejects_bad_arguments():
     assert call(_dp(kv_heads=3)) == -1                          # must divide heads = 2
     assert lib.hils_decode_workspace_size(ctypes.byref(_dp(kv_heads=1)), 0) > 0   # divides: accepted
     assert lib.hils_decode_workspace_size(ctypes.byref(_dp(kv_heads=3)), 0) == 0
+    # paged caches: a short block table row or an empty pool is rejected
+    assert call(_dp(block_table=FAKE + (11 << 32), block_table_stride=15, num_pages=100)) == -1
+    assert call(_dp(block_table=FAKE + (11 << 32), block_table_stride=16, num_pages=0)) == -1
+    assert call(_dp(block_table=FAKE + (11 << 32) + 2, block_table_stride=16, num_pages=100)) == -3
     assert call(_dp(), kv=None) == -1
     assert call(_dp(), kv=FAKE + (4 << 32) + 2) == -3
     assert call(_dp(), ws=None) == -4

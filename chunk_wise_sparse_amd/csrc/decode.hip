@@ -807,7 +807,9 @@ __global__ __launch_bounds__(kFusedWaves * 64) void decode_fused_kernel(const De
   __shared__ CandSelSmem sel;
   __shared__ float sp[NWV][64];
   __shared__ float wsum[NWV][D];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  // With grouped-query heads the G pairs that share a key/value head go to one XCD (one L2), so
+  // their landmark and chunk reads are shared there.
+  const int bh = a.G > 1 ? (int)xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);

@@ -1126,6 +1126,41 @@ hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Union probe for the automatic mode: workgroup s takes sampled 128-row group s * total / S and
+// adds the number of distinct chunks its rows selected to *out (zeroed by the caller's launch).
+__global__ __launch_bounds__(256) void union_probe_kernel(const int32_t* idx, int H, int L, int k, int gpr,
+                                                          uint32_t total_groups, uint32_t* out) {
+  extern __shared__ uint32_t bits[];
+  const uint32_t gsel = (uint32_t)(((uint64_t)blockIdx.x * total_groups) / gridDim.x);
+  const int bh = (int)(gsel / gpr), q0 = (int)(gsel % gpr) * 128;
+  const int rows = min(128, L - q0);
+  const int nwords = ((q0 + rows - 1) / 64 + 1 + 31) / 32;
+  for (int x = threadIdx.x; x < nwords; x += 256) bits[x] = 0u;
+  __syncthreads();
+  const int32_t* p = idx + ((size_t)bh * L + q0) * k;
+  for (int x = threadIdx.x; x < rows * k; x += 256) {
+    const int j = p[x];
+    if (j >= 0 && j < nwords * 32) atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  uint32_t c = 0;
+  for (int x = threadIdx.x; x < nwords; x += 256) c += __popc(bits[x]);
+  if (c) atomicAdd(out, c);
+  (void)H;
+}
+
+hipError_t launch_union_probe(const int32_t* idx, int B, int H, int L, int k, uint32_t* total, int* groups,
+                              hipStream_t st) {
+  const int gpr = (L + 127) / 128;             // 128-row groups per (batch, head)
+  const uint32_t all = (uint32_t)B * H * gpr;
+  const int S = all < 256u ? (int)all : 256;
+  *groups = S;
+  const size_t bm = (size_t)(((L + 63) / 64 + 31) / 32) * 4;
+  hipLaunchKernelGGL(cm_zero_kernel, dim3(1), dim3(256), 0, st, total, 1);
+  hipLaunchKernelGGL(union_probe_kernel, dim3(S), dim3(256), bm, st, idx, H, L, k, gpr, all, total);
+  return hipGetLastError();
+}
+
 template hipError_t launch_chunk_attention_cm<64>(const CmArgs&, hipStream_t);
 template hipError_t launch_chunk_attention_cm<128>(const CmArgs&, hipStream_t);
 

@@ -51,7 +51,7 @@ size_t elem_bytes(int dtype) { return dtype == HILS_DTYPE_BF16 ? 2 : 4; }
 // Prefill
 // ---------------------------------------------------------------------------------------------
 struct PrefillLayout {
-  size_t tcode, idx, w, cm_cnt, cm_off, cm_cur, cm_toff, cm_ent, cm_partial, total;
+  size_t tcode, idx, w, probe, cm_cnt, cm_off, cm_cur, cm_toff, cm_ent, cm_partial, total;
 };
 
 int check_prefill_params(const hils_prefill_params* p) {
@@ -82,9 +82,9 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
   if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
     return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
-  if (p->attn_mode != HILS_ATTN_UNION && p->attn_mode != HILS_ATTN_CHUNK_MAJOR)
+  if (p->attn_mode != HILS_ATTN_UNION && p->attn_mode != HILS_ATTN_CHUNK_MAJOR && p->attn_mode != HILS_ATTN_AUTO)
     return fail(HILS_ERR_UNSUPPORTED, "attn_mode %d is not supported", p->attn_mode);
-  if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR && p->dtype != HILS_DTYPE_BF16)
+  if (p->attn_mode != HILS_ATTN_UNION && p->dtype != HILS_DTYPE_BF16)
     return fail(HILS_ERR_UNSUPPORTED, "the chunk-major attention mode is bf16 only");
   const double bhld = (double)p->batch * p->heads * p->seq_len * p->head_dim;
   if (bhld > 4e18 / 8 || (double)p->batch * p->heads * (p->seq_len / 64) > 2147483647.0)
@@ -102,7 +102,9 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   if (!with_sel) off += align_up(B * H * S * k * sizeof(int32_t));
   L.w = off;
   if (!with_sel) off += align_up(B * H * S * k * sizeof(float));
-  if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR) {  // one (batch, head) pair at a time
+  if (p->attn_mode != HILS_ATTN_UNION) {       // chunk-major: one (batch, head) pair at a time
+    L.probe = off;                             // union probe counter (auto mode)
+    off += align_up(4);
     const size_t N = S / 64, d = p->head_dim;
     L.cm_cnt = off;
     off += align_up(N * 4);
@@ -168,7 +170,19 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   aa.topk = p->topk;
   aa.scale = scale;
   if constexpr (sizeof(T) == 2) {
-    if (p->attn_mode == HILS_ATTN_CHUNK_MAJOR) {
+    bool chunk_major = p->attn_mode == HILS_ATTN_CHUNK_MAJOR;
+    if (p->attn_mode == HILS_ATTN_AUTO) {      // measure the selection's overlap, then choose
+      uint32_t* probe = reinterpret_cast<uint32_t*>(ws + L.probe);
+      int groups = 0;
+      if ((e = hils::launch_union_probe(idx, p->batch, p->heads, p->seq_len, p->topk, probe, &groups, st)) !=
+          hipSuccess)
+        return e;
+      uint32_t total = 0;
+      if ((e = hipMemcpyAsync(&total, probe, 4, hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+      chunk_major = groups > 0 && (double)total / groups > 8.0 * p->topk;
+    }
+    if (chunk_major) {
       hils::CmArgs ca;
       ca.cnt = reinterpret_cast<uint32_t*>(ws + L.cm_cnt);
       ca.off = reinterpret_cast<uint32_t*>(ws + L.cm_off);

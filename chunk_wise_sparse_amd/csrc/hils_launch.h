@@ -120,6 +120,10 @@ template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st);
 template <int D>
 hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st);
+// Sum over up to 256 sampled 128-row groups of the number of distinct chunks their rows selected
+// (one uint32 at *total, overwritten); the number of groups sampled is returned in *groups.
+hipError_t launch_union_probe(const int32_t* idx, int B, int H, int L, int k, uint32_t* total,
+                              int* groups, hipStream_t st);
 
 template <typename T>
 hipError_t launch_decode_tcode(const T* hid, const T* w_down, float* tcode, int B, int D, int r,

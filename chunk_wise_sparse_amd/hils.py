@@ -20,6 +20,7 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 ATTN_UNION = 0
 ATTN_CHUNK_MAJOR = 1
+ATTN_AUTO = 2
 STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", -3: "HILS_ERR_ALIGNMENT",
           -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
@@ -163,8 +164,9 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
             out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0):
     """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
     w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
-    attn_mode: ATTN_UNION (0) or ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
-    between neighbouring rows).
+    attn_mode: ATTN_UNION (0), ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
+    between neighbouring rows) or ATTN_AUTO (2, bf16; measures the overlap and picks one; waits
+    on the stream once).
 
     Returns o [B,H,L,d], or (o, idx [B,H,L,k] int32, w [B,H,L,k] float32)."""
     import torch

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 4
+#define HILS_ABI_VERSION 5
 
 typedef enum {
   HILS_OK = 0,
@@ -69,8 +69,12 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  *     into per-chunk row lists and each chunk is attended only by the rows that chose it; one
  *     bf16 partial output per (row, slot) in the workspace, summed in slot order.  For
  *     selections with little overlap between neighbouring rows.  The workspace grows by about
- *     seq_len * topk * (2 * head_dim + 4) bytes. */
-typedef enum { HILS_ATTN_UNION = 0, HILS_ATTN_CHUNK_MAJOR = 1 } hils_attn_mode;
+ *     seq_len * topk * (2 * head_dim + 4) bytes.
+ *   HILS_ATTN_AUTO (2, bf16 only): after the selection, the union size of up to 256 sampled
+ *     128-row groups is measured on the GPU and the call waits for it on the host (one stream
+ *     synchronisation, so not for graph capture), then takes the chunk-major mode when the mean
+ *     union exceeds 8 * topk chunks (union walk otherwise).  Workspace as for mode 1. */
+typedef enum { HILS_ATTN_UNION = 0, HILS_ATTN_CHUNK_MAJOR = 1, HILS_ATTN_AUTO = 2 } hils_attn_mode;
 /* Grouped-query attention (both calls): kv_heads > 0 must divide heads; query head h then uses
  * key/value head h / (heads / kv_heads), and k, v, lmk (prefill) or k_cache, v_cache, lmk
  * (decode) hold kv_heads heads instead of heads.  Landmarks belong to the key/value head.

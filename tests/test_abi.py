@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 4
+    assert lib.hils_abi_version() == 5
 
 
 def _pp(**kw):
@@ -55,7 +55,8 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
     (dict(head_dim=96), -2), (dict(chunk=32), -2), (dict(topk=0), -2), (dict(topk=65), -2),
     (dict(seq_len=2000), -2), (dict(q_tile=32), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
     (dict(dtype=7), -2), (dict(batch=0), -1), (dict(heads=-1), -1), (dict(scale=float("nan")), -1),
-    (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=2), -2),
+    (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=3), -2),
+    (dict(attn_mode=2), -2),                                   # auto is bf16 only
     (dict(kv_heads=3), -1), (dict(kv_heads=-1), -1), (dict(kv_heads=4), -1),   # must divide heads = 2
     (dict(attn_mode=1), -2),                                   # chunk-major is bf16 only
 ])
@@ -93,7 +94,7 @@ def test_prefill_workspace_size():
     # chunk-major: per-chunk counters and offsets, the list and the bf16 partials of one pair
     pc = _pp(dtype=hils.DTYPE_BF16, attn_mode=1)
     N = 2048 // 64
-    cm = 2 * a256(N * 4) + 2 * a256((N + 1) * 4) + a256(2048 * 4 * 4) + a256(2048 * 4 * 64 * 2)
+    cm = 256 + 2 * a256(N * 4) + 2 * a256((N + 1) * 4) + a256(2048 * 4 * 4) + a256(2048 * 4 * 64 * 2)
     assert lib.hils_prefill_workspace_size(ctypes.byref(pc), 1) == t + cm
 
 

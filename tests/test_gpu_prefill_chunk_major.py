@@ -94,3 +94,23 @@ def test_chunk_major_edge_sizes(lib, cfg):
     _torch().cuda.synchronize()
     rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
     _compare(inp, cfg, o, idx, w, rows)
+
+
+@pytest.mark.parametrize("q_mode,expect", [("iid", CM), ("walk", hils.ATTN_UNION)])
+def test_auto_mode_choice(lib, q_mode, expect):
+    """attn_mode = AUTO measures the selection's overlap: i.i.d. queries over 256 chunks with
+    k = 4 (about 55 k distinct chunks per 128-row group) take the chunk-major mode, random-walk
+    queries (about 2 k) the union walk.  The two modes round differently, so the output
+    identifies the mode taken."""
+    torch = _torch()
+    cfg = synth.PrefillConfig(f"auto_{q_mode}", 1, 4, 16384, 128, 64, 4 if q_mode == "iid" else 16, "bf16",
+                              16, 256, q_mode=q_mode, h_mode=q_mode)
+    print(f"[case] {cfg}", flush=True)
+    dev = synth.make_prefill_inputs_torch(cfg, "cuda")
+    o_a, idx_a, _ = _run(lib, dev, cfg, attn_mode=hils.ATTN_AUTO)
+    o_e, idx_e, _ = _run(lib, dev, cfg, attn_mode=expect)
+    o_o, _, _ = _run(lib, dev, cfg, attn_mode=CM if expect == hils.ATTN_UNION else hils.ATTN_UNION)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_e)
+    assert torch.equal(o_a, o_e)
+    assert not torch.equal(o_a, o_o)

@@ -114,3 +114,15 @@ def test_auto_mode_choice(lib, q_mode, expect):
     assert torch.equal(idx_a, idx_e)
     assert torch.equal(o_a, o_e)
     assert not torch.equal(o_a, o_o)
+
+
+@pytest.mark.parametrize("mode", [CM, hils.ATTN_AUTO])
+def test_chunk_major_selection_in_workspace(lib, mode):
+    """Without selection outputs, idx / w live in the workspace beside the mode's own lists and
+    partials: the output must equal the run that returns the selection."""
+    cfg = synth.PrefillConfig("bf16_8k_k8_ws", 1, 2, 8192, 128, 64, 8, "bf16", 16, 256)
+    dev = _to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)
+    o1, _, _ = _run(lib, dev, cfg, attn_mode=mode)
+    o2 = hils.prefill(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["h"], dev["w_down"], dev["w_up"],
+                      topk=cfg.topk, attn_mode=mode)
+    assert _torch().equal(o1, o2)

@@ -28,7 +28,7 @@ What the method computes (sources are the pages' titles and sections):
        delta_q = W_up W_down h, with h the token's hidden state, adapts the
        query for chunk-level mass estimation.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1 one scale s (default 1/sqrt(d)) serves both softmax levels;
   R2 candidates of query i are the causal chunks j <= floor(i/C), its own chunk
      included and scored like the others (not forced in);

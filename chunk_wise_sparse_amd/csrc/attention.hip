@@ -10,7 +10,7 @@
 // takes consecutive queries of one (batch, head) - several 64-query chunks - and walks the union
 // of their selected chunks in ascending order.  Each union chunk's K and V are staged once in
 // LDS and shared by all waves.
-//   chunk_attention_block_kernel (bf16, k <= 32) and chunk_attention_block2_kernel (bf16,
+//   chunk_attention_block_kernel (bf16, k <= 32) and chunk_attention_block64_kernel (bf16,
 //     k <= 64): 128 queries, eight waves of one 16-row MFMA block each; a wave computes the
 //     chunks its 16 rows selected.
 //   chunk_attention_kernel (fp32, or sequences not a multiple of 128): wave w owns rows
@@ -21,10 +21,10 @@
 //   S^T[key][q] = K . Q^T  : A = K rows (LDS), B = raw q (registers);
 //                            lane (m, g) holds query m and keys 16*kb + 4g + rr;
 //   O^T[d][q] += V^T . P'^T: A = V^T via LDS transpose reads, B = P' = p * (w_j / l_j).
-// K and V are loaded into registers and then written to LDS.  The k <= 32 one-block kernel
-// keeps one LDS stage and the next chunk in registers (two barriers per chunk); the other two
-// compute chunk t from one of two stages while chunk t+1 is written to the other and chunk t+2
-// is in flight.
+// K and V are loaded into registers and then written to LDS.  The one-block kernels keep one LDS
+// stage and the next chunk in registers (two barriers per chunk); the two-block kernel computes
+// chunk t from one of two stages while chunk t+1 is written to the other and chunk t+2 is in
+// flight.
 //
 // Chunk-major mode (cm_* kernels, bf16, chosen by the caller): for selections whose rows share
 // few chunks, one (batch, head) pair at a time is turned into per-chunk row lists, each chunk's
@@ -389,6 +389,220 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
 }
 
 // ------------------------------------------------------------------------------------------
+// bf16, 32 < k <= 64: the k <= 32 kernel below with only the chunk indices staged in LDS (the
+// weights, which a staged copy would double, are read from memory one match ahead: nw0 is the
+// row's next match, nw1 the one after).  17 KiB of indices beside one K/V stage: two
+// workgroups per CU.  (A copy of the selection kept entirely in memory, read per match, with
+// two K/V stages was 12 % slower.)
+template <int D, int QG, int KMAX>
+struct BlockSelSmem64 {
+  alignas(16) char k[64 * BlockKLayout<D>::LD];
+  alignas(16) char v[AttnLayout<bf16, D>::VBYTES];
+  int nunion;
+  uint16_t sidx[QG * (KMAX + 1)];
+};
+
+// bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
+// computes only the chunks its own 16 rows selected (no second block riding along), and a wave
+// needs about half the registers of the two-block kernel above: two workgroups (four waves per
+// SIMD) share a CU.  Same staging and union walk as above: the group's selection staged in LDS,
+// one LDS stage, the next chunk in registers, two barriers per chunk.
+template <int D>
+__global__ __launch_bounds__(512, 2) void chunk_attention_block64_kernel(const AttnArgs a) {
+  constexpr int NW = 8, QG = 16 * NW, KMAX = 64;
+  typedef BlockSelSmem64<D, QG, KMAX> Smem;
+  typedef AttnLayout<bf16, D> Lay;
+  constexpr int NF = D / 32;                 // QK^T steps over d
+  constexpr int NP = 2;                      // PV steps over the 64 keys
+  constexpr int VE = 8;                      // elements per 16-byte vector
+  constexpr int NT = NW * 64;                // threads
+  constexpr int NV = 64 * Lay::VPR / NT;     // 16-byte vectors per thread per tensor per chunk
+  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
+  __shared__ Smem sm;
+  extern __shared__ uint32_t bitmap[];       // ceil(N / 32) words
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int groups = a.L / QG;
+  const uint32_t total = (uint32_t)a.B * a.H * groups;
+  const uint32_t gid = xcd_remap(blockIdx.x, total);
+  const int bh = gid / groups;
+  const int q0 = (int)(gid % groups) * QG;   // first query position of the group
+  const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
+  const int k = a.topk;
+  const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
+  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const size_t row0 = (size_t)bh * a.L;
+
+  // Stage the group's selections and build the union bitmap (causal chunks only).
+  const int nwords = (c_last + 1 + 31) >> 5;
+  for (int x = tid; x < nwords; x += NT) bitmap[x] = 0u;
+  if (tid == 0) sm.nunion = 0;
+  for (int r = tid; r < QG; r += NT) sm.sidx[r * ks + k] = (uint16_t)0xFFFF;   // end sentinel
+  __syncthreads();
+  for (int x = tid; x < QG * k; x += NT) {
+    const int r = x / k, e = x - r * k;
+    const int j = a.idx[(row0 + q0) * k + x];
+    const bool ok = j >= 0 && j <= c_last;
+    sm.sidx[r * ks + e] = ok ? (uint16_t)j : (uint16_t)0xFFFF;
+    if (ok) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  {
+    int cnt = 0;
+    for (int x = tid; x < nwords; x += NT) cnt += __popc(bitmap[x]);
+    cnt = (int)wave_sum((float)cnt);   // exact: at most 65536
+    if (lane == 0) atomicAdd(&sm.nunion, cnt);
+  }
+
+  // This lane's row: 16 * wave + m of the group.
+  const int rloc = 16 * wave + m, qpos = q0 + rloc, crow = qpos >> 6;
+  int ptr = 0;
+  const float* rw = a.w + (row0 + qpos) * k;
+  float nw0 = rw[0], nw1 = k > 1 ? rw[1] : 0.f;
+  bf16x8 qf[NF];
+  {
+    const bf16* qp = static_cast<const bf16*>(a.q) + (row0 + qpos) * D + g * (D / 4);
+#pragma unroll
+    for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
+  }
+#pragma unroll
+  for (int st = 0; st < NF; ++st) asm volatile("" ::"v"(qf[st]));
+  f32x4 acc_o[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
+
+  auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
+    const bf16* kc = Kb + (size_t)j * 64 * D;
+    const bf16* vc = Vb + (size_t)j * 64 * D;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+    }
+  };
+  auto store_kv = [&](const u32x4 (&kr)[NV], const u32x4 (&vr)[NV]) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      const int row = v / Lay::VPR, p = v % Lay::VPR;
+      *reinterpret_cast<u32x4*>(sm.k + BlockKLayout<D>::off(row, p)) = kr[u];
+      const int e = p * VE;                  // first element of the vector
+      *reinterpret_cast<u32x4*>(sm.v + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
+    }
+  };
+
+  __syncthreads();
+  int wi = 0;
+  uint32_t cur = bitmap[0];
+  auto next_chunk = [&]() -> int {
+    while (cur == 0u && wi + 1 < nwords) cur = bitmap[++wi];
+    if (cur == 0u) return -1;
+    const int j = wi * 32 + __builtin_ctz(cur);
+    cur &= cur - 1u;
+    return j;
+  };
+
+  const float zs = a.scale * 1.4426950408889634f;
+  auto compute = [&](int j) {
+    // The row's selection is ascending with a sentinel after entry k-1, so ptr stays <= k.
+    const bool sel = sm.sidx[rloc * ks + ptr] == (uint16_t)j;
+    const float wq = sel ? nw0 : 0.f;
+    if (sel) {
+      ++ptr;
+      nw0 = nw1;
+      nw1 = ptr + 1 < k ? rw[ptr + 1] : 0.f;
+    }
+    if (!__any(sel)) return;
+    const char* kbuf = sm.k;
+    const char* vbuf = sm.v;
+    // S^T: lane (m, g) holds query row m and keys 16 kb + 4 g + rr.
+    float sv[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int st = 0; st < NF; ++st)
+        acc = Mfma<bf16>::mma(load_frag<bf16>(reinterpret_cast<const bf16*>(kbuf + BlockKLayout<D>::off(kb * 16 + m, g * NF + st))), qf[st], acc);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
+    }
+    if (j == crow) {                         // wave-uniform: the block's rows share a chunk
+      const int ql = qpos & 63;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (kb * 16 + 4 * g + rr > ql) sv[kb * 4 + rr] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+    mx = col_max(mx) * zs;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
+      sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], zs, -mx));
+      l += sv[i];
+    }
+    l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
+    const float f = wq * __builtin_amdgcn_rcpf(l);
+    bf16x8 pf[NP];
+#pragma unroll
+    for (int st = 0; st < NP; ++st)
+#pragma unroll
+      for (int z = 0; z < 8; ++z) pf[st][z] = bf16_rne(sv[st * 8 + z] * f);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int st = 0; st < NP; ++st)
+        acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st), pf[st], acc_o[db]);
+  };
+
+  const int U = sm.nunion;
+  int jl = -1;                               // last chunk returned by the iterator
+  auto advance = [&]() -> int {
+    const int j = next_chunk();
+    if (j >= 0) jl = j;
+    return j >= 0 ? j : jl;
+  };
+  // compute c_t; barrier; the registers holding c_{t+1} go to LDS and c_{t+2} is loaded into
+  // them; barrier.  Loads and stores are unconditional (past the end of the union they repeat
+  // its last chunk) so that the compiler's wait counts stay exact across the loop.
+  u32x4 kr[NV], vr[NV];
+  if (U > 0) {
+    int cj = advance();
+    load_kv(cj, kr, vr);
+    store_kv(kr, vr);
+    int cn = advance();
+    load_kv(cn, kr, vr);
+    __syncthreads();
+    for (int t = 0; t < U; ++t) {
+      compute(cj);
+      __syncthreads();
+      store_kv(kr, vr);
+      const int cn2 = advance();
+      load_kv(cn2, kr, vr);
+      __syncthreads();
+      cj = cn;
+      cn = cn2;
+    }
+  }
+
+  // O^T fragments: lane holds its row's d = 16*db + 4g + rr.
+  bf16* op = static_cast<bf16*>(a.o) + (row0 + qpos) * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    bf16x4 out;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
+    *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
+  }
+}
+
 // bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
 // computes only the chunks its own 16 rows selected (no second block riding along), and a wave
 // needs about half the registers of the two-block kernel above: two workgroups (four waves per
@@ -569,218 +783,6 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const Att
       store_kv(kr, vr);
       const int cn2 = advance();
       load_kv(cn2, kr, vr);
-      __syncthreads();
-      cj = cn;
-      cn = cn2;
-    }
-  }
-
-  // O^T fragments: lane holds its row's d = 16*db + 4g + rr.
-  bf16* op = static_cast<bf16*>(a.o) + (row0 + qpos) * D;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    bf16x4 out;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
-    *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
-  }
-}
-
-// bf16, 32 < k <= 64: the same one-block waves, but the selection is not staged (128 rows x 65
-// entries would take half a CU's LDS): each lane keeps its row's next two selected chunks and
-// weights in registers, read from memory one match ahead.  LDS holds only the union bitmap and
-// two K/V stages, so two workgroups (four waves per SIMD) share a CU.  One barrier per union
-// chunk: the registers holding chunk t+1 go to the free stage, chunk t+2 is loaded into them,
-// and chunk t is computed from the other stage.  (For k <= 32 the staged selection fits beside
-// one stage and is cheaper than these per-match loads.)
-template <typename T, int D>
-struct BlockSmem {
-  alignas(16) char k[2][AttnLayout<T, D>::KBYTES];
-  alignas(16) char v[2][AttnLayout<T, D>::VBYTES];
-  int nunion;
-};
-
-template <int D>
-__global__ __launch_bounds__(512, 2) void chunk_attention_block2_kernel(const AttnArgs a) {
-  constexpr int NW = 8, QG = 16 * NW;
-  typedef BlockSmem<bf16, D> Smem;
-  typedef AttnLayout<bf16, D> Lay;
-  constexpr int NF = D / 32;                 // QK^T steps over d
-  constexpr int NP = 2;                      // PV steps over the 64 keys
-  constexpr int VE = 8;                      // elements per 16-byte vector
-  constexpr int NT = NW * 64;                // threads
-  constexpr int NV = 64 * Lay::VPR / NT;     // 16-byte vectors per thread per tensor per chunk
-  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
-  __shared__ Smem sm;
-  extern __shared__ uint32_t bitmap[];       // ceil(N / 32) words
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 15, g = lane >> 4;
-  const int groups = a.L / QG;
-  const uint32_t total = (uint32_t)a.B * a.H * groups;
-  const uint32_t gid = xcd_remap(blockIdx.x, total);
-  const int bh = gid / groups;
-  const int q0 = (int)(gid % groups) * QG;   // first query position of the group
-  const int c_last = (q0 + QG - 1) >> 6;     // last chunk a row of the group may select
-  const int k = a.topk;
-  const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
-  const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
-  const size_t row0 = (size_t)bh * a.L;
-
-  // Union bitmap of the group's selections (causal chunks only).
-  const int nwords = (c_last + 1 + 31) >> 5;
-  for (int x = tid; x < nwords; x += NT) bitmap[x] = 0u;
-  if (tid == 0) sm.nunion = 0;
-  __syncthreads();
-  for (int x = tid; x < QG * k; x += NT) {
-    const int j = a.idx[(row0 + q0) * k + x];
-    if (j >= 0 && j <= c_last) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  {
-    int cnt = 0;
-    for (int x = tid; x < nwords; x += NT) cnt += __popc(bitmap[x]);
-    cnt = (int)wave_sum((float)cnt);   // exact: at most 65536
-    if (lane == 0) atomicAdd(&sm.nunion, cnt);
-  }
-
-  // This lane's row: 16 * wave + m of the group.  Its selection is ascending; padding (-1) and
-  // entries past the causal range never match a union chunk.
-  const int rloc = 16 * wave + m, qpos = q0 + rloc, crow = qpos >> 6;
-  const int32_t* ridx = a.idx + (row0 + qpos) * k;
-  const float* rw = a.w + (row0 + qpos) * k;
-  auto sel_at = [&](int e) -> int { return e < k ? ridx[e] : -1; };
-  auto w_at = [&](int e) -> float { return e < k ? rw[e] : 0.f; };
-  int ptr = 0;                               // entries of the row already matched
-  int nj0 = sel_at(0), nj1 = sel_at(1);
-  float nw0 = w_at(0), nw1 = w_at(1);
-
-  bf16x8 qf[NF];
-  {
-    const bf16* qp = static_cast<const bf16*>(a.q) + (row0 + qpos) * D + g * (D / 4);
-#pragma unroll
-    for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
-  }
-#pragma unroll
-  for (int st = 0; st < NF; ++st) asm volatile("" ::"v"(qf[st]));
-  f32x4 acc_o[D / 16];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
-
-  auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
-    const bf16* kc = Kb + (size_t)j * 64 * D;
-    const bf16* vc = Vb + (size_t)j * 64 * D;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int v = tid + NT * u;
-      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
-      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
-    }
-  };
-  auto store_kv = [&](int s, const u32x4 (&kr)[NV], const u32x4 (&vr)[NV]) {
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int v = tid + NT * u;
-      const int row = v / Lay::VPR, p = v % Lay::VPR;
-      *reinterpret_cast<u32x4*>(sm.k[s] + BlockKLayout<D>::off(row, p)) = kr[u];
-      const int e = p * VE;                  // first element of the vector
-      *reinterpret_cast<u32x4*>(sm.v[s] + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
-    }
-  };
-
-  __syncthreads();
-  int wi = 0;
-  uint32_t cur = bitmap[0];
-  auto next_chunk = [&]() -> int {
-    while (cur == 0u && wi + 1 < nwords) cur = bitmap[++wi];
-    if (cur == 0u) return -1;
-    const int j = wi * 32 + __builtin_ctz(cur);
-    cur &= cur - 1u;
-    return j;
-  };
-
-  const float zs = a.scale * 1.4426950408889634f;
-  auto compute = [&](int j, int s) {
-    const bool sel = nj0 == j;
-    const float wq = sel ? nw0 : 0.f;
-    if (sel) {                               // next match: shift, read the entry after it
-      ++ptr;
-      nj0 = nj1;
-      nw0 = nw1;
-      nj1 = sel_at(ptr + 1);
-      nw1 = w_at(ptr + 1);
-    }
-    if (!__any(sel)) return;
-    const char* kbuf = sm.k[s];
-    const char* vbuf = sm.v[s];
-    // S^T: lane (m, g) holds query row m and keys 16 kb + 4 g + rr.
-    float sv[16];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int st = 0; st < NF; ++st)
-        acc = Mfma<bf16>::mma(load_frag<bf16>(reinterpret_cast<const bf16*>(kbuf + BlockKLayout<D>::off(kb * 16 + m, g * NF + st))), qf[st], acc);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sv[kb * 4 + rr] = acc[rr];
-    }
-    if (j == crow) {                         // wave-uniform: the block's rows share a chunk
-      const int ql = qpos & 63;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (kb * 16 + 4 * g + rr > ql) sv[kb * 4 + rr] = -INFINITY;
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-    mx = col_max(mx) * zs;
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
-      sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], zs, -mx));
-      l += sv[i];
-    }
-    l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
-    const float f = wq * __builtin_amdgcn_rcpf(l);
-    bf16x8 pf[NP];
-#pragma unroll
-    for (int st = 0; st < NP; ++st)
-#pragma unroll
-      for (int z = 0; z < 8; ++z) pf[st][z] = bf16_rne(sv[st * 8 + z] * f);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int st = 0; st < NP; ++st)
-        acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(vbuf, m, g, db, st), pf[st], acc_o[db]);
-  };
-
-  const int U = sm.nunion;
-  int jl = -1;                               // last chunk returned by the iterator
-  auto advance = [&]() -> int {
-    const int j = next_chunk();
-    if (j >= 0) jl = j;
-    return j >= 0 ? j : jl;
-  };
-  // Iteration t: the registers (chunk t+1) go to stage (t+1) & 1, chunk t+2 is loaded into
-  // them, chunk t is computed from stage t & 1; barrier.  Stage (t+1) & 1 was last read in
-  // iteration t-1, before its barrier.  Loads and stores are unconditional (past the end of
-  // the union they repeat its last chunk) so that the compiler's wait counts stay exact.
-  u32x4 kr[NV], vr[NV];
-  if (U > 0) {
-    int cj = advance();
-    load_kv(cj, kr, vr);
-    store_kv(0, kr, vr);
-    int cn = advance();
-    load_kv(cn, kr, vr);
-    __syncthreads();
-    for (int t = 0; t < U; ++t) {
-      store_kv((t + 1) & 1, kr, vr);
-      const int cn2 = advance();
-      load_kv(cn2, kr, vr);
-      compute(cj, t & 1);
       __syncthreads();
       cj = cn;
       cn = cn2;
@@ -1165,7 +1167,7 @@ template hipError_t launch_chunk_attention_cm<64>(const CmArgs&, hipStream_t);
 template hipError_t launch_chunk_attention_cm<128>(const CmArgs&, hipStream_t);
 
 // Queries per workgroup: bf16 takes 128 (eight one-block waves, two workgroups per CU; the
-// selection staged in LDS for k <= 32, read from memory for k <= 64); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with
+// selection staged in LDS for k <= 32, its chunk indices only for k <= 64); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with
 // two stages, so that the staged selection fits LDS; 64 when the sequence does not split that
 // way.
 template <typename T, int D>
@@ -1180,7 +1182,7 @@ hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
         if (a.topk <= 32)
           hipLaunchKernelGGL((chunk_attention_block_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
         else
-          hipLaunchKernelGGL((chunk_attention_block2_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
+          hipLaunchKernelGGL((chunk_attention_block64_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
         return hipGetLastError();
       }
     }

@@ -402,14 +402,13 @@ struct BlockSelSmem64 {
   uint16_t sidx[QG * (KMAX + 1)];
 };
 
-// bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
-// computes only the chunks its own 16 rows selected (no second block riding along), and a wave
-// needs about half the registers of the two-block kernel above: two workgroups (four waves per
-// SIMD) share a CU.  Same staging and union walk as above: the group's selection staged in LDS,
-// one LDS stage, the next chunk in registers, two barriers per chunk.
-template <int D>
-__global__ __launch_bounds__(512, 2) void chunk_attention_block64_kernel(const AttnArgs a) {
-  constexpr int NW = 8, QG = 16 * NW, KMAX = 64;
+// bf16, 32 < k <= 64: one 16-row MFMA block per wave, NW waves per 16*NW-query workgroup (eight
+// by default: two workgroups, four waves per SIMD, share a CU).  Only the group's chunk indices
+// are staged in LDS; each lane reads its row's weights from memory one match ahead.  One K/V
+// stage, the next chunk held in registers, two barriers per chunk.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block64_kernel(const AttnArgs a) {
+  constexpr int QG = 16 * NW, KMAX = 64;
   typedef BlockSelSmem64<D, QG, KMAX> Smem;
   typedef AttnLayout<bf16, D> Lay;
   constexpr int NF = D / 32;                 // QK^T steps over d
@@ -603,14 +602,16 @@ __global__ __launch_bounds__(512, 2) void chunk_attention_block64_kernel(const A
   }
 }
 
-// bf16, k <= 32: one 16-row MFMA block per wave, eight waves per 128-query workgroup.  A wave
-// computes only the chunks its own 16 rows selected (no second block riding along), and a wave
-// needs about half the registers of the two-block kernel above: two workgroups (four waves per
-// SIMD) share a CU.  Same staging and union walk as above: the group's selection staged in LDS,
-// one LDS stage, the next chunk in registers, two barriers per chunk.
-template <int D>
-__global__ __launch_bounds__(512, 2) void chunk_attention_block_kernel(const AttnArgs a) {
-  constexpr int NW = 8, QG = 16 * NW, KMAX = 32;
+// bf16, k <= 32: one 16-row MFMA block per wave, NW waves per 16*NW-query workgroup (eight by
+// default).  A wave computes only the chunks its own 16 rows selected (no second block riding
+// along), and a wave needs about half the registers of the two-block kernel above: at eight
+// waves two workgroups (four waves per SIMD) share a CU.  Same staging and union walk as above:
+// the group's selection staged in LDS, one LDS stage, the next chunk in registers, two barriers
+// per chunk.  A row's result depends only on its own selection (rows that did not choose a
+// chunk add exact zeros), so it is the same for every NW.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block_kernel(const AttnArgs a) {
+  constexpr int QG = 16 * NW, KMAX = 32;
   typedef AttnSmem<bf16, D, QG, KMAX, 1> Smem;
   typedef AttnLayout<bf16, D> Lay;
   constexpr int NF = D / 32;                 // QK^T steps over d
@@ -1166,26 +1167,34 @@ hipError_t launch_union_probe(const int32_t* idx, int B, int H, int L, int k, ui
 template hipError_t launch_chunk_attention_cm<64>(const CmArgs&, hipStream_t);
 template hipError_t launch_chunk_attention_cm<128>(const CmArgs&, hipStream_t);
 
-// Queries per workgroup: bf16 takes 128 (eight one-block waves, two workgroups per CU; the
-// selection staged in LDS for k <= 32, its chunk indices only for k <= 64); otherwise 256 (8 waves, k <= 32) or 128 (4 waves) with
-// two stages, so that the staged selection fits LDS; 64 when the sequence does not split that
-// way.
+// Queries per workgroup: bf16 takes a.q_tile (16, 32, 64 or 128 one-block waves of 16 rows; the
+// caller guarantees L % q_tile == 0); at 128, two workgroups share a CU, with the selection staged
+// in LDS for k <= 32 and its chunk indices only for k <= 64.  fp32 (a correctness path) keeps
+// the two-block kernel: 256 queries (8 waves, k <= 32), 128 (4 waves) or 64 with two stages, so
+// that the staged selection fits LDS.  Every choice gives the same result.
+template <int D, int NW>
+static void launch_block(const AttnArgs& a, uint32_t bhs, size_t bm, hipStream_t st) {
+  const dim3 grid(bhs * (a.L / (16 * NW))), block(64 * NW);
+  if (a.topk <= 32)
+    hipLaunchKernelGGL((chunk_attention_block_kernel<D, NW>), grid, block, bm, st, a);
+  else
+    hipLaunchKernelGGL((chunk_attention_block64_kernel<D, NW>), grid, block, bm, st, a);
+}
+
 template <typename T, int D>
 hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
   const uint32_t bhs = (uint32_t)a.B * a.H;
   const size_t bm = (size_t)((a.N + 31) / 32) * 4;   // union bitmap (dynamic LDS)
-  if constexpr (sizeof(T) == 4 && D == 128) {   // 32 KiB per tensor per chunk: 64-query groups
+  if constexpr (sizeof(T) == 2) {
+    switch (a.q_tile) {
+      case 16: launch_block<D, 1>(a, bhs, bm, st); break;
+      case 32: launch_block<D, 2>(a, bhs, bm, st); break;
+      case 64: launch_block<D, 4>(a, bhs, bm, st); break;
+      default: launch_block<D, 8>(a, bhs, bm, st); break;
+    }
+  } else if constexpr (D == 128) {              // 32 KiB per tensor per chunk: 64-query groups
     hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
   } else {
-    if constexpr (sizeof(T) == 2) {
-      if (a.L % 128 == 0) {
-        if (a.topk <= 32)
-          hipLaunchKernelGGL((chunk_attention_block_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
-        else
-          hipLaunchKernelGGL((chunk_attention_block64_kernel<D>), dim3(bhs * (a.L / 128)), dim3(512), bm, st, a);
-        return hipGetLastError();
-      }
-    }
     if (a.topk <= 32 && a.L % 256 == 0) {
       hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), bm, st, a);
     } else if (a.L % 128 == 0) {

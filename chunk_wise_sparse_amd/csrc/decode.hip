@@ -778,7 +778,7 @@ __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeAr
 }
 
 // ------------------------------------------------------------------------------------------
-// Fused decode step: one workgroup of 8 waves per (sequence, head) scores the pair's landmarks,
+// Fused decode step: one workgroup of 4 waves per (sequence, head) scores the pair's landmarks,
 // selects and gathers, with the scores kept in LDS (n <= kFusedMaxChunks).  Used when there are
 // at least as many pairs as compute units, so that every compute unit streams its pairs' data
 // without a kernel boundary between the stages.

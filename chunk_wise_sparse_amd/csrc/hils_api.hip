@@ -71,8 +71,8 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "more than 65535 chunks per sequence");
   if (p->dtype == HILS_DTYPE_FP32 && p->head_dim == 128 && p->seq_len / p->chunk > 16384)
     return fail(HILS_ERR_UNSUPPORTED, "fp32 with head_dim 128 supports at most 16384 chunks");
-  if (p->q_tile != 0 && p->q_tile != 64)
-    return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (64)", p->q_tile);
+  if (p->q_tile != 0 && p->q_tile != 16 && p->q_tile != 32 && p->q_tile != 64 && p->q_tile != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (16, 32, 64 or 128)", p->q_tile);
   if (p->qcal_rank < 0 || p->qcal_rank > 64)
     return fail(HILS_ERR_UNSUPPORTED, "qcal_rank %d outside [0, 64]", p->qcal_rank);
   if (p->qcal_rank > 0 && (p->hidden <= 0 || p->hidden % 128 != 0))
@@ -90,6 +90,14 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (bhld > 4e18 / 8 || (double)p->batch * p->heads * (p->seq_len / 64) > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
   return HILS_OK;
+}
+
+// Queries that share one staged copy of each union chunk: the caller's q_tile (default 128),
+// halved until it divides the sequence (seq_len is a multiple of 64).
+int effective_q_tile(const hils_prefill_params* p) {
+  int qt = p->q_tile > 0 ? p->q_tile : 128;
+  while (p->seq_len % qt != 0) qt >>= 1;
+  return qt;
 }
 
 PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
@@ -168,10 +176,13 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   aa.L = p->seq_len;
   aa.N = p->seq_len / 64;
   aa.topk = p->topk;
+  aa.q_tile = effective_q_tile(p);
   aa.scale = scale;
   if constexpr (sizeof(T) == 2) {
     bool chunk_major = p->attn_mode == HILS_ATTN_CHUNK_MAJOR;
     if (p->attn_mode == HILS_ATTN_AUTO) {      // measure the selection's overlap, then choose
+      // The choice waits on the host for one counter: not possible inside a stream capture
+      // (checked before anything is enqueued, in hils_prefill_fwd).
       uint32_t* probe = reinterpret_cast<uint32_t*>(ws + L.probe);
       int groups = 0;
       if ((e = hils::launch_union_probe(idx, p->batch, p->heads, p->seq_len, p->topk, probe, &groups, st)) !=
@@ -398,11 +409,18 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
     for (const Range& b : out)
       if (&a != &b && overlap(a, b)) return fail(HILS_ERR_INVALID_ARG, "%s overlaps %s", a.name, b.name);
   }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->attn_mode == HILS_ATTN_AUTO) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(s, &cs);
+    if (ce != hipSuccess) return hip_fail(ce, "hils_prefill_fwd: hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(HILS_ERR_UNSUPPORTED, "attn_mode HILS_ATTN_AUTO waits on the host and cannot be captured");
+  }
   char* ws = static_cast<char*>(workspace);
   float* tcode = qcal ? reinterpret_cast<float*>(ws + L.tcode) : nullptr;
   int32_t* idx = with_sel ? sel_idx : reinterpret_cast<int32_t*>(ws + L.idx);
   float* w = with_sel ? sel_w : reinterpret_cast<float*>(ws + L.w);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (p->dtype == HILS_DTYPE_BF16) {
     err = p->head_dim == 64
@@ -494,6 +512,6 @@ const char* hils_status_string(int status) {
   }
 }
 
-const char* hils_last_error(void) { return g_last_error.c_str(); }
+const char* hils_last_hip_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

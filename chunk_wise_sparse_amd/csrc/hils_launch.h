@@ -28,6 +28,7 @@ struct AttnArgs {
   void* o;              // [B,H,L,d]
   int B, H, L, N, topk;
   int G;                // query heads per key/value head
+  int q_tile;           // bf16: queries per workgroup (16, 32, 64 or 128), dividing L
   float scale;
 };
 

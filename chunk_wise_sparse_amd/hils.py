@@ -24,7 +24,7 @@ ATTN_AUTO = 2
 STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", -3: "HILS_ERR_ALIGNMENT",
           -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
-            "hils_prefill_fwd", "hils_decode_fwd", "hils_status_string", "hils_last_error"]
+            "hils_prefill_fwd", "hils_decode_fwd", "hils_status_string", "hils_last_hip_error"]
 
 
 class PrefillParams(ctypes.Structure):
@@ -74,7 +74,7 @@ def load(path: str = LIB_PATH):
     lib.hils_decode_fwd.restype = i32
     lib.hils_status_string.argtypes = [i32]
     lib.hils_status_string.restype = ctypes.c_char_p
-    lib.hils_last_error.restype = ctypes.c_char_p
+    lib.hils_last_hip_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -83,7 +83,7 @@ def check(status: int, what: str):
     if status != HILS_OK:
         lib = load()
         msg = lib.hils_status_string(status).decode()
-        detail = lib.hils_last_error().decode()
+        detail = lib.hils_last_hip_error().decode()
         raise RuntimeError(f"{what} failed: {STATUS.get(status, status)} ({msg}): {detail}")
 
 
@@ -160,7 +160,7 @@ def _stream_handle(device):
 
 
 def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
-            q_tile: int = 64, scale: Optional[float] = None, return_selection: bool = False,
+            q_tile: int = 0, scale: Optional[float] = None, return_selection: bool = False,
             out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0):
     """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
     w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).

@@ -24,7 +24,7 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and nothing is
  *     synchronised; results are valid once the caller synchronises that stream.
  *   - All checks a host can make run before any launch; on failure nothing is enqueued and a
- *     negative status is returned.  Launch failures return HILS_ERR_HIP; hils_last_error()
+ *     negative status is returned.  Launch failures return HILS_ERR_HIP; hils_last_hip_error()
  *     gives the message (per thread).
  *   - The library allocates no device memory.  Scratch comes from the caller's workspace, of
  *     at least *_workspace_size() bytes, 256-byte aligned.
@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 5
+#define HILS_ABI_VERSION 6
 
 typedef enum {
   HILS_OK = 0,
@@ -56,13 +56,18 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
 
 /* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk == 64;
  * 1 <= topk <= 64; seq_len a positive multiple of chunk with seq_len / chunk <= 65535
- * (<= 16384 for fp32 with head_dim 128); q_tile == 64 (or 0 for the default);
- * 0 <= qcal_rank <= 64; hidden a positive multiple of 128 when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
+ * (<= 16384 for fp32 with head_dim 128); 0 <= qcal_rank <= 64; hidden a positive multiple of
+ * 128 when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
+ * q_tile: how many consecutive queries share one staged copy of each chunk of their union (the
+ *   M adjacent queries of the pages' kernel, HiLS explainer, "Engineering details",
+ *   hardware-efficient kernel item): 16, 32, 64 or 128, 0 = 128.  If seq_len is not a multiple,
+ *   the largest of these that divides it is used.  It applies to bf16 in the union mode (fp32
+ *   keeps a fixed grouping); the results are bitwise the same for every q_tile.
  * stage_events: optional array of n_stage_events hipEvent_t handles (NULL if unused); when it
  * holds at least 4 events, event 0 is recorded before the first kernel and events 1..3 after the
  * Q-Cal, chunk-selection and chunk-attention kernels, on `stream`.
  * attn_mode selects how the chunk attention is organised; both compute the same result:
- *   HILS_ATTN_UNION (0): each group of 128 consecutive queries stages the union of the chunks
+ *   HILS_ATTN_UNION (0): each group of q_tile consecutive queries stages the union of the chunks
  *     its rows selected, once per group; best when neighbouring rows share most chunks (the
  *     pages report high overlap between adjacent tokens for trained models).
  *   HILS_ATTN_CHUNK_MAJOR (1, bf16 only): per (batch, head) pair the selections are inverted
@@ -72,8 +77,10 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  *     seq_len * topk * (2 * head_dim + 4) bytes.
  *   HILS_ATTN_AUTO (2, bf16 only): after the selection, the union size of up to 256 sampled
  *     128-row groups is measured on the GPU and the call waits for it on the host (one stream
- *     synchronisation, so not for graph capture), then takes the chunk-major mode when the mean
- *     union exceeds 8 * topk chunks (union walk otherwise).  Workspace as for mode 1. */
+ *     synchronisation), then takes the chunk-major mode when the mean union exceeds 8 * topk
+ *     chunks (union walk otherwise).  Workspace as for mode 1.  This is the one mode that waits
+ *     on the host: on a stream that is being captured it returns HILS_ERR_UNSUPPORTED before
+ *     anything is enqueued. */
 typedef enum { HILS_ATTN_UNION = 0, HILS_ATTN_CHUNK_MAJOR = 1, HILS_ATTN_AUTO = 2 } hils_attn_mode;
 /* Grouped-query attention (both calls): kv_heads > 0 must divide heads; query head h then uses
  * key/value head h / (heads / kv_heads), and k, v, lmk (prefill) or k_cache, v_cache, lmk
@@ -122,8 +129,11 @@ typedef struct hils_decode_params {
 int hils_abi_version(void);
 
 /* Workspace bytes needed by one call with these parameters; 0 if the parameters are invalid.
- * The size depends on whether sel_idx / sel_w will be passed (if both are given they double as
- * scratch and the workspace shrinks): pass with_selection = 1 when both will be non-NULL. */
+ * with_selection: 1 when the call will pass sel_idx and sel_w (both non-NULL), 0 when both will
+ * be NULL.  The selection (chunk indices and weights, [B, H, L, k] each for prefill) is always
+ * computed and always read back by the attention stage; when the caller asks for it, the
+ * caller's buffers hold it and the workspace leaves it out (at the 128K workload that is 1 GiB
+ * less), otherwise the workspace holds it.  The sizes differ by exactly that much. */
 size_t hils_prefill_workspace_size(const hils_prefill_params* p, int with_selection);
 size_t hils_decode_workspace_size(const hils_decode_params* p, int with_selection);
 
@@ -145,8 +155,10 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
  *   q         [B, H, d]               the new token's raw query
  *   k_cache, v_cache [B, H, Lmax, d]  caches; rows >= kv_len[b] are never read
  *   lmk       [B, H, ceil(Lmax / C), d] landmark keys (chunks at or beyond kv_len are ignored)
- *   kv_len    [B] int32, device       1 <= kv_len[b] <= Lmax (not checked on the host: values
- *                                     outside that range are undefined behaviour)
+ *   kv_len    [B] int32, device       valid lengths are 1 <= kv_len[b] <= Lmax.  The host cannot
+ *                                     read them; the kernels clamp every value into that range
+ *                                     (a value below 1 acts as 1, one above Lmax as Lmax), so an
+ *                                     out-of-range length never reads outside the caches.
  *   h         [B, D]; w_down [r, D]; w_up [H*d, r] (NULL iff qcal_rank == 0)
  *   o         [B, H, d]
  *   sel_idx, sel_w [B, H, k]          optional, as for prefill. */
@@ -157,8 +169,9 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
 
 /* Static description of a status code. */
 const char* hils_status_string(int status);
-/* Message of the last HILS_ERR_HIP / validation failure on the calling thread ("" if none). */
-const char* hils_last_error(void);
+/* Message of the last failed call on the calling thread: the HIP runtime's error text for
+ * HILS_ERR_HIP, or what the validation rejected ("" after a successful call). */
+const char* hils_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -343,4 +343,44 @@ def pin_hand_worked_example():
     assert abs(r["o"][0] - 4.0) < 1e-12
 
 
+# ---------------------------------------------------------------------------------------------
+# Fusion over a supplied selection (used where the GPU's selection differs within the tie band)
+# ---------------------------------------------------------------------------------------------
+
+def pin_given_selection_matches_own_rows():
+    """Given the oracle's own selection and its scores, the fusion reproduces the oracle's row
+    output exactly, padded rows (fewer candidates than k) included."""
+    inp = _small_inputs(20, L=320, d=16, C=64)
+    rows = [(0, 0, 5), (0, 1, 64), (0, 0, 130), (0, 1, 200), (0, 0, 319)]
+    res = O.prefill_rows(inp, rows, 64, 3, "fp32")
+    for (b, h, i) in rows:
+        r = res[(b, h, i)]
+        sig = np.array([r["sigma"][j] if j >= 0 else 0.0 for j in r["idx"]], dtype=np.float32)
+        got = O.attend_given_selection(inp["q"][b, h, i], inp["k"][b, h], inp["v"][b, h], r["idx"], sig, i, 64,
+                                       1.0 / 4.0)
+        assert np.array_equal(got, r["o"]), (i, np.abs(got - r["o"]).max())
+
+
+def pin_given_selection_matrix_form():
+    """Arbitrary (non-top-k) selections, padded with -1: the fusion equals the two-level sum
+    written in matrix form, sum_j softmax(s sigma_G)_j * softmax(a over chunk j's visible keys) V."""
+    g = _rng(21)
+    L, d, C = 384, 8, 64
+    s = 0.3
+    q, k, v = (g.standard_normal((L, d)) for _ in range(3))
+    a_all = s * (q @ k.T)
+    for i, sel, nsel in ((383, [0, 2, 5], 3), (200, [1, 3, -1, -1], 2), (70, [1, -1], 1), (300, [4, 0, 2], 3)):
+        sel = np.array(sel)
+        valid = sel[sel >= 0]
+        sig = np.zeros(len(sel), np.float32)
+        sig[:nsel] = g.standard_normal(nsel).astype(np.float32) * 3
+        wts = scipy.special.softmax(s * sig[:nsel].astype(np.float64))
+        want = np.zeros(d)
+        for wj, j in zip(wts, valid):
+            hi = min((j + 1) * C, i + 1)
+            want += wj * (scipy.special.softmax(a_all[i, j * C:hi]) @ v[j * C:hi])
+        got = O.attend_given_selection(q[i], k, v, sel, sig, i, C, s)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (i, sel, np.abs(got - want).max())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -74,6 +74,12 @@ def check_rows(res: Dict[tuple, dict], gpu_o: Dict[tuple, np.ndarray], gpu_idx: 
             g = gpu_idx[key]
             sig = np.array([r["sigma"][j] if j >= 0 else 0.0 for j in g], dtype=np.float32)
             ref_o = O.attend_given_selection(q_row, keys, values, g, sig, row_pos(key), chunk, scale)
+            # the GPU weights must be the inter-chunk softmax over the GPU's own selection
+            nsel = int((g >= 0).sum())
+            ref_w = O.inter_chunk_weights(sig[:nsel], scale)
+            max_w = max(max_w, float(np.abs(gpu_w[key][:nsel] - ref_w).max()))
+            if np.any(gpu_w[key][nsel:] != 0.0):
+                errors.append(f"{key}: nonzero weight padding")
         d = np.abs(gpu_o[key].astype(np.float64) - ref_o)
         max_abs = max(max_abs, float(d.max()))
         sum_abs += float(d.sum())
@@ -93,12 +99,17 @@ def assert_within(stats: dict, dtype: str):
 
 
 def sample_rows(B: int, H: int, L: int, per_head: int, seed: int = 0, chunk: int = 64) -> List[tuple]:
-    """Rows of the first and last tiles, chunk boundaries and uniform random rows, per (b, h)."""
+    """Per (b, h): eight fixed rows (first and last tiles, chunk boundaries, the middle) plus
+    per_head distinct uniform random rows outside the first two chunks, where the selection
+    has choices to make."""
     g = np.random.default_rng(seed)
     rows = []
+    lo = min(2 * chunk, L - 1)
     for b in range(B):
         for h in range(H):
             fixed = {0, 1, chunk - 1, chunk, L - chunk, L - 1, L // 2, L // 2 - 1}
-            rnd = set(int(x) for x in g.integers(0, L, size=max(0, per_head - len(fixed))))
+            pool = L - lo
+            n = min(per_head, pool)
+            rnd = set(int(x) + lo for x in g.choice(pool, size=n, replace=False)) if n > 0 else set()
             rows += [(b, h, i) for i in sorted(fixed | rnd)]
     return rows

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 5
+    assert lib.hils_abi_version() == 6
 
 
 def _pp(**kw):
@@ -53,7 +53,7 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(chunk=32), -2), (dict(topk=0), -2), (dict(topk=65), -2),
-    (dict(seq_len=2000), -2), (dict(q_tile=32), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
+    (dict(seq_len=2000), -2), (dict(q_tile=48), -2), (dict(q_tile=256), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
     (dict(dtype=7), -2), (dict(batch=0), -1), (dict(heads=-1), -1), (dict(scale=float("nan")), -1),
     (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=3), -2),
     (dict(attn_mode=2), -2),                                   # auto is bf16 only
@@ -63,7 +63,7 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
 def test_prefill_rejects_bad_params(kw, status):
     lib = hils.load()
     assert _prefill(lib, _pp(**kw)) == status
-    assert lib.hils_last_error().decode() != ""
+    assert lib.hils_last_hip_error().decode() != ""
     assert lib.hils_prefill_workspace_size(ctypes.byref(_pp(**kw)), 0) == 0
 
 

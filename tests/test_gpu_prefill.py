@@ -6,6 +6,7 @@ import pytest
 
 from chunk_wise_sparse_amd import synth
 from oracle import hils_oracle as O
+import oracle_pool
 from parity import assert_within, check_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +33,7 @@ def _run(lib, dev, cfg, **kw):
 
 def _compare(inp, cfg, o, idx, w, rows, scale=None):
     s = (1.0 / math.sqrt(cfg.head_dim)) if scale is None else scale
-    res = O.prefill_rows(inp, rows, cfg.chunk, cfg.topk, cfg.dtype, scale=scale)
+    res = oracle_pool.prefill_rows(inp, rows, cfg.chunk, cfg.topk, cfg.dtype, scale=scale)
     rset = sorted(res)
     bi = np.array([r[0] for r in rset]); hi = np.array([r[1] for r in rset]); ii = np.array([r[2] for r in rset])
     import torch
@@ -150,7 +151,7 @@ def test_prefill_without_selection_output(lib):
     assert _torch().equal(o1, o2)
 
 
-@pytest.mark.parametrize("name,per_head", [("prefill_32k", 12), ("prefill_128k", 4)])
+@pytest.mark.parametrize("name,per_head", [("prefill_32k", 48), ("prefill_128k", 64)])
 def test_prefill_full_size_sampled(lib, name, per_head):
     """Full-size workloads in the launch configuration the benchmark times; sampled rows."""
     torch = _torch()
@@ -173,17 +174,17 @@ def test_prefill_full_size_sampled(lib, name, per_head):
 
 @pytest.mark.parametrize("name", ["prefill_512k_walk", "prefill_512k_iid"])
 def test_prefill_512k_sampled(lib, name):
-    """The 512K-token prefill (k = 64) in the benchmark's launch configuration: rows of three
-    heads against the oracle (only those heads are copied back)."""
+    """The 512K-token prefill (k = 64) in the benchmark's launch configuration: 8 fixed and 32
+    random rows of each of eight heads against the oracle (only those heads are copied back)."""
     torch = _torch()
     cfg = synth.CONFIGS[name]
     print(f"[case] full size {cfg}", flush=True)
     dev = synth.make_prefill_inputs_torch(cfg, "cuda")
     o, idx, w = _run(lib, dev, cfg)
     torch.cuda.synchronize()
-    heads = [0, 13, cfg.heads - 1]
+    heads = [0, 4, 9, 13, 18, 22, 27, cfg.heads - 1]
     d = cfg.head_dim
-    rows = sample_rows(1, len(heads), cfg.seq_len, 10, seed=11)
+    rows = sample_rows(1, len(heads), cfg.seq_len, 32, seed=11)
     sub = {key: dev[key][:, heads].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
     pos = sorted({r[2] for r in rows})
     h_sub = np.zeros((1, cfg.seq_len, cfg.hidden), dtype=np.float32)
@@ -194,3 +195,52 @@ def test_prefill_512k_sampled(lib, name):
     sub_cfg = synth.PrefillConfig(cfg.name, 1, len(heads), cfg.seq_len, d, cfg.chunk, cfg.topk, cfg.dtype,
                                   cfg.qcal_rank, cfg.hidden)
     _compare(sub, sub_cfg, o[:, heads], idx[:, heads], w[:, heads], rows)
+
+
+# fp32 dispatch branches: the two-block kernel with 4 waves and 64 list entries (d = 64 with
+# k > 32 or L % 256 != 0), with 2 waves (d = 64 with L % 128 != 0; d = 128 always), and the
+# generic selection kernel's k > 32 form.  Every row is compared.
+FP32_BRANCHES = [
+    synth.PrefillConfig("fp32_d64_k40", 1, 1, 3072, 64, 64, 40, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d64_k64", 1, 1, 4608, 64, 64, 64, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d128_k40", 1, 1, 3072, 128, 64, 40, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d128_k64", 1, 1, 4608, 128, 64, 64, "fp32", 0, 0),
+    synth.PrefillConfig("fp32_d64_L640", 1, 2, 640, 64, 64, 4, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d64_L1152", 1, 2, 1152, 64, 64, 8, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d64_L576", 1, 2, 576, 64, 64, 4, "fp32", 8, 128),
+    synth.PrefillConfig("fp32_d64_L704", 2, 1, 704, 64, 64, 3, "fp32", 0, 0),
+]
+
+
+@pytest.mark.parametrize("cfg", FP32_BRANCHES, ids=lambda c: c.name)
+def test_prefill_fp32_branches_all_rows(lib, cfg):
+    print(f"[case] prefill all rows {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    o, idx, w = _run(lib, _to_dev(inp, cfg.dtype), cfg)
+    _torch().cuda.synchronize()
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, o, idx, w, rows)
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.PrefillConfig("qtile_bf16_k16", 1, 2, 4096, 128, 64, 16, "bf16", 16, 256, q_mode="walk"),
+    synth.PrefillConfig("qtile_bf16_k48", 1, 2, 4096, 64, 64, 48, "bf16", 8, 128),
+    synth.PrefillConfig("qtile_bf16_L576", 1, 1, 576, 128, 64, 4, "bf16", 0, 0),
+    synth.PrefillConfig("qtile_fp32", 1, 1, 2048, 64, 64, 8, "fp32", 8, 128),
+], ids=lambda c: c.name)
+def test_prefill_q_tile_bitwise(lib, cfg):
+    """The union group size (q_tile = 16, 32, 64, 128) changes which rows share a staged chunk,
+    not any row's result: outputs and selections are bitwise identical.  One run is also checked
+    against the oracle on every row."""
+    torch = _torch()
+    print(f"[case] q_tile sweep {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    dev = _to_dev(inp, cfg.dtype)
+    runs = {qt: _run(lib, dev, cfg, q_tile=qt) for qt in (16, 32, 64, 128, 0)}
+    torch.cuda.synchronize()
+    ref = runs[128]
+    for qt, r in runs.items():
+        for x, y in zip(r, ref):
+            assert torch.equal(x, y), f"q_tile {qt} differs from q_tile 128"
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, *runs[16], rows)

@@ -56,7 +56,24 @@ def _topk_smallest(sigma, k):
     return out
 
 
+def _given_weights_over_padding(q_row, keys, values, idx, sigma_selected, i, chunk, scale):
+    idx = np.asarray(idx)
+    w = O.inter_chunk_weights(np.asarray(sigma_selected), scale)     # padded entries included
+    return O.attend_row(q_row, keys, values, idx, w, i, chunk, scale)
+
+
+def _given_sigma_reversed(q_row, keys, values, idx, sigma_selected, i, chunk, scale,
+                          _o=O.attend_given_selection):
+    idx = np.asarray(idx)
+    sig = np.array(sigma_selected, dtype=np.float32)
+    n = int((idx >= 0).sum())
+    sig[:n] = sig[:n][::-1]
+    return _o(q_row, keys, values, idx, sig, i, chunk, scale)
+
+
 MUTATIONS = {
+    "given_selection_weights_over_padding": ("attend_given_selection", _given_weights_over_padding),
+    "given_selection_sigma_reversed": ("attend_given_selection", _given_sigma_reversed),
     "qcal_dropped": ("calibrated_query", lambda q, h, wd, wu, dt: O.round_to_run_dtype(q, dt)),
     "qcal_wrong_head": ("prefill_rows", _wrong_head_prefill_rows),
     "qcal_sign_flipped": ("qcal_offset", lambda h, wd, wu, _o=O.qcal_offset: -_o(h, wd, wu)),

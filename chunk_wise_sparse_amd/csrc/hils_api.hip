@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "hils.h"
@@ -435,11 +436,14 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   return HILS_OK;
 }
 
-int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_cache,
-                    const void* v_cache, const void* lmk, const int32_t* kv_len, const void* h,
-                    const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+int decode_entry(const hils_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                 const void* lmk, const int32_t* kv_len, const void* h, const void* w_down,
+                 const void* w_up, void* o, int32_t* sel_idx, float* sel_w, void* workspace,
+                 size_t workspace_bytes, void* stream, const char* who) {
   int st = check_decode_params(p);
   if (st != HILS_OK) return st;
   if (!q || !k_cache || !v_cache || !lmk || !kv_len || !o)
@@ -496,8 +500,69 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
               ? run_decode<float, 64>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
               : run_decode<float, 128>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
   }
-  if (err != hipSuccess) return hip_fail(err, "hils_decode_fwd");
+  if (err != hipSuccess) return hip_fail(err, who);
   return HILS_OK;
+}
+
+// Scratch of hils_decode_fwd_noalloc: one copy per GPU, held until the process ends.  In host
+// code `scratch` only names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress with that GPU current, once, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)HILS_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hils_decode_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HILS_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hils_decode_fwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & (kWsAlign - 1)))
+      return fail(HILS_ERR_HIP, "hils_decode_fwd_noalloc: static scratch at %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_cache,
+                    const void* v_cache, const void* lmk, const int32_t* kv_len, const void* h,
+                    const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return decode_entry(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, sel_idx, sel_w, workspace,
+                      workspace_bytes, stream, "hils_decode_fwd");
+}
+
+int hils_decode_fwd_noalloc(const hils_decode_params* p, const void* q, const void* k_cache,
+                            const void* v_cache, const void* lmk, const int32_t* kv_len, const void* h,
+                            const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
+                            void* stream) {
+  g_last_error.clear();
+  int st = check_decode_params(p);
+  if (st != HILS_OK) return st;
+  if ((sel_idx == nullptr) != (sel_w == nullptr))
+    return fail(HILS_ERR_INVALID_ARG, "sel_idx and sel_w must be both NULL or both non-NULL");
+  const size_t need = decode_layout(p, sel_idx != nullptr).total;
+  if (need > kStaticScratchBytes)
+    return fail(HILS_ERR_WORKSPACE, "hils_decode_fwd_noalloc: %zu bytes of scratch needed, the static scratch holds %zu",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != HILS_OK) return st;
+  return decode_entry(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, sel_idx, sel_w, ws,
+                      kStaticScratchBytes, stream, "hils_decode_fwd_noalloc");
 }
 
 const char* hils_status_string(int status) {

@@ -24,7 +24,9 @@ ATTN_AUTO = 2
 STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", -3: "HILS_ERR_ALIGNMENT",
           -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
-            "hils_prefill_fwd", "hils_decode_fwd", "hils_status_string", "hils_last_hip_error"]
+            "hils_prefill_fwd", "hils_decode_fwd", "hils_decode_fwd_noalloc", "hils_status_string",
+            "hils_last_hip_error"]
+STATIC_SCRATCH_BYTES = 64 << 20   # HILS_STATIC_SCRATCH_BYTES
 
 
 class PrefillParams(ctypes.Structure):
@@ -72,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.hils_prefill_fwd.restype = i32
     lib.hils_decode_fwd.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 11 + [vp, sz, vp]
     lib.hils_decode_fwd.restype = i32
+    lib.hils_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 11 + [vp]
+    lib.hils_decode_fwd_noalloc.restype = i32
     lib.hils_status_string.argtypes = [i32]
     lib.hils_status_string.restype = ctypes.c_char_p
     lib.hils_last_hip_error.restype = ctypes.c_char_p
@@ -197,11 +201,12 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
 def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, topk: int,
            chunk: int = 64, scale: Optional[float] = None, return_selection: bool = False,
            out=None, workspace=None, events: Optional[StageEvents] = None, block_table=None,
-           max_kv_len: Optional[int] = None):
+           max_kv_len: Optional[int] = None, no_alloc: bool = False):
     """HiLS decode step.  q [B,H,d]; caches [B,Hkv,Lmax,d]; lmk [B,Hkv,ceil(Lmax/C),d] (Hkv divides
     H); kv_len [B] int32 (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k]).
     Paged caches: block_table [B, S] int32 (device) and caches [pages, Hkv, C, d]; chunk j of
-    sequence b is page block_table[b, j]; max_kv_len (<= S * C) is then required."""
+    sequence b is page block_table[b, j]; max_kv_len (<= S * C) is then required.
+    no_alloc: call hils_decode_fwd_noalloc (the library's static scratch; no workspace)."""
     import torch
     lib = load()
     B, H, d = q.shape
@@ -227,6 +232,12 @@ def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, 
     if return_selection:
         idx = torch.empty((B, H, topk), dtype=torch.int32, device=q.device)
         w = torch.empty((B, H, topk), dtype=torch.float32, device=q.device)
+    if no_alloc:
+        st = lib.hils_decode_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lmk),
+                                         kv_len.data_ptr(), _ptr(h), _ptr(w_down), _ptr(w_up), _ptr(o), _ptr(idx),
+                                         _ptr(w), _stream_handle(q.device))
+        check(st, "hils_decode_fwd_noalloc")
+        return (o, idx, w) if return_selection else o
     need = lib.hils_decode_workspace_size(ctypes.byref(p), 1 if return_selection else 0)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -167,6 +167,23 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
                     const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* hils_decode_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops and harnesses that forbid hipMalloc.  The arguments are those of
+ * hils_decode_fwd without the workspace; scratch comes from a buffer of
+ * HILS_STATIC_SCRATCH_BYTES that the library holds in device memory, one per GPU, from the first
+ * call on that GPU (with it current) until the process ends.  The call allocates and frees
+ * nothing.  Calls whose hils_decode_workspace_size() exceeds HILS_STATIC_SCRATCH_BYTES return
+ * HILS_ERR_WORKSPACE before anything is enqueued (64 MiB covers, for instance, 8 sequences x 32
+ * heads at 512K tokens, k = 64, d = 128, which needs about 9 MiB).  Every call on one GPU shares
+ * that GPU's buffer: calls that overlap in time on one GPU (two streams, two threads) race and
+ * must be serialised by the caller.  No kernel relies on the buffer's contents from an earlier
+ * call.  Results are bitwise those of hils_decode_fwd. */
+#define HILS_STATIC_SCRATCH_BYTES (64u << 20)
+int hils_decode_fwd_noalloc(const hils_decode_params* p, const void* q, const void* k_cache,
+                            const void* v_cache, const void* lmk, const int32_t* kv_len, const void* h,
+                            const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
+                            void* stream);
+
 /* Static description of a status code. */
 const char* hils_status_string(int status);
 /* Message of the last failed call on the calling thread: the HIP runtime's error text for

@@ -136,3 +136,19 @@ def test_status_strings():
     lib = hils.load()
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.hils_status_string(code).decode()
+
+
+def test_decode_noalloc_rejects_oversized():
+    """The no-allocation decode entry checks its scratch need against the static buffer before
+    touching the device (fake pointers: the call must fail first)."""
+    lib = hils.load()
+    p = _dp(batch=256, heads=64, max_kv_len=64 * 8192, head_dim=128, topk=64, qcal_rank=0, hidden=0,
+            dtype=hils.DTYPE_BF16)
+    need = lib.hils_decode_workspace_size(ctypes.byref(p), 0)
+    assert need > hils.STATIC_SCRATCH_BYTES
+    st = lib.hils_decode_fwd_noalloc(ctypes.byref(p), FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32),
+                                     FAKE + (4 << 32), None, None, None, FAKE + (8 << 32), None, None, None)
+    assert st == -4, st
+    assert "static scratch" in lib.hils_last_hip_error().decode()
+    assert lib.hils_decode_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
+                                       None) == -1

@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attention.hip", "decode.hip"]
+SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attention.hip", "decode.hip",
+           "dense.hip"]
 LIB = os.path.join(PKG, "libhils.so")
 # Per-file flags.  Selection and attention take finite scores only, so NaN handling is dropped
 # there (max/min then need no NaN quieting of their operands).
@@ -20,6 +21,7 @@ FILE_FLAGS = {
     # MFMA results in ordinary VGPRs (no accumulation-register copies before the VALU work)
     "select_fast.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attention.hip": ["-fno-honor-nans"],
+    "dense.hip": ["-fno-honor-nans"],
 }
 ARCH = "gfx950"
 

@@ -565,6 +565,130 @@ int hils_decode_fwd_noalloc(const hils_decode_params* p, const void* q, const vo
                       kStaticScratchBytes, stream, "hils_decode_fwd_noalloc");
 }
 
+}  // extern "C"
+
+namespace {
+
+int check_dense_params(const hils_dense_params* p, bool prefill) {
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch <= 0 || p->heads <= 0 || p->seq_len <= 0 || p->head_dim <= 0)
+    return fail(HILS_ERR_INVALID_ARG, "batch, heads, seq_len and head_dim must be positive");
+  if (p->dtype != HILS_DTYPE_BF16 && p->dtype != HILS_DTYPE_FP32)
+    return fail(HILS_ERR_UNSUPPORTED, "dtype %d is not supported", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
+  if (prefill && p->seq_len % 64 != 0)
+    return fail(HILS_ERR_UNSUPPORTED, "seq_len %d is not a multiple of 64", p->seq_len);
+  if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
+    return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
+  if (!(isfinite(p->scale))) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
+  if ((double)p->batch * p->heads * (double)p->seq_len > 4e18 / 1024 ||
+      (double)p->batch * p->heads * (p->seq_len / 64 + 1) > 2147483647.0)
+    return fail(HILS_ERR_UNSUPPORTED, "problem too large");
+  return HILS_OK;
+}
+
+size_t dense_decode_ws(const hils_dense_params* p) {
+  const int pairs = p->batch * p->heads;
+  return align_up((size_t)pairs * hils::dense_decode_splits(pairs, p->seq_len) * (p->head_dim + 2) * 4);
+}
+
+int check_overlaps(const Range* in, size_t nin, const Range* out, size_t nout) {
+  for (size_t a = 0; a < nout; ++a) {
+    for (size_t b = 0; b < nin; ++b)
+      if (overlap(out[a], in[b])) return fail(HILS_ERR_INVALID_ARG, "%s overlaps input %s", out[a].name, in[b].name);
+    for (size_t b = 0; b < nout; ++b)
+      if (a != b && overlap(out[a], out[b]))
+        return fail(HILS_ERR_INVALID_ARG, "%s overlaps %s", out[a].name, out[b].name);
+  }
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hils_dense_prefill_fwd(const hils_dense_params* p, const void* q, const void* k, const void* v, void* o,
+                           void* stream) {
+  g_last_error.clear();
+  int st = check_dense_params(p, true);
+  if (st != HILS_OK) return st;
+  if (!q || !k || !v || !o) return fail(HILS_ERR_INVALID_ARG, "a required tensor is NULL");
+  for (const void* ptr : {q, k, v, (const void*)o})
+    if (!aligned16(ptr)) return fail(HILS_ERR_ALIGNMENT, "a tensor is not 16-byte aligned");
+  const size_t e = elem_bytes(p->dtype), B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim;
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;
+  const Range in[] = {{q, B * H * S * d * e, "q"}, {k, B * Hk * S * d * e, "k"}, {v, B * Hk * S * d * e, "v"}};
+  const Range out[] = {{o, B * H * S * d * e, "o"}};
+  if ((st = check_overlaps(in, 3, out, 1)) != HILS_OK) return st;
+  hils::DenseArgs a;
+  a.q = q;
+  a.key = k;
+  a.val = v;
+  a.o = o;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.L = p->seq_len;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (p->dtype == HILS_DTYPE_BF16)
+    err = d == 64 ? hils::launch_dense_prefill<hils::bf16, 64>(a, s) : hils::launch_dense_prefill<hils::bf16, 128>(a, s);
+  else
+    err = d == 64 ? hils::launch_dense_prefill<float, 64>(a, s) : hils::launch_dense_prefill<float, 128>(a, s);
+  if (err != hipSuccess) return hip_fail(err, "hils_dense_prefill_fwd");
+  return HILS_OK;
+}
+
+size_t hils_dense_decode_workspace_size(const hils_dense_params* p) {
+  g_last_error.clear();
+  if (check_dense_params(p, false) != HILS_OK) return 0;
+  return dense_decode_ws(p);
+}
+
+int hils_dense_decode_fwd(const hils_dense_params* p, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_len, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_dense_params(p, false);
+  if (st != HILS_OK) return st;
+  if (!q || !k_cache || !v_cache || !kv_len || !o) return fail(HILS_ERR_INVALID_ARG, "a required tensor is NULL");
+  for (const void* ptr : {q, k_cache, v_cache, (const void*)o})
+    if (!aligned16(ptr)) return fail(HILS_ERR_ALIGNMENT, "a tensor is not 16-byte aligned");
+  if ((uintptr_t)kv_len & 3u) return fail(HILS_ERR_ALIGNMENT, "kv_len is not 4-byte aligned");
+  const size_t need = dense_decode_ws(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((uintptr_t)workspace & (kWsAlign - 1)) return fail(HILS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+  const size_t e = elem_bytes(p->dtype), B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim;
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;
+  const Range in[] = {{q, B * H * d * e, "q"}, {k_cache, B * Hk * S * d * e, "k_cache"},
+                      {v_cache, B * Hk * S * d * e, "v_cache"}, {kv_len, B * 4, "kv_len"}};
+  const Range out[] = {{o, B * H * d * e, "o"}, {workspace, need, "workspace"}};
+  if ((st = check_overlaps(in, 4, out, 2)) != HILS_OK) return st;
+  hils::DenseDecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.partial = static_cast<float*>(workspace);
+  a.o = o;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.Lmax = p->seq_len;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (p->dtype == HILS_DTYPE_BF16)
+    err = d == 64 ? hils::launch_dense_decode<hils::bf16, 64>(a, s) : hils::launch_dense_decode<hils::bf16, 128>(a, s);
+  else
+    err = d == 64 ? hils::launch_dense_decode<float, 64>(a, s) : hils::launch_dense_decode<float, 128>(a, s);
+  if (err != hipSuccess) return hip_fail(err, "hils_dense_decode_fwd");
+  return HILS_OK;
+}
+
 const char* hils_status_string(int status) {
   switch (status) {
     case HILS_OK: return "ok";

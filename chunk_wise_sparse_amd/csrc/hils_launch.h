@@ -109,6 +109,33 @@ struct DecodeArgs {
   float scale;
 };
 
+// Dense causal attention (the full-attention baseline): prefill over [B,H,L,d] (L % 64 == 0) and
+// one decode step over caches [B,H/G,Lmax,d] with per-sequence lengths kv_len.
+struct DenseArgs {
+  const void* q;        // [B,H,L,d]
+  const void* key;      // [B,H/G,L,d]
+  const void* val;      // [B,H/G,L,d]
+  void* o;              // [B,H,L,d]
+  int B, H, L, G;
+  float scale;
+};
+struct DenseDecodeArgs {
+  const void* q;        // [B,H,d]
+  const void* k_cache;  // [B,H/G,Lmax,d]
+  const void* v_cache;
+  const int32_t* kv_len;
+  float* partial;       // [B*H, splits, d + 2] workspace: (m, l, acc) per span
+  void* o;              // [B,H,d]
+  int B, H, Lmax, G;
+  float scale;
+};
+template <typename T, int D>
+hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t st);
+template <typename T, int D>
+hipError_t launch_dense_decode(const DenseDecodeArgs& a, hipStream_t st);
+// Spans per (sequence, head) pair of the dense decode step.
+int dense_decode_splits(int pairs, int lmax);
+
 template <typename T>
 hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,
                                     int r, hipStream_t st);

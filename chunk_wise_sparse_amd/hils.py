@@ -25,7 +25,8 @@ STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", 
           -4: "HILS_ERR_WORKSPACE", -5: "HILS_ERR_HIP"}
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
             "hils_prefill_fwd", "hils_decode_fwd", "hils_decode_fwd_noalloc", "hils_status_string",
-            "hils_last_hip_error"]
+            "hils_last_hip_error", "hils_dense_prefill_fwd", "hils_dense_decode_workspace_size",
+            "hils_dense_decode_fwd"]
 STATIC_SCRATCH_BYTES = 64 << 20   # HILS_STATIC_SCRATCH_BYTES
 
 
@@ -46,6 +47,12 @@ class DecodeParams(ctypes.Structure):
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("block_table", ctypes.c_void_p),
                 ("block_table_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+class DenseParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,6 +83,12 @@ def load(path: str = LIB_PATH):
     lib.hils_decode_fwd.restype = i32
     lib.hils_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 11 + [vp]
     lib.hils_decode_fwd_noalloc.restype = i32
+    lib.hils_dense_prefill_fwd.argtypes = [ctypes.POINTER(DenseParams)] + [vp] * 5
+    lib.hils_dense_prefill_fwd.restype = i32
+    lib.hils_dense_decode_workspace_size.argtypes = [ctypes.POINTER(DenseParams)]
+    lib.hils_dense_decode_workspace_size.restype = sz
+    lib.hils_dense_decode_fwd.argtypes = [ctypes.POINTER(DenseParams)] + [vp] * 6 + [sz, vp]
+    lib.hils_dense_decode_fwd.restype = i32
     lib.hils_status_string.argtypes = [i32]
     lib.hils_status_string.restype = ctypes.c_char_p
     lib.hils_last_hip_error.restype = ctypes.c_char_p
@@ -250,3 +263,37 @@ def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, 
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+def dense_prefill(q, k, v, *, scale: Optional[float] = None, out=None):
+    """Dense causal attention (the full-attention baseline).  q [B,H,L,d]; k, v [B,Hkv,L,d]."""
+    import torch
+    lib = load()
+    B, H, L, d = q.shape
+    _require([("q", q), ("k", k), ("v", v)], q.device, q.dtype)
+    p = DenseParams(B, H, L, d, int(k.shape[1]), 0.0 if scale is None else float(scale), _dtype_code(q))
+    o = out if out is not None else torch.empty_like(q)
+    st = lib.hils_dense_prefill_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream_handle(q.device))
+    check(st, "hils_dense_prefill_fwd")
+    return o
+
+
+def dense_decode(q, k_cache, v_cache, kv_len, *, scale: Optional[float] = None, out=None, workspace=None):
+    """Dense attention of one new token per sequence over its cache.  q [B,H,d];
+    caches [B,Hkv,Lmax,d]; kv_len [B] int32 (device)."""
+    import torch
+    lib = load()
+    B, H, d = q.shape
+    _require([("q", q), ("k_cache", k_cache), ("v_cache", v_cache)], q.device, q.dtype)
+    if kv_len.dtype != torch.int32 or kv_len.device != q.device or not kv_len.is_contiguous():
+        raise ValueError("kv_len must be a contiguous int32 tensor on the query's device")
+    p = DenseParams(B, H, int(k_cache.shape[2]), d, int(k_cache.shape[1]), 0.0 if scale is None else float(scale),
+                    _dtype_code(q))
+    o = out if out is not None else torch.empty_like(q)
+    need = lib.hils_dense_decode_workspace_size(ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.hils_dense_decode_fwd(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_len.data_ptr(),
+                                   _ptr(o), workspace.data_ptr(), need, _stream_handle(q.device))
+    check(st, "hils_dense_decode_fwd")
+    return o

@@ -167,6 +167,31 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
                     const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dense causal attention: the full-attention baseline the pages compare HiLS with
+ * [HiLS explainer (molayo1419.me), "Numerical results": prefill and per-decode-step speed at 512K
+ * against full attention on the same hardware].  o_i = sum_t softmax_t(scale q_i . k_t) v_t over
+ * every key t <= i (prefill) or over the cache's kv_len[b] keys (decode).  No chunks, no
+ * selection.  Same conventions as above (device buffers, stream, checks before any launch,
+ * kv_heads for grouped-query attention, clamped kv_len, paged caches not supported).
+ * Supported: head_dim in {64, 128}; prefill seq_len a positive multiple of 64.
+ * seq_len is the sequence length for prefill and the cache capacity (max_kv_len) for decode. */
+typedef struct hils_dense_params {
+  int32_t batch, heads, seq_len, head_dim;
+  int32_t kv_heads;            /* 0 = heads */
+  float scale;                 /* <= 0: 1/sqrt(head_dim) */
+  int32_t dtype;               /* hils_dtype */
+} hils_dense_params;
+/* q [B, H, L, d]; k, v [B, kv heads, L, d]; o [B, H, L, d].  No workspace. */
+int hils_dense_prefill_fwd(const hils_dense_params* p, const void* q, const void* k, const void* v, void* o,
+                           void* stream);
+/* Workspace of one dense decode step: per (sequence, head) the (max, sum, d partial sums) of each
+ * span of the cache, fp32; 0 if the parameters are invalid. */
+size_t hils_dense_decode_workspace_size(const hils_dense_params* p);
+/* q [B, H, d]; k_cache, v_cache [B, kv heads, seq_len, d]; kv_len [B] int32 on the device;
+ * o [B, H, d]. */
+int hils_dense_decode_fwd(const hils_dense_params* p, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_len, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* hils_decode_fwd for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops and harnesses that forbid hipMalloc.  The arguments are those of
  * hils_decode_fwd without the workspace; scratch comes from a buffer of

@@ -60,7 +60,8 @@ import numpy as np
 __all__ = [
     "round_to_bf16", "round_to_run_dtype", "qcal_offset", "calibrated_query", "landmark_scores",
     "select_top_k", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
-    "prefill", "decode", "attend_given_selection",
+    "prefill", "decode", "attend_given_selection", "dense_attention_row", "dense_causal_rows",
+    "dense_decode",
 ]
 
 
@@ -304,3 +305,54 @@ def attend_given_selection(q_row, keys, values, idx, sigma_selected, i, chunk, s
     w = np.zeros(len(idx))
     w[valid] = inter_chunk_weights(np.asarray(sigma_selected)[valid], scale)
     return attend_row(q_row, keys, values, idx, w, i, chunk, scale)
+
+
+# ------------------------------------------------------------------------------------------
+# Full (dense) attention: the baseline HiLS is compared with ([P3] "Numerical results": prefill
+# and per-decode-step latency against full attention on the same hardware; [P1] Model
+# Description: the exact attention mass of a chunk comes from the full QK product)
+# ------------------------------------------------------------------------------------------
+
+def dense_attention_row(q_row, keys, values, scale) -> np.ndarray:
+    """Softmax attention of one query over every given key, float64 [d]."""
+    q = np.asarray(q_row, dtype=np.float64)
+    k = np.asarray(keys, dtype=np.float64)
+    a = scale * (k @ q)
+    p = np.exp(a - a.max())
+    p = p / p.sum()
+    return p @ np.asarray(values, dtype=np.float64)
+
+
+def _causal_end(i: int) -> int:
+    """Query position i sees keys 0..i."""
+    return i + 1
+
+
+def dense_causal_rows(inp: Dict[str, np.ndarray], rows: Iterable[tuple],
+                      scale: Optional[float] = None) -> Dict[tuple, np.ndarray]:
+    """Dense causal attention for selected (b, h, i) rows of q, k, v [B, H, L, d] (raw q, no
+    Q-Cal).  Returns {(b, h, i): o [d] float64}."""
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    d = q.shape[-1]
+    s = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    out = {}
+    for (b, h, i) in rows:
+        e = _causal_end(i)
+        out[(b, h, i)] = dense_attention_row(q[b, h, i], k[b, h, :e], v[b, h, :e], s)
+    return out
+
+
+def dense_decode(inp: Dict[str, np.ndarray], scale: Optional[float] = None,
+                 pairs: Optional[Iterable[tuple]] = None) -> Dict[tuple, np.ndarray]:
+    """Dense attention of q [B, H, d] over the first kv_len[b] keys of k_cache / v_cache
+    [B, H, Lmax, d] (the new token's key and value included).  Returns {(b, h): o [d]}."""
+    q, kc, vc, kv_len = inp["q"], inp["k_cache"], inp["v_cache"], inp["kv_len"]
+    B, H, d = q.shape
+    s = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    out = {}
+    for (b, h) in pairs:
+        e = _causal_end(int(kv_len[b]) - 1)
+        out[(b, h)] = dense_attention_row(q[b, h], kc[b, h, :e], vc[b, h, :e], s)
+    return out

@@ -383,4 +383,71 @@ def pin_given_selection_matrix_form():
         assert np.allclose(got, want, rtol=0, atol=1e-12), (i, sel, np.abs(got - want).max())
 
 
+# ---------------------------------------------------------------------------------------------
+# Dense (full) attention baseline
+# ---------------------------------------------------------------------------------------------
+
+def pin_dense_equals_one_chunk_hils():
+    """With one chunk (L = C) HiLS is dense causal attention, through its own code path."""
+    inp = _small_inputs(22, L=64, d=16, C=64, r=0)
+    rows = [(0, h, i) for h in range(2) for i in (0, 1, 17, 40, 63)]
+    dense = O.dense_causal_rows(inp, rows)
+    hils = O.prefill_rows(inp, rows, 64, 1, "fp32")
+    for row in rows:
+        assert np.allclose(dense[row], hils[row]["o"], rtol=0, atol=1e-12), row
+
+
+def pin_dense_exact_chunk_mass_hils():
+    """HiLS over every chunk with each landmark set to its chunk's exact log attention mass equals
+    dense causal attention (several chunks, the own chunk truncated)."""
+    g = _rng(23)
+    L, d, C, s = 320, 16, 64, 0.25
+    q, k, v = (g.standard_normal((L, d)).astype(np.float32) for _ in range(3))
+    inp = dict(q=q[None, None], k=k[None, None], v=v[None, None])
+    for i in (0, 70, 191, 250, 319):
+        c = i // C
+        a = s * (k[: i + 1].astype(np.float64) @ q[i].astype(np.float64))
+        lse = np.array([scipy.special.logsumexp(a[j * C:min((j + 1) * C, i + 1)]) for j in range(c + 1)])
+        qq = q[i].astype(np.float64)
+        lmk = np.zeros((L // C, d), dtype=np.float32)
+        lmk[: c + 1] = (np.outer(lse / s, qq) / qq.dot(qq)).astype(np.float32)
+        r = O.prefill_rows(dict(inp, lmk=lmk[None, None]), [(0, 0, i)], C, c + 1, "fp32", scale=s)[(0, 0, i)]
+        want = O.dense_causal_rows(inp, [(0, 0, i)], scale=s)[(0, 0, i)]
+        assert np.allclose(r["o"], want, rtol=0, atol=2e-5), (i, np.abs(r["o"] - want).max())
+
+
+def pin_dense_equal_keys_mean():
+    """All keys equal: the weights are uniform and row i returns the mean of v_0..v_i."""
+    g = _rng(24)
+    L, d = 200, 8
+    k = np.tile(g.standard_normal(d), (L, 1))
+    inp = dict(q=g.standard_normal((1, 1, L, d)), k=k[None, None], v=g.standard_normal((1, 1, L, d)))
+    res = O.dense_causal_rows(inp, [(0, 0, i) for i in (0, 1, 99, 199)], scale=0.7)
+    for (_, _, i), o in res.items():
+        assert np.allclose(o, inp["v"][0, 0, : i + 1].mean(axis=0), rtol=0, atol=1e-12), i
+
+
+def pin_dense_scale_sharpens_to_argmax():
+    """A large scale sends all weight to the best visible key (one-hot limit)."""
+    g = _rng(25)
+    L, d = 96, 8
+    q, k, v = (g.standard_normal((L, d)) for _ in range(3))
+    inp = dict(q=q[None, None], k=k[None, None], v=v[None, None])
+    for i in (5, 50, 95):
+        best = int(np.argmax(k[: i + 1] @ q[i]))
+        o = O.dense_causal_rows(inp, [(0, 0, i)], scale=1e4)[(0, 0, i)]
+        assert np.allclose(o, v[best], rtol=0, atol=1e-9), i
+
+
+def pin_dense_decode_matches_prefill_row():
+    inp = _small_inputs(26, L=256, C=64, r=0)
+    for (h, i) in ((0, 0), (1, 63), (0, 64), (1, 200), (0, 255)):
+        dec_in = dict(q=inp["q"][:, :, i], k_cache=inp["k"], v_cache=inp["v"], kv_len=np.array([i + 1], np.int32))
+        dec = O.dense_decode(dec_in, pairs=[(0, h)])[(0, h)]
+        pre = O.dense_causal_rows(inp, [(0, h, i)])[(0, h, i)]
+        assert np.array_equal(dec, pre), (h, i)
+        hils = O.prefill_rows(inp, [(0, h, i)], 64, 4, "fp32")[(0, h, i)]
+        assert (i >= 64) == (not np.allclose(dec, hils["o"], atol=1e-9)), (h, i)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -72,6 +72,12 @@ def _given_sigma_reversed(q_row, keys, values, idx, sigma_selected, i, chunk, sc
 
 
 MUTATIONS = {
+    "dense_attends_next_key": ("_causal_end", lambda i: i + 2),
+    "dense_misses_itself": ("_causal_end", lambda i: max(i, 1)),
+    "dense_unscaled": ("dense_attention_row",
+                       lambda q, K, V, s, _o=O.dense_attention_row: _o(q, K, V, 1.0)),
+    "dense_keys_values_swapped": ("dense_attention_row",
+                                  lambda q, K, V, s, _o=O.dense_attention_row: _o(q, V, K, s)),
     "given_selection_weights_over_padding": ("attend_given_selection", _given_weights_over_padding),
     "given_selection_sigma_reversed": ("attend_given_selection", _given_sigma_reversed),
     "qcal_dropped": ("calibrated_query", lambda q, h, wd, wu, dt: O.round_to_run_dtype(q, dt)),

@@ -61,7 +61,7 @@ __all__ = [
     "round_to_bf16", "round_to_run_dtype", "qcal_offset", "calibrated_query", "landmark_scores",
     "select_top_k", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
     "prefill", "decode", "attend_given_selection", "dense_attention_row", "dense_causal_rows",
-    "dense_decode",
+    "dense_decode", "chunk_backward", "inter_chunk_backward", "prefill_backward",
 ]
 
 
@@ -82,6 +82,8 @@ def round_to_bf16(x) -> np.ndarray:
 
 
 def round_to_run_dtype(x, dtype: str) -> np.ndarray:
+    if dtype == "fp64":       # no rounding at all: the gradient checks' finite differences
+        return np.asarray(x, dtype=np.float64)
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     if dtype == "fp32":
         return x32
@@ -107,7 +109,13 @@ def qcal_offset(h_row: np.ndarray, w_down: np.ndarray, w_up_head: np.ndarray) ->
 
 def calibrated_query(q_row: np.ndarray, h_row: Optional[np.ndarray], w_down: Optional[np.ndarray],
                      w_up_head: Optional[np.ndarray], dtype: str) -> np.ndarray:
-    """q~ = round_dtype(fp32(q + fp32(delta_q)))  (R7).  Without Q-Cal (r = 0) q~ = q."""
+    """q~ = round_dtype(fp32(q + fp32(delta_q)))  (R7).  Without Q-Cal (r = 0) q~ = q.
+    dtype "fp64" keeps everything in float64."""
+    if dtype == "fp64":
+        q64 = np.asarray(q_row, dtype=np.float64)
+        if w_down is None or w_down.shape[0] == 0:
+            return q64
+        return q64 + qcal_offset(h_row, w_down, w_up_head)
     q32 = np.asarray(q_row, dtype=np.float32)
     if w_down is None or w_down.shape[0] == 0:
         return round_to_run_dtype(q32, dtype)
@@ -121,11 +129,13 @@ def calibrated_query(q_row: np.ndarray, h_row: Optional[np.ndarray], w_down: Opt
 # ------------------------------------------------------------------------------------------
 
 def landmark_scores(q_tilde: np.ndarray, lmk_rows: np.ndarray) -> np.ndarray:
-    """sigma_j = q~ . lmk_j for every given landmark row, float64 dot rounded to fp32 (R7)."""
+    """sigma_j = q~ . lmk_j for every given landmark row, float64 dot rounded to fp32 (R7); a
+    float64 q~ (dtype "fp64") keeps float64 scores."""
     qt = np.asarray(q_tilde, dtype=np.float64)
-    out = np.empty(lmk_rows.shape[0], dtype=np.float32)
+    exact = np.asarray(q_tilde).dtype == np.float64
+    out = np.empty(lmk_rows.shape[0], dtype=np.float64 if exact else np.float32)
     for j in range(lmk_rows.shape[0]):
-        out[j] = np.float32(np.dot(lmk_rows[j].astype(np.float64), qt))
+        out[j] = np.dot(lmk_rows[j].astype(np.float64), qt)
     return out
 
 
@@ -138,7 +148,7 @@ def select_top_k(sigma: np.ndarray, k: int) -> np.ndarray:
 
     Repeatedly takes the best remaining candidate; np.argmax returns the first
     (smallest) index among equal maxima, which is the tie rule R3."""
-    s = np.asarray(sigma, dtype=np.float32).astype(np.float64)
+    s = np.asarray(sigma).astype(np.float64)
     n = s.shape[0]
     taken = np.zeros(n, dtype=bool)
     chosen = []
@@ -355,4 +365,99 @@ def dense_decode(inp: Dict[str, np.ndarray], scale: Optional[float] = None,
     for (b, h) in pairs:
         e = _causal_end(int(kv_len[b]) - 1)
         out[(b, h)] = dense_attention_row(q[b, h], kc[b, h, :e], vc[b, h, :e], s)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# Backward pass: gradients of a loss through the forward above.  The pages train the selection
+# end to end: the landmark scores sit inside the forward attention, so the next-token loss sends
+# gradients into the landmark keys ([P3] "Core idea": gradients flow into the landmark
+# representations; [P2]: the chunk scores are learned from the language-modelling loss).
+# Readings: the top-k choice is a fixed index set (not differentiable); the rounding of q~ to the
+# run dtype passes gradients through unchanged; the loss is sum(dout * o) for a given dout.
+# ------------------------------------------------------------------------------------------
+
+def chunk_backward(q_row, keys, values, w_j, dout_row, scale):
+    """One (row, chunk) term w_j * o_j with o_j = softmax(scale * K q) V over the chunk's visible
+    keys.  Returns (dq [d], dK [n, d], dV [n, d], dw_j = dout . o_j), float64."""
+    q = np.asarray(q_row, dtype=np.float64)
+    K = np.asarray(keys, dtype=np.float64)
+    V = np.asarray(values, dtype=np.float64)
+    g = np.asarray(dout_row, dtype=np.float64)
+    a = scale * (K @ q)
+    p = np.exp(a - a.max())
+    p = p / p.sum()
+    o_j = p @ V
+    dw = float(g @ o_j)                   # d(loss)/d(w_j)
+    dp = w_j * (V @ g)                    # d(loss)/d(p_t) for the weighted term
+    da = p * (dp - float(p @ dp))         # softmax backward
+    dq = scale * (da @ K)
+    dK = scale * np.outer(da, q)
+    dV = np.outer(w_j * p, g)
+    return dq, dK, dV, dw
+
+
+def inter_chunk_backward(w, dw, scale):
+    """d(loss)/d(sigma_j) for w = softmax(scale * sigma) over the selection, given dw_j."""
+    w = np.asarray(w, dtype=np.float64)
+    dw = np.asarray(dw, dtype=np.float64)
+    return scale * w * (dw - float(w @ dw))
+
+
+def prefill_backward(inp: Dict[str, np.ndarray], dout: np.ndarray, chunk: int, topk: int, dtype: str,
+                     scale: Optional[float] = None, sel_idx: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dout * o) for the prefill of inp (as prefill_rows) with respect to q, k,
+    v, lmk and, with Q-Cal, h, w_down and w_up.  The selection is the forward's own, or sel_idx
+    [B,H,L,k] when given.  Returns float64 arrays keyed dq, dk, dv, dlmk (and dh, dw_down,
+    dw_up with Q-Cal).  Also returns dsigma [B,H,L,k] (zero on padding)."""
+    q, k, v, lmk = inp["q"], inp["k"], inp["v"], inp["lmk"]
+    B, H, L, d = q.shape
+    s = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    w_down = inp.get("w_down")
+    qcal = w_down is not None and w_down.shape[0] > 0
+    out = dict(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(v.shape), dlmk=np.zeros(lmk.shape),
+               dsigma=np.zeros((B, H, L, topk)))
+    if qcal:
+        r, D = w_down.shape
+        w_up = inp["w_up"].astype(np.float64)
+        out.update(dh=np.zeros((B, L, D)), dw_down=np.zeros((r, D)), dw_up=np.zeros((H * d, r)))
+        dt = np.zeros((B, L, r))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                # forward of row i (steps 1-4)
+                hid = inp["h"][b, i] if qcal else None
+                qt = calibrated_query(q[b, h, i], hid, w_down if qcal else None, _w_up_head(inp.get("w_up"), h, d),
+                                      dtype)
+                c = i // chunk
+                sigma = landmark_scores(qt, lmk[b, h, : c + 1])
+                idx = select_top_k(sigma, topk) if sel_idx is None else np.asarray(sel_idx[b, h, i])
+                js = [int(j) for j in idx if j >= 0]
+                w = inter_chunk_weights(np.asarray([sigma[j] for j in js]), s)
+                # steps 5-6 backward, chunk by chunk
+                dws = np.zeros(len(js))
+                for n, j in enumerate(js):
+                    lo, hi = _visible_range(j, chunk, i)
+                    dq_j, dK, dV, dws[n] = chunk_backward(q[b, h, i], k[b, h, lo:hi], v[b, h, lo:hi], w[n],
+                                                         dout[b, h, i], s)
+                    out["dq"][b, h, i] += dq_j
+                    out["dk"][b, h, lo:hi] += dK
+                    out["dv"][b, h, lo:hi] += dV
+                # step 4 backward, then step 2 (scores) and step 1 (Q-Cal)
+                dsig = inter_chunk_backward(w, dws, s)
+                out["dsigma"][b, h, i, : len(js)] = dsig
+                dqt = np.zeros(d)
+                for n, j in enumerate(js):
+                    dqt += dsig[n] * lmk[b, h, j].astype(np.float64)
+                    out["dlmk"][b, h, j] += dsig[n] * np.asarray(qt, dtype=np.float64)
+                out["dq"][b, h, i] += dqt             # q~ = q + delta_q: rounding passes gradients
+                if qcal:
+                    t = w_down.astype(np.float64) @ inp["h"][b, i].astype(np.float64)
+                    out["dw_up"][h * d:(h + 1) * d] += np.outer(dqt, t)
+                    dt[b, i] += w_up[h * d:(h + 1) * d].T @ dqt
+    if qcal:
+        for b in range(B):
+            for i in range(L):
+                out["dw_down"] += np.outer(dt[b, i], inp["h"][b, i].astype(np.float64))
+                out["dh"][b, i] = w_down.astype(np.float64).T @ dt[b, i]
     return out

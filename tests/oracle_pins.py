@@ -450,4 +450,81 @@ def pin_dense_decode_matches_prefill_row():
         assert (i >= 64) == (not np.allclose(dec, hils["o"], atol=1e-9)), (h, i)
 
 
+# ---------------------------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------------------------
+
+def _bwd_case(seed, B=1, H=2, L=16, d=4, C=4, r=2, D=6):
+    g = _rng(seed)
+    inp = dict(q=g.standard_normal((B, H, L, d)), k=g.standard_normal((B, H, L, d)),
+               v=g.standard_normal((B, H, L, d)), lmk=g.standard_normal((B, H, L // C, d)))
+    if r:
+        inp.update(h=g.standard_normal((B, L, D)), w_down=0.5 * g.standard_normal((r, D)),
+                   w_up=0.5 * g.standard_normal((H * d, r)))
+    return inp, g.standard_normal((B, H, L, d))
+
+
+def _loss(inp, dout, C, k, scale):
+    o, idx, _ = O.prefill(inp, C, k, "fp64", scale=scale)
+    return float(np.sum(o * dout)), idx
+
+
+def pin_backward_finite_differences():
+    """Every gradient entry against central differences of sum(dout * o) of the float64 forward
+    (the selection stays the same under the perturbations, checked)."""
+    C, k, s, eps = 4, 2, 0.6, 1e-5
+    inp, dout = _bwd_case(27)
+    grads = O.prefill_backward(inp, dout, C, k, "fp64", scale=s)
+    _, idx0 = _loss(inp, dout, C, k, s)
+    names = dict(q="dq", k="dk", v="dv", lmk="dlmk", h="dh", w_down="dw_down", w_up="dw_up")
+    for name, gname in names.items():
+        x = inp[name]
+        num = np.zeros(x.shape)
+        for pos in np.ndindex(*x.shape):
+            old = x[pos]
+            x[pos] = old + eps
+            lp, ip = _loss(inp, dout, C, k, s)
+            x[pos] = old - eps
+            lm, im = _loss(inp, dout, C, k, s)
+            x[pos] = old
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), (name, pos)
+            num[pos] = (lp - lm) / (2 * eps)
+        scale_ = max(1.0, float(np.abs(num).max()))
+        assert np.allclose(grads[gname], num, rtol=0, atol=1e-7 * scale_), \
+            (name, float(np.abs(grads[gname] - num).max()))
+
+
+def pin_backward_single_chunk_is_dense_gradient():
+    """One chunk, k = 1, no Q-Cal: HiLS is dense causal attention, whose gradients have the
+    textbook matrix form dV = P^T dO, dS = P * (dO V^T - rowsum(P * dO V^T)), dQ = s dS K,
+    dK = s dS^T Q; the single inter-chunk weight is 1, so the landmark gets no gradient."""
+    g = _rng(28)
+    L, d, s = 64, 8, 0.4
+    q, k, v, dout = (g.standard_normal((L, d)) for _ in range(4))
+    inp = dict(q=q[None, None], k=k[None, None], v=v[None, None], lmk=g.standard_normal((1, 1, 1, d)))
+    grads = O.prefill_backward(inp, dout[None, None], 64, 1, "fp64", scale=s)
+    a = s * q @ k.T
+    a[np.triu_indices(L, 1)] = -np.inf
+    P = scipy.special.softmax(a, axis=1)
+    dP = dout @ v.T
+    dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    assert np.allclose(grads["dv"][0, 0], P.T @ dout, rtol=0, atol=1e-12)
+    assert np.allclose(grads["dq"][0, 0], s * dS @ k, rtol=0, atol=1e-12)
+    assert np.allclose(grads["dk"][0, 0], s * dS.T @ q, rtol=0, atol=1e-12)
+    assert np.all(grads["dlmk"] == 0.0)
+
+
+def pin_backward_shift_invariances():
+    """Adding one vector to every landmark shifts all of a row's scores equally (the weights do
+    not change): the landmark gradients sum to zero.  Adding one vector to every key of a chunk
+    shifts that chunk's visible scores equally: each chunk's key gradients sum to zero."""
+    C, k = 4, 3
+    inp, dout = _bwd_case(29, L=20, r=2)
+    grads = O.prefill_backward(inp, dout, C, k, "fp64", scale=0.5)
+    assert np.allclose(grads["dlmk"].sum(axis=2), 0.0, rtol=0, atol=1e-12)
+    dk = grads["dk"].reshape(1, 2, 20 // C, C, -1).sum(axis=3)
+    assert np.allclose(dk, 0.0, rtol=0, atol=1e-12)
+    assert np.abs(grads["dlmk"]).max() > 1e-3 and np.abs(grads["dk"]).max() > 1e-3
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -71,7 +71,33 @@ def _given_sigma_reversed(q_row, keys, values, idx, sigma_selected, i, chunk, sc
     return _o(q_row, keys, values, idx, sig, i, chunk, scale)
 
 
+def _chunk_bwd_dv_unweighted(q, K, V, w_j, g, scale, _o=O.chunk_backward):
+    dq, dK, dV, dw = _o(q, K, V, w_j, g, scale)
+    return dq, dK, dV / max(w_j, 1e-300), dw
+
+
+def _chunk_bwd_dk_unscaled(q, K, V, w_j, g, scale, _o=O.chunk_backward):
+    dq, dK, dV, dw = _o(q, K, V, w_j, g, scale)
+    return dq, dK / scale, dV, dw
+
+
+def _chunk_bwd_no_softmax_centering(q, K, V, w_j, g, scale):
+    q, K, V, g = (np.asarray(x, dtype=np.float64) for x in (q, K, V, g))
+    a = scale * (K @ q)
+    p = np.exp(a - a.max())
+    p /= p.sum()
+    dp = w_j * (V @ g)
+    da = p * dp
+    return scale * (da @ K), scale * np.outer(da, q), np.outer(w_j * p, g), float(g @ (p @ V))
+
+
 MUTATIONS = {
+    "bwd_dsigma_not_centred": ("inter_chunk_backward", lambda w, dw, s: s * np.asarray(w) * np.asarray(dw)),
+    "bwd_dsigma_unscaled": ("inter_chunk_backward",
+                            lambda w, dw, s, _o=O.inter_chunk_backward: _o(w, dw, 1.0) if s != 1.0 else 2 * _o(w, dw, s)),
+    "bwd_dv_unweighted": ("chunk_backward", _chunk_bwd_dv_unweighted),
+    "bwd_dk_unscaled": ("chunk_backward", _chunk_bwd_dk_unscaled),
+    "bwd_softmax_not_centred": ("chunk_backward", _chunk_bwd_no_softmax_centering),
     "dense_attends_next_key": ("_causal_end", lambda i: i + 2),
     "dense_misses_itself": ("_causal_end", lambda i: max(i, 1)),
     "dense_unscaled": ("dense_attention_row",
@@ -106,9 +132,11 @@ def test_some_pin_catches(name, monkeypatch):
     attr, fake = MUTATIONS[name]
     monkeypatch.setattr(O, attr, fake)
     caught = []
-    for pin in oracle_pins.ALL_PINS:
+    # the finite-difference pin is the slowest: it runs only if no other pin catches the mutation
+    for pin in sorted(oracle_pins.ALL_PINS, key=lambda p: p.__name__ == "pin_backward_finite_differences"):
         try:
             pin()
         except Exception:
             caught.append(pin.__name__)
+            break
     assert caught, f"no pin catches mutation {name}"

@@ -1,0 +1,796 @@
+// Backward pass of the HiLS prefill.
+//
+// The pages train the chunk selection end to end: the landmark scores are part of the forward
+// attention, so the language-modelling loss sends gradients into the landmark keys [HiLS
+// Attention explainer (molayo1419.me), "Core idea": gradients reach the landmark
+// representations; "HiLS Attention Extrapolates 64x at 90% Retrieval Accuracy": the retrieval
+// scores are learned from the loss].  Given dout = dL/do, the gradients are, per row i with
+// selection j in sel(i), weights w_j = softmax(s sigma), chunk softmax p_jt over the visible
+// keys t of chunk j and o_j = sum_t p_jt v_t:
+//   dw_j      = dout . o_j                            (= sum_t p_jt (dout . v_t))
+//   dsigma_j  = s w_j (dw_j - sum_j' w_j' dw_j')
+//   ds_jt     = w_j p_jt (dout . v_t - dw_j)           (softmax backward of chunk j)
+//   dq       += s sum_t ds_jt k_t + sum_j dsigma_j lmk_j   (the second term through q~;
+//                                                         its rounding passes gradients)
+//   dk_t     += s ds_jt q_i;   dv_t += w_j p_jt dout_i;   dlmk_j += dsigma_j q~_i
+//   Q-Cal: dW_up[h] += dq~_i t_i^T, dt_i = sum_h W_up[h]^T dq~_i, dW_down += dt_i h_i^T,
+//          dh_i = W_down^T dt_i.
+// The top-k choice is a fixed index set (no gradient).  Every (row, chunk) term is local to its
+// chunk of 64 keys, so nothing has to be carried between chunks except dsigma's sum.
+//
+// Kernels (in launch order):
+//   bwd_qtilde_kernel     q~ = round(q + W_up t) of every row (Q-Cal only), for dlmk.
+//   bwd_row_kernel        row-major: a workgroup takes one chunk's 64 query rows (four 16-row
+//                         MFMA blocks) and walks the union of their selections, staging each
+//                         chunk's K (two layouts) and V once; per selected (row, chunk) it forms
+//                         S^T = K q^T, dP^T = V dout^T, the chunk softmax, dw and ds, and
+//                         accumulates dq^T += K^T ds^T; it writes dq (fp32), the chunk's
+//                         log-sum-exp and dw per (row, slot), then dsigma per (row, slot).
+//   bwd_dqtilde_kernel    dq~ = sum_j dsigma_j lmk_j; dq = dq_attn + dq~ (dq~ kept for Q-Cal).
+//   bwd_count/scan/fill   per key/value head: the selections of its query heads inverted into
+//                         per-chunk lists of (row, slot), ordered by (head, row) - no atomics
+//                         decide the order, so every sum below runs in a fixed order.
+//   bwd_chunk_kernel      chunk-major: one workgroup per chunk walks its list in blocks of 16
+//                         rows (q, dout, q~ gathered into LDS); wave w owns keys 16w..16w+15
+//                         and accumulates dK, dV with MFMA, the chunk's softmax rebuilt from the
+//                         saved log-sum-exp; dlmk_j = sum dsigma q~ on the side.
+//   bwd_dt / split-K GEMMs / bwd_dh   the Q-Cal factors' gradients.
+#include <float.h>
+
+#include "attn_tiles.h"
+#include "hils_device.h"
+#include "hils_launch.h"
+
+namespace hils {
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// q~ for every row (Q-Cal): the same fp32 sum and one rounding to the run dtype as the forward.
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_qtilde_kernel(const BwdArgs a) {
+  const size_t n = (size_t)a.B * a.H * a.L * a.d;
+  const T* q = static_cast<const T*>(a.q);
+  const T* wu = static_cast<const T*>(a.w_up);
+  T* qt = static_cast<T*>(a.qt);
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
+    const int e = (int)(x % a.d);
+    const size_t row = x / a.d;
+    const int i = (int)(row % a.L);
+    const size_t bh = row / a.L;
+    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+    const float* t = a.tcode + ((size_t)b * a.L + i) * a.r;
+    const T* w = wu + ((size_t)h * a.d + e) * a.r;
+    float dq = 0.f;
+    for (int c = 0; c < a.r; ++c) dq = fmaf(to_f32(w[c]), t[c], dq);
+    qt[x] = from_f32<T>(to_f32(q[x]) + dq);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Row-major pass.
+// ------------------------------------------------------------------------------------------
+template <typename T, int D>
+struct BwdRowSmem {
+  typedef AttnLayout<T, D> Lay;
+  alignas(16) char kr[Lay::KBYTES];    // K rows: A operand of S^T
+  alignas(16) char kd[Lay::VBYTES];    // K, d-block-major: A operand of dQ^T (transposed reads)
+  alignas(16) char vr[Lay::KBYTES];    // V rows: A operand of dP^T
+  int nunion;
+  uint16_t sidx[64 * 65];
+  float sw[64 * 65];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_row_kernel(const BwdArgs a) {
+  constexpr int NT = 256;
+  typedef AttnLayout<T, D> Lay;
+  typedef Mfma<T> M;
+  constexpr int KPL = M::KPL;
+  constexpr int NF = D / 4 / KPL;            // S^T steps over d
+  constexpr int NP = 64 / M::K;              // dQ^T steps over the 64 keys
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int NV = 64 * Lay::VPR / NT;     // 16-byte vectors per thread per tensor per chunk
+  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
+  __shared__ BwdRowSmem<T, D> sm;
+  extern __shared__ uint32_t bitmap[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int N = a.L / 64;
+  const uint32_t total = (uint32_t)a.B * a.H * N;
+  const uint32_t gid = xcd_remap(blockIdx.x, total);
+  const int bh = gid / N;
+  const int c = N - 1 - (int)(gid % N);      // the group's chunk; longest groups first
+  const int q0 = c * 64;
+  const int k = a.k, ks = k + 1;
+  const int kvp = kv_pair(bh, a.H, a.G);
+  const T* Kb = static_cast<const T*>(a.k_in) + (size_t)kvp * a.L * D;
+  const T* Vb = static_cast<const T*>(a.v_in) + (size_t)kvp * a.L * D;
+  const size_t row0 = (size_t)bh * a.L;
+
+  const int nwords = (c + 1 + 31) >> 5;
+  for (int x = tid; x < nwords; x += NT) bitmap[x] = 0u;
+  if (tid == 0) sm.nunion = 0;
+  for (int r = tid; r < 64; r += NT) sm.sidx[r * ks + k] = (uint16_t)0xFFFF;
+  __syncthreads();
+  for (int x = tid; x < 64 * k; x += NT) {
+    const int r = x / k, e = x - r * k;
+    const int j = a.idx[(row0 + q0) * k + x];
+    const bool ok = j >= 0 && j <= c;
+    sm.sidx[r * ks + e] = ok ? (uint16_t)j : (uint16_t)0xFFFF;
+    sm.sw[r * ks + e] = a.w[(row0 + q0) * k + x];
+    if (ok) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  {
+    int cnt = 0;
+    for (int x = tid; x < nwords; x += NT) cnt += __popc(bitmap[x]);
+    cnt = (int)wave_sum((float)cnt);
+    if (lane == 0) atomicAdd(&sm.nunion, cnt);
+  }
+
+  const int rloc = 16 * wave + m, qpos = q0 + rloc;
+  const size_t grow = row0 + qpos;
+  int ptr = 0;
+  typename M::frag qf[NF], df[NF];
+  {
+    const T* qp = static_cast<const T*>(a.q) + grow * D + g * (D / 4);
+    const T* dp = static_cast<const T*>(a.dout) + grow * D + g * (D / 4);
+#pragma unroll
+    for (int st = 0; st < NF; ++st) {
+      qf[st] = load_frag<T>(qp + st * KPL);
+      df[st] = load_frag<T>(dp + st * KPL);
+    }
+  }
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = zero4();
+  float dsum = 0.f;                          // sum over the row's chunks of w_j dw_j
+
+  auto koff = [&](int row, int e) -> int {
+    if constexpr (sizeof(T) == 2) return BlockKLayout<D>::off(row, e / VE);
+    else return row * Lay::KLD + e * 4;
+  };
+  auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
+    const T* kc = Kb + (size_t)j * 64 * D;
+    const T* vc = Vb + (size_t)j * 64 * D;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+    }
+  };
+  auto store_kv = [&](const u32x4 (&kr)[NV], const u32x4 (&vr)[NV]) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = tid + NT * u;
+      const int row = v / Lay::VPR, p = v % Lay::VPR;
+      const int e = p * VE;
+      *reinterpret_cast<u32x4*>(sm.kr + koff(row, e)) = kr[u];
+      *reinterpret_cast<u32x4*>(sm.vr + koff(row, e)) = vr[u];
+      *reinterpret_cast<u32x4*>(sm.kd + (e >> 4) * Lay::VDB + row * (16 * (int)sizeof(T)) +
+                                (e & 15) * (int)sizeof(T)) = kr[u];
+    }
+  };
+
+  const float zs = a.scale * 1.4426950408889634f;
+  auto compute = [&](int j) {
+    const int e = rloc * ks + ptr;
+    const bool sel = sm.sidx[e] == (uint16_t)j;
+    const float wq = sel ? sm.sw[e] : 0.f;
+    const int slot = ptr;
+    ptr += sel ? 1 : 0;
+    if (!__any(sel)) return;
+    // S^T and dP^T: lane (m, g) holds row m and keys 16 kb + 4 g + rr.
+    float sv[16], pv[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 s4 = zero4(), p4 = zero4();
+#pragma unroll
+      for (int st = 0; st < NF; ++st) {
+        const int off = koff(kb * 16 + m, g * (D / 4) + st * KPL);
+        s4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.kr + off)), qf[st], s4);
+        p4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.vr + off)), df[st], p4);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        sv[kb * 4 + rr] = s4[rr];
+        pv[kb * 4 + rr] = p4[rr];
+      }
+    }
+    if (j == c) {                            // the rows' own chunk: keys after the row masked
+      const int ql = qpos & 63;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (kb * 16 + 4 * g + rr > ql) sv[kb * 4 + rr] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+    mx = col_max(mx) * zs;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], zs, -mx));
+      l += sv[i];
+    }
+    l = col_sum(l);
+    const float inv = 1.0f / l;
+    float dw = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] *= inv;                          // p
+      dw = fmaf(sv[i], pv[i], dw);
+    }
+    dw = col_sum(dw);
+    if (sel && g == 0) {
+      a.lse[grow * k + slot] = mx + __log2f(l);
+      a.dw[grow * k + slot] = dw;
+    }
+    dsum = fmaf(wq, dw, dsum);
+    // ds = w p (dP - dw), as the B operand of dQ^T = K^T ds^T.
+    typename M::frag sf[NP];
+#pragma unroll
+    for (int st = 0; st < NP; ++st) {
+      if constexpr (KPL == 1) {
+        sf[st] = wq * sv[st] * (pv[st] - dw);
+      } else {
+#pragma unroll
+        for (int z = 0; z < KPL; ++z) sf[st][z] = bf16_rne(wq * sv[st * KPL + z] * (pv[st * KPL + z] - dw));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int st = 0; st < NP; ++st) {
+        typename M::frag ka;
+        if constexpr (KPL == 1) ka = v_frag_f32<Lay::VDB>(sm.kd, m, g, db, st);
+        else ka = v_frag_bf16<Lay::VDB>(sm.kd, m, g, db, st);
+        acc[db] = M::mma(ka, sf[st], acc[db]);
+      }
+  };
+
+  __syncthreads();                           // every wave's union count has landed
+  int wi = 0;
+  uint32_t cur = bitmap[0];
+  auto next_chunk = [&]() -> int {
+    while (cur == 0u && wi + 1 < nwords) cur = bitmap[++wi];
+    if (cur == 0u) return -1;
+    const int j = wi * 32 + __builtin_ctz(cur);
+    cur &= cur - 1u;
+    return j;
+  };
+  const int U = sm.nunion;
+  int jl = -1;
+  auto advance = [&]() -> int {
+    const int j = next_chunk();
+    if (j >= 0) jl = j;
+    return j >= 0 ? j : jl;
+  };
+  u32x4 kr[NV], vr[NV];
+  if (U > 0) {
+    int cj = advance();
+    load_kv(cj, kr, vr);
+    store_kv(kr, vr);
+    int cn = advance();
+    load_kv(cn, kr, vr);
+    __syncthreads();
+    for (int t = 0; t < U; ++t) {
+      compute(cj);
+      __syncthreads();
+      store_kv(kr, vr);
+      const int cn2 = advance();
+      load_kv(cn2, kr, vr);
+      __syncthreads();
+      cj = cn;
+      cn = cn2;
+    }
+  }
+
+  // dq from the chunk attention (fp32; dq~ is added by the next kernel).  Lane holds d = 16 db +
+  // 4 g + rr of its row.
+  float* dq = a.dqbuf + grow * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    f32x4 o;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) o[rr] = a.scale * acc[db][rr];
+    *reinterpret_cast<f32x4*>(dq + db * 16 + 4 * g) = o;
+  }
+  // dsigma per slot; the lane that wrote the row's dw reads it back (same thread, in order).
+  if (g == 0) {
+    const int keff = min(k, c + 1);
+    for (int s = 0; s < k; ++s) {
+      float ds = 0.f;
+      if (s < keff) ds = a.scale * sm.sw[rloc * ks + s] * (a.dw[grow * k + s] - dsum);
+      a.dsig[grow * k + s] = ds;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dq~ = sum_j dsigma_j lmk_j per row; dq = dq_attn + dq~ (rounded once); dq~ stays in dqbuf
+// for the Q-Cal gradients.
+// ------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dqtilde_kernel(const BwdArgs a) {
+  constexpr int TPR = D / 4;                 // threads per row, 4 elements each
+  constexpr int RPW = 256 / TPR;             // rows per workgroup
+  const size_t nrows = (size_t)a.B * a.H * a.L;
+  const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  if (row >= nrows) return;
+  const int e0 = (threadIdx.x % TPR) * 4;
+  const int bh = (int)(row / a.L);
+  const int N = a.L / 64;
+  const T* lmk = static_cast<const T*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * N * D + e0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.k; ++s) {
+    const int j = a.idx[row * a.k + s];
+    if (j < 0 || j >= N) break;              // padding sits at the end
+    const float ds = a.dsig[row * a.k + s];
+    const T* lr = lmk + (size_t)j * D;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) acc[z] = fmaf(ds, to_f32(lr[z]), acc[z]);
+  }
+  float* dqb = a.dqbuf + row * D + e0;
+  T* dq = static_cast<T*>(a.dq) + row * D + e0;
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    dq[z] = from_f32<T>(dqb[z] + acc[z]);
+    dqb[z] = acc[z];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Per key/value head: the selections of its G query heads as per-chunk lists of
+// (g * L + i) << 6 | slot, each list in ascending (g, i) order.  Row blocks of kBwdRB rows over
+// the G * L rows: counts per (block, chunk), an exclusive scan down each chunk's column and
+// across chunks, then each block fills its rows in order.
+// ------------------------------------------------------------------------------------------
+constexpr int kBwdRB = 128;
+
+// The G query heads of key/value head bk = b * Hk + hk are consecutive heads, so their G * L
+// rows of idx are contiguous; block rblk holds rows rblk * kBwdRB .. of them (fewer in the last).
+__device__ __forceinline__ const int32_t* bwd_idx_rows(const BwdArgs& a, int bk, int rblk) {
+  const int Hk = a.H / a.G;
+  const int b = bk / Hk, hk = bk % Hk;
+  return a.idx + (((size_t)b * a.H + hk * a.G) * a.L + (size_t)rblk * kBwdRB) * a.k;
+}
+__device__ __forceinline__ int bwd_block_rows(const BwdArgs& a, int rblk) {
+  return min(kBwdRB, a.G * a.L - rblk * kBwdRB);
+}
+
+__global__ __launch_bounds__(256) void bwd_count_kernel(const BwdArgs a, int bk) {
+  extern __shared__ uint32_t cnt[];
+  const int N = a.L / 64, rblk = blockIdx.x;
+  for (int j = threadIdx.x; j < N; j += 256) cnt[j] = 0u;
+  __syncthreads();
+  const int32_t* idx = bwd_idx_rows(a, bk, rblk);
+  const int nr = bwd_block_rows(a, rblk);
+  for (int x = threadIdx.x; x < nr * a.k; x += 256) {
+    const int j = idx[x];
+    if (j >= 0 && j < N) atomicAdd(&cnt[j], 1u);
+  }
+  __syncthreads();
+  uint32_t* out = a.rbcnt + (size_t)rblk * N;
+  for (int j = threadIdx.x; j < N; j += 256) out[j] = cnt[j];
+}
+
+// Exclusive prefix down each chunk's column (in place) and the chunk's total.
+__global__ __launch_bounds__(256) void bwd_colscan_kernel(const BwdArgs a, int nrb) {
+  const int N = a.L / 64;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= N) return;
+  uint32_t s = 0;
+  for (int rb = 0; rb < nrb; ++rb) {
+    const uint32_t v = a.rbcnt[(size_t)rb * N + j];
+    a.rbcnt[(size_t)rb * N + j] = s;
+    s += v;
+  }
+  a.choff[j] = s;                            // totals; turned into offsets next
+}
+
+__global__ __launch_bounds__(1024) void bwd_offscan_kernel(const BwdArgs a) {
+  __shared__ uint32_t part[1024];
+  const int N = a.L / 64, t = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int b0 = min(N, t * per), e0 = min(N, b0 + per);
+  uint32_t s = 0;
+  for (int i = b0; i < e0; ++i) s += a.choff[i];
+  part[t] = s;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const uint32_t v = t >= d ? part[t - d] : 0u;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  uint32_t p = part[t] - s;
+  for (int i = b0; i < e0; ++i) {
+    const uint32_t v = a.choff[i];
+    a.choff[i] = p;
+    p += v;
+  }
+  if (t == 1023) a.choff[N] = part[1023];
+}
+
+// One wave per row block: the block's selections are staged in LDS, then its rows are appended
+// in order (a row's chunks are distinct, so the lanes of one row never share a cursor).
+__global__ __launch_bounds__(64) void bwd_fill_kernel(const BwdArgs a, int bk) {
+  extern __shared__ uint32_t lds[];
+  const int N = a.L / 64, rblk = blockIdx.x, k = a.k, lane = threadIdx.x;
+  uint32_t* cur = lds;                       // N cursors
+  int32_t* sel = reinterpret_cast<int32_t*>(lds + N);   // kBwdRB * k staged indices
+  const int32_t* idx = bwd_idx_rows(a, bk, rblk);
+  const int nr = bwd_block_rows(a, rblk);
+  for (int j = lane; j < N; j += 64) cur[j] = a.choff[j] + a.rbcnt[(size_t)rblk * N + j];
+  for (int x = lane; x < nr * k; x += 64) sel[x] = idx[x];
+  __syncthreads();
+  // One wave: its LDS accesses complete in program order, so row r + 1 reads the cursors row r
+  // advanced.
+  const uint32_t r0 = (uint32_t)rblk * kBwdRB;
+  for (int r = 0; r < nr; ++r) {
+    if (lane < k) {
+      const int j = sel[r * k + lane];
+      if (j >= 0 && j < N) {
+        const uint32_t p = cur[j];
+        cur[j] = p + 1;
+        a.ent[p] = ((r0 + r) << 6) | (uint32_t)lane;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Chunk-major pass: dK, dV and dlmk of one chunk of key/value head bk per workgroup.
+// ------------------------------------------------------------------------------------------
+template <typename T, int D>
+struct BwdChunkSmem {
+  static constexpr int RB = 16 * (int)sizeof(T);      // bytes of one row within a d-block
+  static constexpr int DBS = 16 * RB + 32;             // d-block stride: 16 rows + pad
+  alignas(16) char qs[(D / 16) * DBS];                 // gathered q rows, d-block-major
+  alignas(16) char ds[(D / 16) * DBS];                 // gathered dout rows
+  alignas(16) char ts[(D / 16) * DBS];                 // gathered q~ rows
+  float rw[16], rlse[16], rdw[16], rsig[16];
+  int rpos[16];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a, int bk) {
+  typedef BwdChunkSmem<T, D> S;
+  typedef Mfma<T> M;
+  constexpr int KPL = M::KPL;
+  constexpr int NF = D / 4 / KPL;            // S steps over d
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int VPR = D / VE;                // 16-byte vectors per row
+  __shared__ S sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int N = a.L / 64, j = blockIdx.x;
+  const int Hk = a.H / a.G, b = bk / Hk, hk = bk % Hk;
+  const size_t kvoff = (size_t)bk * a.L * D;
+  const int key = 16 * wave + n;             // this lane's key within the chunk (B operands)
+  const int kpos = j * 64 + key;
+  const T* krow = static_cast<const T*>(a.k_in) + kvoff + (size_t)kpos * D + g * (D / 4);
+  const T* vrow = static_cast<const T*>(a.v_in) + kvoff + (size_t)kpos * D + g * (D / 4);
+  typename M::frag kf[NF], vf[NF];
+#pragma unroll
+  for (int st = 0; st < NF; ++st) {
+    kf[st] = load_frag<T>(krow + st * KPL);
+    vf[st] = load_frag<T>(vrow + st * KPL);
+  }
+  f32x4 dk[D / 16], dv[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) dk[db] = dv[db] = zero4();
+  float dl = 0.f;                            // dlmk, dim wave * D/4 + lane (lanes < D/4)
+  const float zs = a.scale * 1.4426950408889634f;
+  const T* qt_base = static_cast<const T*>(a.r > 0 ? a.qt : a.q);
+
+  const uint32_t e0 = a.choff[j], e1 = a.choff[j + 1];
+  for (uint32_t base = e0; base < e1; base += 16) {
+    // gather 16 rows (rows past the list are zero and get weight 0)
+    for (int v = tid; v < 16 * VPR; v += 256) {
+      const int r = v / VPR, p = v % VPR;
+      const uint32_t x = base + r;
+      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = qv, tv = qv;
+      if (x < e1) {
+        const uint32_t en = a.ent[x];
+        const int gi = (int)(en >> 6), gq = gi / a.L, i = gi % a.L;
+        const size_t row = ((size_t)b * a.H + hk * a.G + gq) * a.L + i;
+        qv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + row * D + p * VE);
+        dv4 = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + row * D + p * VE);
+        tv = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
+      }
+      const int e = p * VE;
+      const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
+      *reinterpret_cast<u32x4*>(sm.qs + off) = qv;
+      *reinterpret_cast<u32x4*>(sm.ds + off) = dv4;
+      *reinterpret_cast<u32x4*>(sm.ts + off) = tv;
+    }
+    if (tid < 16) {
+      const uint32_t x = base + tid;
+      float w = 0.f, lse = INFINITY, dwv = 0.f, sg = 0.f;
+      int pos = -1;
+      if (x < e1) {
+        const uint32_t en = a.ent[x];
+        const int slot = (int)(en & 63u), gi = (int)(en >> 6), gq = gi / a.L, i = gi % a.L;
+        const size_t rs = (((size_t)b * a.H + hk * a.G + gq) * a.L + i) * a.k + slot;
+        w = a.w[rs];
+        lse = a.lse[rs];
+        dwv = a.dw[rs];
+        sg = a.dsig[rs];
+        pos = i;
+      }
+      sm.rw[tid] = w;
+      sm.rlse[tid] = lse;
+      sm.rdw[tid] = dwv;
+      sm.rsig[tid] = sg;
+      sm.rpos[tid] = pos;
+    }
+    __syncthreads();
+    // S[q][key] = Q K^T and dP[q][key] = dout V^T: lane (n, g) holds key n of the wave and rows
+    // q = 4 g + rr.
+    f32x4 s4 = zero4(), p4 = zero4();
+#pragma unroll
+    for (int st = 0; st < NF; ++st) {
+      const int e = g * (D / 4) + st * KPL;
+      const int off = (e >> 4) * S::DBS + n * S::RB + (e & 15) * (int)sizeof(T);
+      s4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.qs + off)), kf[st], s4);
+      p4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.ds + off)), vf[st], p4);
+    }
+    float pw[4], dsv[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int q = 4 * g + rr;
+      const int pos = sm.rpos[q];
+      float p = __builtin_amdgcn_exp2f(fmaf(s4[rr], zs, -sm.rlse[q]));
+      if (pos < kpos) p = 0.f;               // the key lies after the row (or no row)
+      const float w = sm.rw[q];
+      pw[rr] = w * p;
+      dsv[rr] = w * p * (p4[rr] - sm.rdw[q]);
+    }
+    // dV[key][e] += sum_q (w p)[q][key] dout[q][e];  dK[key][e] += sum_q ds[q][key] q[q][e].
+    // MFMA with the 16 rows as the contraction: A = (w p)^T / ds^T (lane (n, g): key n, rows
+    // 4 g..4 g + 3), B = the row tiles (column e, rows 4 g..4 g + 3).
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      if constexpr (KPL == 1) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          // contraction index (g, st) is row 4 g + st
+          const int off = db * S::DBS + (4 * g + st) * S::RB + n * 4;
+          const float dov = *reinterpret_cast<const float*>(sm.ds + off);
+          const float qv = *reinterpret_cast<const float*>(sm.qs + off);
+          dv[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pw[st], dov, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(dsv[st], qv, dk[db], 0, 0, 0);
+        }
+      } else {
+        // transposed read: lane (n, g) gets column n of rows 4 g..4 g + 3 of d-block db
+        const int off = db * S::DBS + (4 * g + (n >> 2)) * S::RB + 8 * (n & 3);
+        const short4v dob = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.ds + off));
+        const short4v qb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.qs + off));
+        bf16x4 pa, sa;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pa[rr] = bf16_rne(pw[rr]);
+          sa[rr] = bf16_rne(dsv[rr]);
+        }
+        dv[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, pa), dob, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, sa), qb, dk[db], 0, 0, 0);
+      }
+    }
+    // dlmk: dims wave * D/4 + lane, summed over the 16 rows in order.
+    if (lane < D / 4) {
+      const int e = wave * (D / 4) + lane;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const T tv = *reinterpret_cast<const T*>(sm.ts + (e >> 4) * S::DBS + q * S::RB + (e & 15) * (int)sizeof(T));
+        dl = fmaf(sm.rsig[q], to_f32(tv), dl);
+      }
+    }
+    __syncthreads();
+  }
+  // outputs: lane (n, g) holds rows (keys) 16 wave + 4 g + rr, column e = 16 db + n
+  T* dko = static_cast<T*>(a.dk) + kvoff + (size_t)j * 64 * D;
+  T* dvo = static_cast<T*>(a.dv) + kvoff + (size_t)j * 64 * D;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const size_t o = (size_t)(16 * wave + 4 * g + rr) * D + 16 * db + n;
+      dko[o] = from_f32<T>(a.scale * dk[db][rr]);
+      dvo[o] = from_f32<T>(dv[db][rr]);
+    }
+  if (lane < D / 4)
+    static_cast<T*>(a.dlmk)[((size_t)bk * N + j) * D + wave * (D / 4) + lane] = from_f32<T>(dl);
+}
+
+// ------------------------------------------------------------------------------------------
+// Q-Cal gradients.  tok = b * L + i indexes the B * L tokens.
+// ------------------------------------------------------------------------------------------
+// dt[tok][c] = sum_{h, e} dq~[b, h, i, e] W_up[h d + e][c]; 64 tokens per workgroup, thread
+// (token tid / 4, codes tid % 4 + 4 u).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dt_kernel(const BwdArgs a) {
+  __shared__ float xs[64][65];               // dq~ tile: 64 tokens x 64 of H*d
+  __shared__ float ws[64][64];               // W_up tile: 64 of H*d x r (r <= 64)
+  const int tid = threadIdx.x;
+  const int ntok = a.B * a.L;
+  const int tok0 = blockIdx.x * 64;
+  const int tl = tid >> 2, cq = tid & 3;
+  const T* wu = static_cast<const T*>(a.w_up);
+  float acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+  const int HD = a.H * a.d;
+  for (int k0 = 0; k0 < HD; k0 += 64) {
+    const int h = k0 / a.d, e0 = k0 % a.d;
+    for (int x = tid; x < 64 * 64; x += 256) {
+      const int t = x >> 6, kk = x & 63;
+      const int tok = tok0 + t;
+      float v = 0.f;
+      if (tok < ntok) {
+        const int b = tok / a.L, i = tok % a.L;
+        v = a.dqbuf[(((size_t)b * a.H + h) * a.L + i) * a.d + e0 + kk];
+      }
+      xs[t][kk] = v;
+      const int kr = x >> 6, c = x & 63;
+      ws[kr][c] = c < a.r ? to_f32(wu[(size_t)(k0 + kr) * a.r + c]) : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 64; ++kk) {
+      const float xv = xs[tl][kk];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = fmaf(xv, ws[kk][cq + 4 * u], acc[u]);
+    }
+    __syncthreads();
+  }
+  const int tok = tok0 + tl;
+  if (tok < ntok) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = cq + 4 * u;
+      if (c < a.r) a.dt[(size_t)tok * a.r + c] = acc[u];
+    }
+  }
+}
+
+// Split-K outer-product sums over tokens: part[s][x][c] = sum over the tokens of split s of
+// X(tok, x) * Y[tok][c], Y = [tokens, r] fp32.  kind 0: X = dq~ (x over H*d), Y = t (for
+// dW_up); kind 1: X = h (x over hidden), Y = dt (for dW_down).  64 x-columns per workgroup,
+// thread (column tid % 64, codes tid / 64 + 4 u).
+template <typename T, int KIND>
+__global__ __launch_bounds__(256) void bwd_splitk_kernel(const BwdArgs a, int X, int tok_per_split) {
+  __shared__ float xs[64][65];
+  __shared__ float ys[64][65];
+  const int tid = threadIdx.x;
+  const int ntok = a.B * a.L;
+  const int x0 = blockIdx.x * 64, s = blockIdx.y;
+  const int t_begin = s * tok_per_split, t_end = min(ntok, t_begin + tok_per_split);
+  const int xl = tid & 63, cq = tid >> 6;
+  const float* Y = KIND == 0 ? a.tcode : a.dt;
+  float acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
+    for (int v = tid; v < 64 * 64; v += 256) {
+      const int t = v >> 6, c = v & 63;
+      const int tok = t0 + t;
+      float xv = 0.f, yv = 0.f;
+      if (tok < t_end) {
+        if constexpr (KIND == 0) {
+          const int b = tok / a.L, i = tok % a.L, x = x0 + c, h = x / a.d, e = x % a.d;
+          xv = a.dqbuf[(((size_t)b * a.H + h) * a.L + i) * a.d + e];
+        } else {
+          xv = to_f32(static_cast<const T*>(a.h)[(size_t)tok * a.Dh + x0 + c]);
+        }
+        yv = c < a.r ? Y[(size_t)tok * a.r + c] : 0.f;
+      }
+      xs[t][c] = xv;
+      ys[t][c] = yv;
+    }
+    __syncthreads();
+    for (int t = 0; t < 64; ++t) {
+      const float xv = xs[t][xl];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = fmaf(xv, ys[t][cq + 4 * u], acc[u]);
+    }
+    __syncthreads();
+  }
+  float* part = a.gpart + (size_t)s * X * 64;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) part[(size_t)(x0 + xl) * 64 + cq + 4 * u] = acc[u];
+}
+
+// out = sum of the splits in order.  kind 0: out[x][c] ([H*d, r]); kind 1: out[c][x] ([r, hidden]).
+template <typename T, int KIND>
+__global__ __launch_bounds__(256) void bwd_splitk_reduce_kernel(const BwdArgs a, int X, int splits, void* out) {
+  const size_t n = (size_t)X * a.r;
+  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (size_t)gridDim.x * 256) {
+    int x, c;
+    if constexpr (KIND == 0) {
+      x = (int)(v / a.r);
+      c = (int)(v % a.r);
+    } else {
+      c = (int)(v / X);
+      x = (int)(v % X);
+    }
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += a.gpart[((size_t)sp * X + x) * 64 + c];
+    static_cast<T*>(out)[v] = from_f32<T>(s);
+  }
+}
+
+// dh[tok][x] = sum_c dt[tok][c] W_down[c][x]; 64 tokens x 64 columns per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(const BwdArgs a) {
+  __shared__ float ts[64][65];
+  __shared__ float ws[64][64];
+  const int tid = threadIdx.x, ntok = a.B * a.L;
+  const int tok0 = blockIdx.x * 64, x0 = blockIdx.y * 64;
+  const T* wd = static_cast<const T*>(a.w_down);
+  for (int v = tid; v < 64 * 64; v += 256) {
+    const int t = v >> 6, c = v & 63;
+    ts[t][c] = (tok0 + t < ntok && c < a.r) ? a.dt[(size_t)(tok0 + t) * a.r + c] : 0.f;
+    const int cr = v >> 6, x = v & 63;
+    ws[cr][x] = cr < a.r ? to_f32(wd[(size_t)cr * a.Dh + x0 + x]) : 0.f;
+  }
+  __syncthreads();
+  const int xl = tid & 63, tq = tid >> 6;
+  for (int t = tq; t < 64; t += 4) {
+    float s = 0.f;
+    for (int c = 0; c < a.r; ++c) s = fmaf(ts[t][c], ws[c][xl], s);
+    if (tok0 + t < ntok) static_cast<T*>(a.dh)[(size_t)(tok0 + t) * a.Dh + x0 + xl] = from_f32<T>(s);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launcher.
+// ------------------------------------------------------------------------------------------
+size_t bwd_rbcnt_words(int G, int L, int N) { return (size_t)((G * L + kBwdRB - 1) / kBwdRB) * N; }
+int bwd_splits(int ntok) { return max(1, min(256, ntok / 1024)); }
+
+template <typename T, int D>
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
+  const int N = a.L / 64, ntok = a.B * a.L;
+  if (a.r > 0) {
+    hipLaunchKernelGGL(bwd_qtilde_kernel<T>, dim3(4096), dim3(256), 0, st, a);
+  }
+  const size_t bm = (size_t)((N + 31) / 32) * 4;
+  hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3((uint32_t)a.B * a.H * N), dim3(256), bm, st, a);
+  constexpr int RPW = 256 / (D / 4);
+  const size_t nrows = (size_t)a.B * a.H * a.L;
+  hipLaunchKernelGGL((bwd_dqtilde_kernel<T, D>), dim3((unsigned)((nrows + RPW - 1) / RPW)), dim3(256), 0, st, a);
+  const int nrb = (a.G * a.L + kBwdRB - 1) / kBwdRB;
+  const int Hk = a.H / a.G;
+  for (int bk = 0; bk < a.B * Hk; ++bk) {
+    hipLaunchKernelGGL(bwd_count_kernel, dim3(nrb), dim3(256), (size_t)N * 4, st, a, bk);
+    hipLaunchKernelGGL(bwd_colscan_kernel, dim3((N + 255) / 256), dim3(256), 0, st, a, nrb);
+    hipLaunchKernelGGL(bwd_offscan_kernel, dim3(1), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(nrb), dim3(64), (size_t)(N + kBwdRB * a.k) * 4, st, a, bk);
+    hipLaunchKernelGGL((bwd_chunk_kernel<T, D>), dim3(N), dim3(256), 0, st, a, bk);
+  }
+  if (a.r > 0) {
+    hipLaunchKernelGGL(bwd_dt_kernel<T>, dim3((ntok + 63) / 64), dim3(256), 0, st, a);
+    const int S = bwd_splits(ntok), per = (ntok + S - 1) / S;
+    const int HD = a.H * a.d;
+    hipLaunchKernelGGL((bwd_splitk_kernel<T, 0>), dim3(HD / 64, S), dim3(256), 0, st, a, HD, per);
+    hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 0>), dim3(1024), dim3(256), 0, st, a, HD, S, a.dw_up);
+    hipLaunchKernelGGL((bwd_splitk_kernel<T, 1>), dim3(a.Dh / 64, S), dim3(256), 0, st, a, a.Dh, per);
+    hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 1>), dim3(1024), dim3(256), 0, st, a, a.Dh, S, a.dw_down);
+    hipLaunchKernelGGL(bwd_dh_kernel<T>, dim3((ntok + 63) / 64, a.Dh / 64), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_prefill_bwd<bf16, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_prefill_bwd<bf16, 128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_prefill_bwd<float, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_prefill_bwd<float, 128>(const BwdArgs&, hipStream_t);
+
+}  // namespace hils

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -686,6 +687,153 @@ int hils_dense_decode_fwd(const hils_dense_params* p, const void* q, const void*
   else
     err = d == 64 ? hils::launch_dense_decode<float, 64>(a, s) : hils::launch_dense_decode<float, 128>(a, s);
   if (err != hipSuccess) return hip_fail(err, "hils_dense_decode_fwd");
+  return HILS_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t tcode, qt, dqbuf, lse, dw, dsig, dt, rbcnt, choff, ent, gpart, total;
+};
+
+BwdLayout bwd_layout(const hils_prefill_params* p) {
+  BwdLayout L{};
+  const size_t B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim, k = p->topk, r = p->qcal_rank;
+  const size_t e = elem_bytes(p->dtype), N = S / 64;
+  const int G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.tcode = take(r ? B * S * r * 4 : 0);
+  L.qt = take(r ? B * H * S * d * e : 0);
+  L.dqbuf = take(B * H * S * d * 4);
+  L.lse = take(B * H * S * k * 4);
+  L.dw = take(B * H * S * k * 4);
+  L.dsig = take(B * H * S * k * 4);
+  L.dt = take(r ? B * S * r * 4 : 0);
+  L.rbcnt = take(hils::bwd_rbcnt_words(G, (int)S, (int)N) * 4);
+  L.choff = take((N + 1) * 4);
+  L.ent = take((size_t)G * S * k * 4);
+  const size_t X = std::max(H * d, (size_t)(r ? p->hidden : 0));
+  L.gpart = take(r ? (size_t)hils::bwd_splits((int)(B * S)) * X * 64 * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+int check_bwd_params(const hils_prefill_params* p) {
+  int st = check_prefill_params(p);
+  if (st != HILS_OK) return st;
+  if (p->seq_len / 64 > 16384) return fail(HILS_ERR_UNSUPPORTED, "the backward pass supports at most 16384 chunks");
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hils_prefill_bwd_workspace_size(const hils_prefill_params* p) {
+  g_last_error.clear();
+  if (check_bwd_params(p) != HILS_OK) return 0;
+  return bwd_layout(p).total;
+}
+
+int hils_prefill_bwd(const hils_prefill_params* p, const void* q, const void* k, const void* v, const void* lmk,
+                     const void* h, const void* w_down, const void* w_up, const int32_t* sel_idx,
+                     const float* sel_w, const void* dout, void* dq, void* dk, void* dv, void* dlmk, void* dh,
+                     void* dw_down, void* dw_up, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_bwd_params(p);
+  if (st != HILS_OK) return st;
+  if (!q || !k || !v || !lmk || !sel_idx || !sel_w || !dout || !dq || !dk || !dv || !dlmk)
+    return fail(HILS_ERR_INVALID_ARG, "a required tensor is NULL");
+  const bool qcal = p->qcal_rank > 0;
+  const bool all_q = h && w_down && w_up && dh && dw_down && dw_up;
+  const bool none_q = !h && !w_down && !w_up && !dh && !dw_down && !dw_up;
+  if (qcal ? !all_q : !none_q)
+    return fail(HILS_ERR_INVALID_ARG, "h, w_down, w_up, dh, dw_down and dw_up must be given iff qcal_rank > 0");
+  const void* ptrs[] = {q, k, v, lmk, h, w_down, w_up, sel_idx, sel_w, dout, dq, dk, dv, dlmk, dh, dw_down, dw_up};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(HILS_ERR_ALIGNMENT, "a tensor is not 16-byte aligned");
+  const BwdLayout L = bwd_layout(p);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((uintptr_t)workspace & (kWsAlign - 1)) return fail(HILS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+  const size_t e = elem_bytes(p->dtype);
+  const size_t B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim, kk = p->topk;
+  const size_t r = p->qcal_rank, D = p->hidden;
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;
+  const size_t qb = B * H * S * d * e, kb = B * Hk * S * d * e, lb = B * Hk * (S / 64) * d * e;
+  const Range in[] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {lmk, lb, "lmk"},
+                      {h, qcal ? B * S * D * e : 0, "h"}, {w_down, qcal ? r * D * e : 0, "w_down"},
+                      {w_up, qcal ? H * d * r * e : 0, "w_up"}, {sel_idx, B * H * S * kk * 4, "sel_idx"},
+                      {sel_w, B * H * S * kk * 4, "sel_w"}, {dout, qb, "dout"}};
+  const Range out[] = {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {dlmk, lb, "dlmk"},
+                       {dh, qcal ? B * S * D * e : 0, "dh"}, {dw_down, qcal ? r * D * e : 0, "dw_down"},
+                       {dw_up, qcal ? H * d * r * e : 0, "dw_up"}, {workspace, L.total, "workspace"}};
+  if ((st = check_overlaps(in, sizeof(in) / sizeof(in[0]), out, sizeof(out) / sizeof(out[0]))) != HILS_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hils::BwdArgs a;
+  a.q = q;
+  a.k_in = k;
+  a.v_in = v;
+  a.lmk = lmk;
+  a.h = h;
+  a.w_down = w_down;
+  a.w_up = w_up;
+  a.idx = sel_idx;
+  a.w = sel_w;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlmk = dlmk;
+  a.dh = dh;
+  a.dw_down = dw_down;
+  a.dw_up = dw_up;
+  a.tcode = reinterpret_cast<float*>(ws + L.tcode);
+  a.qt = ws + L.qt;
+  a.dqbuf = reinterpret_cast<float*>(ws + L.dqbuf);
+  a.lse = reinterpret_cast<float*>(ws + L.lse);
+  a.dw = reinterpret_cast<float*>(ws + L.dw);
+  a.dsig = reinterpret_cast<float*>(ws + L.dsig);
+  a.dt = reinterpret_cast<float*>(ws + L.dt);
+  a.rbcnt = reinterpret_cast<uint32_t*>(ws + L.rbcnt);
+  a.choff = reinterpret_cast<uint32_t*>(ws + L.choff);
+  a.ent = reinterpret_cast<uint32_t*>(ws + L.ent);
+  a.gpart = reinterpret_cast<float*>(ws + L.gpart);
+  a.B = p->batch;
+  a.H = p->heads;
+  a.L = p->seq_len;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.d = p->head_dim;
+  a.k = p->topk;
+  a.r = p->qcal_rank;
+  a.Dh = p->hidden;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (qcal) {
+    if (p->dtype == HILS_DTYPE_BF16)
+      err = hils::launch_prefill_qcal_code<hils::bf16>(static_cast<const hils::bf16*>(h),
+                                                       static_cast<const hils::bf16*>(w_down), a.tcode,
+                                                       p->batch * p->seq_len, p->hidden, p->qcal_rank, s);
+    else
+      err = hils::launch_prefill_qcal_code<float>(static_cast<const float*>(h), static_cast<const float*>(w_down),
+                                                  a.tcode, p->batch * p->seq_len, p->hidden, p->qcal_rank, s);
+  }
+  if (err == hipSuccess) {
+    if (p->dtype == HILS_DTYPE_BF16)
+      err = d == 64 ? hils::launch_prefill_bwd<hils::bf16, 64>(a, s) : hils::launch_prefill_bwd<hils::bf16, 128>(a, s);
+    else
+      err = d == 64 ? hils::launch_prefill_bwd<float, 64>(a, s) : hils::launch_prefill_bwd<float, 128>(a, s);
+  }
+  if (err != hipSuccess) return hip_fail(err, "hils_prefill_bwd");
   return HILS_OK;
 }
 

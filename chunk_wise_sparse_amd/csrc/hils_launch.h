@@ -136,6 +136,31 @@ hipError_t launch_dense_decode(const DenseDecodeArgs& a, hipStream_t st);
 // Spans per (sequence, head) pair of the dense decode step.
 int dense_decode_splits(int pairs, int lmax);
 
+// Backward pass of the prefill (the selection held fixed).  Workspace pointers are described
+// where they are laid out (hils_api.hip).
+struct BwdArgs {
+  const void *q, *k_in, *v_in, *lmk, *h, *w_down, *w_up;
+  const int32_t* idx;   // [B,H,L,k] the forward's selection
+  const float* w;       // [B,H,L,k] the forward's inter-chunk weights
+  const void* dout;     // [B,H,L,d]
+  void *dq, *dk, *dv, *dlmk, *dh, *dw_down, *dw_up;
+  float* tcode;         // [B*L, r] Q-Cal code
+  void* qt;             // [B,H,L,d] q~ (run dtype)
+  float* dqbuf;         // [B,H,L,d] dq of the chunk attention, then dq~
+  float *lse, *dw, *dsig;   // [B,H,L,k] per (row, slot)
+  float* dt;            // [B*L, r]
+  uint32_t* rbcnt;      // [row blocks, N] counts, then their exclusive prefix per chunk
+  uint32_t* choff;      // [N + 1] chunk list offsets
+  uint32_t* ent;        // [G*L*k] list entries (g*L + i) << 6 | slot
+  float* gpart;         // [splits, max(H*d, hidden), 64] split-K partials
+  int B, H, L, G, d, k, r, Dh;
+  float scale;
+};
+template <typename T, int D>
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
+size_t bwd_rbcnt_words(int G, int L, int N);
+int bwd_splits(int ntok);
+
 template <typename T>
 hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,
                                     int r, hipStream_t st);

@@ -26,7 +26,7 @@ STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", 
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
             "hils_prefill_fwd", "hils_decode_fwd", "hils_decode_fwd_noalloc", "hils_status_string",
             "hils_last_hip_error", "hils_dense_prefill_fwd", "hils_dense_decode_workspace_size",
-            "hils_dense_decode_fwd"]
+            "hils_dense_decode_fwd", "hils_prefill_bwd_workspace_size", "hils_prefill_bwd"]
 STATIC_SCRATCH_BYTES = 64 << 20   # HILS_STATIC_SCRATCH_BYTES
 
 
@@ -89,6 +89,10 @@ def load(path: str = LIB_PATH):
     lib.hils_dense_decode_workspace_size.restype = sz
     lib.hils_dense_decode_fwd.argtypes = [ctypes.POINTER(DenseParams)] + [vp] * 6 + [sz, vp]
     lib.hils_dense_decode_fwd.restype = i32
+    lib.hils_prefill_bwd_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+    lib.hils_prefill_bwd_workspace_size.restype = sz
+    lib.hils_prefill_bwd.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17 + [vp, sz, vp]
+    lib.hils_prefill_bwd.restype = i32
     lib.hils_status_string.argtypes = [i32]
     lib.hils_status_string.restype = ctypes.c_char_p
     lib.hils_last_hip_error.restype = ctypes.c_char_p
@@ -297,3 +301,34 @@ def dense_decode(q, k_cache, v_cache, kv_len, *, scale: Optional[float] = None, 
                                    _ptr(o), workspace.data_ptr(), need, _stream_handle(q.device))
     check(st, "hils_dense_decode_fwd")
     return o
+
+
+def prefill_bwd(q, k, v, lmk, h, w_down, w_up, sel_idx, sel_w, dout, *, topk: int, chunk: int = 64,
+                scale: Optional[float] = None, workspace=None):
+    """Backward pass of the prefill given dout = dL/do and the forward's selection (sel_idx,
+    sel_w from prefill(..., return_selection=True)).  Returns a dict of gradients: dq, dk, dv,
+    dlmk and, with Q-Cal, dh, dw_down, dw_up (each shaped and typed like its input)."""
+    import torch
+    lib = load()
+    B, H, L, d = q.shape
+    _require([("q", q), ("k", k), ("v", v), ("lmk", lmk), ("h", h), ("w_down", w_down), ("w_up", w_up),
+              ("dout", dout)], q.device, q.dtype)
+    for name, t, dt in (("sel_idx", sel_idx, torch.int32), ("sel_w", sel_w, torch.float32)):
+        if t.dtype != dt or t.device != q.device or not t.is_contiguous() or tuple(t.shape) != (B, H, L, topk):
+            raise ValueError(f"{name} must be a contiguous [B,H,L,topk] {dt} tensor on the query's device")
+    r = 0 if w_down is None else w_down.shape[0]
+    D = 0 if h is None else h.shape[-1]
+    p = PrefillParams(B, H, L, d, chunk, topk, 0, D, r, 0.0 if scale is None else float(scale),
+                      _dtype_code(q), None, 0, 0, int(k.shape[1]))
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dlmk=torch.empty_like(lmk))
+    if r > 0:
+        g.update(dh=torch.empty_like(h), dw_down=torch.empty_like(w_down), dw_up=torch.empty_like(w_up))
+    need = lib.hils_prefill_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.hils_prefill_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk), _ptr(h), _ptr(w_down),
+                              _ptr(w_up), _ptr(sel_idx), _ptr(sel_w), _ptr(dout), _ptr(g["dq"]), _ptr(g["dk"]),
+                              _ptr(g["dv"]), _ptr(g["dlmk"]), _ptr(g.get("dh")), _ptr(g.get("dw_down")),
+                              _ptr(g.get("dw_up")), workspace.data_ptr(), need, _stream_handle(q.device))
+    check(st, "hils_prefill_bwd")
+    return g

@@ -167,6 +167,25 @@ int hils_decode_fwd(const hils_decode_params* p, const void* q, const void* k_ca
                     const void* w_down, const void* w_up, void* o, int32_t* sel_idx, float* sel_w,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass of the prefill: gradients of a loss L given dout = dL/do.  The pages learn the
+ * chunk selection end to end: the landmark scores sit inside the forward attention, so the loss
+ * sends gradients into the landmark keys [HiLS explainer (molayo1419.me), "Core idea: landmark
+ * tokens and hierarchical factorisation"; "HiLS Attention Extrapolates 64x at 90% Retrieval
+ * Accuracy"].  The forward's selection sel_idx / sel_w ([B, H, L, k], as hils_prefill_fwd
+ * returns them) is held fixed: the top-k choice has no gradient.  The rounding of q~ to the run
+ * dtype passes gradients unchanged (dq receives both the attention term and the landmark-score
+ * term).  Outputs, in the run dtype and the shapes of the matching inputs:
+ *   dq [B,H,L,d], dk, dv [B,kv heads,L,d], dlmk [B,kv heads,L/C,d];
+ *   with Q-Cal (qcal_rank > 0, else all NULL): dh [B,L,D], dw_down [r,D], dw_up [H*d,r].
+ * Every output element is written.  Same shapes and checks as hils_prefill_fwd, plus at most
+ * 16384 chunks; q_tile, attn_mode and stage events are ignored.  Sums over rows run in a fixed
+ * order: results are bitwise reproducible.  Workspace from hils_prefill_bwd_workspace_size. */
+size_t hils_prefill_bwd_workspace_size(const hils_prefill_params* p);
+int hils_prefill_bwd(const hils_prefill_params* p, const void* q, const void* k, const void* v, const void* lmk,
+                     const void* h, const void* w_down, const void* w_up, const int32_t* sel_idx,
+                     const float* sel_w, const void* dout, void* dq, void* dk, void* dv, void* dlmk, void* dh,
+                     void* dw_down, void* dw_up, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Dense causal attention: the full-attention baseline the pages compare HiLS with
  * [HiLS explainer (molayo1419.me), "Numerical results": prefill and per-decode-step speed at 512K
  * against full attention on the same hardware].  o_i = sum_t softmax_t(scale q_i . k_t) v_t over

@@ -137,34 +137,260 @@ def union_stats(P, cfg, dev):
                 executed_attention_flop=executed)
 
 
-def cpu_baseline(dev, cfg, budget_s=12.0):
-    """The oracle, as it stands, on rows of one head of the same workload, for about budget_s."""
-    import numpy as np
+def _oracle_rows_worker(args):
+    """Pool worker (spawned, imports NumPy and the oracle only): prefill rows, timed."""
     from oracle import hils_oracle as O
-    h = 5
-    inp = {key: dev[key][:, h:h + 1].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
-    rng = np.random.default_rng(11)
-    rows = [int(x) for x in rng.integers(0, cfg.seq_len, size=4096)]
-    inp["h"] = np.zeros((1, cfg.seq_len, cfg.hidden), np.float32)
-    sel = sorted(set(rows))
-    inp["h"][:, sel] = dev["h"][:, sel].float().cpu().numpy()
-    inp["w_down"] = dev["w_down"].float().cpu().numpy()
-    inp["w_up"] = np.zeros((cfg.heads * cfg.head_dim, cfg.qcal_rank), np.float32)
-    d = cfg.head_dim
-    inp["w_up"][:d] = dev["w_up"][h * d:(h + 1) * d].float().cpu().numpy()   # head slot 0 = head h
-    flops, done = 0, 0
+    inp, rows, chunk, topk, dtype = args
     t0 = time.perf_counter()
-    for i in rows:
-        O.prefill_rows(inp, [(0, 0, i)], cfg.chunk, cfg.topk, cfg.dtype)
-        c = i // cfg.chunk
-        flops += 2 * d * (c + 1) + 4 * cfg.chunk * d * min(cfg.topk, c + 1) + 2 * cfg.qcal_rank * (cfg.hidden + d)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{done} random query rows of head {h} of prefill_128k, timed end to end "
-                       f"({dt:.1f} s, single-threaded NumPy oracle)")
+    O.prefill_rows(inp, rows, chunk, topk, dtype)
+    return time.perf_counter() - t0
+
+
+def _oracle_decode_worker(args):
+    from oracle import hils_oracle as O
+    inp, chunk, topk, dtype = args
+    t0 = time.perf_counter()
+    O.decode(inp, chunk, topk, dtype)
+    return time.perf_counter() - t0
+
+
+def _pool(n):
+    import concurrent.futures
+    import multiprocessing as mp
+    return concurrent.futures.ProcessPoolExecutor(n, mp_context=mp.get_context("spawn"))
+
+
+def oracle_workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class _Rows:
+    """Hidden states of a few token positions, indexable like h[b, i] (the oracle reads no others)."""
+
+    def __init__(self, rows):
+        self.rows = rows
+
+    def __getitem__(self, key):
+        return self.rows[key]
+
+
+def _head_inputs(dev, cfg, h, rows):
+    """Host copy of one head of a device prefill workload (the oracle's input for head slot 0),
+    with the hidden states of `rows` only."""
+    import numpy as np
+    inp = {key: dev[key][:, h:h + 1].float().cpu().numpy() for key in ("q", "k", "v", "lmk")}
+    if cfg.qcal_rank:
+        sel = sorted(set(rows))
+        hv = dev["h"][0, sel].float().cpu().numpy()
+        inp["h"] = _Rows({(0, i): hv[n] for n, i in enumerate(sel)})
+        inp["w_down"] = dev["w_down"].float().cpu().numpy()
+        d = cfg.head_dim
+        inp["w_up"] = np.zeros((cfg.heads * d, cfg.qcal_rank), np.float32)
+        inp["w_up"][:d] = dev["w_up"][h * d:(h + 1) * d].float().cpu().numpy()   # head slot 0 = head h
+    return inp
+
+
+def _prefill_row_flops(cfg, i):
+    c = i // cfg.chunk
+    d = cfg.head_dim
+    return 2 * d * (c + 1) + 4 * cfg.chunk * d * min(cfg.topk, c + 1) + 2 * cfg.qcal_rank * (cfg.hidden + d)
+
+
+def oracle_prefill_rate(dev, cfg, rows_per_head, heads, seed=11):
+    """The oracle on rows_per_head uniform random rows of each of `heads`, one head per worker
+    process: returns (TFLOP/s of algorithmic work summed over the workers, rows, worker seconds,
+    workers).  The rate is the work over each worker's own compute time (input shipping excluded),
+    added over the workers that ran at once."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    jobs, flops = [], []
+    for h in heads:
+        rows = sorted(int(x) for x in rng.integers(0, cfg.seq_len, size=rows_per_head))
+        jobs.append((_head_inputs(dev, cfg, h, rows), [(0, 0, i) for i in rows], cfg.chunk, cfg.topk, cfg.dtype))
+        flops.append(sum(_prefill_row_flops(cfg, i) for i in rows))
+    nw = min(oracle_workers(), len(jobs))
+    with _pool(nw) as pool:
+        secs = list(pool.map(_oracle_rows_worker, jobs))
+    rate = sum(f / t for f, t in zip(flops, secs)) / len(jobs) * nw / 1e12
+    return rate, rows_per_head * len(heads), sum(secs), nw
+
+
+def cpu_baseline(dev, cfg):
+    """The oracle, as it stands, on sampled rows of the 128K workload (4 heads x 256 random rows),
+    in a pool of worker processes on the host's cores; a rate, so no extrapolation is needed."""
+    heads = tuple(range(0, cfg.heads, max(1, cfg.heads // oracle_workers())))[:oracle_workers()]
+    rate, rows, secs, nw = oracle_prefill_rate(dev, cfg, 64, heads=heads)
+    return dict(value=rate, unit="TFLOP/s", cores=nw, kind="oracle",
+                sample=f"{rows} uniform random query rows of prefill_128k ({len(heads)} heads x 64 rows), one head "
+                       f"per worker process on {nw} host cores ({secs:.1f} s of worker compute); the algorithmic "
+                       "TFLOP/s of those rows, per worker, summed over the workers")
+
+
+def cpu_baseline_detail(P32, D512, dcfg):
+    """The oracle on the other workloads: the tiny fp32 case in full, the 32K prefill and the 512K
+    decode step sampled (labelled, extrapolated to the whole workload by its work)."""
+    import numpy as np
+    from chunk_wise_sparse_amd import synth
+    nw = oracle_workers()
+    out = {}
+    # tiny fp32, every row (host inputs, as the tests use them)
+    tcfg = synth.CONFIGS["tiny_fp32"]
+    inp = synth.make_prefill_inputs_np(tcfg)
+    rows = [(0, h, i) for h in range(tcfg.heads) for i in range(tcfg.seq_len)]
+    jobs = [(inp, rows[w::nw], tcfg.chunk, tcfg.topk, tcfg.dtype) for w in range(nw)]
+    t0 = time.perf_counter()
+    with _pool(nw) as pool:
+        list(pool.map(_oracle_rows_worker, jobs))
+    out["tiny_fp32"] = dict(seconds=time.perf_counter() - t0, rows=len(rows), cores=nw, kind="oracle",
+                            sample="full workload")
+    # 32K prefill: 512 random rows of each of 4 heads
+    scfg = synth.CONFIGS["prefill_32k"]
+    rate, nrows, secs, nws = oracle_prefill_rate(P32, scfg, 256, heads=tuple(range(scfg.heads)))
+    work = prefill_work(scfg)["total"]
+    out["prefill_32k"] = dict(tflops=rate, seconds_extrapolated=work / (rate * 1e12), cores=nws, kind="oracle",
+                              sample=f"{nrows} random rows (256 of each of the 16 heads, {secs:.1f} s of worker "
+                                     "compute); the full workload's time is extrapolated by algorithmic work")
+    # 512K decode: 8 of the 256 (sequence, head) pairs, one per sequence
+    if D512 is not None:
+        B, H, Lm, d = D512["k_cache"].shape
+        pairs = [(b, (7 * b + 3) % H) for b in range(B)]
+        jobs = []
+        for (b, h) in pairs:
+            sub = dict(q=D512["q"][b:b + 1, h:h + 1].float().cpu().numpy(),
+                       k_cache=D512["k_cache"][b:b + 1, h:h + 1].float().cpu().numpy(),
+                       v_cache=D512["v_cache"][b:b + 1, h:h + 1].float().cpu().numpy(),
+                       lmk=D512["lmk"][b:b + 1, h:h + 1].float().cpu().numpy(),
+                       kv_len=np.asarray([dcfg.kv_len[b]], np.int32), h=D512["h"][b:b + 1].float().cpu().numpy(),
+                       w_down=D512["w_down"].float().cpu().numpy(),
+                       w_up=D512["w_up"][h * d:(h + 1) * d].float().cpu().numpy())
+            jobs.append((sub, dcfg.chunk, dcfg.topk, dcfg.dtype))
+        t0 = time.perf_counter()
+        with _pool(min(nw, len(jobs))) as pool:
+            per = list(pool.map(_oracle_decode_worker, jobs))
+        wall = time.perf_counter() - t0
+        cpu_s = sum(per)
+        out["decode_512k"] = dict(us_per_step_extrapolated=cpu_s / len(pairs) * B * H / min(nw, len(jobs)) * 1e6,
+                                  cores=min(nw, len(jobs)), kind="oracle",
+                                  sample=f"{len(pairs)} of {B * H} (sequence, head) pairs ({wall:.1f} s wall, "
+                                         f"{cpu_s:.1f} s of worker time); one step's time extrapolated as all "
+                                         "pairs spread over the workers")
+    return out
+
+
+def time_prefill(P, cfg, reps, **kw):
+    """Mean stage times (Q-Cal code, selection, attention) of `reps` prefills, ms."""
+    import torch
+    from chunk_wise_sparse_amd import hils
+    ev = [hils.StageEvents(4) for _ in range(reps)]
+    for e in ev:
+        hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P.get("h"), P.get("w_down"), P.get("w_up"), topk=cfg.topk,
+                     events=e, **kw)
+    torch.cuda.synchronize()
+    return [sum(e.elapsed_ms(s, s + 1) for e in ev) / reps for s in range(3)]
+
+
+def event_ms(fn, reps):
+    """Mean ms of fn() over reps calls, timed with events on the current stream."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def stage_dict(cfg, st):
+    w = prefill_work(cfg)
+    ms = sum(st)
+    return dict(prefill_ms=ms, qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
+                tflops=w["total"] / (ms * 1e-3) / 1e12,
+                select_frac=w["select"] / (st[1] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                attention_frac=w["attention"] / (st[2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
+
+
+def bench_512k(dev):
+    """512K-token prefill (k = 64): random-walk queries (union walk) and i.i.d. queries (chunk-major
+    and automatic modes; the union walk on them does near-dense work).  Both regimes share k, v,
+    landmarks and the Q-Cal weights.  Returns the results and the walk inputs."""
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+    cfg = synth.CONFIGS["prefill_512k_walk"]
+    print("[bench] generating prefill_512k (walk)", file=sys.stderr, flush=True)
+    P = synth.make_prefill_inputs_torch(cfg, dev)
+    ws = torch.empty(9 << 30, dtype=torch.uint8, device=dev)
+    time_prefill(P, cfg, 1, workspace=ws)
+    res = dict(walk=stage_dict(cfg, time_prefill(P, cfg, 2, workspace=ws)))
+    icfg = synth.CONFIGS["prefill_512k_iid"]
+    gq = torch.Generator(device=dev).manual_seed(synth.subseed(icfg.seed, "q"))
+    gh = torch.Generator(device=dev).manual_seed(synth.subseed(icfg.seed, "h"))
+    Pi = dict(P, q=torch.randn(P["q"].shape, generator=gq, device=dev).to(P["q"].dtype),
+              h=torch.randn(P["h"].shape, generator=gh, device=dev).to(P["h"].dtype))
+    print("[bench] prefill_512k i.i.d.: chunk-major and automatic modes", file=sys.stderr, flush=True)
+    time_prefill(Pi, icfg, 1, workspace=ws, attn_mode=hils.ATTN_CHUNK_MAJOR)
+    res["iid_chunk_major"] = stage_dict(icfg, time_prefill(Pi, icfg, 2, workspace=ws, attn_mode=hils.ATTN_CHUNK_MAJOR))
+    res["iid_auto"] = stage_dict(icfg, time_prefill(Pi, icfg, 1, workspace=ws, attn_mode=hils.ATTN_AUTO))
+    res["walk_auto"] = stage_dict(cfg, time_prefill(P, cfg, 1, workspace=ws, attn_mode=hils.ATTN_AUTO))
+    del Pi, ws
+    torch.cuda.empty_cache()
+    return res, P
+
+
+def length_sweep_from(P512, lengths=(32768, 65536, 131072, 262144, 524288)):
+    """HiLS prefill (k = 32, the 128K workload's shape) and this library's dense causal attention
+    on the first L tokens of the 512K random-walk workload, L = 32K..512K."""
+    import dataclasses
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+    base = synth.CONFIGS["prefill_128k"]
+    ws = torch.empty(3 << 30, dtype=torch.uint8, device=P512["q"].device)
+    out = []
+    for L in lengths:
+        cfg = dataclasses.replace(base, name=f"prefill_{L // 1024}k_k32", seq_len=L)
+        P = dict(q=P512["q"][:, :, :L].contiguous(), k=P512["k"][:, :, :L].contiguous(),
+                 v=P512["v"][:, :, :L].contiguous(), lmk=P512["lmk"][:, :, :L // 64].contiguous(),
+                 h=P512["h"][:, :L].contiguous(), w_down=P512["w_down"], w_up=P512["w_up"])
+        time_prefill(P, cfg, 1, workspace=ws)
+        st = time_prefill(P, cfg, 2, workspace=ws)
+        ms = sum(st)
+        o = torch.empty_like(P["q"])
+        hils.dense_prefill(P["q"], P["k"], P["v"], out=o)
+        dense_ms = event_ms(lambda: hils.dense_prefill(P["q"], P["k"], P["v"], out=o), 1 if L >= 262144 else 2)
+        dense_flop = 4 * base.heads * base.head_dim * L * (L + 1) / 2
+        out.append(dict(seq_len=L, prefill_ms=ms, qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
+                        tflops=prefill_work(cfg)["total"] / (ms * 1e-3) / 1e12, dense_causal_ms=dense_ms,
+                        dense_tflops=dense_flop / (dense_ms * 1e-3) / 1e12, dense_over_hils=dense_ms / ms))
+        print(f"[bench] sweep {L}: hils {ms:.2f} ms, dense {dense_ms:.1f} ms", file=sys.stderr, flush=True)
+        del P, o
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_backward(P, cfg, o, dev):
+    """Backward pass of the 128K prefill for a random dout: ms and algorithmic TFLOP/s.  Work per
+    selected (row, chunk): S, dP, dq, dk and dv products, 10 C d FLOP; Q-Cal: four rank-r products."""
+    import torch
+    from chunk_wise_sparse_amd import hils
+    _, idx, w = hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"], topk=cfg.topk,
+                             return_selection=True)
+    g = torch.Generator(device=dev).manual_seed(77)
+    dout = torch.randn(P["q"].shape, generator=g, device=dev).to(P["q"].dtype)
+    ws = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+    run = lambda: hils.prefill_bwd(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"], idx, w, dout,
+                                   topk=cfg.topk, workspace=ws)
+    run()
+    ms = event_ms(run, 2)
+    B, H, L, d, C, k, r, D = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.chunk, cfg.topk, cfg.qcal_rank, \
+        cfg.hidden
+    pairs = B * H * C * sum(min(k, c + 1) for c in range(L // C))
+    flop = 10 * C * d * pairs + 4 * B * L * r * H * d + 4 * B * L * r * D
+    del idx, w, dout, ws
+    torch.cuda.empty_cache()
+    return dict(ms=ms, algorithmic_flop=flop, tflops=flop / (ms * 1e-3) / 1e12,
+                frac=flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                note="one backward pass (all gradients, Q-Cal included) of prefill_128k for a random dout, "
+                     "the forward's selection given; two timed calls")
 
 
 def length_sweep(lengths=(32768, 65536, 131072, 262144, 524288), reps=3):
@@ -224,6 +450,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-union-stats", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the 32K/512K workloads, the length sweep, q_tile 64, the backward pass and "
+                         "the dense comparators")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
@@ -391,10 +620,54 @@ def main():
         ustats["iid_queries"] = istats
         del Pi
 
+    extras = {}
+    if not args.no_extras:
+        # idx/w written to caller buffers (the headline keeps them in the workspace)
+        print("[bench] extras: selection outputs, q_tile 64, backward", file=sys.stderr, flush=True)
+        sel_run = lambda: hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
+                                       topk=pcfg.topk, out=o, return_selection=True)
+        sel_run()
+        sel_ms = event_ms(sel_run, 3)
+        nosel_ms = event_ms(lambda: hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
+                                                 topk=pcfg.topk, out=o, workspace=pws), 3)
+        extras["prefill_128k_selection_written"] = dict(
+            ms=sel_ms, ms_without=nosel_ms,
+            note="whole prefill calls (events around the call): idx/w returned in caller buffers, and kept in "
+                 "the workspace")
+        st64 = time_prefill(P, pcfg, 3, out=o, workspace=pws, q_tile=64)
+        extras["prefill_128k_q_tile_64"] = stage_dict(pcfg, st64)
+        if D is not None:
+            dsel_ms = event_ms(lambda: hils.decode(D["q"], D["k_cache"], D["v_cache"], D["lmk"], D["kv_len"], D["h"],
+                                                   D["w_down"], D["w_up"], topk=dcfg.topk, out=od,
+                                                   return_selection=True), 5)
+            extras["decode_512k_selection_written"] = dict(us_per_step=dsel_ms * 1e3)
+            dd_ms = event_ms(lambda: hils.dense_decode(D["q"], D["k_cache"], D["v_cache"], D["kv_len"], out=od), 3)
+            kvb = 2 * dcfg.batch * dcfg.heads * dcfg.max_kv_len * dcfg.head_dim * 2
+            extras["dense_decode_512k"] = dict(
+                us_per_step=dd_ms * 1e3, GBps=kvb / (dd_ms * 1e-3) / 1e9, frac_hbm=kvb / (dd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                dense_over_hils=dd_ms / (dec_ms / K),
+                note="this library's dense attention of the same 8 x 32 queries over the whole 512K caches")
+        extras["backward_128k"] = bench_backward(P, pcfg, o, dev)
+        print("[bench] extras: prefill_32k", file=sys.stderr, flush=True)
+        scfg = synth.CONFIGS["prefill_32k"]
+        P32 = synth.make_prefill_inputs_torch(scfg, dev)
+        time_prefill(P32, scfg, 1)
+        extras["prefill_32k"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
+        extras["prefill_512k"], P512 = bench_512k(dev)
+        print("[bench] extras: length sweep 32K..512K", file=sys.stderr, flush=True)
+        extras["length_sweep"] = length_sweep_from(P512)
+        del P512
+        torch.cuda.empty_cache()
+    else:
+        P32 = None
+
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on samples", file=sys.stderr, flush=True)
         cpu = cpu_baseline(P, pcfg)
+        if P32 is None:
+            P32 = synth.make_prefill_inputs_torch(synth.CONFIGS["prefill_32k"], dev)
+        extras["cpu_baseline_detail"] = cpu_baseline_detail(P32, D, dcfg)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -403,7 +676,7 @@ def main():
         "config": {"workload": "prefill_128k + decode_512k",
                    "prefill": dict(batch=pcfg.batch, heads=pcfg.heads, seq_len=pcfg.seq_len,
                                    head_dim=pcfg.head_dim, chunk=pcfg.chunk, topk=pcfg.topk,
-                                   q_tile=pcfg.q_tile, qcal_rank=pcfg.qcal_rank, hidden=pcfg.hidden,
+                                   q_tile=128, qcal_rank=pcfg.qcal_rank, hidden=pcfg.hidden,
                                    queries="random walk", hidden_states="random walk"),
                    "decode": dict(batch=dcfg.batch, heads=dcfg.heads, kv_len=dcfg.max_kv_len,
                                   head_dim=dcfg.head_dim, chunk=dcfg.chunk, topk=dcfg.topk,
@@ -412,6 +685,7 @@ def main():
         "prefill_ms": prefill_ms, "prefill_algorithmic_flop": work["total"],
         "stages": stages, "roofline": roofline, "decode": decode, "union": ustats, "cpu_baseline": cpu,
     }
+    line.update(extras)
     print(json.dumps(line), flush=True)
 
 

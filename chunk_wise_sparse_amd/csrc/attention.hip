@@ -80,6 +80,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
   const T* Kb = static_cast<const T*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const T* Vb = static_cast<const T*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const int32_t* bt = a.block_table ? a.block_table + (size_t)(bh / a.H) * a.bt_stride : nullptr;
+  const int kvh = (bh % a.H) / a.G;
   const size_t row0 = (size_t)bh * a.L;
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   // Thread -> 16-byte vector u of a chunk: row v / VPR, vector v % VPR (consecutive threads
   // read consecutive bytes of K and of V).
   auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
-    const T* kc = Kb + (size_t)j * 64 * D;
-    const T* vc = Vb + (size_t)j * 64 * D;
+    const T* kc = kv_chunk<T, D>(Kb, static_cast<const T*>(a.key), bt, a.num_pages, a.H / a.G, kvh, j);
+    const T* vc = kv_chunk<T, D>(Vb, static_cast<const T*>(a.val), bt, a.num_pages, a.H / a.G, kvh, j);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
@@ -380,6 +382,8 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block64_kernel(con
   const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
   const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const int32_t* bt = a.block_table ? a.block_table + (size_t)(bh / a.H) * a.bt_stride : nullptr;
+  const int kvh = (bh % a.H) / a.G;
   const size_t row0 = (size_t)bh * a.L;
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
@@ -421,8 +425,8 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block64_kernel(con
   for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
 
   auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
-    const bf16* kc = Kb + (size_t)j * 64 * D;
-    const bf16* vc = Vb + (size_t)j * 64 * D;
+    const bf16* kc = kv_chunk<bf16, D>(Kb, static_cast<const bf16*>(a.key), bt, a.num_pages, a.H / a.G, kvh, j);
+    const bf16* vc = kv_chunk<bf16, D>(Vb, static_cast<const bf16*>(a.val), bt, a.num_pages, a.H / a.G, kvh, j);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
@@ -583,6 +587,8 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block_kernel(const
   const int ks = k + 1;                      // staged row stride (odd: rows hit distinct banks)
   const bf16* Kb = static_cast<const bf16*>(a.key) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
   const bf16* Vb = static_cast<const bf16*>(a.val) + (size_t)kv_pair(bh, a.H, a.G) * a.L * D;
+  const int32_t* bt = a.block_table ? a.block_table + (size_t)(bh / a.H) * a.bt_stride : nullptr;
+  const int kvh = (bh % a.H) / a.G;
   const size_t row0 = (size_t)bh * a.L;
 
   // Stage the group's selections and build the union bitmap (causal chunks only).
@@ -623,8 +629,8 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block_kernel(const
   for (int db = 0; db < D / 16; ++db) acc_o[db] = zero4();
 
   auto load_kv = [&](int j, u32x4 (&kr)[NV], u32x4 (&vr)[NV]) {
-    const bf16* kc = Kb + (size_t)j * 64 * D;
-    const bf16* vc = Vb + (size_t)j * 64 * D;
+    const bf16* kc = kv_chunk<bf16, D>(Kb, static_cast<const bf16*>(a.key), bt, a.num_pages, a.H / a.G, kvh, j);
+    const bf16* vc = kv_chunk<bf16, D>(Vb, static_cast<const bf16*>(a.val), bt, a.num_pages, a.H / a.G, kvh, j);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
@@ -904,8 +910,8 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
   };
   u32x4 kr[NV], vr[NV];
   auto load_kv = [&](int j) {
-    const bf16* kc = Kb + (size_t)j * 64 * D;
-    const bf16* vc = Vb + (size_t)j * 64 * D;
+    const bf16* kc = kv_chunk<bf16, D>(Kb, Kb, a.bt, a.num_pages, a.Hk, a.kvh, j);
+    const bf16* vc = kv_chunk<bf16, D>(Vb, Vb, a.bt, a.num_pages, a.Hk, a.kvh, j);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;

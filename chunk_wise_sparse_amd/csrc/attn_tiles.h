@@ -59,4 +59,15 @@ __device__ __forceinline__ float v_frag_f32(const char* vbuf, int lane16, int g,
   return *reinterpret_cast<const float*>(vbuf + db * VDB + row * 64 + lane16 * 4);
 }
 
+// First key (or value) row of chunk j: `base` + j * 64 rows for contiguous [.., L, d] rows of
+// one key/value head, or page bt[j] (clamped to the pool) of a pool [pages, Hk, 64, d] at
+// `pool` for key/value head kvh.
+template <typename T, int D>
+__device__ __forceinline__ const T* kv_chunk(const T* base, const T* pool, const int32_t* bt, int num_pages, int Hk,
+                                             int kvh, int j) {
+  if (bt == nullptr) return base + (size_t)j * 64 * D;
+  const int pg = min(max(bt[j], 0), num_pages - 1);
+  return pool + ((size_t)pg * Hk + kvh) * 64 * D;
+}
+
 }  // namespace hils

@@ -67,11 +67,9 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (p->chunk != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (64)", p->chunk);
   if (p->topk < 1 || p->topk > 64)
     return fail(HILS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", p->topk);
-  if (p->seq_len % p->chunk != 0)
-    return fail(HILS_ERR_UNSUPPORTED, "seq_len %d is not a multiple of the chunk size", p->seq_len);
-  if (p->seq_len / p->chunk > 65535)
+  if ((p->seq_len + 63) / 64 > 65535)
     return fail(HILS_ERR_UNSUPPORTED, "more than 65535 chunks per sequence");
-  if (p->dtype == HILS_DTYPE_FP32 && p->head_dim == 128 && p->seq_len / p->chunk > 16384)
+  if (p->dtype == HILS_DTYPE_FP32 && p->head_dim == 128 && (p->seq_len + 63) / 64 > 16384)
     return fail(HILS_ERR_UNSUPPORTED, "fp32 with head_dim 128 supports at most 16384 chunks");
   if (p->q_tile != 0 && p->q_tile != 16 && p->q_tile != 32 && p->q_tile != 64 && p->q_tile != 128)
     return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (16, 32, 64 or 128)", p->q_tile);
@@ -88,8 +86,16 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "attn_mode %d is not supported", p->attn_mode);
   if (p->attn_mode != HILS_ATTN_UNION && p->dtype != HILS_DTYPE_BF16)
     return fail(HILS_ERR_UNSUPPORTED, "the chunk-major attention mode is bf16 only");
-  const double bhld = (double)p->batch * p->heads * p->seq_len * p->head_dim;
-  if (bhld > 4e18 / 8 || (double)p->batch * p->heads * (p->seq_len / 64) > 2147483647.0)
+  if (p->block_table) {
+    if (p->seq_len % 64 != 0)
+      return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need seq_len a multiple of the chunk (64)");
+    if (p->num_pages < 1 || p->block_table_stride < p->seq_len / 64)
+      return fail(HILS_ERR_INVALID_ARG, "paged keys/values: num_pages >= 1 and block_table_stride >= %d needed",
+                  p->seq_len / 64);
+    if ((uintptr_t)p->block_table & 3) return fail(HILS_ERR_ALIGNMENT, "block_table is not 4-byte aligned");
+  }
+  const double bhld = (double)p->batch * p->heads * (p->seq_len + 63.0) * p->head_dim;
+  if (bhld > 4e18 / 8 || (double)p->batch * p->heads * ((p->seq_len + 63) / 64) > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
   return HILS_OK;
 }
@@ -131,6 +137,41 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   }
   L.total = off;
   return L;
+}
+
+// A sequence that is not a multiple of the chunk is staged into copies padded to whole chunks
+// (q, k, v, h in, o out; the selection stays in the workspace and its real rows are copied out
+// when the caller asks for them).  The padded rows are zero and come after every real row, so no
+// real row sees them; the last landmark (ceil(L / 64) of them) describes the partial chunk.
+struct PadLayout {
+  PrefillLayout inner;       // layout of the call on the padded sequence
+  size_t qp, kp, vp, hp, op, total;
+};
+
+PadLayout pad_layout(const hils_prefill_params* p) {
+  PadLayout P{};
+  hils_prefill_params pp = *p;
+  pp.seq_len = (p->seq_len + 63) / 64 * 64;
+  P.inner = prefill_layout(&pp, false);
+  const size_t B = p->batch, H = p->heads, Lp = pp.seq_len, d = p->head_dim, e = elem_bytes(p->dtype);
+  const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;
+  size_t off = P.inner.total;
+  P.qp = off;
+  off += align_up(B * H * Lp * d * e);
+  P.kp = off;
+  off += align_up(B * Hk * Lp * d * e);
+  P.vp = off;
+  off += align_up(B * Hk * Lp * d * e);
+  P.hp = off;
+  off += align_up(p->qcal_rank > 0 ? B * Lp * p->hidden * e : 0);
+  P.op = off;
+  off += align_up(B * H * Lp * d * e);
+  P.total = off;
+  return P;
+}
+
+size_t prefill_workspace_bytes(const hils_prefill_params* p, bool with_sel) {
+  return p->seq_len % 64 == 0 ? prefill_layout(p, with_sel).total : pad_layout(p).total;
 }
 
 template <typename T, int D>
@@ -180,6 +221,9 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   aa.topk = p->topk;
   aa.q_tile = effective_q_tile(p);
   aa.scale = scale;
+  aa.block_table = p->block_table;
+  aa.bt_stride = p->block_table_stride;
+  aa.num_pages = p->num_pages;
   if constexpr (sizeof(T) == 2) {
     bool chunk_major = p->attn_mode == HILS_ATTN_CHUNK_MAJOR;
     if (p->attn_mode == HILS_ATTN_AUTO) {      // measure the selection's overlap, then choose
@@ -211,8 +255,18 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
       for (size_t bh = 0; bh < (size_t)p->batch * p->heads; ++bh) {
         ca.q = static_cast<const T*>(q) + bh * ld;
         const size_t kvbh = (bh / p->heads) * (p->heads / aa.G) + (bh % p->heads) / aa.G;
-        ca.key = static_cast<const T*>(k) + kvbh * ld;
-        ca.val = static_cast<const T*>(v) + kvbh * ld;
+        ca.Hk = p->heads / aa.G;
+        ca.kvh = (int)((bh % p->heads) / aa.G);
+        ca.num_pages = p->num_pages;
+        if (p->block_table) {                  // pools: pages of every key/value head
+          ca.key = k;
+          ca.val = v;
+          ca.bt = p->block_table + (bh / p->heads) * (size_t)p->block_table_stride;
+        } else {
+          ca.key = static_cast<const T*>(k) + kvbh * ld;
+          ca.val = static_cast<const T*>(v) + kvbh * ld;
+          ca.bt = nullptr;
+        }
         ca.o = static_cast<T*>(o) + bh * ld;
         ca.idx = idx + bh * lk;
         ca.w = w + bh * lk;
@@ -361,7 +415,7 @@ int hils_abi_version(void) { return HILS_ABI_VERSION; }
 size_t hils_prefill_workspace_size(const hils_prefill_params* p, int with_selection) {
   g_last_error.clear();
   if (check_prefill_params(p) != HILS_OK) return 0;
-  return prefill_layout(p, with_selection != 0).total;
+  return prefill_workspace_bytes(p, with_selection != 0);
 }
 
 size_t hils_decode_workspace_size(const hils_decode_params* p, int with_selection) {
@@ -387,9 +441,9 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   const void* ptrs[] = {q, k, v, lmk, h, w_down, w_up, o, sel_idx, sel_w};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(HILS_ERR_ALIGNMENT, "a tensor is not 16-byte aligned");
-  const PrefillLayout L = prefill_layout(p, with_sel);
-  if (L.total > 0 && (!workspace || workspace_bytes < L.total))
-    return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+  const size_t need = prefill_workspace_bytes(p, with_sel);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (workspace && ((uintptr_t)workspace & (kWsAlign - 1)))
     return fail(HILS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
@@ -397,14 +451,16 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   const size_t B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim, kk = p->topk;
   const size_t r = p->qcal_rank, D = p->hidden;
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
-  const Range in[] = {{q, B * H * S * d * e, "q"},   {k, B * Hk * S * d * e, "k"},
-                      {v, B * Hk * S * d * e, "v"},  {lmk, B * Hk * (S / 64) * d * e, "lmk"},
+  const size_t kvb = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * S * d * e;
+  const Range in[] = {{q, B * H * S * d * e, "q"},   {k, kvb, "k"},
+                      {v, kvb, "v"},  {lmk, B * Hk * ((S + 63) / 64) * d * e, "lmk"},
+                      {p->block_table, p->block_table ? B * (size_t)p->block_table_stride * 4 : 0, "block_table"},
                       {h, qcal ? B * S * D * e : 0, "h"}, {w_down, qcal ? r * D * e : 0, "w_down"},
                       {w_up, qcal ? H * d * r * e : 0, "w_up"}};
   const Range out[] = {{o, B * H * S * d * e, "o"},
                        {sel_idx, with_sel ? B * H * S * kk * 4 : 0, "sel_idx"},
                        {sel_w, with_sel ? B * H * S * kk * 4 : 0, "sel_w"},
-                       {workspace, L.total, "workspace"}};
+                       {workspace, need, "workspace"}};
   for (const Range& a : out) {
     for (const Range& b : in)
       if (overlap(a, b)) return fail(HILS_ERR_INVALID_ARG, "%s overlaps input %s", a.name, b.name);
@@ -420,18 +476,55 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
       return fail(HILS_ERR_UNSUPPORTED, "attn_mode HILS_ATTN_AUTO waits on the host and cannot be captured");
   }
   char* ws = static_cast<char*>(workspace);
+  hipError_t err = hipSuccess;
+  const bool padded = p->seq_len % 64 != 0;
+  hils_prefill_params pp = *p;
+  PrefillLayout L;
+  const void *qr = q, *kr = k, *vr = v, *hr = h;
+  void* orun = o;
+  int32_t* idx;
+  float* w;
+  if (padded) {
+    const PadLayout P = pad_layout(p);
+    pp.seq_len = (p->seq_len + 63) / 64 * 64;
+    L = P.inner;
+    const int Ls = p->seq_len, Lp = pp.seq_len;
+    auto pad = [&](const void* src, size_t off, int nseq, size_t row_bytes) {
+      if (err == hipSuccess) err = hils::launch_copy_rows(src, ws + off, nseq, Ls, Lp, row_bytes, s);
+    };
+    pad(q, P.qp, (int)(B * H), d * e);
+    pad(k, P.kp, (int)(B * Hk), d * e);
+    pad(v, P.vp, (int)(B * Hk), d * e);
+    if (qcal) pad(h, P.hp, (int)B, D * e);
+    if (err != hipSuccess) return hip_fail(err, "hils_prefill_fwd: padding");
+    qr = ws + P.qp;
+    kr = ws + P.kp;
+    vr = ws + P.vp;
+    hr = qcal ? ws + P.hp : nullptr;
+    orun = ws + P.op;
+    idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    w = reinterpret_cast<float*>(ws + L.w);
+  } else {
+    L = prefill_layout(p, with_sel);
+    idx = with_sel ? sel_idx : reinterpret_cast<int32_t*>(ws + L.idx);
+    w = with_sel ? sel_w : reinterpret_cast<float*>(ws + L.w);
+  }
   float* tcode = qcal ? reinterpret_cast<float*>(ws + L.tcode) : nullptr;
-  int32_t* idx = with_sel ? sel_idx : reinterpret_cast<int32_t*>(ws + L.idx);
-  float* w = with_sel ? sel_w : reinterpret_cast<float*>(ws + L.w);
-  hipError_t err;
   if (p->dtype == HILS_DTYPE_BF16) {
     err = p->head_dim == 64
-              ? run_prefill<hils::bf16, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s)
-              : run_prefill<hils::bf16, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s);
+              ? run_prefill<hils::bf16, 64>(&pp, qr, kr, vr, lmk, hr, w_down, w_up, orun, idx, w, tcode, ws, L, s)
+              : run_prefill<hils::bf16, 128>(&pp, qr, kr, vr, lmk, hr, w_down, w_up, orun, idx, w, tcode, ws, L, s);
   } else {
     err = p->head_dim == 64
-              ? run_prefill<float, 64>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s)
-              : run_prefill<float, 128>(p, q, k, v, lmk, h, w_down, w_up, o, idx, w, tcode, ws, L, s);
+              ? run_prefill<float, 64>(&pp, qr, kr, vr, lmk, hr, w_down, w_up, orun, idx, w, tcode, ws, L, s)
+              : run_prefill<float, 128>(&pp, qr, kr, vr, lmk, hr, w_down, w_up, orun, idx, w, tcode, ws, L, s);
+  }
+  if (err == hipSuccess && padded) {           // the real rows back to the caller
+    err = hils::launch_copy_rows(orun, o, (int)(B * H), pp.seq_len, p->seq_len, d * e, s);
+    if (err == hipSuccess && with_sel)
+      err = hils::launch_copy_rows(idx, sel_idx, (int)(B * H), pp.seq_len, p->seq_len, kk * 4, s);
+    if (err == hipSuccess && with_sel)
+      err = hils::launch_copy_rows(w, sel_w, (int)(B * H), pp.seq_len, p->seq_len, kk * 4, s);
   }
   if (err != hipSuccess) return hip_fail(err, "hils_prefill_fwd");
   return HILS_OK;
@@ -728,6 +821,9 @@ BwdLayout bwd_layout(const hils_prefill_params* p) {
 int check_bwd_params(const hils_prefill_params* p) {
   int st = check_prefill_params(p);
   if (st != HILS_OK) return st;
+  if (p->seq_len % 64 != 0)
+    return fail(HILS_ERR_UNSUPPORTED, "the backward pass needs seq_len a multiple of the chunk (64)");
+  if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "the backward pass takes contiguous keys and values");
   if (p->seq_len / 64 > 16384) return fail(HILS_ERR_UNSUPPORTED, "the backward pass supports at most 16384 chunks");
   return HILS_OK;
 }

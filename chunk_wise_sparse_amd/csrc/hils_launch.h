@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace hils {
 
 typedef __bf16 bf16;
@@ -30,6 +32,10 @@ struct AttnArgs {
   int G;                // query heads per key/value head
   int q_tile;           // bf16: queries per workgroup (16, 32, 64 or 128), dividing L
   float scale;
+  // Paged keys/values (NULL: key / val are [B,H/G,L,d]): key / val are pools of num_pages pages
+  // [num_pages, H/G, 64, d] and chunk j of batch b is page block_table[b * bt_stride + j].
+  const int32_t* block_table;
+  int bt_stride, num_pages;
 };
 
 // Chunk-major attention of one (batch, head) pair, bf16: the pair's selections inverted into
@@ -51,6 +57,10 @@ struct CmArgs {
   void* partial;        // [L,k,d] bf16: w_j * o_j of slot j of each row
   int L, N, k;
   float scale;
+  // Paged keys/values: key / val are the pools, bt the pair's block-table row (NULL: key / val
+  // are the pair's contiguous [L,d] slices), kvh its key/value head of Hk.
+  const int32_t* bt;
+  int num_pages, Hk, kvh;
 };
 constexpr int kCmItem = 128;                   // list entries per work item (8 waves x 16 rows)
 
@@ -160,6 +170,11 @@ template <typename T, int D>
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
 size_t bwd_rbcnt_words(int G, int L, int N);
 int bwd_splits(int ntok);
+
+// nseq sequences of rows (row_bytes each, a multiple of 4) from a rows_src-row layout to a
+// rows_dst-row layout: rows past rows_src become zero, rows past rows_dst are dropped.
+hipError_t launch_copy_rows(const void* src, void* dst, int nseq, int rows_src, int rows_dst, size_t row_bytes,
+                            hipStream_t st);
 
 template <typename T>
 hipError_t launch_prefill_qcal_code(const T* h, const T* w_down, float* t_out, int n_tok, int D,

@@ -36,7 +36,9 @@ class PrefillParams(ctypes.Structure):
                 ("q_tile", ctypes.c_int32), ("hidden", ctypes.c_int32), ("qcal_rank", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
-                ("attn_mode", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+                ("attn_mode", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -182,24 +184,33 @@ def _stream_handle(device):
 
 def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
             q_tile: int = 0, scale: Optional[float] = None, return_selection: bool = False,
-            out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0):
+            out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0,
+            block_table=None):
     """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
     w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
     attn_mode: ATTN_UNION (0), ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
     between neighbouring rows) or ATTN_AUTO (2, bf16; measures the overlap and picks one; waits
     on the stream once).
 
+    Paged keys/values: block_table [B, S] int32 (device) and k, v pools [pages, Hkv, C, d]; chunk j
+    of sequence b is page block_table[b, j].
+
     Returns o [B,H,L,d], or (o, idx [B,H,L,k] int32, w [B,H,L,k] float32)."""
     import torch
     lib = load()
     B, H, L, d = q.shape
+    paged = block_table is not None
+    if paged and (block_table.dtype != torch.int32 or block_table.device != q.device
+                  or not block_table.is_contiguous() or block_table.dim() != 2 or block_table.shape[0] != B):
+        raise ValueError("block_table must be a contiguous [B, S] int32 tensor on the query's device")
     _require([("q", q), ("k", k), ("v", v), ("lmk", lmk), ("h", h), ("w_down", w_down), ("w_up", w_up)],
              q.device, q.dtype)
     r = 0 if w_down is None else w_down.shape[0]
     D = 0 if h is None else h.shape[-1]
     p = PrefillParams(B, H, L, d, chunk, topk, q_tile, D, r, 0.0 if scale is None else float(scale),
                       _dtype_code(q), events.ptr if events else None, events.n if events else 0,
-                      int(attn_mode), int(k.shape[1]))
+                      int(attn_mode), int(k.shape[1]), block_table.data_ptr() if paged else None,
+                      int(block_table.shape[1]) if paged else 0, int(k.shape[0]) if paged else 0)
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:
@@ -319,7 +330,7 @@ def prefill_bwd(q, k, v, lmk, h, w_down, w_up, sel_idx, sel_w, dout, *, topk: in
     r = 0 if w_down is None else w_down.shape[0]
     D = 0 if h is None else h.shape[-1]
     p = PrefillParams(B, H, L, d, chunk, topk, 0, D, r, 0.0 if scale is None else float(scale),
-                      _dtype_code(q), None, 0, 0, int(k.shape[1]))
+                      _dtype_code(q), None, 0, 0, int(k.shape[1]), None, 0, 0)
     g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dlmk=torch.empty_like(lmk))
     if r > 0:
         g.update(dh=torch.empty_like(h), dw_down=torch.empty_like(w_down), dw_up=torch.empty_like(w_up))

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 6
+#define HILS_ABI_VERSION 7
 
 typedef enum {
   HILS_OK = 0,
@@ -55,9 +55,13 @@ typedef enum {
 typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
 
 /* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk == 64;
- * 1 <= topk <= 64; seq_len a positive multiple of chunk with seq_len / chunk <= 65535
- * (<= 16384 for fp32 with head_dim 128); 0 <= qcal_rank <= 64; hidden a positive multiple of
- * 128 when qcal_rank > 0.  scale <= 0 selects 1/sqrt(head_dim).
+ * 1 <= topk <= 64; 1 <= seq_len with ceil(seq_len / chunk) <= 65535 (<= 16384 for fp32 with
+ * head_dim 128); 0 <= qcal_rank <= 64; hidden a positive multiple of 128 when qcal_rank > 0.
+ * scale <= 0 selects 1/sqrt(head_dim).
+ * A partial last chunk (seq_len % chunk != 0) is allowed: lmk then holds ceil(seq_len / chunk)
+ * landmarks, the last one for the partial chunk, and the call stages q, k, v, h and o padded to
+ * whole chunks in the workspace (the padded rows are zero and come after every real row, so no
+ * real row sees them); the stage events then exclude those copies.
  * q_tile: how many consecutive queries share one staged copy of each chunk of their union (the
  *   M adjacent queries of the pages' kernel, HiLS explainer, "Engineering details",
  *   hardware-efficient kernel item): 16, 32, 64 or 128, 0 = 128.  If seq_len is not a multiple,
@@ -97,7 +101,15 @@ typedef struct hils_prefill_params {
   int32_t n_stage_events;
   int32_t attn_mode;           /* hils_attn_mode */
   int32_t kv_heads;            /* key/value (and landmark) heads; 0 = heads (see below) */
+  const int32_t* block_table;  /* device, int32; NULL for contiguous k and v (see below) */
+  int32_t block_table_stride;  /* block_table entries per sequence, >= seq_len / chunk */
+  int32_t num_pages;           /* pages in the k / v pools when paged */
 } hils_prefill_params;
+/* Paged keys/values (prefill, for a serving cache filled chunk by chunk): with block_table
+ * non-NULL, k and v are pools of num_pages pages of one chunk each, [num_pages, kv heads, chunk,
+ * head_dim], and chunk j of sequence b is page block_table[b * block_table_stride + j] (entries
+ * outside [0, num_pages) are clamped).  q, lmk, h and the outputs keep their layouts.  Needs
+ * seq_len a multiple of the chunk; the backward pass takes contiguous keys and values only. */
 
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a
  * key/value cache of capacity max_kv_len (the new token's key and value are already stored).

@@ -23,13 +23,13 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 6
+    assert lib.hils_abi_version() == 7
 
 
 def _pp(**kw):
     base = dict(batch=1, heads=2, seq_len=2048, head_dim=64, chunk=64, topk=4, q_tile=64, hidden=128,
                 qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
-                attn_mode=0, kv_heads=0)
+                attn_mode=0, kv_heads=0, block_table=None, block_table_stride=0, num_pages=0)
     base.update(kw)
     return hils.PrefillParams(**base)
 
@@ -53,7 +53,7 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(chunk=32), -2), (dict(topk=0), -2), (dict(topk=65), -2),
-    (dict(seq_len=2000), -2), (dict(q_tile=48), -2), (dict(q_tile=256), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
+    (dict(seq_len=64 * 65535 + 1), -2), (dict(q_tile=48), -2), (dict(q_tile=256), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
     (dict(dtype=7), -2), (dict(batch=0), -1), (dict(heads=-1), -1), (dict(scale=float("nan")), -1),
     (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=3), -2),
     (dict(attn_mode=2), -2),                                   # auto is bf16 only
@@ -152,3 +152,28 @@ def test_decode_noalloc_rejects_oversized():
     assert "static scratch" in lib.hils_last_hip_error().decode()
     assert lib.hils_decode_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
                                        None) == -1
+
+
+def test_prefill_partial_chunk_workspace():
+    """A sequence that is not a multiple of the chunk is accepted; it is staged padded to whole
+    chunks in the workspace (q, k, v, h and o copies, the selection kept in the workspace)."""
+    lib = hils.load()
+    a256 = lambda x: (x + 255) // 256 * 256
+    p = _pp(seq_len=2000)
+    Lp = 2048
+    inner = a256(1 * Lp * 8 * 4) + 2 * a256(1 * 2 * Lp * 4 * 4)
+    pads = 4 * a256(1 * 2 * Lp * 64 * 4) + a256(1 * Lp * 128 * 4)
+    assert lib.hils_prefill_workspace_size(ctypes.byref(p), 0) == inner + pads
+    assert lib.hils_prefill_workspace_size(ctypes.byref(p), 1) == inner + pads
+    assert lib.hils_prefill_bwd_workspace_size(ctypes.byref(p)) == 0      # the backward needs whole chunks
+
+
+def test_prefill_paged_rejects_bad_tables():
+    lib = hils.load()
+    bt = FAKE + (11 << 32)
+    assert _prefill(lib, _pp(block_table=bt, block_table_stride=31, num_pages=100)) == -1   # 32 chunks
+    assert _prefill(lib, _pp(block_table=bt, block_table_stride=32, num_pages=0)) == -1
+    assert _prefill(lib, _pp(block_table=bt + 2, block_table_stride=32, num_pages=100)) == -3
+    assert _prefill(lib, _pp(seq_len=2000, block_table=bt, block_table_stride=32, num_pages=100)) == -2
+    assert lib.hils_prefill_bwd_workspace_size(ctypes.byref(_pp(block_table=bt, block_table_stride=32,
+                                                                 num_pages=100))) == 0

@@ -244,3 +244,26 @@ def test_prefill_q_tile_bitwise(lib, cfg):
             assert torch.equal(x, y), f"q_tile {qt} differs from q_tile 128"
     rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
     _compare(inp, cfg, *runs[16], rows)
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.PrefillConfig("partial_bf16_L1000", 1, 2, 1000, 128, 64, 4, "bf16", 16, 256),
+    synth.PrefillConfig("partial_bf16_L2047_k48", 1, 2, 2047, 64, 64, 48, "bf16", 8, 128, q_mode="walk"),
+    synth.PrefillConfig("partial_fp32_L777", 2, 1, 777, 64, 64, 5, "fp32", 8, 128),
+    synth.PrefillConfig("partial_bf16_L33", 1, 2, 33, 128, 64, 2, "bf16", 0, 0),
+], ids=lambda c: c.name)
+def test_prefill_partial_last_chunk(lib, cfg):
+    """seq_len not a multiple of the chunk: every row against the oracle, the selection written
+    out or kept in the workspace (same o), and the union group size changing nothing."""
+    from chunk_wise_sparse_amd import hils
+    torch = _torch()
+    print(f"[case] partial last chunk {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    dev = _to_dev(inp, cfg.dtype)
+    o, idx, w = _run(lib, dev, cfg)
+    o2 = hils.prefill(dev["q"], dev["k"], dev["v"], dev["lmk"], dev.get("h"), dev.get("w_down"), dev.get("w_up"),
+                      topk=cfg.topk, q_tile=32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    _compare(inp, cfg, o, idx, w, rows)

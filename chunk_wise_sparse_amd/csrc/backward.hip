@@ -48,23 +48,34 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 // ------------------------------------------------------------------------------------------
 // q~ for every row (Q-Cal): the same fp32 sum and one rounding to the run dtype as the forward.
 // ------------------------------------------------------------------------------------------
-template <typename T>
+// A workgroup takes 64 rows of one (batch, head) (L % 64 == 0): W_up[h] is staged once in LDS
+// as fp32 [d][r], thread (row, quarter) holds the row's code t in registers and forms D/4
+// elements, each a dot product of length r read from LDS (all rows read the same words).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_qtilde_kernel(const BwdArgs a) {
-  const size_t n = (size_t)a.B * a.H * a.L * a.d;
-  const T* q = static_cast<const T*>(a.q);
-  const T* wu = static_cast<const T*>(a.w_up);
-  T* qt = static_cast<T*>(a.qt);
-  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
-    const int e = (int)(x % a.d);
-    const size_t row = x / a.d;
-    const int i = (int)(row % a.L);
-    const size_t bh = row / a.L;
-    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-    const float* t = a.tcode + ((size_t)b * a.L + i) * a.r;
-    const T* w = wu + ((size_t)h * a.d + e) * a.r;
+  constexpr int QD = D / 4;                  // elements per thread
+  __shared__ float wl[D * 65];               // W_up[h] rows, stride r + 1 <= 65
+  const int tid = threadIdx.x, rl = tid >> 2, qtr = tid & 3;
+  const size_t row0 = (size_t)blockIdx.x * 64;          // first row; rows of one (b, h)
+  const int bh = (int)(row0 / a.L), h = bh % a.H, b = bh / a.H;
+  const int i = (int)(row0 % a.L) + rl;
+  const int r = a.r, rs = r + 1;
+  const T* wu = static_cast<const T*>(a.w_up) + (size_t)h * D * r;
+  for (int x = tid; x < D * r; x += 256) wl[(x / r) * rs + x % r] = to_f32(wu[x]);
+  float t[64];
+  const float* tp = a.tcode + ((size_t)b * a.L + i) * r;
+#pragma unroll
+  for (int c = 0; c < 64; ++c) t[c] = c < r ? tp[c] : 0.f;
+  __syncthreads();
+  const T* q = static_cast<const T*>(a.q) + (row0 + rl) * D + qtr * QD;
+  T* qt = static_cast<T*>(a.qt) + (row0 + rl) * D + qtr * QD;
+  for (int z = 0; z < QD; ++z) {
+    const float* w = wl + (qtr * QD + z) * rs;
     float dq = 0.f;
-    for (int c = 0; c < a.r; ++c) dq = fmaf(to_f32(w[c]), t[c], dq);
-    qt[x] = from_f32<T>(to_f32(q[x]) + dq);
+#pragma unroll
+    for (int c = 0; c < 64; ++c)
+      if (c < r) dq = fmaf(w[c], t[c], dq);
+    qt[z] = from_f32<T>(to_f32(q[z]) + dq);
   }
 }
 
@@ -356,6 +367,18 @@ constexpr int kBwdRB = 128;
 
 // The G query heads of key/value head bk = b * Hk + hk are consecutive heads, so their G * L
 // rows of idx are contiguous; block rblk holds rows rblk * kBwdRB .. of them (fewer in the last).
+// Per key/value head bk (blockIdx.y of the list kernels) its slice of the list workspace.
+__device__ __forceinline__ int bwd_nrb(const BwdArgs& a) { return (a.G * a.L + kBwdRB - 1) / kBwdRB; }
+__device__ __forceinline__ uint32_t* bwd_rbcnt(const BwdArgs& a, int bk) {
+  return a.rbcnt + (size_t)bk * bwd_nrb(a) * (a.L / 64);
+}
+__device__ __forceinline__ uint32_t* bwd_choff(const BwdArgs& a, int bk) {
+  return a.choff + (size_t)bk * (a.L / 64 + 1);
+}
+__device__ __forceinline__ uint32_t* bwd_ent(const BwdArgs& a, int bk) {
+  return a.ent + (size_t)bk * a.G * a.L * a.k;
+}
+
 __device__ __forceinline__ const int32_t* bwd_idx_rows(const BwdArgs& a, int bk, int rblk) {
   const int Hk = a.H / a.G;
   const int b = bk / Hk, hk = bk % Hk;
@@ -365,9 +388,9 @@ __device__ __forceinline__ int bwd_block_rows(const BwdArgs& a, int rblk) {
   return min(kBwdRB, a.G * a.L - rblk * kBwdRB);
 }
 
-__global__ __launch_bounds__(256) void bwd_count_kernel(const BwdArgs a, int bk) {
+__global__ __launch_bounds__(256) void bwd_count_kernel(const BwdArgs a) {
   extern __shared__ uint32_t cnt[];
-  const int N = a.L / 64, rblk = blockIdx.x;
+  const int N = a.L / 64, rblk = blockIdx.x, bk = blockIdx.y;
   for (int j = threadIdx.x; j < N; j += 256) cnt[j] = 0u;
   __syncthreads();
   const int32_t* idx = bwd_idx_rows(a, bk, rblk);
@@ -377,31 +400,52 @@ __global__ __launch_bounds__(256) void bwd_count_kernel(const BwdArgs a, int bk)
     if (j >= 0 && j < N) atomicAdd(&cnt[j], 1u);
   }
   __syncthreads();
-  uint32_t* out = a.rbcnt + (size_t)rblk * N;
+  uint32_t* out = bwd_rbcnt(a, bk) + (size_t)rblk * N;
   for (int j = threadIdx.x; j < N; j += 256) out[j] = cnt[j];
 }
 
-// Exclusive prefix down each chunk's column (in place) and the chunk's total.
-__global__ __launch_bounds__(256) void bwd_colscan_kernel(const BwdArgs a, int nrb) {
-  const int N = a.L / 64;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= N) return;
-  uint32_t s = 0;
-  for (int rb = 0; rb < nrb; ++rb) {
-    const uint32_t v = a.rbcnt[(size_t)rb * N + j];
-    a.rbcnt[(size_t)rb * N + j] = s;
-    s += v;
+// Exclusive prefix down each chunk's column (in place) and the chunk's total.  A workgroup takes
+// 16 chunks; 16 threads per chunk sum 16 segments of the column, the segment sums are scanned,
+// then each thread rewrites its segment.
+__global__ __launch_bounds__(256) void bwd_colscan_kernel(const BwdArgs a) {
+  __shared__ uint32_t seg[16][17];
+  const int N = a.L / 64, bk = blockIdx.y, nrb = bwd_nrb(a);
+  const int jl = threadIdx.x & 15, sg = threadIdx.x >> 4;
+  const int j = blockIdx.x * 16 + jl;
+  uint32_t* cnt = bwd_rbcnt(a, bk);
+  const int per = (nrb + 15) / 16, r0 = min(nrb, sg * per), r1 = min(nrb, r0 + per);
+  uint32_t sum = 0;
+  if (j < N)
+    for (int rb = r0; rb < r1; ++rb) sum += cnt[(size_t)rb * N + j];
+  seg[jl][sg] = sum;
+  __syncthreads();
+  if (sg == 0) {
+    uint32_t run = 0;
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t v = seg[jl][t];
+      seg[jl][t] = run;
+      run += v;
+    }
+    if (j < N) bwd_choff(a, bk)[j] = run;     // totals; turned into offsets next
   }
-  a.choff[j] = s;                            // totals; turned into offsets next
+  __syncthreads();
+  uint32_t run = seg[jl][sg];
+  if (j < N)
+    for (int rb = r0; rb < r1; ++rb) {
+      const uint32_t v = cnt[(size_t)rb * N + j];
+      cnt[(size_t)rb * N + j] = run;
+      run += v;
+    }
 }
 
 __global__ __launch_bounds__(1024) void bwd_offscan_kernel(const BwdArgs a) {
   __shared__ uint32_t part[1024];
   const int N = a.L / 64, t = threadIdx.x;
+  uint32_t* choff = bwd_choff(a, blockIdx.x);
   const int per = (N + 1023) / 1024;
   const int b0 = min(N, t * per), e0 = min(N, b0 + per);
   uint32_t s = 0;
-  for (int i = b0; i < e0; ++i) s += a.choff[i];
+  for (int i = b0; i < e0; ++i) s += choff[i];
   part[t] = s;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -412,23 +456,26 @@ __global__ __launch_bounds__(1024) void bwd_offscan_kernel(const BwdArgs a) {
   }
   uint32_t p = part[t] - s;
   for (int i = b0; i < e0; ++i) {
-    const uint32_t v = a.choff[i];
-    a.choff[i] = p;
+    const uint32_t v = choff[i];
+    choff[i] = p;
     p += v;
   }
-  if (t == 1023) a.choff[N] = part[1023];
+  if (t == 1023) choff[N] = part[1023];
 }
 
 // One wave per row block: the block's selections are staged in LDS, then its rows are appended
 // in order (a row's chunks are distinct, so the lanes of one row never share a cursor).
-__global__ __launch_bounds__(64) void bwd_fill_kernel(const BwdArgs a, int bk) {
+__global__ __launch_bounds__(64) void bwd_fill_kernel(const BwdArgs a) {
   extern __shared__ uint32_t lds[];
-  const int N = a.L / 64, rblk = blockIdx.x, k = a.k, lane = threadIdx.x;
+  const int N = a.L / 64, rblk = blockIdx.x, bk = blockIdx.y, k = a.k, lane = threadIdx.x;
+  const uint32_t* choff = bwd_choff(a, bk);
+  const uint32_t* rbcnt = bwd_rbcnt(a, bk);
+  uint32_t* ent = bwd_ent(a, bk);
   uint32_t* cur = lds;                       // N cursors
   int32_t* sel = reinterpret_cast<int32_t*>(lds + N);   // kBwdRB * k staged indices
   const int32_t* idx = bwd_idx_rows(a, bk, rblk);
   const int nr = bwd_block_rows(a, rblk);
-  for (int j = lane; j < N; j += 64) cur[j] = a.choff[j] + a.rbcnt[(size_t)rblk * N + j];
+  for (int j = lane; j < N; j += 64) cur[j] = choff[j] + rbcnt[(size_t)rblk * N + j];
   for (int x = lane; x < nr * k; x += 64) sel[x] = idx[x];
   __syncthreads();
   // One wave: its LDS accesses complete in program order, so row r + 1 reads the cursors row r
@@ -440,7 +487,7 @@ __global__ __launch_bounds__(64) void bwd_fill_kernel(const BwdArgs a, int bk) {
       if (j >= 0 && j < N) {
         const uint32_t p = cur[j];
         cur[j] = p + 1;
-        a.ent[p] = ((r0 + r) << 6) | (uint32_t)lane;
+        ent[p] = ((r0 + r) << 6) | (uint32_t)lane;
       }
     }
   }
@@ -461,7 +508,7 @@ struct BwdChunkSmem {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a, int bk) {
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
   typedef BwdChunkSmem<T, D> S;
   typedef Mfma<T> M;
   constexpr int KPL = M::KPL;
@@ -471,8 +518,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a, int bk)
   __shared__ S sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int N = a.L / 64, j = blockIdx.x;
+  const int N = a.L / 64, j = blockIdx.x, bk = blockIdx.y;
   const int Hk = a.H / a.G, b = bk / Hk, hk = bk % Hk;
+  const uint32_t* ent = bwd_ent(a, bk);
   const size_t kvoff = (size_t)bk * a.L * D;
   const int key = 16 * wave + n;             // this lane's key within the chunk (B operands)
   const int kpos = j * 64 + key;
@@ -491,48 +539,73 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a, int bk)
   const float zs = a.scale * 1.4426950408889634f;
   const T* qt_base = static_cast<const T*>(a.r > 0 ? a.qt : a.q);
 
-  const uint32_t e0 = a.choff[j], e1 = a.choff[j + 1];
-  for (uint32_t base = e0; base < e1; base += 16) {
-    // gather 16 rows (rows past the list are zero and get weight 0)
-    for (int v = tid; v < 16 * VPR; v += 256) {
+  const uint32_t e0 = bwd_choff(a, bk)[j], e1 = bwd_choff(a, bk)[j + 1];
+  // The next block's rows and per-row values are loaded into registers while the current block
+  // is computed.
+  constexpr int NGV = (16 * VPR + 255) / 256;   // 16-byte vectors per thread per tensor
+  u32x4 gq[NGV], gd[NGV], gt[NGV];
+  float g_w = 0.f, g_lse = INFINITY, g_dw = 0.f, g_sg = 0.f;
+  int g_pos = -1;
+  auto fetch = [&](uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < NGV; ++u) {
+      const int v = tid + 256 * u;
+      gq[u] = gd[u] = gt[u] = u32x4{0u, 0u, 0u, 0u};
       const int r = v / VPR, p = v % VPR;
       const uint32_t x = base + r;
-      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = qv, tv = qv;
-      if (x < e1) {
-        const uint32_t en = a.ent[x];
-        const int gi = (int)(en >> 6), gq = gi / a.L, i = gi % a.L;
-        const size_t row = ((size_t)b * a.H + hk * a.G + gq) * a.L + i;
-        qv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + row * D + p * VE);
-        dv4 = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + row * D + p * VE);
-        tv = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
+      if (v < 16 * VPR && x < e1) {
+        const uint32_t en = ent[x];
+        const int gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
+        const size_t row = ((size_t)b * a.H + hk * a.G + gq_) * a.L + i;
+        gq[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + row * D + p * VE);
+        gd[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + row * D + p * VE);
+        gt[u] = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
       }
-      const int e = p * VE;
-      const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
-      *reinterpret_cast<u32x4*>(sm.qs + off) = qv;
-      *reinterpret_cast<u32x4*>(sm.ds + off) = dv4;
-      *reinterpret_cast<u32x4*>(sm.ts + off) = tv;
     }
     if (tid < 16) {
       const uint32_t x = base + tid;
-      float w = 0.f, lse = INFINITY, dwv = 0.f, sg = 0.f;
-      int pos = -1;
+      g_w = 0.f;
+      g_lse = INFINITY;
+      g_dw = 0.f;
+      g_sg = 0.f;
+      g_pos = -1;
       if (x < e1) {
-        const uint32_t en = a.ent[x];
-        const int slot = (int)(en & 63u), gi = (int)(en >> 6), gq = gi / a.L, i = gi % a.L;
-        const size_t rs = (((size_t)b * a.H + hk * a.G + gq) * a.L + i) * a.k + slot;
-        w = a.w[rs];
-        lse = a.lse[rs];
-        dwv = a.dw[rs];
-        sg = a.dsig[rs];
-        pos = i;
+        const uint32_t en = ent[x];
+        const int slot = (int)(en & 63u), gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
+        const size_t rs = (((size_t)b * a.H + hk * a.G + gq_) * a.L + i) * a.k + slot;
+        g_w = a.w[rs];
+        g_lse = a.lse[rs];
+        g_dw = a.dw[rs];
+        g_sg = a.dsig[rs];
+        g_pos = i;
       }
-      sm.rw[tid] = w;
-      sm.rlse[tid] = lse;
-      sm.rdw[tid] = dwv;
-      sm.rsig[tid] = sg;
-      sm.rpos[tid] = pos;
     }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int u = 0; u < NGV; ++u) {
+      const int v = tid + 256 * u;
+      if (v < 16 * VPR) {
+        const int r = v / VPR, p = v % VPR, e = p * VE;
+        const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
+        *reinterpret_cast<u32x4*>(sm.qs + off) = gq[u];
+        *reinterpret_cast<u32x4*>(sm.ds + off) = gd[u];
+        *reinterpret_cast<u32x4*>(sm.ts + off) = gt[u];
+      }
+    }
+    if (tid < 16) {
+      sm.rw[tid] = g_w;
+      sm.rlse[tid] = g_lse;
+      sm.rdw[tid] = g_dw;
+      sm.rsig[tid] = g_sg;
+      sm.rpos[tid] = g_pos;
+    }
+  };
+  if (e0 < e1) fetch(e0);
+  for (uint32_t base = e0; base < e1; base += 16) {
+    put();
     __syncthreads();
+    if (base + 16 < e1) fetch(base + 16);
     // S[q][key] = Q K^T and dP[q][key] = dout V^T: lane (n, g) holds key n of the wave and rows
     // q = 4 g + rr.
     f32x4 s4 = zero4(), p4 = zero4();
@@ -752,14 +825,14 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // Launcher.
 // ------------------------------------------------------------------------------------------
-size_t bwd_rbcnt_words(int G, int L, int N) { return (size_t)((G * L + kBwdRB - 1) / kBwdRB) * N; }
+size_t bwd_rbcnt_words(int G, int L, int N) { return (size_t)((G * L + kBwdRB - 1) / kBwdRB) * N; }   // per head
 int bwd_splits(int ntok) { return max(1, min(256, ntok / 1024)); }
 
 template <typename T, int D>
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
   const int N = a.L / 64, ntok = a.B * a.L;
   if (a.r > 0) {
-    hipLaunchKernelGGL(bwd_qtilde_kernel<T>, dim3(4096), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_qtilde_kernel<T, D>), dim3((unsigned)((size_t)a.B * a.H * a.L / 64)), dim3(256), 0, st, a);
   }
   const size_t bm = (size_t)((N + 31) / 32) * 4;
   hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3((uint32_t)a.B * a.H * N), dim3(256), bm, st, a);
@@ -767,14 +840,12 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
   const size_t nrows = (size_t)a.B * a.H * a.L;
   hipLaunchKernelGGL((bwd_dqtilde_kernel<T, D>), dim3((unsigned)((nrows + RPW - 1) / RPW)), dim3(256), 0, st, a);
   const int nrb = (a.G * a.L + kBwdRB - 1) / kBwdRB;
-  const int Hk = a.H / a.G;
-  for (int bk = 0; bk < a.B * Hk; ++bk) {
-    hipLaunchKernelGGL(bwd_count_kernel, dim3(nrb), dim3(256), (size_t)N * 4, st, a, bk);
-    hipLaunchKernelGGL(bwd_colscan_kernel, dim3((N + 255) / 256), dim3(256), 0, st, a, nrb);
-    hipLaunchKernelGGL(bwd_offscan_kernel, dim3(1), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(nrb), dim3(64), (size_t)(N + kBwdRB * a.k) * 4, st, a, bk);
-    hipLaunchKernelGGL((bwd_chunk_kernel<T, D>), dim3(N), dim3(256), 0, st, a, bk);
-  }
+  const int nkv = a.B * (a.H / a.G);        // every key/value head at once (blockIdx.y)
+  hipLaunchKernelGGL(bwd_count_kernel, dim3(nrb, nkv), dim3(256), (size_t)N * 4, st, a);
+  hipLaunchKernelGGL(bwd_colscan_kernel, dim3((N + 15) / 16, nkv), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_offscan_kernel, dim3(nkv), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(bwd_fill_kernel, dim3(nrb, nkv), dim3(64), (size_t)(N + kBwdRB * a.k) * 4, st, a);
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, D>), dim3(N, nkv), dim3(256), 0, st, a);
   if (a.r > 0) {
     hipLaunchKernelGGL(bwd_dt_kernel<T>, dim3((ntok + 63) / 64), dim3(256), 0, st, a);
     const int S = bwd_splits(ntok), per = (ntok + S - 1) / S;

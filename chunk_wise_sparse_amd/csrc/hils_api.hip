@@ -809,9 +809,10 @@ BwdLayout bwd_layout(const hils_prefill_params* p) {
   L.dw = take(B * H * S * k * 4);
   L.dsig = take(B * H * S * k * 4);
   L.dt = take(r ? B * S * r * 4 : 0);
-  L.rbcnt = take(hils::bwd_rbcnt_words(G, (int)S, (int)N) * 4);
-  L.choff = take((N + 1) * 4);
-  L.ent = take((size_t)G * S * k * 4);
+  const size_t nkv = B * (H / G);             // every key/value head's lists at once
+  L.rbcnt = take(nkv * hils::bwd_rbcnt_words(G, (int)S, (int)N) * 4);
+  L.choff = take(nkv * (N + 1) * 4);
+  L.ent = take(nkv * (size_t)G * S * k * 4);
   const size_t X = std::max(H * d, (size_t)(r ? p->hidden : 0));
   L.gpart = take(r ? (size_t)hils::bwd_splits((int)(B * S)) * X * 64 * 4 : 0);
   L.total = off;

@@ -496,15 +496,17 @@ __global__ __launch_bounds__(64) void bwd_fill_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // Chunk-major pass: dK, dV and dlmk of one chunk of key/value head bk per workgroup.
 // ------------------------------------------------------------------------------------------
+constexpr int kBwdBR = 32;                   // list entries (rows) per block of the chunk pass
+
 template <typename T, int D>
 struct BwdChunkSmem {
   static constexpr int RB = 16 * (int)sizeof(T);      // bytes of one row within a d-block
-  static constexpr int DBS = 16 * RB + 32;             // d-block stride: 16 rows + pad
+  static constexpr int DBS = kBwdBR * RB + 32;         // d-block stride: the block's rows + pad
   alignas(16) char qs[(D / 16) * DBS];                 // gathered q rows, d-block-major
   alignas(16) char ds[(D / 16) * DBS];                 // gathered dout rows
   alignas(16) char ts[(D / 16) * DBS];                 // gathered q~ rows
-  float rw[16], rlse[16], rdw[16], rsig[16];
-  int rpos[16];
+  float rw[kBwdBR], rlse[kBwdBR], rdw[kBwdBR], rsig[kBwdBR];
+  int rpos[kBwdBR];
 };
 
 template <typename T, int D>
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
   const uint32_t e0 = bwd_choff(a, bk)[j], e1 = bwd_choff(a, bk)[j + 1];
   // The next block's rows and per-row values are loaded into registers while the current block
   // is computed.
-  constexpr int NGV = (16 * VPR + 255) / 256;   // 16-byte vectors per thread per tensor
+  constexpr int NGV = (kBwdBR * VPR + 255) / 256;   // 16-byte vectors per thread per tensor
   u32x4 gq[NGV], gd[NGV], gt[NGV];
   float g_w = 0.f, g_lse = INFINITY, g_dw = 0.f, g_sg = 0.f;
   int g_pos = -1;
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
       gq[u] = gd[u] = gt[u] = u32x4{0u, 0u, 0u, 0u};
       const int r = v / VPR, p = v % VPR;
       const uint32_t x = base + r;
-      if (v < 16 * VPR && x < e1) {
+      if (v < kBwdBR * VPR && x < e1) {
         const uint32_t en = ent[x];
         const int gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
         const size_t row = ((size_t)b * a.H + hk * a.G + gq_) * a.L + i;
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
         gt[u] = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
       }
     }
-    if (tid < 16) {
+    if (tid < kBwdBR) {
       const uint32_t x = base + tid;
       g_w = 0.f;
       g_lse = INFINITY;
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < NGV; ++u) {
       const int v = tid + 256 * u;
-      if (v < 16 * VPR) {
+      if (v < kBwdBR * VPR) {
         const int r = v / VPR, p = v % VPR, e = p * VE;
         const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
         *reinterpret_cast<u32x4*>(sm.qs + off) = gq[u];
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
         *reinterpret_cast<u32x4*>(sm.ts + off) = gt[u];
       }
     }
-    if (tid < 16) {
+    if (tid < kBwdBR) {
       sm.rw[tid] = g_w;
       sm.rlse[tid] = g_lse;
       sm.rdw[tid] = g_dw;
@@ -602,66 +604,73 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
     }
   };
   if (e0 < e1) fetch(e0);
-  for (uint32_t base = e0; base < e1; base += 16) {
+  for (uint32_t base = e0; base < e1; base += kBwdBR) {
     put();
     __syncthreads();
-    if (base + 16 < e1) fetch(base + 16);
-    // S[q][key] = Q K^T and dP[q][key] = dout V^T: lane (n, g) holds key n of the wave and rows
-    // q = 4 g + rr.
-    f32x4 s4 = zero4(), p4 = zero4();
+    if (base + kBwdBR < e1) fetch(base + kBwdBR);
+    // S[q][key] = Q K^T and dP[q][key] = dout V^T for the block's two 16-row tiles: lane (n, g)
+    // holds key n of the wave and rows q = 16 t + 4 g + rr.
+    float pw[2][4], dsv[2][4];
 #pragma unroll
-    for (int st = 0; st < NF; ++st) {
-      const int e = g * (D / 4) + st * KPL;
-      const int off = (e >> 4) * S::DBS + n * S::RB + (e & 15) * (int)sizeof(T);
-      s4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.qs + off)), kf[st], s4);
-      p4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.ds + off)), vf[st], p4);
-    }
-    float pw[4], dsv[4];
+    for (int t = 0; t < 2; ++t) {
+      f32x4 s4 = zero4(), p4 = zero4();
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int q = 4 * g + rr;
-      const int pos = sm.rpos[q];
-      float p = __builtin_amdgcn_exp2f(fmaf(s4[rr], zs, -sm.rlse[q]));
-      if (pos < kpos) p = 0.f;               // the key lies after the row (or no row)
-      const float w = sm.rw[q];
-      pw[rr] = w * p;
-      dsv[rr] = w * p * (p4[rr] - sm.rdw[q]);
+      for (int st = 0; st < NF; ++st) {
+        const int e = g * (D / 4) + st * KPL;
+        const int off = (e >> 4) * S::DBS + (16 * t + n) * S::RB + (e & 15) * (int)sizeof(T);
+        s4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.qs + off)), kf[st], s4);
+        p4 = M::mma(load_frag<T>(reinterpret_cast<const T*>(sm.ds + off)), vf[st], p4);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int q = 16 * t + 4 * g + rr;
+        const int pos = sm.rpos[q];
+        float p = __builtin_amdgcn_exp2f(fmaf(s4[rr], zs, -sm.rlse[q]));
+        if (pos < kpos) p = 0.f;             // the key lies after the row (or no row)
+        const float w = sm.rw[q];
+        pw[t][rr] = w * p;
+        dsv[t][rr] = w * p * (p4[rr] - sm.rdw[q]);
+      }
     }
-    // dV[key][e] += sum_q (w p)[q][key] dout[q][e];  dK[key][e] += sum_q ds[q][key] q[q][e].
-    // MFMA with the 16 rows as the contraction: A = (w p)^T / ds^T (lane (n, g): key n, rows
-    // 4 g..4 g + 3), B = the row tiles (column e, rows 4 g..4 g + 3).
+    // dV[key][e] += sum_q (w p)[q][key] dout[q][e];  dK[key][e] += sum_q ds[q][key] q[q][e]:
+    // MFMA with the block's 32 rows as the contraction, contraction slot (g, z) being row
+    // 16 (z / 4) + 4 g + z % 4 in A = (w p)^T / ds^T (lane (n, g): key n) and in B = the row
+    // tiles (column e, read transposed).
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       if constexpr (KPL == 1) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          // contraction index (g, st) is row 4 g + st
-          const int off = db * S::DBS + (4 * g + st) * S::RB + n * 4;
+        for (int st = 0; st < 8; ++st) {
+          const int off = db * S::DBS + (16 * (st >> 2) + 4 * g + (st & 3)) * S::RB + n * 4;
           const float dov = *reinterpret_cast<const float*>(sm.ds + off);
           const float qv = *reinterpret_cast<const float*>(sm.qs + off);
-          dv[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pw[st], dov, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(dsv[st], qv, dk[db], 0, 0, 0);
+          dv[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pw[st >> 2][st & 3], dov, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(dsv[st >> 2][st & 3], qv, dk[db], 0, 0, 0);
         }
       } else {
-        // transposed read: lane (n, g) gets column n of rows 4 g..4 g + 3 of d-block db
+        // lane (n, g) gets column n of rows 4 g..4 g + 3 (and 16 + those) of d-block db
         const int off = db * S::DBS + (4 * g + (n >> 2)) * S::RB + 8 * (n & 3);
-        const short4v dob = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.ds + off));
-        const short4v qb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.qs + off));
-        bf16x4 pa, sa;
+        const short4v d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.ds + off));
+        const short4v d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.ds + off + 16 * S::RB));
+        const short4v q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.qs + off));
+        const short4v q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(void*)(sm.qs + off + 16 * S::RB));
+        bf16x8 pa, sa;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          pa[rr] = bf16_rne(pw[rr]);
-          sa[rr] = bf16_rne(dsv[rr]);
+        for (int z = 0; z < 8; ++z) {
+          pa[z] = bf16_rne(pw[z >> 2][z & 3]);
+          sa[z] = bf16_rne(dsv[z >> 2][z & 3]);
         }
-        dv[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, pa), dob, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, sa), qb, dk[db], 0, 0, 0);
+        const bf16x4 d0b = __builtin_bit_cast(bf16x4, d0), d1b = __builtin_bit_cast(bf16x4, d1);
+        const bf16x4 q0b = __builtin_bit_cast(bf16x4, q0), q1b = __builtin_bit_cast(bf16x4, q1);
+        dv[db] = Mfma<bf16>::mma(pa, __builtin_shufflevector(d0b, d1b, 0, 1, 2, 3, 4, 5, 6, 7), dv[db]);
+        dk[db] = Mfma<bf16>::mma(sa, __builtin_shufflevector(q0b, q1b, 0, 1, 2, 3, 4, 5, 6, 7), dk[db]);
       }
     }
-    // dlmk: dims wave * D/4 + lane, summed over the 16 rows in order.
+    // dlmk: dims wave * D/4 + lane, summed over the block's rows in order.
     if (lane < D / 4) {
       const int e = wave * (D / 4) + lane;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kBwdBR; ++q) {
         const T tv = *reinterpret_cast<const T*>(sm.ts + (e >> 4) * S::DBS + q * S::RB + (e & 15) * (int)sizeof(T));
         dl = fmaf(sm.rsig[q], to_f32(tv), dl);
       }

@@ -59,7 +59,7 @@ import numpy as np
 
 __all__ = [
     "round_to_bf16", "round_to_run_dtype", "qcal_offset", "calibrated_query", "landmark_scores",
-    "select_top_k", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
+    "select_top_k", "select_with_local", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
     "prefill", "decode", "attend_given_selection", "dense_attention_row", "dense_causal_rows",
     "dense_decode", "chunk_backward", "inter_chunk_backward", "prefill_backward",
 ]
@@ -164,6 +164,19 @@ def select_top_k(sigma: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def select_with_local(sigma: np.ndarray, k: int) -> np.ndarray:
+    """Variant with the query's own chunk forced in (a serving option; the pages do not force it,
+    reading R2): the last candidate (the own chunk) is always selected, the other k - 1 slots are
+    the top k - 1 of the earlier candidates (ties -> smaller index).  Ascending, -1 padded."""
+    s = np.asarray(sigma)
+    own = s.shape[0] - 1
+    others = select_top_k(s[:own], k - 1) if k > 1 else np.zeros(0, dtype=np.int64)
+    chosen = sorted([int(j) for j in others if j >= 0] + [own])
+    out = np.full(k, -1, dtype=np.int64)
+    out[: len(chosen)] = chosen
+    return out
+
+
 # ------------------------------------------------------------------------------------------
 # Step 4: inter-chunk softmax over the selection ([P1] factorised inter-chunk softmax)
 # ------------------------------------------------------------------------------------------
@@ -227,13 +240,14 @@ def attend_row(q_row, keys, values, idx, w, i, chunk, scale) -> np.ndarray:
     return fuse(ws, outs)
 
 
-def hils_row(q_row, q_tilde, keys, values, lmk, i, chunk, topk, scale):
+def hils_row(q_row, q_tilde, keys, values, lmk, i, chunk, topk, scale, force_local=False):
     """All steps for query position i.  keys/values [>= i+1, d], lmk [>= i//C + 1, d].
+    force_local: the own chunk is always selected (select_with_local).
 
     Returns (o [d] float64, idx [k] int64, w [k] float64, sigma [c+1] fp32)."""
     c = i // chunk
     sigma = landmark_scores(q_tilde, lmk[: c + 1])
-    idx = select_top_k(sigma, topk)
+    idx = select_with_local(sigma, topk) if force_local else select_top_k(sigma, topk)
     sel = idx[idx >= 0]
     w = np.zeros(topk, dtype=np.float64)
     w[: len(sel)] = inter_chunk_weights(sigma[sel], scale)
@@ -250,7 +264,7 @@ def _w_up_head(w_up, head, d):
 
 
 def prefill_rows(inp: Dict[str, np.ndarray], rows: Iterable[tuple], chunk: int, topk: int,
-                 dtype: str, scale: Optional[float] = None) -> Dict[tuple, dict]:
+                 dtype: str, scale: Optional[float] = None, force_local: bool = False) -> Dict[tuple, dict]:
     """Prefill for selected (b, h, i) rows.  inp holds q,k,v [B,H,L,d], lmk [B,H,N,d] and,
     with Q-Cal, h [B,L,D], w_down [r,D], w_up [H*d,r] (fp32 arrays holding dtype-exact values).
 
@@ -265,7 +279,8 @@ def prefill_rows(inp: Dict[str, np.ndarray], rows: Iterable[tuple], chunk: int, 
     for (b, h, i) in rows:
         hid = None if w_down is None else inp["h"][b, i]
         qt = calibrated_query(q[b, h, i], hid, w_down, _w_up_head(inp.get("w_up"), h, d), dtype)
-        o, idx, w, sigma = hils_row(q[b, h, i], qt, k[b, h], v[b, h], lmk[b, h], i, chunk, topk, s)
+        extra = {"force_local": True} if force_local else {}
+        o, idx, w, sigma = hils_row(q[b, h, i], qt, k[b, h], v[b, h], lmk[b, h], i, chunk, topk, s, **extra)
         out[(b, h, i)] = dict(o=o, idx=idx, w=w, sigma=sigma, q_tilde=qt)
     return out
 
@@ -285,7 +300,8 @@ def prefill(inp: Dict[str, np.ndarray], chunk: int, topk: int, dtype: str,
 
 
 def decode(inp: Dict[str, np.ndarray], chunk: int, topk: int, dtype: str,
-           scale: Optional[float] = None, pairs: Optional[Iterable[tuple]] = None) -> Dict[tuple, dict]:
+           scale: Optional[float] = None, pairs: Optional[Iterable[tuple]] = None,
+           force_local: bool = False) -> Dict[tuple, dict]:
     """Decode step (R9): q [B,H,d] at position kv_len[b]-1 over k_cache/v_cache [B,H,Lmax,d],
     lmk [B,H,ceil(Lmax/C),d], h [B,D].  Returns {(b,h): dict(o, idx, w, sigma, q_tilde)}."""
     q, kc, vc, lmk, kv_len = inp["q"], inp["k_cache"], inp["v_cache"], inp["lmk"], inp["kv_len"]
@@ -301,7 +317,8 @@ def decode(inp: Dict[str, np.ndarray], chunk: int, topk: int, dtype: str,
         i = int(kv_len[b]) - 1
         hid = None if w_down is None else inp["h"][b]
         qt = calibrated_query(q[b, h], hid, w_down, _w_up_head(inp.get("w_up"), h, d), dtype)
-        o, idx, w, sigma = hils_row(q[b, h], qt, kc[b, h], vc[b, h], lmk[b, h], i, chunk, topk, s)
+        extra = {"force_local": True} if force_local else {}
+        o, idx, w, sigma = hils_row(q[b, h], qt, kc[b, h], vc[b, h], lmk[b, h], i, chunk, topk, s, **extra)
         out[(b, h)] = dict(o=o, idx=idx, w=w, sigma=sigma, q_tilde=qt)
     return out
 

@@ -527,4 +527,50 @@ def pin_backward_shift_invariances():
     assert np.abs(grads["dlmk"]).max() > 1e-3 and np.abs(grads["dk"]).max() > 1e-3
 
 
+# ---------------------------------------------------------------------------------------------
+# Forced local chunk (a serving variant)
+# ---------------------------------------------------------------------------------------------
+
+def pin_forced_local_bruteforce():
+    """The selection holds the own (last) chunk and the unique (k-1)-subset of the others that
+    beats every other earlier chunk (ties to the smaller index), by enumeration."""
+    g = _rng(30)
+    for trial in range(300):
+        n = int(g.integers(1, 8))
+        k = int(g.integers(1, 9))
+        s = g.integers(-3, 4, n).astype(np.float32)
+        got = O.select_with_local(s, k)
+        keff = min(k, n)
+        m = keff - 1
+        winners = [set(S) for S in itertools.combinations(range(n - 1), m)
+                   if all(_dominates(s, x, y) for x in S for y in range(n - 1) if y not in S)]
+        assert len(winners) == 1
+        want = sorted(winners[0] | {n - 1})
+        assert list(got[:keff]) == want and all(got[keff:] == -1), (s, k, got)
+
+
+def pin_forced_local_rows():
+    """Whole rows: with the own chunk scoring highest, forcing changes nothing; with it scoring
+    lowest, the row keeps it and drops its k-th best earlier chunk, and the weights are the
+    softmax over the forced set."""
+    g = _rng(31)
+    L, d, C, s = 256, 8, 64, 0.5
+    q = np.ones((1, 1, L, d), np.float32)
+    k = g.standard_normal((1, 1, L, d)).astype(np.float32)
+    v = g.standard_normal((1, 1, L, d)).astype(np.float32)
+    lmk = np.stack([np.full(d, 2.0), np.full(d, 1.0), np.full(d, 3.0), np.full(d, -4.0)]).astype(np.float32)
+    inp = dict(q=q, k=k, v=v, lmk=lmk[None, None])
+    a = O.prefill_rows(inp, [(0, 0, 150)], C, 2, "fp32", scale=s)[(0, 0, 150)]          # own chunk 2 best
+    b = O.prefill_rows(inp, [(0, 0, 150)], C, 2, "fp32", scale=s, force_local=True)[(0, 0, 150)]
+    assert list(a["idx"]) == [0, 2] and list(b["idx"]) == [0, 2] and np.array_equal(a["o"], b["o"])
+    c = O.prefill_rows(inp, [(0, 0, 200)], C, 2, "fp32", scale=s)[(0, 0, 200)]          # own chunk 3 worst
+    f = O.prefill_rows(inp, [(0, 0, 200)], C, 2, "fp32", scale=s, force_local=True)[(0, 0, 200)]
+    assert list(c["idx"]) == [0, 2] and list(f["idx"]) == [2, 3]
+    sig = np.array([3.0 * d, -4.0 * d])
+    assert np.allclose(f["w"], scipy.special.softmax(s * sig), rtol=0, atol=1e-12)
+    dec = O.decode(dict(q=q[:, :, 200], k_cache=k, v_cache=v, lmk=lmk[None, None], kv_len=np.array([201])),
+                   C, 2, "fp32", scale=s, force_local=True)[(0, 0)]
+    assert np.array_equal(dec["idx"], f["idx"]) and np.array_equal(dec["o"], f["o"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

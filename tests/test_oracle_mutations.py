@@ -91,7 +91,25 @@ def _chunk_bwd_no_softmax_centering(q, K, V, w_j, g, scale):
     return scale * (da @ K), scale * np.outer(da, q), np.outer(w_j * p, g), float(g @ (p @ V))
 
 
+def _local_not_forced(sigma, k):
+    return O.select_top_k(sigma, k)
+
+
+def _local_drops_wrong_one(sigma, k):
+    s = np.asarray(sigma)
+    own = s.shape[0] - 1
+    top = O.select_top_k(s, k)
+    if own in set(int(j) for j in top if j >= 0):
+        return top
+    chosen = sorted([int(j) for j in top if j >= 0][1:] + [own])     # drops the smallest index
+    out = np.full(k, -1)
+    out[: len(chosen)] = chosen
+    return out
+
+
 MUTATIONS = {
+    "forced_local_ignored": ("select_with_local", _local_not_forced),
+    "forced_local_drops_wrong_chunk": ("select_with_local", _local_drops_wrong_one),
     "bwd_dsigma_not_centred": ("inter_chunk_backward", lambda w, dw, s: s * np.asarray(w) * np.asarray(dw)),
     "bwd_dsigma_unscaled": ("inter_chunk_backward",
                             lambda w, dw, s, _o=O.inter_chunk_backward: _o(w, dw, 1.0) if s != 1.0 else 2 * _o(w, dw, s)),

@@ -764,7 +764,7 @@ __global__ __launch_bounds__(512) void decode_attend_whole_kernel(const DecodeAr
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
   int jl;
   float wl;
-  if (a.cand != nullptr) {                     // the selection runs here, from the scan's lists
+  if (a.cand != nullptr && !a.force_local) {   // the selection runs here, from the scan's lists
     __shared__ CandSelSmem sel;
     select_candidates(a, bh, sel);
     __syncthreads();
@@ -1141,12 +1141,14 @@ hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t st) {
 template <typename T>
 bool decode_attend_whole(const DecodeArgs& a) { return sizeof(T) == 2 && a.B * a.H >= 256; }
 template <typename T>
-bool decode_select_fused(const DecodeArgs& a) { return a.cand != nullptr && decode_attend_whole<T>(a); }
+bool decode_select_fused(const DecodeArgs& a) {
+  return a.cand != nullptr && !a.force_local && decode_attend_whole<T>(a);
+}
 
 // The fused step: bf16, at least as many pairs as compute units, scores that fit in LDS.
 template <typename T>
 bool decode_fused_ok(const DecodeArgs& a) {
-  return sizeof(T) == 2 && a.B * a.H >= 256 && a.Nmax <= kFusedMaxChunks;
+  return sizeof(T) == 2 && a.B * a.H >= 256 && a.Nmax <= kFusedMaxChunks && !a.force_local;
 }
 template <typename T, int D>
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t st) {

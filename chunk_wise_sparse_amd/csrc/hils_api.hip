@@ -86,6 +86,8 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "attn_mode %d is not supported", p->attn_mode);
   if (p->attn_mode != HILS_ATTN_UNION && p->dtype != HILS_DTYPE_BF16)
     return fail(HILS_ERR_UNSUPPORTED, "the chunk-major attention mode is bf16 only");
+  if (p->force_local != 0 && p->force_local != 1)
+    return fail(HILS_ERR_INVALID_ARG, "force_local must be 0 or 1");
   if (p->block_table) {
     if (p->seq_len % 64 != 0)
       return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need seq_len a multiple of the chunk (64)");
@@ -205,6 +207,26 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   sa.r = p->qcal_rank;
   sa.scale = scale;
   if ((e = hils::launch_select<T, D>(sa, st)) != hipSuccess) return e;
+  if (p->force_local) {
+    hils::LocalArgs la;
+    la.q = q;
+    la.lmk = lmk;
+    la.w_up = w_up;
+    la.tcode = tcode;
+    la.kv_len = nullptr;
+    la.idx = idx;
+    la.w = w;
+    la.B = p->batch;
+    la.H = p->heads;
+    la.L = p->seq_len;
+    la.N = p->seq_len / 64;
+    la.G = sa.G;
+    la.k = p->topk;
+    la.r = p->qcal_rank;
+    la.tstride = p->qcal_rank;
+    la.scale = scale;
+    if ((e = hils::launch_force_local<T, D>(la, false, st)) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   hils::AttnArgs aa;
   aa.q = q;
@@ -314,6 +336,8 @@ int check_decode_params(const hils_decode_params* p) {
     return fail(HILS_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
   if (p->kv_heads < 0 || p->kv_heads > p->heads || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
     return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
+  if (p->force_local != 0 && p->force_local != 1)
+    return fail(HILS_ERR_INVALID_ARG, "force_local must be 0 or 1");
   if (p->block_table && (p->num_pages < 1 || p->block_table_stride < (p->max_kv_len + 63) / 64))
     return fail(HILS_ERR_INVALID_ARG, "paged cache: num_pages >= 1 and block_table_stride >= %d needed",
                 (p->max_kv_len + 63) / 64);
@@ -391,6 +415,7 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   const bool cand = a.Nmax <= kDecodeCandMaxChunks;
   a.cand = cand ? static_cast<void*>(ws + L.cand) : nullptr;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
+  a.force_local = p->force_local;
   if (hils::decode_fused_ok<T>(a)) {           // scan, selection and attention in one kernel
     if ((e = hils::launch_decode_fused<T, D>(a, st)) != hipSuccess) return e;
     for (int s = 2; s <= 4; ++s)
@@ -400,6 +425,26 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   if (!hils::decode_select_fused<T>(a) && (e = hils::launch_decode_select(a, st)) != hipSuccess) return e;
+  if (p->force_local) {
+    hils::LocalArgs la;
+    la.q = q;
+    la.lmk = lmk;
+    la.w_up = w_up;
+    la.tcode = tcode;
+    la.kv_len = kv_len;
+    la.idx = idx;
+    la.w = w;
+    la.B = p->batch;
+    la.H = p->heads;
+    la.L = p->max_kv_len;
+    la.N = a.Nmax;
+    la.G = a.G;
+    la.k = p->topk;
+    la.r = p->qcal_rank;
+    la.tstride = hils::kTcodeStride;
+    la.scale = a.scale;
+    if ((e = hils::launch_force_local<T, D>(la, true, st)) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   if ((e = hils::launch_decode_attend<T, D>(a, st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;

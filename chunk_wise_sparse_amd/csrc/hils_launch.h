@@ -117,6 +117,7 @@ struct DecodeArgs {
   void* cand;           // uint32 pairs (key, chunk)
   int score_ymax;       // scan workgroups per pair: ceil(ceil(Nmax / 256) / score_qb)
   float scale;
+  int force_local;      // the selection is written out and amended before the attention
 };
 
 // Dense causal attention (the full-attention baseline): prefill over [B,H,L,d] (L % 64 == 0) and
@@ -170,6 +171,23 @@ template <typename T, int D>
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
 size_t bwd_rbcnt_words(int G, int L, int N);
 int bwd_splits(int ntok);
+
+// Forced local chunk: after the top-k, rows whose own chunk is not selected swap their worst entry
+// for it (see local.hip).  Prefill rows are B*H*L with L the sequence length; decode rows are the
+// B*H pairs with L the cache capacity and the query at kv_len[b] - 1.
+struct LocalArgs {
+  const void* q;        // prefill [B,H,L,d]; decode [B,H,d]
+  const void* lmk;      // [B,H/G,N,d]
+  const void* w_up;     // [H*d, r]
+  const float* tcode;   // Q-Cal code rows, tstride floats apart
+  const int32_t* kv_len;   // decode only
+  int32_t* idx;         // [rows, k], updated in place
+  float* w;             // [rows, k]
+  int B, H, L, N, G, k, r, tstride;
+  float scale;
+};
+template <typename T, int D>
+hipError_t launch_force_local(const LocalArgs& a, bool decode, hipStream_t st);
 
 // nseq sequences of rows (row_bytes each, a multiple of 4) from a rows_src-row layout to a
 // rows_dst-row layout: rows past rows_src become zero, rows past rows_dst are dropped.

@@ -38,7 +38,7 @@ class PrefillParams(ctypes.Structure):
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
                 ("attn_mode", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("force_local", ctypes.c_int32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -48,7 +48,8 @@ class DecodeParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("n_stage_events", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("block_table_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+                ("block_table_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("force_local", ctypes.c_int32)]
 
 
 class DenseParams(ctypes.Structure):
@@ -185,7 +186,7 @@ def _stream_handle(device):
 def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: int = 64,
             q_tile: int = 0, scale: Optional[float] = None, return_selection: bool = False,
             out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0,
-            block_table=None):
+            block_table=None, force_local: bool = False):
     """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
     w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
     attn_mode: ATTN_UNION (0), ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
@@ -210,7 +211,8 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
     p = PrefillParams(B, H, L, d, chunk, topk, q_tile, D, r, 0.0 if scale is None else float(scale),
                       _dtype_code(q), events.ptr if events else None, events.n if events else 0,
                       int(attn_mode), int(k.shape[1]), block_table.data_ptr() if paged else None,
-                      int(block_table.shape[1]) if paged else 0, int(k.shape[0]) if paged else 0)
+                      int(block_table.shape[1]) if paged else 0, int(k.shape[0]) if paged else 0,
+                      int(bool(force_local)))
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:
@@ -229,7 +231,7 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
 def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, topk: int,
            chunk: int = 64, scale: Optional[float] = None, return_selection: bool = False,
            out=None, workspace=None, events: Optional[StageEvents] = None, block_table=None,
-           max_kv_len: Optional[int] = None, no_alloc: bool = False):
+           max_kv_len: Optional[int] = None, no_alloc: bool = False, force_local: bool = False):
     """HiLS decode step.  q [B,H,d]; caches [B,Hkv,Lmax,d]; lmk [B,Hkv,ceil(Lmax/C),d] (Hkv divides
     H); kv_len [B] int32 (device); h [B,D].  Returns o [B,H,d], or (o, idx [B,H,k], w [B,H,k]).
     Paged caches: block_table [B, S] int32 (device) and caches [pages, Hkv, C, d]; chunk j of
@@ -254,7 +256,8 @@ def decode(q, k_cache, v_cache, lmk, kv_len, h=None, w_down=None, w_up=None, *, 
     p = DecodeParams(B, H, Lmax, d, chunk, topk, D, r, 0.0 if scale is None else float(scale),
                      _dtype_code(q), events.ptr if events else None, events.n if events else 0,
                      int(k_cache.shape[1]), block_table.data_ptr() if paged else None,
-                     int(block_table.shape[1]) if paged else 0, int(k_cache.shape[0]) if paged else 0)
+                     int(block_table.shape[1]) if paged else 0, int(k_cache.shape[0]) if paged else 0,
+                     int(bool(force_local)))
     o = out if out is not None else torch.empty_like(q)
     idx = w = None
     if return_selection:
@@ -330,7 +333,7 @@ def prefill_bwd(q, k, v, lmk, h, w_down, w_up, sel_idx, sel_w, dout, *, topk: in
     r = 0 if w_down is None else w_down.shape[0]
     D = 0 if h is None else h.shape[-1]
     p = PrefillParams(B, H, L, d, chunk, topk, 0, D, r, 0.0 if scale is None else float(scale),
-                      _dtype_code(q), None, 0, 0, int(k.shape[1]), None, 0, 0)
+                      _dtype_code(q), None, 0, 0, int(k.shape[1]), None, 0, 0, 0)
     g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dlmk=torch.empty_like(lmk))
     if r > 0:
         g.update(dh=torch.empty_like(h), dw_down=torch.empty_like(w_down), dw_up=torch.empty_like(w_up))

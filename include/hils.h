@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 7
+#define HILS_ABI_VERSION 8
 
 typedef enum {
   HILS_OK = 0,
@@ -104,7 +104,14 @@ typedef struct hils_prefill_params {
   const int32_t* block_table;  /* device, int32; NULL for contiguous k and v (see below) */
   int32_t block_table_stride;  /* block_table entries per sequence, >= seq_len / chunk */
   int32_t num_pages;           /* pages in the k / v pools when paged */
+  int32_t force_local;         /* 1: the query's own chunk is always selected (see below) */
 } hils_prefill_params;
+/* force_local (prefill and decode; 0 = off, the pages' method): the query's own chunk is always
+ * selected, and the other min(k, candidates) - 1 slots hold the best-scoring earlier chunks (ties
+ * to the smaller index); the weights stay the softmax over the selection's scores.  Computed by
+ * amending the ordinary top-k (a row whose own chunk is missing swaps its worst entry for it),
+ * so decode then runs its selection as a separate stage.  The backward pass takes the selection
+ * as given and needs no flag. */
 /* Paged keys/values (prefill, for a serving cache filled chunk by chunk): with block_table
  * non-NULL, k and v are pools of num_pages pages of one chunk each, [num_pages, kv heads, chunk,
  * head_dim], and chunk j of sequence b is page block_table[b * block_table_stride + j] (entries
@@ -131,6 +138,7 @@ typedef struct hils_decode_params {
   const int32_t* block_table;  /* device, int32; NULL for contiguous caches (see below) */
   int32_t block_table_stride;  /* block_table entries per sequence, >= ceil(max_kv_len / chunk) */
   int32_t num_pages;           /* pages in the k_cache / v_cache pools when paged */
+  int32_t force_local;         /* 1: the query's own chunk is always selected (as prefill) */
 } hils_decode_params;
 /* Paged caches (decode): with block_table non-NULL, k_cache and v_cache are pools of num_pages
  * pages of one chunk each, [num_pages, kv heads, chunk, head_dim], and chunk j of sequence b is

@@ -21,8 +21,8 @@ def _init(inp):
 
 def _prefill_slice(args):
     from oracle import hils_oracle as O
-    rows, chunk, topk, dtype, scale = args
-    return O.prefill_rows(_INP, rows, chunk, topk, dtype, scale=scale)
+    rows, chunk, topk, dtype, scale, force_local = args
+    return O.prefill_rows(_INP, rows, chunk, topk, dtype, scale=scale, force_local=force_local)
 
 
 def workers() -> int:
@@ -31,18 +31,19 @@ def workers() -> int:
 
 
 def prefill_rows(inp: Dict, rows: Iterable[tuple], chunk: int, topk: int, dtype: str,
-                 scale: Optional[float] = None, min_rows_per_worker: int = 64) -> Dict[tuple, dict]:
+                 scale: Optional[float] = None, min_rows_per_worker: int = 64,
+                 force_local: bool = False) -> Dict[tuple, dict]:
     rows = list(rows)
     n = min(workers(), max(1, len(rows) // min_rows_per_worker))
     if n <= 1:
         from oracle import hils_oracle as O
-        return O.prefill_rows(inp, rows, chunk, topk, dtype, scale=scale)
+        return O.prefill_rows(inp, rows, chunk, topk, dtype, scale=scale, force_local=force_local)
     # interleave rows so that every slice holds early (cheap) and late (costly) rows
     slices = [rows[i::n] for i in range(n)]
     # A worker that fails to start breaks the pool (BrokenProcessPool) instead of being respawned.
     with concurrent.futures.ProcessPoolExecutor(n, mp_context=mp.get_context("spawn"), initializer=_init,
                                                 initargs=(inp,)) as pool:
-        parts = list(pool.map(_prefill_slice, [(s, chunk, topk, dtype, scale) for s in slices]))
+        parts = list(pool.map(_prefill_slice, [(s, chunk, topk, dtype, scale, force_local) for s in slices]))
     out = {}
     for p in parts:
         out.update(p)

@@ -58,7 +58,9 @@ def check_rows(res: Dict[tuple, dict], gpu_o: Dict[tuple, np.ndarray], gpu_idx: 
     n_diff = 0
     errors: List[str] = []
     for key, r in res.items():
-        ok, same, msg = selection_ok(r["sigma"], r["idx"], gpu_idx[key])
+        # rank_sigma: the scores the selection ranks by, where they differ from sigma (a forced
+        # own chunk ranks first); sigma itself stays the weights' input
+        ok, same, msg = selection_ok(r.get("rank_sigma", r["sigma"]), r["idx"], gpu_idx[key])
         if not ok:
             errors.append(f"{key}: {msg}")
             continue

@@ -23,13 +23,14 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 7
+    assert lib.hils_abi_version() == 8
 
 
 def _pp(**kw):
     base = dict(batch=1, heads=2, seq_len=2048, head_dim=64, chunk=64, topk=4, q_tile=64, hidden=128,
                 qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
-                attn_mode=0, kv_heads=0, block_table=None, block_table_stride=0, num_pages=0)
+                attn_mode=0, kv_heads=0, block_table=None, block_table_stride=0, num_pages=0,
+                force_local=0)
     base.update(kw)
     return hils.PrefillParams(**base)
 
@@ -37,7 +38,7 @@ def _pp(**kw):
 def _dp(**kw):
     base = dict(batch=2, heads=2, max_kv_len=1000, head_dim=64, chunk=64, topk=4, hidden=128,
                 qcal_rank=8, scale=0.0, dtype=hils.DTYPE_FP32, stage_events=None, n_stage_events=0,
-                kv_heads=0, block_table=None, block_table_stride=0, num_pages=0)
+                kv_heads=0, block_table=None, block_table_stride=0, num_pages=0, force_local=0)
     base.update(kw)
     return hils.DecodeParams(**base)
 
@@ -59,6 +60,7 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
     (dict(attn_mode=2), -2),                                   # auto is bf16 only
     (dict(kv_heads=3), -1), (dict(kv_heads=-1), -1), (dict(kv_heads=4), -1),   # must divide heads = 2
     (dict(attn_mode=1), -2),                                   # chunk-major is bf16 only
+    (dict(force_local=2), -1),
 ])
 def test_prefill_rejects_bad_params(kw, status):
     lib = hils.load()

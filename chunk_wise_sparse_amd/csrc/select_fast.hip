@@ -9,13 +9,14 @@
 //
 // With C = 64 the 64 queries of tile c share the candidate set {0..c}, so scoring is a GEMM
 // [64 queries x d] x [d x (c+1)] done with v_mfma_f32_32x32x16_bf16: A = 32 landmark rows,
-// B = q~ of 32 queries (registers, two column blocks).  The tiles of a workgroup are
-// consecutive chunks of one (batch, head), so they need the same landmark blocks: each block is
-// loaded once, straight from global memory into an LDS ring (global_load_lds_dwordx4, no
-// registers), and read by all the workgroup's waves.  The output of block jb holds, at lane (col, half),
-// query column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap per element
-// pair moves both halves of a query's 32 rows into one lane, so lane l owns query
-// 32*(l/32) + l%32 and all of its scores.
+// B = q~ of 32 queries (registers, two column blocks).  The d order of the contraction is the
+// one in which the Q-Cal MFMA delivers its output, so q~ is formed in registers.  The tiles of
+// a workgroup are consecutive chunks of one (batch, head), so they need the same landmark
+// blocks: each block is loaded once (global -> registers several blocks ahead -> LDS) and read
+// by all the workgroup's waves.  The output of block jb holds, at lane (col, half), query
+// column col and landmark rows 8(e/4) + 4 half + e%4; one v_permlane32_swap per element pair
+// moves both halves of a query's 32 rows into one lane, so lane l owns query 32*(l/32) + l%32
+// and all of its scores.
 //
 // Exact top-k in two passes over the landmarks:
 //   pass 1: per slot the two largest scores, a slot being a landmark row within a 32-row block
@@ -26,13 +27,13 @@
 //           fit the list.
 //   pass 2: every score >= tau is appended, in ascending chunk order, to the query's LDS list
 //           ([position][query] so the 64 lanes write distinct banks).  A list that could
-//           overflow is cut to its exact top-kq first (from a register copy of its keys) and
-//           tau is raised above the cut value (later chunks lose ties); with the tight tau of
-//           pass 1 this is rare.
+//           overflow is cut to its exact top-kq first and tau is raised above the cut value
+//           (later chunks lose ties); with the tight tau of pass 1 this is rare.
 //   final:  the kq-th largest theta of the list (a sorting network for lists of up to 64
 //           entries, else a bisection over the order-preserving 32-bit keys); entries > theta
 //           and the first (kq - #>theta) entries == theta are kept in list order, then the
-//           inter-chunk softmax.
+//           inter-chunk softmax.  The wave's output rows are staged in LDS and leave as 16-byte
+//           stores.
 // Scores are finite by contract: this file is compiled with -fno-honor-nans, so max/min skip
 // NaN quieting.
 #include <float.h>
@@ -50,7 +51,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Per k range: tiles per workgroup, list capacity per query (>= kq + 8) and the number of
 // pass-1 slots per query (rows of a 32-landmark block, times the block parity for k > 32).
-// k <= 64 takes one workgroup per CU (LDS), so one wave per SIMD, with room for 512 registers.
+// Both take one workgroup per CU (LDS); k <= 64 has one wave per SIMD, with room for 512
+// registers.
 template <int KQ> struct SelCfg;
 template <> struct SelCfg<32> { static constexpr int kTiles = 8, kCap = 47, kPar = 1; };
 template <> struct SelCfg<64> { static constexpr int kTiles = 4, kCap = 88, kPar = 2; };
@@ -121,14 +123,10 @@ template <int D, int KQ>
 struct GroupSmem {
   static constexpr int kCap = SelCfg<KQ>::kCap;
   static constexpr int RB = 2 * D;             // landmark row bytes
-  static constexpr int QLD = D + 8;            // q~ staging row stride (elements)
   alignas(16) char ring[2][32 * RB];           // 32-landmark blocks, even / odd block index
-  union {
-    bf16 qt[64 * QLD];                         // q~ [query][d], before the sweeps
-    struct {
-      float s[kCap * 64];                      // [position][query] candidate scores
-      uint16_t j[kCap * 64];                   // [position][query] candidate chunks
-    } list;
+  struct {
+    float s[kCap * 64];                        // [row][query] candidate scores
+    uint16_t j[kCap * 64];                     // [row][query] candidate chunks
   } w[SelCfg<KQ>::kTiles];
 };
 
@@ -139,6 +137,7 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   constexpr int kTiles = SelCfg<KQ>::kTiles, kCap = SelCfg<KQ>::kCap, kPar = SelCfg<KQ>::kPar;
   constexpr int NS = D / 16;                   // MFMA k-steps over d
   typedef GroupSmem<D, KQ> Smem;
+  static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
@@ -158,39 +157,78 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   const int q0 = c * 64;
   const bf16* Q = static_cast<const bf16*>(a.q) + (size_t)bh * a.L * D;
   const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.N * D;
-  float* ls = &sm.w[wave].list.s[lane];        // this lane's list, stride 64
-  uint16_t* lj = &sm.w[wave].list.j[lane];
+  // This lane's list: row i at ls[64 i], lj[64 i].
+  float* ls = &sm.w[wave].s[lane];
+  uint16_t* lj = &sm.w[wave].j[lane];
 
-  // ---------------- q~ as the B operand: query 32 cb + col, d = 16 s + 8 half + z -----------
+  // ---------------- q~ as the B operand ------------------------------------------------------
+  // Lane (col, half) holds query 32 cb + col.  The d order of the scoring contraction is the
+  // order in which the Q-Cal MFMA below delivers its output rows: k-slot z of step s at lane
+  // half h is d(s, h, z) = 16 s + 8 (z / 4) + 4 h + z % 4, so q~ is formed in registers.  The
+  // landmark rows are laid out in LDS in the same order (see the ring).
   bf16x8 qf[2][NS];
-  if (a.r > 0) {
-    // delta_q^T[d][query] = sum_r W_up[hd*D + d][r] t[query][r]; t (fp32) is split into three
-    // bf16 parts so that every product is exact and the sum is accumulated in fp32.
-    constexpr int NRS = 4;                     // r <= 64, 16 per step
-    const int nrs = (a.r + 15) >> 4;
-    bf16x8 tb[3][2][NRS];
-    // With r a multiple of 8 every 8-slot run is a whole, 16-byte aligned piece of a row.
-    const bool vec = (a.r & 7) == 0;
+  auto load_q = [&](int cb) {
+    const bf16* qrow = Q + (size_t)(q0 + 32 * cb + col) * D;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(qrow + 16 * st + 4 * half);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(qrow + 16 * st + 8 + 4 * half);
+      qf[cb][st] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  // delta_q^T[d][query] = sum_r W_up[hd*D + d][r] t[query][r]; t (fp32) is split into three bf16
+  // parts so that every product is exact and the sum is accumulated in fp32.  VEC: r is a
+  // multiple of 8, so every 8-slot run is a whole 16-byte piece of a row.  Loads are
+  // unconditional (indices clamped into the row, values past r zeroed after the load) and each
+  // variant is straight-line code, so the compiler keeps the loads in flight together.
+  auto qcal = [&](auto vec_c, auto nrs_c) {
+    constexpr bool VEC = decltype(vec_c)::value;
+    constexpr int NRS = decltype(nrs_c)::value;   // 16-wide r steps: r <= 16 NRS
+    const int r = a.r, nrs = (r + 15) >> 4;
+    const bf16* WU = static_cast<const bf16*>(a.w_up) + (size_t)hd * D * r;
+    // W_up fragment of rows 32 db + col, r-slots 16 rs + 8 half + z.
+    auto wfrag = [&](int db, int rs) {
+      const bf16* wrow = WU + (size_t)(32 * db + col) * r;
+      const int a0 = 16 * rs + 8 * half;
+      bf16x8 wa;
+      if constexpr (VEC) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(wrow + min(a0, r - 8));
+#pragma unroll
+        for (int z = 0; z < 8; ++z) wa[z] = a0 < r ? v[z] : bf16_rne(0.f);
+      } else {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) {
+          const bf16 v = wrow[min(a0 + z, r - 1)];
+          wa[z] = a0 + z < r ? v : bf16_rne(0.f);
+        }
+      }
+      return wa;
+    };
+    // One query block at a time (registers): t split in three, then the D / 32 row blocks of
+    // W_up, the next one's fragments loading while the current one's MFMAs run.
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const float* tq = a.tcode + ((size_t)b * a.L + q0 + 32 * cb + col) * a.r;
+      load_q(cb);
+      bf16x8 tb[3][NRS];
+      const float* tq = a.tcode + ((size_t)b * a.L + q0 + 32 * cb + col) * r;
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
+        const int a0 = 16 * rs + 8 * half;
         float tv[8];
-        if (vec) {
-          const int a0 = 16 * rs + 8 * half;
-          const f32x4 lo = a0 < a.r ? *reinterpret_cast<const f32x4*>(tq + a0) : zero4();
-          const f32x4 hi = a0 < a.r ? *reinterpret_cast<const f32x4*>(tq + a0 + 4) : zero4();
+        if constexpr (VEC) {
+          const float* pt = tq + min(a0, r - 8);
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(pt);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(pt + 4);
 #pragma unroll
           for (int z = 0; z < 4; ++z) {
-            tv[z] = lo[z];
-            tv[4 + z] = hi[z];
+            tv[z] = a0 < r ? lo[z] : 0.f;
+            tv[4 + z] = a0 < r ? hi[z] : 0.f;
           }
         } else {
 #pragma unroll
           for (int z = 0; z < 8; ++z) {
-            const int ai = 16 * rs + 8 * half + z;
-            tv[z] = (rs < nrs && ai < a.r) ? tq[ai] : 0.f;
+            const float v = tq[min(a0 + z, r - 1)];
+            tv[z] = a0 + z < r ? v : 0.f;
           }
         }
 #pragma unroll
@@ -199,101 +237,115 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
           const bf16 t0 = bf16_rne(t);
           const float r1 = t - to_f32(t0);
           const bf16 t1 = bf16_rne(r1);
-          tb[0][cb][rs][z] = t0;
-          tb[1][cb][rs][z] = t1;
-          tb[2][cb][rs][z] = bf16_rne(r1 - to_f32(t1));
+          tb[0][rs][z] = t0;
+          tb[1][rs][z] = t1;
+          tb[2][rs][z] = bf16_rne(r1 - to_f32(t1));
         }
       }
-    }
-    const bf16* WU = static_cast<const bf16*>(a.w_up) + (size_t)hd * D * a.r;
-    bf16* qt = sm.w[wave].qt;
+      bf16x8 wcur[NRS], wnext[NRS];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      f32x16 acc[2] = {};
-      const bf16* wrow = WU + (size_t)(32 * db + col) * a.r;
+      for (int rs = 0; rs < NRS; ++rs) wcur[rs] = wfrag(0, rs);
 #pragma unroll
-      for (int rs = 0; rs < NRS; ++rs) {
-        if (rs < nrs) {
-          bf16x8 wa;
-          if (vec) {
-            const int a0 = 16 * rs + 8 * half;
-            wa = a0 < a.r ? *reinterpret_cast<const bf16x8*>(wrow + a0) : bf16x8{};
-          } else {
+      for (int db = 0; db < D / 32; ++db) {
+        if (db + 1 < D / 32) {
 #pragma unroll
-            for (int z = 0; z < 8; ++z) {
-              const int ai = 16 * rs + 8 * half + z;
-              wa[z] = ai < a.r ? wrow[ai] : bf16_rne(0.f);
-            }
+          for (int rs = 0; rs < NRS; ++rs) wnext[rs] = wfrag(db + 1, rs);
+        }
+        f32x16 acc = {};
+#pragma unroll
+        for (int rs = 0; rs < NRS; ++rs) {
+          if (rs < nrs) {
+#pragma unroll
+            for (int p = 0; p < 3; ++p) acc = mfma32(wcur[rs], tb[p][rs], acc);
           }
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int p = 0; p < 3; ++p) acc[cb] = mfma32(wa, tb[p][cb][rs], acc[cb]);
         }
-      }
-      // acc[cb][e]: d = 32 db + 8 (e/4) + 4 half + e%4, query 32 cb + col.
+        // acc[e]: query 32 cb + col, d = 32 db + 8 (e / 4) + 4 half + e % 4 = d(2 db + e / 8,
+        // half, e % 8).
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int qr = 32 * cb + col;
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d0 = 32 * db + 8 * a4 + 4 * half;
-          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(Q + (size_t)(q0 + qr) * D + d0);
-          bf16x4 o;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = bf16_rne(to_f32(qv[i]) + acc[cb][4 * a4 + i]);
-          *reinterpret_cast<bf16x4*>(&qt[qr * Smem::QLD + d0]) = o;
+        for (int e = 0; e < 16; ++e) {
+          bf16x8& f = qf[cb][2 * db + e / 8];
+          f[e % 8] = bf16_rne(to_f32(f[e % 8]) + acc[e]);
         }
-      }
-    }
-    __syncthreads();
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        qf[cb][s] = *reinterpret_cast<const bf16x8*>(&qt[(32 * cb + col) * Smem::QLD + 16 * s + 8 * half]);
-  } else {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        qf[cb][s] = *reinterpret_cast<const bf16x8*>(Q + (size_t)(q0 + 32 * cb + col) * D + 16 * s + 8 * half);
-  }
-
-  // ---------------- landmark ring ------------------------------------------------------------
-  // Block jb (landmark rows 32 jb .. 32 jb + 31, clamped to the group's last candidate) is
-  // loaded straight into ring slot jb & 1 as NL = 32 * 2D / 1024 loads of 1 KiB, load li by wave
-  // li % kTiles; lane l of a load lands at its 1 KiB piece + 16 l.
-  auto issue = [&](int jb, int slot) {
-    constexpr int VPR = D / 8;                 // 16-byte vectors per row
-    constexpr int NL = D / 16;                 // loads per block
-    static_assert(NL * 1024 == 32 * Smem::RB, "block size");
-#pragma unroll
-    for (int li0 = 0; li0 < NL; li0 += kTiles) {
-      const int li = li0 + wave;
-      if (li < NL) {
-        const int r = li * (8 * 64 / D) + lane / VPR, p = lane % VPR;
-        const int row = min(32 * jb + r, c_top);
-        const bf16* src = LM + (size_t)row * D + 8 * (p ^ ring_swz<D>(r));
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(sm.ring[slot] + 1024 * li), 16, 0, 0);
+        for (int rs = 0; rs < NRS; ++rs) wcur[rs] = wnext[rs];
       }
     }
   };
-  // The group walks its blocks in order; f(jb, block) runs once the block is in LDS, while the
-  // next block is in flight.  Every wave takes every barrier; f skips blocks past its tile.
+  if (a.r > 0) {
+    constexpr std::integral_constant<int, 2> r32{};
+    constexpr std::integral_constant<int, 4> r64{};
+    if ((a.r & 7) == 0) {
+      if (a.r <= 32) qcal(std::true_type{}, r32);
+      else qcal(std::true_type{}, r64);
+    } else {
+      if (a.r <= 32) qcal(std::false_type{}, r32);
+      else qcal(std::false_type{}, r64);
+    }
+  } else {
+    load_q(0);
+    load_q(1);
+  }
+
+  // ---------------- landmark ring ------------------------------------------------------------
+  // Block jb = landmark rows 32 jb .. 32 jb + 31 (clamped to the group's last candidate).  Each
+  // block goes global -> registers -> LDS: every wave loads D / kTiles bytes per lane of it into
+  // register stage jb % kDepth, and writes them to ring slot jb & 1 one step before the block is
+  // used, so kDepth blocks are in flight while the group computes.  Loads and stores are
+  // unconditional (clamped rows) so the compiler counts the loads in flight instead of draining
+  // them.  In LDS, row r's 16-byte vector v = 2 s + h holds d(s, h, 0..7), stored at position
+  // v ^ ring_swz(r): a global 8-byte piece d = 16 s + 8 g + 4 h' + (0..3) goes to vector
+  // 2 s + h', bytes 8 g .. 8 g + 7.
+  constexpr int kDepth = 4;
+  constexpr int LB = D / kTiles;               // bytes per lane per block: 8, 16 or 32
+  constexpr int UB = LB >= 16 ? 16 : 8;        // bytes per load
+  constexpr int NPW = LB / UB;                 // loads per lane per block
+  typedef typename std::conditional<UB == 16, u32x4, u32x2>::type unit_t;
+  static_assert(32 * Smem::RB == 64 * kTiles * LB, "block size");
+  unit_t stage[kDepth][NPW];
+  auto unit_off = [&](int u) { return (u * kTiles + wave) * 64 * UB + UB * lane; };  // row-major
+  auto gload = [&](int jb, unit_t (&dst)[NPW]) {
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+      const int o = unit_off(u);
+      const int row = min(32 * jb + o / Smem::RB, c_top);
+      dst[u] = *reinterpret_cast<const unit_t*>(LM + (size_t)row * D + (o % Smem::RB) / 2);
+    }
+  };
+  auto lput = [&](int slot, const unit_t (&src)[NPW]) {
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+      const int o = unit_off(u), r = o / Smem::RB, e0 = (o % Smem::RB) / 2;   // first d
+#pragma unroll
+      for (int hp = 0; hp < UB / 8; ++hp) {    // 8-byte pieces d = e0 + 4 hp .. + 3
+        const int d0 = e0 + 4 * hp, st = d0 / 16, g = (d0 / 8) & 1, h = (d0 / 4) & 1;
+        char* dst = sm.ring[slot] + r * Smem::RB + 16 * ((2 * st + h) ^ ring_swz<D>(r)) + 8 * g;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{src[u][2 * hp], src[u][2 * hp + 1]};
+      }
+    }
+  };
+  // The group walks its blocks in order; f(jb, block) runs once the block is in LDS.  The walk
+  // is rounded up to whole kDepth steps; every wave takes every barrier; f skips blocks past
+  // its own tile.
   auto sweep = [&](auto&& f) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) gload(u, stage[u]);
     __syncthreads();                           // no wave still reads the ring
-    issue(0, 0);
-    for (int jb = 0; jb < nbg; ++jb) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();                         // block jb is in LDS; slot (jb + 1) & 1 is free
-      if (jb + 1 < nbg) issue(jb + 1, (jb + 1) & 1);
-      f(jb, sm.ring[jb & 1]);
+    lput(0, stage[0]);
+    gload(kDepth, stage[0]);
+    for (int jb0 = 0; jb0 < nbg; jb0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int jb = jb0 + u;
+        __syncthreads();                       // block jb is in LDS; slot (jb + 1) & 1 is free
+        lput((jb + 1) & 1, stage[(u + 1) % kDepth]);
+        gload(jb + 1 + kDepth, stage[(u + 1) % kDepth]);
+        if (jb < nbg) f(jb, sm.ring[jb & 1]);
+      }
     }
   };
 
   // ---------------- scoring of one 32-landmark block ---------------------------------------
-  // A operand: lane (col, half) takes row col, d = 16 s + 8 half .. + 7.  Rows past the last
+  // A operand: lane (col, half) takes row col, d(s, half, 0..7).  Rows past the last
   // candidate hold later landmarks or repeat the group's last one; their scores are masked.
   auto read_a = [&](const char* blk, bf16x8 (&af)[NS]) {
     const char* rp = blk + col * Smem::RB;
@@ -413,45 +465,46 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   }
 
   // ---------------- pass 2: collect the candidates ------------------------------------------
+  // Every score >= tau is appended, in chunk order, to the lane's list in LDS.
   int cnt = 0;
   {
     // Make room for the next 8 scores: a list that would overflow is cut to its exact top kq
     // first (rare: lists end near kq + a few).  theta = kq-th largest key, bit by bit from the
     // top, counting list entries in LDS; entries > theta and the first kq - #(> theta)
-    // entries == theta stay, in list order.
+    // entries == theta stay, in list order.  The cut runs in rolled loops over the list in LDS
+    // so that it stays small in the unrolled sweep.
     auto make_room = [&](const float (&sc)[32], int h0) {
       if (__any(cnt + 8 > kCap)) {
         int np = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) np += sc[h0 + i] >= tau ? 1 : 0;
         if (cnt + np > kCap) {
-          // The list's keys in registers (-inf past its end), then theta bit by bit.
-          uint32_t key[kCap];
-#pragma unroll
-          for (int i = 0; i < kCap; ++i) key[i] = f32_key(i < cnt ? ls[64 * i] : -INFINITY);
           uint32_t th = 0u;
+#pragma unroll 1
           for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = th | (1u << bit);
             int n = 0;
-#pragma unroll
-            for (int i = 0; i < kCap; ++i) n += key[i] >= cand ? 1 : 0;
+#pragma unroll 1
+            for (int i = 0; i < cnt; ++i) n += f32_key(ls[64 * i]) >= cand ? 1 : 0;
             if (n >= kq) th = cand;
           }
           int ngt = 0;
-#pragma unroll
-          for (int i = 0; i < kCap; ++i) ngt += key[i] > th ? 1 : 0;
+#pragma unroll 1
+          for (int i = 0; i < cnt; ++i) ngt += f32_key(ls[64 * i]) > th ? 1 : 0;
           const int m_eq = kq - ngt;
           int w = 0, eq = 0;
-#pragma unroll
-          for (int i = 0; i < kCap; ++i) {
-            bool keep = key[i] > th;
-            if (i < cnt && key[i] == th) {
+#pragma unroll 1
+          for (int i = 0; i < cnt; ++i) {
+            const float v = ls[64 * i];
+            const uint32_t key = f32_key(v);
+            bool keep = key > th;
+            if (key == th) {
               keep = eq < m_eq;
               ++eq;
             }
             if (keep) {                        // w <= i: entries move towards the front
               const uint16_t jv = lj[64 * i];
-              ls[64 * w] = key_f32(key[i]);
+              ls[64 * w] = v;
               lj[64 * w] = jv;
               ++w;
             }
@@ -461,7 +514,11 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
         }
       }
     };
-    auto collect = [&](int jb, const float (&sc)[32]) {
+    float sc[32];
+    auto keep = [&](int i, float v) { sc[i] = v; };
+    auto collect = [&](int jb, const f32x16& acc0, const f32x16& acc1) {
+      if (jb == nb - 1) for_scores(std::true_type{}, jb, acc0, acc1, keep);
+      else for_scores(std::false_type{}, jb, acc0, acc1, keep);
 #pragma unroll
       for (int h0 = 0; h0 < 32; h0 += 8) {     // at most 8 appends after each check
         make_room(sc, h0);
@@ -475,17 +532,13 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
         }
       }
     };
-    float sc[32];
-    auto keep = [&](int i, float v) { sc[i] = v; };
     sweep([&](int jb, const char* blk) {
       if (jb >= nb) return;
       bf16x8 af[NS];
       read_a(blk, af);
       f32x16 acc0, acc1;
       mma_block(af, acc0, acc1);
-      if (jb == nb - 1) for_scores(std::true_type{}, jb, acc0, acc1, keep);
-      else for_scores(std::false_type{}, jb, acc0, acc1, keep);
-      collect(jb, sc);
+      collect(jb, acc0, acc1);
     });
   }
 
@@ -548,20 +601,46 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
     esum += ev[i];
   }
   const float inv = 1.f / esum;
-  const int qpos = q0 + 32 * half + col;
-  const size_t orow = ((size_t)bh * a.L + qpos) * a.k;
-  int pos = 0;
+  // The output rows go through LDS: the lane's kept entries (chunk order) to positions 0..kq-1
+  // of its staging row (stride k + 1 words; position k takes the writes of entries not kept),
+  // padding (-1, 0) to kq..k-1.  The wave's 64 rows are contiguous in idx and w, so they then
+  // leave as 16-byte stores.  The staging rows reuse the wave's list space, already read.
+  static_assert(sizeof(sm.w[0]) >= 2 * 64 * (KQ + 1) * sizeof(float), "staging rows");
+  const int S = a.k + 1;
+  int* st_i = reinterpret_cast<int*>(&sm.w[wave]);
+  float* st_w = reinterpret_cast<float*>(st_i + 64 * S);
+  {
+    int* ri = st_i + lane * S;
+    float* rw = st_w + lane * S;
+    int pos = 0;
 #pragma unroll
-  for (int i = 0; i < kCap; ++i) {
-    if (kept[i]) {
-      a.idx[orow + pos] = ej[i];
-      a.w[orow + pos] = ev[i] * inv;
-      ++pos;
+    for (int i = 0; i < kCap; ++i) {
+      ri[pos] = ej[i];
+      rw[pos] = ev[i] * inv;
+      pos += kept[i] ? 1 : 0;
+    }
+    for (int p = kq; p < a.k; ++p) {
+      ri[p] = -1;
+      rw[p] = 0.f;
     }
   }
-  for (int p = kq; p < a.k; ++p) {
-    a.idx[orow + p] = -1;
-    a.w[orow + p] = 0.f;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's rows are in LDS
+  const int nw = 64 * a.k;                     // words of the wave's rows (a multiple of 4)
+  const uint32_t mk = ((1u << 20) + a.k - 1) / a.k;   // word / k == (word * mk) >> 20, word < 4096
+  const size_t obase = ((size_t)bh * a.L + q0) * a.k;
+  for (int w0 = 4 * lane; w0 < nw; w0 += 256) {
+    u32x4 vi;
+    f32x4 vw;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const int word = w0 + z;
+      const int row = (int)(((uint32_t)word * mk) >> 20);
+      const int at = row * S + (word - row * a.k);
+      vi[z] = (uint32_t)st_i[at];
+      vw[z] = st_w[at];
+    }
+    *reinterpret_cast<u32x4*>(a.idx + obase + w0) = vi;
+    *reinterpret_cast<f32x4*>(a.w + obase + w0) = vw;
   }
 }
 

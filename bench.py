@@ -651,8 +651,13 @@ def main():
         print("[bench] extras: prefill_32k", file=sys.stderr, flush=True)
         scfg = synth.CONFIGS["prefill_32k"]
         P32 = synth.make_prefill_inputs_torch(scfg, dev)
+        # i.i.d. queries (the workload's recipe): the automatic mode, which picks chunk-major on
+        # them, and the union walk for comparison
+        time_prefill(P32, scfg, 1, attn_mode=hils.ATTN_AUTO)
+        extras["prefill_32k"] = dict(stage_dict(scfg, time_prefill(P32, scfg, 5, attn_mode=hils.ATTN_AUTO)),
+                                     attn_mode="auto")
         time_prefill(P32, scfg, 1)
-        extras["prefill_32k"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
+        extras["prefill_32k"]["union_walk"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
         extras["prefill_512k"], P512 = bench_512k(dev)
         print("[bench] extras: length sweep 32K..512K", file=sys.stderr, flush=True)
         extras["length_sweep"] = length_sweep_from(P512)

@@ -766,6 +766,54 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block_kernel(const
 // depend on which rows share its tile, so the output is deterministic although the lists are
 // filled in arrival order.
 
+// Pair p of the batch (blockIdx.y of the kernels below): its tensors and its list buffers.
+struct CmLists {
+  const int32_t* idx;
+  uint32_t *cnt, *off, *cur, *toff, *ent;
+};
+__device__ __forceinline__ CmLists cm_lists(const CmArgs& a, int p) {
+  const size_t bh = (size_t)a.pair0 + p, lk = (size_t)a.L * a.k;
+  CmLists c;
+  c.idx = a.idx + bh * lk;
+  c.cnt = a.cnt + (size_t)p * a.N;
+  c.off = a.off + (size_t)p * (a.N + 1);
+  c.cur = a.cur + (size_t)p * a.N;
+  c.toff = a.toff + (size_t)p * (a.N + 1);
+  c.ent = a.ent + (size_t)p * lk;
+  return c;
+}
+struct CmPair {
+  const bf16 *q, *key, *val;
+  const float* w;
+  bf16* o;
+  bf16* partial;
+  const int32_t* bt;                           // the pair's block-table row (paged), else NULL
+  int Hk, kvh;                                 // key/value heads per batch row, the pair's one
+};
+template <int D>
+__device__ __forceinline__ CmPair cm_pair(const CmArgs& a, int p) {
+  const size_t bh = (size_t)a.pair0 + p, b = bh / a.H, h = bh % a.H;
+  const size_t ld = (size_t)a.L * D, lk = (size_t)a.L * a.k;
+  CmPair c;
+  c.Hk = a.H / a.G;
+  c.kvh = (int)(h / a.G);
+  const size_t kvbh = b * c.Hk + c.kvh;
+  c.q = static_cast<const bf16*>(a.q) + bh * ld;
+  if (a.bt) {                                  // pools: pages of every key/value head
+    c.key = static_cast<const bf16*>(a.key);
+    c.val = static_cast<const bf16*>(a.val);
+    c.bt = a.bt + b * (size_t)a.bt_stride;
+  } else {
+    c.key = static_cast<const bf16*>(a.key) + kvbh * ld;
+    c.val = static_cast<const bf16*>(a.val) + kvbh * ld;
+    c.bt = nullptr;
+  }
+  c.w = a.w + bh * lk;
+  c.o = static_cast<bf16*>(a.o) + bh * ld;
+  c.partial = static_cast<bf16*>(a.partial) + (size_t)p * lk * D;
+  return c;
+}
+
 __global__ __launch_bounds__(256) void cm_zero_kernel(uint32_t* cnt, int n) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0u;
 }
@@ -774,8 +822,12 @@ __global__ __launch_bounds__(256) void cm_zero_kernel(uint32_t* cnt, int n) {
 // entries and counts it into an LDS histogram first (nchunks <= kCmLdsChunks), so that a chunk
 // costs one global atomic per workgroup instead of one per selection.
 constexpr int kCmLdsChunks = 16384;
-__global__ __launch_bounds__(256) void cm_count_kernel(const int32_t* idx, int n, int nchunks, uint32_t* cnt) {
+__global__ __launch_bounds__(256) void cm_count_kernel(const CmArgs a) {
   extern __shared__ uint32_t hist[];
+  const CmLists c = cm_lists(a, blockIdx.y);
+  const int32_t* idx = c.idx;
+  uint32_t* cnt = c.cnt;
+  const int n = a.L * a.k, nchunks = a.N;
   const int per = (n + gridDim.x - 1) / gridDim.x;
   const int b = min(n, (int)blockIdx.x * per), e = min(n, b + per);
   if (nchunks > kCmLdsChunks) {
@@ -798,9 +850,12 @@ __global__ __launch_bounds__(256) void cm_count_kernel(const int32_t* idx, int n
 
 // One workgroup: off = exclusive prefix of cnt, cur = off, toff = exclusive prefix of
 // ceil(cnt / kCmItem); off[N] and toff[N] are the totals.
-__global__ __launch_bounds__(1024) void cm_scan_kernel(const uint32_t* cnt, int N, uint32_t* off, uint32_t* cur,
-                                                       uint32_t* toff) {
+__global__ __launch_bounds__(1024) void cm_scan_kernel(const CmArgs a) {
   __shared__ uint32_t s_e[1024], s_t[1024];
+  const CmLists c = cm_lists(a, blockIdx.x);
+  const uint32_t* cnt = c.cnt;
+  uint32_t *off = c.off, *cur = c.cur, *toff = c.toff;
+  const int N = a.N;
   const int t = threadIdx.x;
   const int per = (N + 1023) / 1024;
   const int b = min(N, t * per), e = min(N, b + per);
@@ -837,9 +892,12 @@ __global__ __launch_bounds__(1024) void cm_scan_kernel(const uint32_t* cnt, int 
 // chunk's list with one global atomic (LDS histogram, then LDS cursors), over the same slices
 // as cm_count_kernel.  The order inside a chunk's list is arrival order; results do not depend
 // on it.
-__global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t* idx, int n, int k, int nchunks, uint32_t* cur,
-                                                      uint32_t* ent) {
+__global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
   extern __shared__ uint32_t sh[];             // hist[nchunks], base[nchunks]
+  const CmLists c = cm_lists(a, blockIdx.y);
+  const int32_t* idx = c.idx;
+  uint32_t *cur = c.cur, *ent = c.ent;
+  const int n = a.L * a.k, k = a.k, nchunks = a.N;
   const int per = (n + gridDim.x - 1) / gridDim.x;
   const int b = min(n, (int)blockIdx.x * per), e = min(n, b + per);
   if (nchunks > kCmLdsChunks) {
@@ -890,28 +948,30 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int N = a.N, k = a.k;
-  const uint32_t items = a.toff[N];
-  const bf16* Q = static_cast<const bf16*>(a.q);
-  const bf16* Kb = static_cast<const bf16*>(a.key);
-  const bf16* Vb = static_cast<const bf16*>(a.val);
-  bf16* P = static_cast<bf16*>(a.partial);
+  const CmLists cl = cm_lists(a, blockIdx.y);
+  const CmPair cp = cm_pair<D>(a, blockIdx.y);
+  const uint32_t items = cl.toff[N];
+  const bf16* Q = cp.q;
+  const bf16* Kb = cp.key;
+  const bf16* Vb = cp.val;
+  bf16* P = cp.partial;
   const float zs = a.scale * 1.4426950408889634f;
   // The next item's K/V are loaded into registers while the current item is computed.
   auto locate = [&](uint32_t item, int& j, uint32_t& e0, uint32_t& e1) {
     int lo = 0, hi = N;                        // toff[lo] <= item < toff[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.toff[mid] <= item) lo = mid;
+      if (cl.toff[mid] <= item) lo = mid;
       else hi = mid;
     }
     j = lo;
-    e0 = a.off[j] + kCmItem * (item - a.toff[j]);
-    e1 = min(e0 + (uint32_t)kCmItem, a.off[j + 1]);
+    e0 = cl.off[j] + kCmItem * (item - cl.toff[j]);
+    e1 = min(e0 + (uint32_t)kCmItem, cl.off[j + 1]);
   };
   u32x4 kr[NV], vr[NV];
   auto load_kv = [&](int j) {
-    const bf16* kc = kv_chunk<bf16, D>(Kb, Kb, a.bt, a.num_pages, a.Hk, a.kvh, j);
-    const bf16* vc = kv_chunk<bf16, D>(Vb, Vb, a.bt, a.num_pages, a.Hk, a.kvh, j);
+    const bf16* kc = kv_chunk<bf16, D>(Kb, Kb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
+    const bf16* vc = kv_chunk<bf16, D>(Vb, Vb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
@@ -923,7 +983,7 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
   auto load_tile = [&](uint32_t e0_, uint32_t e1_, uint32_t& pe_, bf16x8 (&qf_)[NF]) {
     const uint32_t t0_ = e0_ + 16 * wave;
     if (t0_ < e1_) {
-      pe_ = a.ent[t0_ + m < e1_ ? t0_ + m : t0_];
+      pe_ = cl.ent[t0_ + m < e1_ ? t0_ + m : t0_];
       const bf16* qp = Q + (size_t)(pe_ >> 6) * D + g * (D / 4);
 #pragma unroll
       for (int st = 0; st < NF; ++st) qf_[st] = load_frag<bf16>(qp + st * 8);
@@ -957,7 +1017,7 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
     if (has_next) {
       locate(next, jn, e0n, e1n);
       const uint32_t t0n = e0n + 16 * wave;
-      if (t0n < e1n) pen = a.ent[t0n + m < e1n ? t0n + m : t0n];
+      if (t0n < e1n) pen = cl.ent[t0n + m < e1n ? t0n + m : t0n];
       load_kv(jn);
     }
     const uint32_t t0 = e0 + 16 * wave;
@@ -995,7 +1055,7 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
         l += sc[i];
       }
       l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
-      const float f = a.w[(size_t)r * k + es] * __builtin_amdgcn_rcpf(l);
+      const float f = cp.w[(size_t)r * k + es] * __builtin_amdgcn_rcpf(l);
       bf16x8 pf[NP];
 #pragma unroll
       for (int st = 0; st < NP; ++st)
@@ -1043,8 +1103,9 @@ __global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
   const int r = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
   if (r >= a.L) return;
+  const CmPair cp = cm_pair<D>(a, blockIdx.y);
   const int nv = min(a.k, (r >> 6) + 1);
-  const bf16* P = static_cast<const bf16*>(a.partial) + (size_t)r * a.k * D + t * 8;
+  const bf16* P = cp.partial + (size_t)r * a.k * D + t * 8;
   float acc[8] = {};
   int e = 0;
   for (; e + 4 <= nv; e += 4) {                // four independent loads in flight
@@ -1064,22 +1125,24 @@ __global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
   bf16x8 out;
 #pragma unroll
   for (int z = 0; z < 8; ++z) out[z] = bf16_rne(acc[z]);
-  *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.o) + (size_t)r * D + t * 8) = out;
+  *reinterpret_cast<bf16x8*>(cp.o + (size_t)r * D + t * 8) = out;
 }
 
 template <int D>
 hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st) {
-  const int n = a.L * a.k;
-  const int gb = min((n + 8191) / 8192, 1024);   // workgroups over the entries, 8192+ each
+  const int n = a.L * a.k, np = a.npairs;
+  const int gb = min((n + 8191) / 8192, 1024);   // workgroups per pair over the entries, 8192+ each
   const bool lds = a.N <= kCmLdsChunks;
-  hipLaunchKernelGGL(cm_zero_kernel, dim3(min((a.N + 255) / 256, 1024)), dim3(256), 0, st, a.cnt, a.N);
-  hipLaunchKernelGGL(cm_count_kernel, dim3(gb), dim3(256), lds ? (size_t)a.N * 4 : 0, st, a.idx, n, a.N, a.cnt);
-  hipLaunchKernelGGL(cm_scan_kernel, dim3(1), dim3(1024), 0, st, a.cnt, a.N, a.off, a.cur, a.toff);
-  hipLaunchKernelGGL(cm_fill_kernel, dim3(gb), dim3(256), lds ? (size_t)a.N * 8 : 0, st, a.idx, n, a.k, a.N, a.cur,
-                     a.ent);
-  hipLaunchKernelGGL((cm_attn_kernel<D>), dim3(512), dim3(512), 0, st, a);
+  const int nz = a.N * np;
+  hipLaunchKernelGGL(cm_zero_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, st, a.cnt, nz);
+  hipLaunchKernelGGL(cm_count_kernel, dim3(gb, np), dim3(256), lds ? (size_t)a.N * 4 : 0, st, a);
+  hipLaunchKernelGGL(cm_scan_kernel, dim3(np), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(cm_fill_kernel, dim3(gb, np), dim3(256), lds ? (size_t)a.N * 8 : 0, st, a);
+  // 512 persistent workgroups in all (at least 64 per pair), each pair's own taking its items.
+  const int wpp = max(64, 512 / np);
+  hipLaunchKernelGGL((cm_attn_kernel<D>), dim3(wpp, np), dim3(512), 0, st, a);
   constexpr int RPB = 256 / (D / 8);           // rows per reduce workgroup
-  hipLaunchKernelGGL((cm_reduce_kernel<D>), dim3((a.L + RPB - 1) / RPB), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((cm_reduce_kernel<D>), dim3((a.L + RPB - 1) / RPB, np), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

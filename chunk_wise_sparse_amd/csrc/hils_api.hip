@@ -110,6 +110,25 @@ int effective_q_tile(const hils_prefill_params* p) {
   return qt;
 }
 
+// (batch, head) pairs per chunk-major batch (one launch per stage per batch).  A batch is as
+// large as two budgets allow, and at least one pair: its list and partial buffers within 8 GiB
+// of workspace, and its q, k and v within 160 MiB, so that the chunks its work items stage
+// stay in the 256 MB last-level cache (at 128K that is one pair per batch: two were 2 % and
+// seven 12 % slower).  The batches are then evened out.
+constexpr size_t kCmBatchBytes = (size_t)8 << 30;
+constexpr size_t kCmCacheBytes = (size_t)160 << 20;
+size_t cm_pair_bytes(const hils_prefill_params* p) {
+  const size_t S = p->seq_len, k = p->topk, N = S / 64, d = p->head_dim;
+  return (4 * N + 2) * 4 + S * k * 4 + S * k * d * 2;
+}
+int cm_batch_pairs(const hils_prefill_params* p) {
+  const size_t bh = (size_t)p->batch * p->heads;
+  const size_t qkv = (size_t)p->seq_len * p->head_dim * 2 * 3;
+  const size_t most = std::max<size_t>(1, std::min({bh, kCmBatchBytes / cm_pair_bytes(p), kCmCacheBytes / qkv}));
+  const size_t batches = (bh + most - 1) / most;
+  return (int)((bh + batches - 1) / batches);
+}
+
 PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   PrefillLayout L{};
   const size_t B = p->batch, H = p->heads, S = p->seq_len, k = p->topk, r = p->qcal_rank;
@@ -120,22 +139,22 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   if (!with_sel) off += align_up(B * H * S * k * sizeof(int32_t));
   L.w = off;
   if (!with_sel) off += align_up(B * H * S * k * sizeof(float));
-  if (p->attn_mode != HILS_ATTN_UNION) {       // chunk-major: one (batch, head) pair at a time
+  if (p->attn_mode != HILS_ATTN_UNION) {       // chunk-major: a batch of (batch, head) pairs
     L.probe = off;                             // union probe counter (auto mode)
     off += align_up(4);
-    const size_t N = S / 64, d = p->head_dim;
+    const size_t N = S / 64, d = p->head_dim, P = cm_batch_pairs(p);
     L.cm_cnt = off;
-    off += align_up(N * 4);
+    off += align_up(P * N * 4);
     L.cm_off = off;
-    off += align_up((N + 1) * 4);
+    off += align_up(P * (N + 1) * 4);
     L.cm_cur = off;
-    off += align_up(N * 4);
+    off += align_up(P * N * 4);
     L.cm_toff = off;
-    off += align_up((N + 1) * 4);
+    off += align_up(P * (N + 1) * 4);
     L.cm_ent = off;
-    off += align_up(S * k * 4);
+    off += align_up(P * S * k * 4);
     L.cm_partial = off;
-    off += align_up(S * k * d * 2);
+    off += align_up(P * S * k * d * 2);
   }
   L.total = off;
   return L;
@@ -263,6 +282,12 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
     }
     if (chunk_major) {
       hils::CmArgs ca;
+      ca.q = q;
+      ca.key = k;
+      ca.val = v;
+      ca.o = o;
+      ca.idx = idx;
+      ca.w = w;
       ca.cnt = reinterpret_cast<uint32_t*>(ws + L.cm_cnt);
       ca.off = reinterpret_cast<uint32_t*>(ws + L.cm_off);
       ca.cur = reinterpret_cast<uint32_t*>(ws + L.cm_cur);
@@ -273,25 +298,15 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
       ca.N = p->seq_len / 64;
       ca.k = p->topk;
       ca.scale = scale;
-      const size_t ld = (size_t)p->seq_len * D, lk = (size_t)p->seq_len * p->topk;
-      for (size_t bh = 0; bh < (size_t)p->batch * p->heads; ++bh) {
-        ca.q = static_cast<const T*>(q) + bh * ld;
-        const size_t kvbh = (bh / p->heads) * (p->heads / aa.G) + (bh % p->heads) / aa.G;
-        ca.Hk = p->heads / aa.G;
-        ca.kvh = (int)((bh % p->heads) / aa.G);
-        ca.num_pages = p->num_pages;
-        if (p->block_table) {                  // pools: pages of every key/value head
-          ca.key = k;
-          ca.val = v;
-          ca.bt = p->block_table + (bh / p->heads) * (size_t)p->block_table_stride;
-        } else {
-          ca.key = static_cast<const T*>(k) + kvbh * ld;
-          ca.val = static_cast<const T*>(v) + kvbh * ld;
-          ca.bt = nullptr;
-        }
-        ca.o = static_cast<T*>(o) + bh * ld;
-        ca.idx = idx + bh * lk;
-        ca.w = w + bh * lk;
+      ca.H = p->heads;
+      ca.G = aa.G;
+      ca.bt = p->block_table;
+      ca.bt_stride = p->block_table_stride;
+      ca.num_pages = p->num_pages;
+      const int BH = p->batch * p->heads, P = cm_batch_pairs(p);
+      for (int pair0 = 0; pair0 < BH; pair0 += P) {
+        ca.pair0 = pair0;
+        ca.npairs = std::min(P, BH - pair0);
         if ((e = hils::launch_chunk_attention_cm<D>(ca, st)) != hipSuccess) return e;
       }
       if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;

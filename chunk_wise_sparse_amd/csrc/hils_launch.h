@@ -43,24 +43,28 @@ struct AttnArgs {
 // per (row, slot)), then every row's partials summed in slot order.  Pointers are the pair's
 // slices; cnt / cur hold N words, off / toff N + 1, ent L * k, partial L * k * d bf16.
 struct CmArgs {
-  const void* q;        // [L,d]
-  const void* key;      // [L,d]
-  const void* val;      // [L,d]
-  const int32_t* idx;   // [L,k]
-  const float* w;       // [L,k]
-  void* o;              // [L,d]
-  uint32_t* cnt;        // selections per chunk
-  uint32_t* off;        // first list entry of each chunk (exclusive prefix of cnt)
-  uint32_t* cur;        // fill cursors
-  uint32_t* toff;       // first work item of each chunk (prefix of ceil(cnt / kCmItem))
-  uint32_t* ent;        // list entries (row << 6 | slot), grouped by chunk
-  void* partial;        // [L,k,d] bf16: w_j * o_j of slot j of each row
+  // The batch of (batch, head) pairs pair0 .. pair0 + npairs - 1, one per blockIdx.y of every
+  // chunk-major kernel.  Tensors are the whole [B, H, L, ...] (or [B, Hk, L, d]) ones; the list
+  // buffers hold npairs consecutive per-pair slices.
+  const void* q;        // [B,H,L,d]
+  const void* key;      // [B,Hk,L,d] (paged: the pool)
+  const void* val;      // [B,Hk,L,d] (paged: the pool)
+  const int32_t* idx;   // [B,H,L,k]
+  const float* w;       // [B,H,L,k]
+  void* o;              // [B,H,L,d]
+  uint32_t* cnt;        // [npairs][N] selections per chunk
+  uint32_t* off;        // [npairs][N + 1] first list entry of each chunk (exclusive prefix of cnt)
+  uint32_t* cur;        // [npairs][N] fill cursors
+  uint32_t* toff;       // [npairs][N + 1] first work item of each chunk (prefix of ceil(cnt / kCmItem))
+  uint32_t* ent;        // [npairs][L*k] list entries (row << 6 | slot), grouped by chunk
+  void* partial;        // [npairs][L,k,d] bf16: w_j * o_j of slot j of each row
   int L, N, k;
   float scale;
-  // Paged keys/values: key / val are the pools, bt the pair's block-table row (NULL: key / val
-  // are the pair's contiguous [L,d] slices), kvh its key/value head of Hk.
+  int H, G, pair0, npairs;   // query heads, query heads per key/value head, the batch of pairs
+  // Paged keys/values: key / val are the pools, bt the block table ([B, bt_stride]); NULL: key /
+  // val are contiguous [B, Hk, L, d].
   const int32_t* bt;
-  int num_pages, Hk, kvh;
+  int bt_stride, num_pages;
 };
 constexpr int kCmItem = 128;                   // list entries per work item (8 waves x 16 rows)
 

@@ -35,6 +35,28 @@ def test_chunk_major_long_lists(lib):
     _compare(inp, cfg, o, idx, w, rows)
 
 
+def test_chunk_major_pair_batches(lib):
+    """B = 2, H = 16 at 16K tokens and d = 128: the (batch, head) pairs run in three batches of
+    eleven, eleven and ten (each kernel takes one batch per launch).  The same selection and every
+    row within the bf16 tolerance of the union walk; sampled rows of the last pair against the
+    oracle."""
+    torch = _torch()
+    cfg = synth.PrefillConfig("bf16_pairs_cm", 2, 16, 16384, 128, 64, 16, "bf16", 16, 256)
+    print(f"[case] {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    dev = _to_dev(inp, cfg.dtype)
+    o_u, idx_u, w_u = _run(lib, dev, cfg)
+    o_c, idx_c, w_c = _run(lib, dev, cfg, attn_mode=CM)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_u, idx_c) and torch.equal(w_u, w_c)
+    diff = (o_u.float() - o_c.float()).abs()
+    print(f"[parity] pair batches chunk-major vs union: max {diff.max().item():.3g} "
+          f"mean {diff.mean().item():.3g}", flush=True)
+    assert diff.max().item() <= 2e-2 and diff.mean().item() <= 1e-3
+    rows = [(1, 15, i) for i in sorted({r[2] for r in sample_rows(1, 1, cfg.seq_len, 40, seed=31)})]
+    _compare(inp, cfg, o_c, idx_c, w_c, rows)
+
+
 def test_chunk_major_deterministic(lib):
     cfg = SMALL_BF16[0]
     dev = _to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)

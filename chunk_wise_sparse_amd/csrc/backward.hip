@@ -79,6 +79,114 @@ __global__ __launch_bounds__(256) void bwd_qtilde_kernel(const BwdArgs a) {
   }
 }
 
+// bf16: the forward selection's own arithmetic, so that q~ is the one the forward scored with.
+// One wave per 64 rows of one (batch, head); the offset W_up t by v_mfma_f32_32x32x16_bf16 with t
+// split into three bf16 parts (every product exact, fp32 sums in the same order), then one
+// rounding of q + offset.  Lane (col, half) holds rows 32 cb + col; MFMA output element e is
+// d = 32 db + 8 (e / 4) + 4 half + e % 4.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int D, int NRS, bool VEC>
+__device__ __forceinline__ void qtilde_rows_mfma(const BwdArgs& a, size_t row0, int b, int h, int i0, int lane) {
+  const int col = lane & 31, half = lane >> 5;
+  const int r = a.r, nrs = (r + 15) >> 4;
+  const bf16* WU = static_cast<const bf16*>(a.w_up) + (size_t)h * D * r;
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  bf16* QT = static_cast<bf16*>(a.qt);
+  auto wfrag = [&](int db, int rs) {           // W_up rows 32 db + col, r-slots 16 rs + 8 half + z
+    const bf16* wrow = WU + (size_t)(32 * db + col) * r;
+    const int a0 = 16 * rs + 8 * half;
+    bf16x8 wa;
+    if constexpr (VEC) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(wrow + min(a0, r - 8));
+#pragma unroll
+      for (int z = 0; z < 8; ++z) wa[z] = a0 < r ? v[z] : bf16_rne(0.f);
+    } else {
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        const bf16 v = wrow[min(a0 + z, r - 1)];
+        wa[z] = a0 + z < r ? v : bf16_rne(0.f);
+      }
+    }
+    return wa;
+  };
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int rq = 32 * cb + col;
+    const float* tq = a.tcode + ((size_t)b * a.L + i0 + rq) * r;
+    bf16x8 tb[3][NRS];
+#pragma unroll
+    for (int rs = 0; rs < NRS; ++rs) {
+      const int a0 = 16 * rs + 8 * half;
+      float tv[8];
+      if constexpr (VEC) {
+        const float* pt = tq + min(a0, r - 8);
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(pt);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(pt + 4);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          tv[z] = a0 < r ? lo[z] : 0.f;
+          tv[4 + z] = a0 < r ? hi[z] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) {
+          const float v = tq[min(a0 + z, r - 1)];
+          tv[z] = a0 + z < r ? v : 0.f;
+        }
+      }
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        const float t = tv[z];
+        const bf16 t0 = bf16_rne(t);
+        const float r1 = t - to_f32(t0);
+        const bf16 t1 = bf16_rne(r1);
+        tb[0][rs][z] = t0;
+        tb[1][rs][z] = t1;
+        tb[2][rs][z] = bf16_rne(r1 - to_f32(t1));
+      }
+    }
+    const bf16* qrow = Q + (row0 + rq) * D;
+    bf16* orow = QT + (row0 + rq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      bf16x4 qv[4];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) qv[a4] = *reinterpret_cast<const bf16x4*>(qrow + 32 * db + 8 * a4 + 4 * half);
+      f32x16 acc = {};
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) {
+        if (rs < nrs) {
+          const bf16x8 wa = wfrag(db, rs);
+#pragma unroll
+          for (int p = 0; p < 3; ++p) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, tb[p][rs], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 o;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) o[z] = bf16_rne(to_f32(qv[a4][z]) + acc[4 * a4 + z]);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a4 + 4 * half) = o;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_qtilde_mfma_kernel(const BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row0 = ((size_t)blockIdx.x * 4 + wave) * 64;   // rows of one (b, h): L % 64 == 0
+  if (row0 >= (size_t)a.B * a.H * a.L) return;               // wave-uniform
+  const int bh = (int)(row0 / a.L), h = bh % a.H, b = bh / a.H, i0 = (int)(row0 % a.L);
+  if ((a.r & 7) == 0) {
+    if (a.r <= 32) qtilde_rows_mfma<D, 2, true>(a, row0, b, h, i0, lane);
+    else qtilde_rows_mfma<D, 4, true>(a, row0, b, h, i0, lane);
+  } else {
+    if (a.r <= 32) qtilde_rows_mfma<D, 2, false>(a, row0, b, h, i0, lane);
+    else qtilde_rows_mfma<D, 4, false>(a, row0, b, h, i0, lane);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Row-major pass.
 // ------------------------------------------------------------------------------------------
@@ -330,31 +438,75 @@ __global__ __launch_bounds__(256, 2) void bwd_row_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dqtilde_kernel(const BwdArgs a) {
-  constexpr int TPR = D / 4;                 // threads per row, 4 elements each
+  constexpr int TPR = D / 8;                 // threads per row, 8 elements each
   constexpr int RPW = 256 / TPR;             // rows per workgroup
   const size_t nrows = (size_t)a.B * a.H * a.L;
   const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / TPR;
   if (row >= nrows) return;
-  const int e0 = (threadIdx.x % TPR) * 4;
+  const int e0 = (threadIdx.x % TPR) * 8;
   const int bh = (int)(row / a.L);
   const int N = a.L / 64;
   const T* lmk = static_cast<const T*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * N * D + e0;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.k; ++s) {
-    const int j = a.idx[row * a.k + s];
-    if (j < 0 || j >= N) break;              // padding sits at the end
-    const float ds = a.dsig[row * a.k + s];
-    const T* lr = lmk + (size_t)j * D;
+  const int32_t* ir = a.idx + row * a.k;
+  const float* dr = a.dsig + row * a.k;
+  float acc[8] = {};
+  // Slots in order, eight at a time so that their landmark loads are in flight together; the
+  // padding at the end of a row adds exact zeros.
+  for (int s0 = 0; s0 < a.k; s0 += 8) {
+    int jj[8];
+    float ds[8];
 #pragma unroll
-    for (int z = 0; z < 4; ++z) acc[z] = fmaf(ds, to_f32(lr[z]), acc[z]);
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, a.k - 1);
+      const int j = ir[s];
+      const bool ok = s0 + u < a.k && j >= 0 && j < N;
+      jj[u] = ok ? j : 0;
+      ds[u] = ok ? dr[s] : 0.f;
+    }
+    float lv[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const T* lr = lmk + (size_t)jj[u] * D;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(lr);
+#pragma unroll
+        for (int z = 0; z < 8; ++z) lv[u][z] = to_f32(x[z]);
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(lr);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(lr + 4);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          lv[u][z] = x0[z];
+          lv[u][4 + z] = x1[z];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int z = 0; z < 8; ++z) acc[z] = fmaf(ds[u], lv[u][z], acc[z]);
   }
   float* dqb = a.dqbuf + row * D + e0;
   T* dq = static_cast<T*>(a.dq) + row * D + e0;
+  const f32x4 q0 = *reinterpret_cast<const f32x4*>(dqb);
+  const f32x4 q1 = *reinterpret_cast<const f32x4*>(dqb + 4);
+  float sum[8];
 #pragma unroll
   for (int z = 0; z < 4; ++z) {
-    dq[z] = from_f32<T>(dqb[z] + acc[z]);
-    dqb[z] = acc[z];
+    sum[z] = q0[z] + acc[z];
+    sum[4 + z] = q1[z] + acc[4 + z];
   }
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 o;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) o[z] = bf16_rne(sum[z]);
+    *reinterpret_cast<bf16x8*>(dq) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(dq) = f32x4{sum[0], sum[1], sum[2], sum[3]};
+    *reinterpret_cast<f32x4*>(dq + 4) = f32x4{sum[4], sum[5], sum[6], sum[7]};
+  }
+  *reinterpret_cast<f32x4*>(dqb) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(dqb + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -841,11 +993,15 @@ template <typename T, int D>
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
   const int N = a.L / 64, ntok = a.B * a.L;
   if (a.r > 0) {
-    hipLaunchKernelGGL((bwd_qtilde_kernel<T, D>), dim3((unsigned)((size_t)a.B * a.H * a.L / 64)), dim3(256), 0, st, a);
+    const size_t tiles = (size_t)a.B * a.H * a.L / 64;
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((bwd_qtilde_mfma_kernel<D>), dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_qtilde_kernel<T, D>), dim3((unsigned)tiles), dim3(256), 0, st, a);
   }
   const size_t bm = (size_t)((N + 31) / 32) * 4;
   hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3((uint32_t)a.B * a.H * N), dim3(256), bm, st, a);
-  constexpr int RPW = 256 / (D / 4);
+  constexpr int RPW = 256 / (D / 8);
   const size_t nrows = (size_t)a.B * a.H * a.L;
   hipLaunchKernelGGL((bwd_dqtilde_kernel<T, D>), dim3((unsigned)((nrows + RPW - 1) / RPW)), dim3(256), 0, st, a);
   const int nrb = (a.G * a.L + kBwdRB - 1) / kBwdRB;

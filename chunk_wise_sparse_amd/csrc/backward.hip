@@ -34,7 +34,7 @@
 //                         rows (q, dout, q~ gathered into LDS); wave w owns keys 16w..16w+15
 //                         and accumulates dK, dV with MFMA, the chunk's softmax rebuilt from the
 //                         saved log-sum-exp; dlmk_j = sum dsigma q~ on the side.
-//   bwd_dt / split-K GEMMs / bwd_dh   the Q-Cal factors' gradients.
+//   bwd_dt / split-K GEMMs / bwd_dh   the Q-Cal factors' gradients, on fp32 MFMA.
 #include <float.h>
 
 #include "attn_tiles.h"
@@ -845,100 +845,168 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Q-Cal gradients.  tok = b * L + i indexes the B * L tokens.
+// Q-Cal gradients.  tok = b * L + i indexes the B * L tokens.  The products run on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32): A lane (i, h) holds row i and contraction slot h, B lane (j, h) holds
+// slot h and column j, and output element e of lane (j, h) is row 8 (e / 4) + 4 h + e % 4,
+// column j.  Which contraction index a slot stands for at a step is free as long as A and B
+// agree; each kernel picks it so that a lane's operands come from one vector load.  NCB is the
+// number of 32-code blocks (r <= 32 * NCB).
 // ------------------------------------------------------------------------------------------
-// dt[tok][c] = sum_{h, e} dq~[b, h, i, e] W_up[h d + e][c]; 64 tokens per workgroup, thread
-// (token tid / 4, codes tid % 4 + 4 u).
-template <typename T>
+__device__ __forceinline__ f32x16 mfma_f32(float x, float y, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, c, 0, 0, 0);
+}
+
+// dt[tok][c] = sum_x dq~[tok][x] W_up[x][c], x = h d + e.  A wave takes 32 tokens and every code;
+// the workgroup's four waves share slices of W_up^T (128 x) staged in LDS as fp32.  In a 32-x
+// step group, step s pairs x = x1 + s (slot 0) with x1 + 16 + s (slot 1): lane (token, h) reads
+// its 16 values of dq~ as four 16-byte loads (d % 16 == 0: they stay inside one head).
+template <typename T, int NCB>
 __global__ __launch_bounds__(256) void bwd_dt_kernel(const BwdArgs a) {
-  __shared__ float xs[64][65];               // dq~ tile: 64 tokens x 64 of H*d
-  __shared__ float ws[64][64];               // W_up tile: 64 of H*d x r (r <= 64)
-  const int tid = threadIdx.x;
-  const int ntok = a.B * a.L;
-  const int tok0 = blockIdx.x * 64;
-  const int tl = tid >> 2, cq = tid & 3;
+  constexpr int XB = 128, NC = 32 * NCB, WS = XB + 4;
+  __shared__ float wt[NC * WS];                // W_up^T slice: [code][x]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int ntok = a.B * a.L, HD = a.H * a.d;
+  const int tb = (blockIdx.x * 4 + wave) * 32;
+  const int tok = tb + li;
+  const bool tv = tok < ntok;
+  const int b = tv ? tok / a.L : 0, i = tv ? tok % a.L : 0;
   const T* wu = static_cast<const T*>(a.w_up);
-  float acc[16];
+  f32x16 acc[NCB];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-  const int HD = a.H * a.d;
-  for (int k0 = 0; k0 < HD; k0 += 64) {
-    const int h = k0 / a.d, e0 = k0 % a.d;
-    for (int x = tid; x < 64 * 64; x += 256) {
-      const int t = x >> 6, kk = x & 63;
-      const int tok = tok0 + t;
-      float v = 0.f;
-      if (tok < ntok) {
-        const int b = tok / a.L, i = tok % a.L;
-        v = a.dqbuf[(((size_t)b * a.H + h) * a.L + i) * a.d + e0 + kk];
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+  for (int x0 = 0; x0 < HD; x0 += XB) {
+    __syncthreads();
+    for (int v = tid; v < XB * NC; v += 256) {
+      const int xr = v / NC, c = v % NC;
+      wt[c * WS + xr] = (c < a.r && x0 + xr < HD) ? to_f32(wu[(size_t)(x0 + xr) * a.r + c]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int xs = 0; xs < XB; xs += 32) {
+      const int x = x0 + xs + 16 * lh;
+      f32x4 xv[4];
+      if (tv && x < HD) {
+        const float* src = a.dqbuf + (((size_t)b * a.H + x / a.d) * a.L + i) * a.d + x % a.d;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xv[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      xs[t][kk] = v;
-      const int kr = x >> 6, c = x & 63;
-      ws[kr][c] = c < a.r ? to_f32(wu[(size_t)(k0 + kr) * a.r + c]) : 0.f;
-    }
-    __syncthreads();
-    for (int kk = 0; kk < 64; ++kk) {
-      const float xv = xs[tl][kk];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) acc[u] = fmaf(xv, ws[kk][cq + 4 * u], acc[u]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float* wr = wt + (32 * cb + li) * WS + xs + 16 * lh;
+        f32x4 wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wv[u] = *reinterpret_cast<const f32x4*>(wr + 4 * u);
+#pragma unroll
+        for (int st = 0; st < 16; ++st) acc[cb] = mfma_f32(xv[st >> 2][st & 3], wv[st >> 2][st & 3], acc[cb]);
+      }
     }
-    __syncthreads();
   }
-  const int tok = tok0 + tl;
-  if (tok < ntok) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = cq + 4 * u;
-      if (c < a.r) a.dt[(size_t)tok * a.r + c] = acc[u];
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int c = 32 * cb + li;
+    if (c < a.r) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = tb + 8 * (e >> 2) + 4 * lh + (e & 3);
+        if (t < ntok) a.dt[(size_t)t * a.r + c] = acc[cb][e];
+      }
     }
   }
 }
 
 // Split-K outer-product sums over tokens: part[s][x][c] = sum over the tokens of split s of
-// X(tok, x) * Y[tok][c], Y = [tokens, r] fp32.  kind 0: X = dq~ (x over H*d), Y = t (for
-// dW_up); kind 1: X = h (x over hidden), Y = dt (for dW_down).  64 x-columns per workgroup,
-// thread (column tid % 64, codes tid / 64 + 4 u).
-template <typename T, int KIND>
+// X[tok][x] Y[tok][c], Y = [tokens, r] fp32.  kind 0: X = dq~ (x over H d), Y = t (for dW_up);
+// kind 1: X = h (x over the hidden size), Y = dt (for dW_down).  A wave takes 128 x as four
+// 32-row output blocks, lane i of block q standing for x = xw + 4 i + q (one vector load of four
+// x per lane and token), and every code; step u pairs tokens t0 + 2 u (slot 0) and t0 + 2 u + 1
+// (slot 1).  The tokens of a split are summed in order.
+template <typename T, int KIND, int NCB>
 __global__ __launch_bounds__(256) void bwd_splitk_kernel(const BwdArgs a, int X, int tok_per_split) {
-  __shared__ float xs[64][65];
-  __shared__ float ys[64][65];
-  const int tid = threadIdx.x;
-  const int ntok = a.B * a.L;
-  const int x0 = blockIdx.x * 64, s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int ntok = a.B * a.L, s = blockIdx.y;
   const int t_begin = s * tok_per_split, t_end = min(ntok, t_begin + tok_per_split);
-  const int xl = tid & 63, cq = tid >> 6;
+  const int xw = (blockIdx.x * 4 + wave) * 128;
+  if (xw >= X) return;                         // wave-uniform; X % 128 == 0 or the tail is masked
+  const int x = xw + 4 * li;
+  const bool xok = x < X;
+  const int xc = xok ? x : 0;                  // a valid address for the masked lanes
   const float* Y = KIND == 0 ? a.tcode : a.dt;
-  float acc[16];
+  int cy[NCB];
+  bool cok[NCB];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
-    for (int v = tid; v < 64 * 64; v += 256) {
-      const int t = v >> 6, c = v & 63;
-      const int tok = t0 + t;
-      float xv = 0.f, yv = 0.f;
-      if (tok < t_end) {
-        if constexpr (KIND == 0) {
-          const int b = tok / a.L, i = tok % a.L, x = x0 + c, h = x / a.d, e = x % a.d;
-          xv = a.dqbuf[(((size_t)b * a.H + h) * a.L + i) * a.d + e];
-        } else {
-          xv = to_f32(static_cast<const T*>(a.h)[(size_t)tok * a.Dh + x0 + c]);
-        }
-        yv = c < a.r ? Y[(size_t)tok * a.r + c] : 0.f;
-      }
-      xs[t][c] = xv;
-      ys[t][c] = yv;
-    }
-    __syncthreads();
-    for (int t = 0; t < 64; ++t) {
-      const float xv = xs[t][xl];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) acc[u] = fmaf(xv, ys[t][cq + 4 * u], acc[u]);
-    }
-    __syncthreads();
+  for (int cb = 0; cb < NCB; ++cb) {
+    cok[cb] = 32 * cb + li < a.r;
+    cy[cb] = cok[cb] ? 32 * cb + li : 0;
   }
+  auto load_x = [&](int tok) -> f32x4 {
+    f32x4 v;
+    if constexpr (KIND == 0) {
+      const int b = tok / a.L, i = tok % a.L;
+      v = *reinterpret_cast<const f32x4*>(a.dqbuf + (((size_t)b * a.H + xc / a.d) * a.L + i) * a.d + xc % a.d);
+    } else if constexpr (sizeof(T) == 2) {
+      const bf16x4 hv = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.h) + (size_t)tok * a.Dh + xc);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) v[z] = to_f32(hv[z]);
+    } else {
+      v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.h) + (size_t)tok * a.Dh + xc);
+    }
+    return xok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  f32x16 acc[4][NCB];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[q][cb] = f32x16{};
+  constexpr int U = 8;                         // token pairs per unrolled step group
+  int t0 = t_begin;
+  for (; t0 + 2 * U <= t_end; t0 += 2 * U) {
+    f32x4 xa[U];
+    float yb[U][NCB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok = t0 + 2 * u + lh;
+      xa[u] = load_x(tok);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float y = Y[(size_t)tok * a.r + cy[cb]];
+        yb[u][cb] = cok[cb] ? y : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[q][cb] = mfma_f32(xa[u][q], yb[u][cb], acc[q][cb]);
+  }
+  for (; t0 < t_end; t0 += 2) {
+    const int tok = t0 + lh;
+    const bool ok = tok < t_end;
+    const f32x4 xv = load_x(ok ? tok : t0);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float y = Y[(size_t)(ok ? tok : t0) * a.r + cy[cb]];
+      const float yv = ok && cok[cb] ? y : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q][cb] = mfma_f32(ok ? xv[q] : 0.f, yv, acc[q][cb]);
+    }
+  }
+  // lane (c, h), element e: x = xw + 4 (8 (e / 4) + 4 h + e % 4) + q
   float* part = a.gpart + (size_t)s * X * 64;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) part[(size_t)(x0 + xl) * 64 + cq + 4 * u] = acc[u];
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int xo = xw + 4 * (8 * (e >> 2) + 4 * lh + (e & 3)) + q;
+        if (xo < X) part[(size_t)xo * 64 + 32 * cb + li] = acc[q][cb][e];
+      }
 }
 
 // out = sum of the splits in order.  kind 0: out[x][c] ([H*d, r]); kind 1: out[c][x] ([r, hidden]).
@@ -960,26 +1028,67 @@ __global__ __launch_bounds__(256) void bwd_splitk_reduce_kernel(const BwdArgs a,
   }
 }
 
-// dh[tok][x] = sum_c dt[tok][c] W_down[c][x]; 64 tokens x 64 columns per workgroup.
-template <typename T>
+// dh[tok][x] = sum_c dt[tok][c] W_down[c][x].  A wave takes 32 tokens and 512 hidden columns in
+// four passes of 128 (four 32-column output blocks, lane j of block q standing for x = x1 + 4 j +
+// q); step st pairs codes st (slot 0) and 16 NCB + st (slot 1).  The tokens' codes are loaded
+// once; W_down is read in 8- or 16-byte pieces (four x per lane and code).
+template <typename T, int NCB>
 __global__ __launch_bounds__(256) void bwd_dh_kernel(const BwdArgs a) {
-  __shared__ float ts[64][65];
-  __shared__ float ws[64][64];
-  const int tid = threadIdx.x, ntok = a.B * a.L;
-  const int tok0 = blockIdx.x * 64, x0 = blockIdx.y * 64;
+  constexpr int NS = 16 * NCB;                 // steps over the codes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int ntok = a.B * a.L;
+  const int tb = blockIdx.x * 32;
+  const int xw = (blockIdx.y * 4 + wave) * 512;
+  if (xw >= a.Dh) return;                      // wave-uniform
   const T* wd = static_cast<const T*>(a.w_down);
-  for (int v = tid; v < 64 * 64; v += 256) {
-    const int t = v >> 6, c = v & 63;
-    ts[t][c] = (tok0 + t < ntok && c < a.r) ? a.dt[(size_t)(tok0 + t) * a.r + c] : 0.f;
-    const int cr = v >> 6, x = v & 63;
-    ws[cr][x] = cr < a.r ? to_f32(wd[(size_t)cr * a.Dh + x0 + x]) : 0.f;
+  float ta[NS];
+  {
+    const int tok = min(tb + li, ntok - 1);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int c = NS * lh + st;
+      const float v = a.dt[(size_t)tok * a.r + min(c, a.r - 1)];
+      ta[st] = c < a.r ? v : 0.f;
+    }
   }
-  __syncthreads();
-  const int xl = tid & 63, tq = tid >> 6;
-  for (int t = tq; t < 64; t += 4) {
-    float s = 0.f;
-    for (int c = 0; c < a.r; ++c) s = fmaf(ts[t][c], ws[c][xl], s);
-    if (tok0 + t < ntok) static_cast<T*>(a.dh)[(size_t)(tok0 + t) * a.Dh + x0 + xl] = from_f32<T>(s);
+  for (int x1 = xw; x1 < min(a.Dh, xw + 512); x1 += 128) {
+    f32x16 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int c = NS * lh + st;
+      float wv[4];
+      const T* src = wd + (size_t)min(c, a.r - 1) * a.Dh + x1 + 4 * li;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x4 w4 = *reinterpret_cast<const bf16x4*>(src);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) wv[z] = to_f32(w4[z]);
+      } else {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) wv[z] = w4[z];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = mfma_f32(ta[st], c < a.r ? wv[q] : 0.f, acc[q]);
+    }
+    // lane (j, h), element e: token tb + 8 (e / 4) + 4 h + e % 4, x = x1 + 4 j + q
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = tb + 8 * (e >> 2) + 4 * lh + (e & 3);
+      if (t < ntok) {
+        T* dst = static_cast<T*>(a.dh) + (size_t)t * a.Dh + x1 + 4 * li;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[q][e]);
+          *reinterpret_cast<bf16x4*>(dst) = o;
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][e], acc[1][e], acc[2][e], acc[3][e]};
+        }
+      }
+    }
   }
 }
 
@@ -988,6 +1097,19 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 size_t bwd_rbcnt_words(int G, int L, int N) { return (size_t)((G * L + kBwdRB - 1) / kBwdRB) * N; }   // per head
 int bwd_splits(int ntok) { return max(1, min(256, ntok / 1024)); }
+
+template <typename T, int NCB>
+void launch_qcal_grads(const BwdArgs& a, hipStream_t st) {
+  const int ntok = a.B * a.L;
+  hipLaunchKernelGGL((bwd_dt_kernel<T, NCB>), dim3((ntok + 127) / 128), dim3(256), 0, st, a);
+  const int S = bwd_splits(ntok), per = (ntok + S - 1) / S;
+  const int HD = a.H * a.d;
+  hipLaunchKernelGGL((bwd_splitk_kernel<T, 0, NCB>), dim3((HD + 511) / 512, S), dim3(256), 0, st, a, HD, per);
+  hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 0>), dim3(1024), dim3(256), 0, st, a, HD, S, a.dw_up);
+  hipLaunchKernelGGL((bwd_splitk_kernel<T, 1, NCB>), dim3((a.Dh + 511) / 512, S), dim3(256), 0, st, a, a.Dh, per);
+  hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 1>), dim3(1024), dim3(256), 0, st, a, a.Dh, S, a.dw_down);
+  hipLaunchKernelGGL((bwd_dh_kernel<T, NCB>), dim3((ntok + 31) / 32, (a.Dh + 2047) / 2048), dim3(256), 0, st, a);
+}
 
 template <typename T, int D>
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
@@ -1012,14 +1134,8 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(bwd_fill_kernel, dim3(nrb, nkv), dim3(64), (size_t)(N + kBwdRB * a.k) * 4, st, a);
   hipLaunchKernelGGL((bwd_chunk_kernel<T, D>), dim3(N, nkv), dim3(256), 0, st, a);
   if (a.r > 0) {
-    hipLaunchKernelGGL(bwd_dt_kernel<T>, dim3((ntok + 63) / 64), dim3(256), 0, st, a);
-    const int S = bwd_splits(ntok), per = (ntok + S - 1) / S;
-    const int HD = a.H * a.d;
-    hipLaunchKernelGGL((bwd_splitk_kernel<T, 0>), dim3(HD / 64, S), dim3(256), 0, st, a, HD, per);
-    hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 0>), dim3(1024), dim3(256), 0, st, a, HD, S, a.dw_up);
-    hipLaunchKernelGGL((bwd_splitk_kernel<T, 1>), dim3(a.Dh / 64, S), dim3(256), 0, st, a, a.Dh, per);
-    hipLaunchKernelGGL((bwd_splitk_reduce_kernel<T, 1>), dim3(1024), dim3(256), 0, st, a, a.Dh, S, a.dw_down);
-    hipLaunchKernelGGL(bwd_dh_kernel<T>, dim3((ntok + 63) / 64, a.Dh / 64), dim3(256), 0, st, a);
+    if (a.r <= 32) launch_qcal_grads<T, 1>(a, st);
+    else launch_qcal_grads<T, 2>(a, st);
   }
   return hipGetLastError();
 }

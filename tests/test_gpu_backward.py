@@ -35,6 +35,10 @@ CASES = [
     # 64 chunks, k = 32: the selection's two-pass regime and long per-chunk lists
     (synth.PrefillConfig("bwd_bf16_4k_k32", 1, 2, 4096, 128, 64, 32, "bf16", 32, 512, q_mode="walk",
                          h_mode="walk"), 0),
+    # Q-Cal rank above 32 (two 32-code blocks), H d and hidden not multiples of 512, and split-K
+    # splits of 1046 and 1044 tokens (ragged 16-token groups)
+    (synth.PrefillConfig("bwd_bf16_r36_ragged", 1, 3, 3136, 64, 64, 8, "bf16", 36, 384), 0),
+    (synth.PrefillConfig("bwd_fp32_r40", 1, 2, 1152, 128, 64, 6, "fp32", 40, 256), 0),
 ]
 
 

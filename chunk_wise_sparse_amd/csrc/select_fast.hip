@@ -521,6 +521,12 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
       else for_scores(std::false_type{}, jb, acc0, acc1, keep);
 #pragma unroll
       for (int h0 = 0; h0 < 32; h0 += 8) {     // at most 8 appends after each check
+        // Most groups of 8 hold no candidate for any of the wave's queries: one wave-wide test
+        // of the group maximum skips the eight per-score branches.
+        float gm = sc[h0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) gm = fmaxf(gm, sc[h0 + i]);
+        if (!__any(gm >= tau)) continue;
         make_room(sc, h0);
 #pragma unroll
         for (int i = h0; i < h0 + 8; ++i) {

@@ -52,7 +52,7 @@ struct AttnSmem {
 
 template <typename T, int D, int NW, int KMAX, int STAGES>
 __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnArgs a) {
-  static_assert(STAGES == 2, "two LDS stages");
+  static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
   constexpr int QG = 32 * NW;                // queries per workgroup
   typedef AttnSmem<T, D, QG, KMAX, STAGES> Smem;
   typedef AttnLayout<T, D> Lay;
@@ -293,13 +293,46 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
     if (j >= 0) jl = j;
     return j >= 0 ? j : jl;
   };
+  if constexpr (STAGES == 1) {
+    // One stage, nothing held in registers between chunks (fp32 at d = 128, where a chunk is
+    // 64 KiB and two chunks in flight would not fit the registers): each chunk is copied into
+    // the stage four vectors per tensor at a time, between two barriers, then computed.
+    constexpr int NC = NV < 4 ? NV : 4;
+    static_assert(NV % NC == 0, "copy pieces");
+    for (int t = 0; t < U; ++t) {
+      const int c = advance();
+      const T* kc = kv_chunk<T, D>(Kb, static_cast<const T*>(a.key), bt, a.num_pages, a.H / a.G, kvh, c);
+      const T* vc = kv_chunk<T, D>(Vb, static_cast<const T*>(a.val), bt, a.num_pages, a.H / a.G, kvh, c);
+      __syncthreads();                       // the previous chunk's compute is done with the stage
+#pragma unroll 1
+      for (int u0 = 0; u0 < NV; u0 += NC) {
+        u32x4 kr[NC], vr[NC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          const int v = tid + NT * (u0 + u);
+          kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+          vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+        }
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          const int v = tid + NT * (u0 + u);
+          const int row = v / Lay::VPR, p = v % Lay::VPR;
+          *reinterpret_cast<u32x4*>(sm.k[0] + row * Lay::KLD + p * 16) = kr[u];
+          const int e = p * VE;
+          *reinterpret_cast<u32x4*>(sm.v[0] + (e >> 4) * Lay::VDB + row * (16 * (int)sizeof(T)) +
+                                    (e & 15) * (int)sizeof(T)) = vr[u];
+        }
+      }
+      __syncthreads();
+      compute(c, 0, true);
+    }
+  } else if (U > 0) {
   // Loads and stores below are unconditional (past the end of the union they repeat its last
   // chunk) so that the compiler's wait counts stay exact across the loop.
   // Iteration t computes c_t from stage t%2 while c_{t+1} sits in register set (t+1)%2 and
   // c_{t+2} is loaded into set t%2; after the compute the registers of c_{t+1} go to stage
   // (t+1)%2 and one barrier publishes them.
-  u32x4 kr[2][NV], vr[2][NV];
-  if (U > 0) {
+    u32x4 kr[2][NV], vr[2][NV];
     const int c0 = advance();
     load_kv(c0, kr[0], vr[0]);
     store_kv(0, kr[0], vr[0]);
@@ -1209,8 +1242,8 @@ hipError_t launch_chunk_attention(const AttnArgs& a, hipStream_t st) {
       case 64: launch_block<D, 4>(a, bhs, bm, st); break;
       default: launch_block<D, 8>(a, bhs, bm, st); break;
     }
-  } else if constexpr (D == 128) {              // 32 KiB per tensor per chunk: 64-query groups
-    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 2>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
+  } else if constexpr (D == 128) {              // 32 KiB per tensor per chunk: 64-query groups, one stage
+    hipLaunchKernelGGL((chunk_attention_kernel<T, D, 2, 64, 1>), dim3(bhs * (a.L / 64)), dim3(128), bm, st, a);
   } else {
     if (a.topk <= 32 && a.L % 256 == 0) {
       hipLaunchKernelGGL((chunk_attention_kernel<T, D, 8, 32, 2>), dim3(bhs * (a.L / 256)), dim3(512), bm, st, a);

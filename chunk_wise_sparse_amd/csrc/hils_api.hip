@@ -69,8 +69,6 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", p->topk);
   if ((p->seq_len + 63) / 64 > 65535)
     return fail(HILS_ERR_UNSUPPORTED, "more than 65535 chunks per sequence");
-  if (p->dtype == HILS_DTYPE_FP32 && p->head_dim == 128 && (p->seq_len + 63) / 64 > 16384)
-    return fail(HILS_ERR_UNSUPPORTED, "fp32 with head_dim 128 supports at most 16384 chunks");
   if (p->q_tile != 0 && p->q_tile != 16 && p->q_tile != 32 && p->q_tile != 64 && p->q_tile != 128)
     return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (16, 32, 64 or 128)", p->q_tile);
   if (p->qcal_rank < 0 || p->qcal_rank > 64)

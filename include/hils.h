@@ -55,8 +55,8 @@ typedef enum {
 typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
 
 /* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk == 64;
- * 1 <= topk <= 64; 1 <= seq_len with ceil(seq_len / chunk) <= 65535 (<= 16384 for fp32 with
- * head_dim 128); 0 <= qcal_rank <= 64; hidden a positive multiple of 128 when qcal_rank > 0.
+ * 1 <= topk <= 64; 1 <= seq_len with ceil(seq_len / chunk) <= 65535; 0 <= qcal_rank <= 64;
+ * hidden a positive multiple of 128 when qcal_rank > 0.
  * scale <= 0 selects 1/sqrt(head_dim).
  * A partial last chunk (seq_len % chunk != 0) is allowed: lmk then holds ceil(seq_len / chunk)
  * landmarks, the last one for the partial chunk, and the call stages q, k, v, h and o padded to

@@ -802,17 +802,20 @@ __global__ __launch_bounds__(NW * 64, 2) void chunk_attention_block_kernel(const
 // Pair p of the batch (blockIdx.y of the kernels below): its tensors and its list buffers.
 struct CmLists {
   const int32_t* idx;
-  uint32_t *cnt, *off, *cur, *toff, *ent;
+  const float* w;
+  uint32_t *cnt, *off, *cur, *toff, *ent, *desc;
 };
 __device__ __forceinline__ CmLists cm_lists(const CmArgs& a, int p) {
   const size_t bh = (size_t)a.pair0 + p, lk = (size_t)a.L * a.k;
   CmLists c;
   c.idx = a.idx + bh * lk;
+  c.w = a.w + bh * lk;
   c.cnt = a.cnt + (size_t)p * a.N;
   c.off = a.off + (size_t)p * (a.N + 1);
   c.cur = a.cur + (size_t)p * a.N;
   c.toff = a.toff + (size_t)p * (a.N + 1);
-  c.ent = a.ent + (size_t)p * lk;
+  c.ent = a.ent + (size_t)p * lk * 2;
+  c.desc = a.desc + (size_t)p * cm_max_items(lk, a.N) * 2;
   return c;
 }
 struct CmPair {
@@ -882,12 +885,13 @@ __global__ __launch_bounds__(256) void cm_count_kernel(const CmArgs a) {
 }
 
 // One workgroup: off = exclusive prefix of cnt, cur = off, toff = exclusive prefix of
-// ceil(cnt / kCmItem); off[N] and toff[N] are the totals.
+// ceil(cnt / kCmItem); off[N] and toff[N] are the totals.  Also the work items in order: item
+// toff[j] + t of chunk j covers list entries off[j] + kCmItem t onward, at most kCmItem of them.
 __global__ __launch_bounds__(1024) void cm_scan_kernel(const CmArgs a) {
   __shared__ uint32_t s_e[1024], s_t[1024];
   const CmLists c = cm_lists(a, blockIdx.x);
   const uint32_t* cnt = c.cnt;
-  uint32_t *off = c.off, *cur = c.cur, *toff = c.toff;
+  uint32_t *off = c.off, *cur = c.cur, *toff = c.toff, *desc = c.desc;
   const int N = a.N;
   const int t = threadIdx.x;
   const int per = (N + 1023) / 1024;
@@ -912,8 +916,13 @@ __global__ __launch_bounds__(1024) void cm_scan_kernel(const CmArgs a) {
     off[i] = pe;
     cur[i] = pe;
     toff[i] = pt;
-    pe += cnt[i];
-    pt += (cnt[i] + kCmItem - 1) / kCmItem;
+    const uint32_t ci = cnt[i], ni = (ci + kCmItem - 1) / kCmItem;
+    for (uint32_t t2 = 0; t2 < ni; ++t2) {
+      const uint32_t rows = min(ci - kCmItem * t2, (uint32_t)kCmItem);
+      *reinterpret_cast<u32x2*>(desc + 2 * (size_t)(pt + t2)) = u32x2{pe + kCmItem * t2, ((uint32_t)i << 8) | rows};
+    }
+    pe += ci;
+    pt += ni;
   }
   if (t == 1023) {
     off[N] = s_e[1023];
@@ -921,7 +930,7 @@ __global__ __launch_bounds__(1024) void cm_scan_kernel(const CmArgs a) {
   }
 }
 
-// List entries (row << 6 | slot), grouped by chunk.  A workgroup reserves its share of each
+// List entries (row << 6 | slot, with the bits of the row's weight for that slot), grouped by chunk.  A workgroup reserves its share of each
 // chunk's list with one global atomic (LDS histogram, then LDS cursors), over the same slices
 // as cm_count_kernel.  The order inside a chunk's list is arrival order; results do not depend
 // on it.
@@ -929,6 +938,7 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
   extern __shared__ uint32_t sh[];             // hist[nchunks], base[nchunks]
   const CmLists c = cm_lists(a, blockIdx.y);
   const int32_t* idx = c.idx;
+  const float* w = c.w;
   uint32_t *cur = c.cur, *ent = c.ent;
   const int n = a.L * a.k, k = a.k, nchunks = a.N;
   const int per = (n + gridDim.x - 1) / gridDim.x;
@@ -938,7 +948,8 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
       const int j = idx[i];
       if (j >= 0 && j < nchunks) {
         const int r = i / k, s = i - r * k;
-        ent[atomicAdd(&cur[j], 1u)] = ((uint32_t)r << 6) | (uint32_t)s;
+        *reinterpret_cast<u32x2*>(ent + 2 * (size_t)atomicAdd(&cur[j], 1u)) =
+            u32x2{((uint32_t)r << 6) | (uint32_t)s, __float_as_uint(w[i])};
       }
     }
     return;
@@ -962,15 +973,18 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
     const int j = idx[i];
     if (j >= 0 && j < nchunks) {
       const int r = i / k, s = i - r * k;
-      ent[base[j] + atomicAdd(&hist[j], 1u)] = ((uint32_t)r << 6) | (uint32_t)s;
+      *reinterpret_cast<u32x2*>(ent + 2 * (size_t)(base[j] + atomicAdd(&hist[j], 1u))) =
+          u32x2{((uint32_t)r << 6) | (uint32_t)s, __float_as_uint(w[i])};
     }
   }
 }
 
-// Persistent: workgroup b takes work items b, b + gridDim.x, ...; item i belongs to the chunk j
-// with toff[j] <= i < toff[j + 1] and covers list entries off[j] + 128 (i - toff[j]) onward.
+// Persistent: workgroup b takes the contiguous run of work items [b I / G, (b + 1) I / G) of its
+// pair (I items, G workgroups per pair); item i belongs to the chunk j with toff[j] <= i <
+// toff[j + 1] and covers list entries off[j] + 128 (i - toff[j]) onward.  Consecutive items
+// mostly belong to one chunk, whose K/V is then staged once for the whole run of them.
 template <int D>
-__global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
+__global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
   constexpr int NT = 512;
   typedef AttnLayout<bf16, D> Lay;
   constexpr int NF = D / 32, NP = 2, VE = 8;
@@ -989,17 +1003,20 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
   const bf16* Vb = cp.val;
   bf16* P = cp.partial;
   const float zs = a.scale * 1.4426950408889634f;
-  // The next item's K/V are loaded into registers while the current item is computed.
-  auto locate = [&](uint32_t item, int& j, uint32_t& e0, uint32_t& e1) {
-    int lo = 0, hi = N;                        // toff[lo] <= item < toff[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cl.toff[mid] <= item) lo = mid;
-      else hi = mid;
-    }
-    j = lo;
-    e0 = cl.off[j] + kCmItem * (item - cl.toff[j]);
-    e1 = min(e0 + (uint32_t)kCmItem, cl.off[j + 1]);
+  // Pipeline: while item n is computed, item n+1's K/V and q rows are in flight, its list entries
+  // (row and weight) arrived one item earlier, and item n+2's descriptor one before that, so no
+  // load waits on another issued in the same step (the vector memory counter completes in issue
+  // order, so such a wait would also drain the prefetches).  Loads are unconditional, indices
+  // clamped into the pair's items and the item's entries.
+  uint32_t item = (uint32_t)((uint64_t)blockIdx.x * items / gridDim.x);
+  const uint32_t end = (uint32_t)((uint64_t)(blockIdx.x + 1) * items / gridDim.x);
+  if (item >= end) return;                     // workgroup-uniform
+  auto ld_desc = [&](uint32_t it) -> u32x2 {
+    return *reinterpret_cast<const u32x2*>(cl.desc + 2 * (size_t)min(it, end - 1u));
+  };
+  auto ld_ent = [&](const u32x2& dsc) -> u32x2 {   // this lane's entry of the item
+    const uint32_t n = dsc[1] & 255u, t = (uint32_t)(16 * wave + m);
+    return *reinterpret_cast<const u32x2*>(cl.ent + 2 * (size_t)(dsc[0] + min(t, n - 1u)));
   };
   u32x4 kr[NV], vr[NV];
   auto load_kv = [&](int j) {
@@ -1012,26 +1029,12 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
       vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
     }
   };
-  // A wave's tile of an item: list entry (row << 6 | slot) and the row's q fragments.
-  auto load_tile = [&](uint32_t e0_, uint32_t e1_, uint32_t& pe_, bf16x8 (&qf_)[NF]) {
-    const uint32_t t0_ = e0_ + 16 * wave;
-    if (t0_ < e1_) {
-      pe_ = cl.ent[t0_ + m < e1_ ? t0_ + m : t0_];
-      const bf16* qp = Q + (size_t)(pe_ >> 6) * D + g * (D / 4);
+  auto load_q = [&](const u32x2& pw, bf16x8 (&qf_)[NF]) {
+    const bf16* qp = Q + (size_t)(pw[0] >> 6) * D + g * (D / 4);
 #pragma unroll
-      for (int st = 0; st < NF; ++st) qf_[st] = load_frag<bf16>(qp + st * 8);
-    }
+    for (int st = 0; st < NF; ++st) qf_[st] = load_frag<bf16>(qp + st * 8);
   };
-  uint32_t item = blockIdx.x;
-  if (item >= items) return;                   // workgroup-uniform
-  int j;
-  uint32_t e0, e1, pe = 0;
-  bf16x8 qf[NF];
-  locate(item, j, e0, e1);
-  load_tile(e0, e1, pe, qf);
-  load_kv(j);
-  for (;;) {
-    __syncthreads();                           // the previous item's LDS reads are done
+  auto put_kv = [&]() {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = tid + NT * u;
@@ -1040,24 +1043,32 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
       const int e = p * VE;
       *reinterpret_cast<u32x4*>(sv_ + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
     }
-    __syncthreads();
-    // The next item: its list entries and K/V are requested now, its q rows after this item's
-    // work (the memory counter drains in issue order, and this item's q are already here).
-    const uint32_t next = item + gridDim.x;
-    const bool has_next = next < items;        // workgroup-uniform
-    int jn = 0;
-    uint32_t e0n = 0, e1n = 0, pen = 0;
-    if (has_next) {
-      locate(next, jn, e0n, e1n);
-      const uint32_t t0n = e0n + 16 * wave;
-      if (t0n < e1n) pen = cl.ent[t0n + m < e1n ? t0n + m : t0n];
-      load_kv(jn);
-    }
-    const uint32_t t0 = e0 + 16 * wave;
-    const bool act = t0 < e1;                  // wave-uniform
-    const bool valid = act && t0 + m < e1;
-    if (act) {
-      const int r = (int)(pe >> 6), es = (int)(pe & 63u);
+  };
+  u32x2 dsc_c = ld_desc(item), dsc_n = ld_desc(item + 1), dsc_nn = ld_desc(item + 2), dsc_3;
+  u32x2 pw_c = ld_ent(dsc_c), pw_n = ld_ent(dsc_n), pw_nn;
+  bf16x8 qf[NF], qn[NF];
+  load_q(pw_c, qf);
+  load_kv((int)(dsc_c[1] >> 8));
+  put_kv();
+  __syncthreads();
+  // Item n+1's K/V (when its chunk differs from item n's) and q rows, item n+2's entries, item
+  // n+3's descriptor: the same loads in the same order before the loop and at the end of each
+  // trip, so the waits in the loop are exact.
+  auto prefetch = [&]() {
+    if ((dsc_n[1] >> 8) != (dsc_c[1] >> 8)) load_kv((int)(dsc_n[1] >> 8));   // workgroup-uniform
+    load_q(pw_n, qn);
+    pw_nn = ld_ent(dsc_nn);
+    dsc_3 = ld_desc(item + 3);
+  };
+  prefetch();
+  for (;;) {
+    const bool has_next = item + 1 < end;      // workgroup-uniform
+    // Every lane computes: a lane past the item's last entry holds a copy of that entry and
+    // writes the same partial, bit for bit, so the stores are unconditional and the memory
+    // counter's waits stay exact.
+    const int j = (int)(dsc_c[1] >> 8);
+    {
+      const int r = (int)(pw_c[0] >> 6), es = (int)(pw_c[0] & 63u);
       float sc[16];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -1088,7 +1099,7 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
         l += sc[i];
       }
       l = col_sum(l);                          // >= 1: the row maximum contributes exp2(0)
-      const float f = cp.w[(size_t)r * k + es] * __builtin_amdgcn_rcpf(l);
+      const float f = __uint_as_float(pw_c[1]) * __builtin_amdgcn_rcpf(l);
       bf16x8 pf[NP];
 #pragma unroll
       for (int st = 0; st < NP; ++st)
@@ -1102,28 +1113,34 @@ __global__ __launch_bounds__(512, 2) void cm_attn_kernel(const CmArgs a) {
 #pragma unroll
         for (int st = 0; st < NP; ++st)
           acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(sv_, m, g, db, st), pf[st], acc_o[db]);
-      if (valid) {
-        bf16* op = P + ((size_t)r * k + es) * D;
+      bf16* op = P + ((size_t)r * k + es) * D;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          bf16x4 out;
+      for (int db = 0; db < D / 16; ++db) {
+        bf16x4 out;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
-          *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
-        }
+        for (int rr = 0; rr < 4; ++rr) out[rr] = bf16_rne(acc_o[db][rr]);
+        *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * g) = out;
       }
     }
+    // Keep the hand-over of the prefetched registers below the compute: a copy scheduled into
+    // it would wait there for the prefetches.
+    __builtin_amdgcn_sched_barrier(0);
     if (!has_next) break;
-    if (e0n + 16 * wave < e1n) {
-      pe = pen;
-      const bf16* qp = Q + (size_t)(pe >> 6) * D + g * (D / 4);
+    ++item;
+    const bool new_chunk = (dsc_n[1] >> 8) != (dsc_c[1] >> 8);   // workgroup-uniform
 #pragma unroll
-      for (int st = 0; st < NF; ++st) qf[st] = load_frag<bf16>(qp + st * 8);
+    for (int st = 0; st < NF; ++st) qf[st] = qn[st];
+    pw_c = pw_n;
+    pw_n = pw_nn;
+    dsc_c = dsc_n;
+    dsc_n = dsc_nn;
+    dsc_nn = dsc_3;
+    if (new_chunk) {
+      __syncthreads();                         // the previous chunk's LDS reads are done
+      put_kv();
+      __syncthreads();
     }
-    item = next;
-    j = jn;
-    e0 = e0n;
-    e1 = e1n;
+    prefetch();
   }
 }
 
@@ -1141,12 +1158,12 @@ __global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
   const bf16* P = cp.partial + (size_t)r * a.k * D + t * 8;
   float acc[8] = {};
   int e = 0;
-  for (; e + 4 <= nv; e += 4) {                // four independent loads in flight
-    bf16x8 x[4];
+  for (; e + 8 <= nv; e += 8) {                // eight independent loads in flight
+    bf16x8 x[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const bf16x8*>(P + (size_t)(e + u) * D);
+    for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(P + (size_t)(e + u) * D));
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int z = 0; z < 8; ++z) acc[z] += to_f32(x[u][z]);
   }

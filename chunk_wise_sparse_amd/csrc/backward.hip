@@ -695,71 +695,74 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(const BwdArgs a) {
 
   const uint32_t e0 = bwd_choff(a, bk)[j], e1 = bwd_choff(a, bk)[j + 1];
   // The next block's rows and per-row values are loaded into registers while the current block
-  // is computed.
-  constexpr int NGV = (kBwdBR * VPR + 255) / 256;   // 16-byte vectors per thread per tensor
+  // is computed, and the list entries that address them one block earlier still, so that no
+  // load waits on an entry load issued in the same step (the vector memory counter completes
+  // in order: such a wait would also drain the loads in flight).  Loads are unconditional:
+  // entries past the list end re-read its last entry, and their per-row values are replaced by
+  // inert ones (w = 0, no position) only when the block is put into LDS.
+  constexpr int NGV = kBwdBR * VPR / 256;   // 16-byte vectors per thread per tensor
+  static_assert(NGV >= 1 && kBwdBR * VPR == 256 * NGV, "gather tile does not split over the threads");
   u32x4 gq[NGV], gd[NGV], gt[NGV];
+  uint32_t en_v[NGV], en_s;                  // entries of the block after the next
+  bool ok_s = false, ok_n = false;
   float g_w = 0.f, g_lse = INFINITY, g_dw = 0.f, g_sg = 0.f;
   int g_pos = -1;
-  auto fetch = [&](uint32_t base) {
+  auto fetch_ent = [&](uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < NGV; ++u) en_v[u] = ent[min(base + (uint32_t)((tid + 256 * u) / VPR), e1 - 1u)];
+    const uint32_t x = base + (uint32_t)(tid % kBwdBR);
+    en_s = ent[min(x, e1 - 1u)];
+    ok_s = x < e1;
+  };
+  auto fetch = [&]() {                       // from the entries in en_v / en_s
 #pragma unroll
     for (int u = 0; u < NGV; ++u) {
-      const int v = tid + 256 * u;
-      gq[u] = gd[u] = gt[u] = u32x4{0u, 0u, 0u, 0u};
-      const int r = v / VPR, p = v % VPR;
-      const uint32_t x = base + r;
-      if (v < kBwdBR * VPR && x < e1) {
-        const uint32_t en = ent[x];
-        const int gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
-        const size_t row = ((size_t)b * a.H + hk * a.G + gq_) * a.L + i;
-        gq[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + row * D + p * VE);
-        gd[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + row * D + p * VE);
-        gt[u] = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
-      }
+      const int p = (tid + 256 * u) % VPR;
+      const uint32_t en = en_v[u];
+      const int gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
+      const size_t row = ((size_t)b * a.H + hk * a.G + gq_) * a.L + i;
+      gq[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + row * D + p * VE);
+      gd[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + row * D + p * VE);
+      gt[u] = *reinterpret_cast<const u32x4*>(qt_base + row * D + p * VE);
     }
-    if (tid < kBwdBR) {
-      const uint32_t x = base + tid;
-      g_w = 0.f;
-      g_lse = INFINITY;
-      g_dw = 0.f;
-      g_sg = 0.f;
-      g_pos = -1;
-      if (x < e1) {
-        const uint32_t en = ent[x];
-        const int slot = (int)(en & 63u), gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
-        const size_t rs = (((size_t)b * a.H + hk * a.G + gq_) * a.L + i) * a.k + slot;
-        g_w = a.w[rs];
-        g_lse = a.lse[rs];
-        g_dw = a.dw[rs];
-        g_sg = a.dsig[rs];
-        g_pos = i;
-      }
-    }
+    const uint32_t en = en_s;
+    const int slot = (int)(en & 63u), gi = (int)(en >> 6), gq_ = gi / a.L, i = gi % a.L;
+    const size_t rs = (((size_t)b * a.H + hk * a.G + gq_) * a.L + i) * a.k + slot;
+    g_w = a.w[rs];
+    g_lse = a.lse[rs];
+    g_dw = a.dw[rs];
+    g_sg = a.dsig[rs];
+    g_pos = i;
+    ok_n = ok_s;
   };
   auto put = [&]() {
 #pragma unroll
     for (int u = 0; u < NGV; ++u) {
       const int v = tid + 256 * u;
-      if (v < kBwdBR * VPR) {
-        const int r = v / VPR, p = v % VPR, e = p * VE;
-        const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
-        *reinterpret_cast<u32x4*>(sm.qs + off) = gq[u];
-        *reinterpret_cast<u32x4*>(sm.ds + off) = gd[u];
-        *reinterpret_cast<u32x4*>(sm.ts + off) = gt[u];
-      }
+      const int r = v / VPR, p = v % VPR, e = p * VE;
+      const int off = (e >> 4) * S::DBS + r * S::RB + (e & 15) * (int)sizeof(T);
+      *reinterpret_cast<u32x4*>(sm.qs + off) = gq[u];
+      *reinterpret_cast<u32x4*>(sm.ds + off) = gd[u];
+      *reinterpret_cast<u32x4*>(sm.ts + off) = gt[u];
     }
     if (tid < kBwdBR) {
-      sm.rw[tid] = g_w;
-      sm.rlse[tid] = g_lse;
-      sm.rdw[tid] = g_dw;
-      sm.rsig[tid] = g_sg;
-      sm.rpos[tid] = g_pos;
+      sm.rw[tid] = ok_n ? g_w : 0.f;
+      sm.rlse[tid] = ok_n ? g_lse : INFINITY;
+      sm.rdw[tid] = ok_n ? g_dw : 0.f;
+      sm.rsig[tid] = ok_n ? g_sg : 0.f;
+      sm.rpos[tid] = ok_n ? g_pos : -1;
     }
   };
-  if (e0 < e1) fetch(e0);
+  if (e0 < e1) {
+    fetch_ent(e0);
+    fetch();
+    fetch_ent(e0 + kBwdBR);
+  }
   for (uint32_t base = e0; base < e1; base += kBwdBR) {
     put();
     __syncthreads();
-    if (base + kBwdBR < e1) fetch(base + kBwdBR);
+    fetch();                                 // the next block (inert past the list end)
+    fetch_ent(base + 2 * kBwdBR);
     // S[q][key] = Q K^T and dP[q][key] = dout V^T for the block's two 16-row tiles: lane (n, g)
     // holds key n of the wave and rows q = 16 t + 4 g + rr.
     float pw[2][4], dsv[2][4];

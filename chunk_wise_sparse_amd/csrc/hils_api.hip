@@ -53,7 +53,7 @@ size_t elem_bytes(int dtype) { return dtype == HILS_DTYPE_BF16 ? 2 : 4; }
 // Prefill
 // ---------------------------------------------------------------------------------------------
 struct PrefillLayout {
-  size_t tcode, idx, w, probe, cm_cnt, cm_off, cm_cur, cm_toff, cm_ent, cm_partial, total;
+  size_t tcode, idx, w, probe, cm_cnt, cm_off, cm_cur, cm_toff, cm_ent, cm_desc, cm_partial, total;
 };
 
 int check_prefill_params(const hils_prefill_params* p) {
@@ -117,7 +117,7 @@ constexpr size_t kCmBatchBytes = (size_t)8 << 30;
 constexpr size_t kCmCacheBytes = (size_t)160 << 20;
 size_t cm_pair_bytes(const hils_prefill_params* p) {
   const size_t S = p->seq_len, k = p->topk, N = S / 64, d = p->head_dim;
-  return (4 * N + 2) * 4 + S * k * 4 + S * k * d * 2;
+  return (4 * N + 2) * 4 + S * k * 8 + hils::cm_max_items(S * k, N) * 8 + S * k * d * 2;
 }
 int cm_batch_pairs(const hils_prefill_params* p) {
   const size_t bh = (size_t)p->batch * p->heads;
@@ -150,7 +150,9 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
     L.cm_toff = off;
     off += align_up(P * (N + 1) * 4);
     L.cm_ent = off;
-    off += align_up(P * S * k * 4);
+    off += align_up(P * S * k * 8);
+    L.cm_desc = off;
+    off += align_up(P * hils::cm_max_items(S * k, N) * 8);
     L.cm_partial = off;
     off += align_up(P * S * k * d * 2);
   }
@@ -291,6 +293,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
       ca.cur = reinterpret_cast<uint32_t*>(ws + L.cm_cur);
       ca.toff = reinterpret_cast<uint32_t*>(ws + L.cm_toff);
       ca.ent = reinterpret_cast<uint32_t*>(ws + L.cm_ent);
+      ca.desc = reinterpret_cast<uint32_t*>(ws + L.cm_desc);
       ca.partial = ws + L.cm_partial;
       ca.L = p->seq_len;
       ca.N = p->seq_len / 64;

@@ -56,7 +56,10 @@ struct CmArgs {
   uint32_t* off;        // [npairs][N + 1] first list entry of each chunk (exclusive prefix of cnt)
   uint32_t* cur;        // [npairs][N] fill cursors
   uint32_t* toff;       // [npairs][N + 1] first work item of each chunk (prefix of ceil(cnt / kCmItem))
-  uint32_t* ent;        // [npairs][L*k] list entries (row << 6 | slot), grouped by chunk
+  uint32_t* ent;        // [npairs][L*k][2] list entries (row << 6 | slot, bits of the weight w),
+                        // grouped by chunk
+  uint32_t* desc;       // [npairs][cm_max_items(L*k, N)][2] work items (first entry, chunk << 8 |
+                        // entries), in item order
   void* partial;        // [npairs][L,k,d] bf16: w_j * o_j of slot j of each row
   int L, N, k;
   float scale;
@@ -67,6 +70,9 @@ struct CmArgs {
   int bt_stride, num_pages;
 };
 constexpr int kCmItem = 128;                   // list entries per work item (8 waves x 16 rows)
+// Work items of one pair: each chunk's list is cut into ceil(count / kCmItem) items, so at most
+// L*k / kCmItem + N of them.
+__host__ __device__ inline size_t cm_max_items(size_t lk, size_t nchunks) { return lk / kCmItem + nchunks + 1; }
 
 // Decode Q-Cal code rows are padded to this many entries (zeros past the rank).
 constexpr int kTcodeStride = 64;

@@ -93,18 +93,21 @@ def test_prefill_workspace_size():
     sel = a256(1 * 2 * 2048 * 4 * 4)
     assert lib.hils_prefill_workspace_size(ctypes.byref(p), 0) == t + 2 * sel
     assert lib.hils_prefill_workspace_size(ctypes.byref(p), 1) == t
-    # chunk-major: per-chunk counters and offsets, the list and the bf16 partials of every pair
-    # of a batch: both pairs here (they fit in 8 GiB)
+    # chunk-major: per-chunk counters and offsets, the list (entry and weight), the work items
+    # (at most L k / 128 + N of them) and the bf16 partials of every pair of a batch: both pairs
+    # here (they fit in 8 GiB)
     pc = _pp(dtype=hils.DTYPE_BF16, attn_mode=1)
     N, P = 2048 // 64, 2
-    cm = (256 + 2 * a256(P * N * 4) + 2 * a256(P * (N + 1) * 4) + a256(P * 2048 * 4 * 4)
-          + a256(P * 2048 * 4 * 64 * 2))
+    items = 2048 * 4 // 128 + N + 1
+    cm = (256 + 2 * a256(P * N * 4) + 2 * a256(P * (N + 1) * 4) + a256(P * 2048 * 4 * 8)
+          + a256(P * items * 8) + a256(P * 2048 * 4 * 64 * 2))
     assert lib.hils_prefill_workspace_size(ctypes.byref(pc), 1) == t + cm
     # a pair's partials alone above 8 GiB: one pair per batch
     L, k, d = 64 * 16384, 64, 128
     pb = _pp(dtype=hils.DTYPE_BF16, attn_mode=1, seq_len=L, topk=k, head_dim=d, qcal_rank=0, hidden=0)
     N = L // 64
-    cm1 = 256 + 2 * a256(N * 4) + 2 * a256((N + 1) * 4) + a256(L * k * 4) + a256(L * k * d * 2)
+    cm1 = (256 + 2 * a256(N * 4) + 2 * a256((N + 1) * 4) + a256(L * k * 8) + a256((L * k // 128 + N + 1) * 8)
+           + a256(L * k * d * 2))
     assert lib.hils_prefill_workspace_size(ctypes.byref(pb), 1) == cm1
 
 

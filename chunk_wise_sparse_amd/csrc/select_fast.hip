@@ -132,7 +132,9 @@ struct GroupSmem {
 
 }  // namespace
 
-template <int D, int KQ>
+// QV = 1: the Q-Cal rank is a multiple of 8 and at most 32 (the one Q-Cal form compiled, which
+// keeps the prologue's registers to that form); QV = 0: any rank, chosen at run time.
+template <int D, int KQ, int QV>
 __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(const SelectArgs a) {
   constexpr int kTiles = SelCfg<KQ>::kTiles, kCap = SelCfg<KQ>::kCap, kPar = SelCfg<KQ>::kPar;
   constexpr int NS = D / 16;                   // MFMA k-steps over d
@@ -271,7 +273,9 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
       }
     }
   };
-  if (a.r > 0) {
+  if constexpr (QV == 1) {
+    qcal(std::true_type{}, std::integral_constant<int, 2>{});
+  } else if (a.r > 0) {
     constexpr std::integral_constant<int, 2> r32{};
     constexpr std::integral_constant<int, 4> r64{};
     if ((a.r & 7) == 0) {
@@ -650,17 +654,20 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   }
 }
 
+template <int D, int KQ>
+void launch_select_fast_k(const SelectArgs& a, hipStream_t st) {
+  constexpr int T = SelCfg<KQ>::kTiles;
+  const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
+  if (a.r > 0 && a.r % 8 == 0 && a.r <= 32)
+    hipLaunchKernelGGL((select_fast_kernel<D, KQ, 1>), dim3(groups), dim3(64 * T), 0, st, a);
+  else
+    hipLaunchKernelGGL((select_fast_kernel<D, KQ, 0>), dim3(groups), dim3(64 * T), 0, st, a);
+}
+
 template <int D>
 hipError_t launch_select_fast(const SelectArgs& a, hipStream_t st) {
-  if (a.k <= 32) {
-    constexpr int T = SelCfg<32>::kTiles;
-    const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
-    hipLaunchKernelGGL((select_fast_kernel<D, 32>), dim3(groups), dim3(64 * T), 0, st, a);
-  } else {
-    constexpr int T = SelCfg<64>::kTiles;
-    const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
-    hipLaunchKernelGGL((select_fast_kernel<D, 64>), dim3(groups), dim3(64 * T), 0, st, a);
-  }
+  if (a.k <= 32) launch_select_fast_k<D, 32>(a, st);
+  else launch_select_fast_k<D, 64>(a, st);
   return hipGetLastError();
 }
 

@@ -59,6 +59,10 @@ SMALL = [
     synth.PrefillConfig("bf16_d64_allchunks", 1, 2, 2048, 64, 64, 64, "bf16", 4, 128),
     synth.PrefillConfig("bf16_d128_noqcal", 1, 3, 640, 128, 64, 3, "bf16", 0, 0),
     synth.PrefillConfig("fp32_d128_k1", 1, 1, 512, 128, 64, 1, "fp32", 64, 128),
+    # the selection's Q-Cal forms at d = 128: rank above 32 (four 16-wide steps) and a rank that
+    # is not a multiple of 8 (element-wise loads)
+    synth.PrefillConfig("bf16_d128_r40", 1, 2, 2048, 128, 64, 16, "bf16", 40, 256),
+    synth.PrefillConfig("bf16_d128_r12_k40", 1, 2, 2048, 128, 64, 40, "bf16", 12, 256),
 ]
 
 

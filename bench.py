@@ -393,53 +393,16 @@ def bench_backward(P, cfg, o, dev):
                      "the forward's selection given; two timed calls")
 
 
-def length_sweep(lengths=(32768, 65536, 131072, 262144, 524288), reps=3):
-    """Prefill time against sequence length on the 128K workload's shape (H = 32, d = 128, k = 32,
-    Q-Cal r = 32, random-walk queries): stage times and algorithmic TFLOP/s per length.  The
-    scoring work grows as L^2 / C and the attention work as L * k * C."""
-    import dataclasses
+def length_sweep():
+    """The --sweep mode: length_sweep_from on the 512K random-walk workload's inputs, one JSON line
+    per length (HiLS prefill stages and this library's dense causal prefill of the same q, k, v)."""
     import torch
     from chunk_wise_sparse_amd import hils, synth
     hils.load()
     dev = torch.device("cuda:0")
-    base = synth.CONFIGS["prefill_128k"]
-    for L in lengths:
-        cfg = dataclasses.replace(base, name=f"prefill_{L // 1024}k_k32", seq_len=L)
-        P = synth.make_prefill_inputs_torch(cfg, dev)
-        o = torch.empty_like(P["q"])
-        ws = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
-        run = lambda e=None: hils.prefill(P["q"], P["k"], P["v"], P["lmk"], P["h"], P["w_down"], P["w_up"],
-                                          topk=cfg.topk, out=o, workspace=ws, events=e)
-        run()
-        ev = [hils.StageEvents(4) for _ in range(reps)]
-        for e in ev:
-            run(e)
-        torch.cuda.synchronize()
-        st = [sum(e.elapsed_ms(s, s + 1) for e in ev) / reps for s in range(3)]
-        w = prefill_work(cfg)
-        ms = sum(st)
-        # Context only: dense causal attention of the same shape through PyTorch's own
-        # scaled_dot_product_attention (not this library), timed with events on its stream.
-        dense_ms = None
-        try:
-            f = torch.nn.functional.scaled_dot_product_attention
-            f(P["q"], P["k"], P["v"], is_causal=True)
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record()
-            for _ in range(reps):
-                f(P["q"], P["k"], P["v"], is_causal=True)
-            a1.record()
-            torch.cuda.synchronize()
-            dense_ms = a0.elapsed_time(a1) / reps
-        except RuntimeError as ex:
-            print(f"[bench] dense attention at {L}: {ex}", file=sys.stderr, flush=True)
-        print(json.dumps(dict(seq_len=L, prefill_ms=ms, qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
-                              tflops=w["total"] / (ms * 1e-3) / 1e12,
-                              select_tflops=w["select"] / (st[1] * 1e-3) / 1e12,
-                              attention_tflops=w["attention"] / (st[2] * 1e-3) / 1e12,
-                              dense_causal_sdpa_ms=dense_ms)), flush=True)
-        del P, o, ws
-        torch.cuda.empty_cache()
+    P512 = synth.make_prefill_inputs_torch(synth.CONFIGS["prefill_512k_walk"], dev)
+    for row in length_sweep_from(P512):
+        print(json.dumps(row), flush=True)
 
 
 def main():
@@ -457,8 +420,8 @@ def main():
                     help="only run plain 1 GiB device copies (counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the prefill of the 128K workload's shape at 32K..512K tokens "
-                         "(one JSON line per length, with PyTorch's dense causal attention of the "
-                         "same shape for context) and exit")
+                         "(one JSON line per length, beside this library's dense causal prefill of "
+                         "the same q, k, v) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

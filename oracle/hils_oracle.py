@@ -49,6 +49,15 @@ Readings taken where the pages are silent:
      own chunk is causally truncated at the query;
   R9 decode: the new token's key/value are already in the cache; the query sits
      at position kv_len-1 and a partial last chunk is allowed.
+
+HoPE ([P3] "Engineering details", hierarchical positional encoding item: rotary position
+encoding on the dimensions inside the pre-training window, no position encoding beyond it):
+  R10 the rotary encoding rotates dimension pairs (2i, 2i+1) by the angle pos * theta_i with
+      theta_i = base^(-2i/d) (its original, interleaved form);
+  R11 a pair is inside the pre-training window when its wavelength 2 pi / theta_i is at most the
+      window's length in tokens; the other pairs are left as they are;
+  R12 the caller applies it to q and k before the attention (prefill rows at positions pos0 + i,
+      a decode query at kv_len - 1); landmarks and the Q-Cal offset see no position.
 """
 from __future__ import annotations
 
@@ -62,6 +71,7 @@ __all__ = [
     "select_top_k", "select_with_local", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
     "prefill", "decode", "attend_given_selection", "dense_attention_row", "dense_causal_rows",
     "dense_decode", "chunk_backward", "inter_chunk_backward", "prefill_backward",
+    "hope_rotated_pairs", "hope_rotate",
 ]
 
 
@@ -478,3 +488,36 @@ def prefill_backward(inp: Dict[str, np.ndarray], dout: np.ndarray, chunk: int, t
                 out["dw_down"] += np.outer(dt[b, i], inp["h"][b, i].astype(np.float64))
                 out["dh"][b, i] = w_down.astype(np.float64).T @ dt[b, i]
     return out
+
+
+# ------------------------------------------------------------------------------------------
+# HoPE ([P3] "Engineering details", hierarchical positional encoding item; R10-R12)
+# ------------------------------------------------------------------------------------------
+
+def hope_rotated_pairs(d: int, rope_base: float, train_len: int) -> np.ndarray:
+    """Indices i of the dimension pairs (2i, 2i+1) that carry the rotary encoding: those whose
+    wavelength 2 pi / theta_i, theta_i = base^(-2i/d), fits in the pre-training window (R10, R11)."""
+    out = []
+    for i in range(d // 2):
+        theta = float(rope_base) ** (-2.0 * i / d)
+        if 2.0 * math.pi / theta <= train_len:
+            out.append(i)
+    return np.asarray(out, dtype=np.int64)
+
+
+def hope_rotate(x: np.ndarray, positions, rope_base: float, train_len: int) -> np.ndarray:
+    """x [..., n, d]: row r (position positions[r]) with each pair of hope_rotated_pairs turned by
+    the angle pos * theta_i (float64); the other pairs unchanged."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    pos = np.broadcast_to(np.asarray(positions, dtype=np.float64), x.shape[-2:-1])
+    out = x.copy()
+    for i in hope_rotated_pairs(d, rope_base, train_len):
+        theta = float(rope_base) ** (-2.0 * i / d)
+        ang = pos * theta
+        c, s_ = np.cos(ang), np.sin(ang)
+        a, b = x[..., 2 * i], x[..., 2 * i + 1]
+        out[..., 2 * i] = a * c - b * s_
+        out[..., 2 * i + 1] = a * s_ + b * c
+    return out
+

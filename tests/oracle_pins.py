@@ -573,4 +573,65 @@ def pin_forced_local_rows():
     assert np.array_equal(dec["idx"], f["idx"]) and np.array_equal(dec["o"], f["o"])
 
 
+# HoPE ([P3] "Engineering details", hierarchical positional encoding item; R10-R12)
+
+def pin_hope_complex_rotation():
+    """With base 16 and d = 8 the pair frequencies are 1, 1/2, 1/4, 1/8 exactly; with a window
+    that holds every wavelength, pair i of a row at position p is the complex number x + iy
+    multiplied by exp(i p theta_i) (cmath, not the oracle's cos/sin)."""
+    import cmath
+    g = _rng(41)
+    x = g.standard_normal((3, 5, 8))
+    pos = np.array([0, 1, 7, 1000, 65535])
+    got = O.hope_rotate(x, pos, 16.0, 10 ** 6)
+    for r in range(5):
+        for i, theta in enumerate((1.0, 0.5, 0.25, 0.125)):
+            for b in range(3):
+                z = complex(x[b, r, 2 * i], x[b, r, 2 * i + 1]) * cmath.exp(1j * pos[r] * theta)
+                assert abs(got[b, r, 2 * i] - z.real) < 1e-9 and abs(got[b, r, 2 * i + 1] - z.imag) < 1e-9, (r, i)
+
+
+def pin_hope_relative_position():
+    """For the rotated pairs the product of a rotated query and key depends only on the key's
+    offset from the query; the unrotated pairs contribute the plain product."""
+    g = _rng(42)
+    d = 64
+    q, k = g.standard_normal(d), g.standard_normal(d)
+    base, win = 10000.0, 512
+    rot = O.hope_rotated_pairs(d, base, win)
+    assert 0 < len(rot) < d // 2
+    ref = None
+    for m in (0, 5, 77, 4096):
+        qm = O.hope_rotate(q[None], [m], base, win)[0]
+        kn = O.hope_rotate(k[None], [m + 9], base, win)[0]
+        v = float(qm @ kn)
+        ref = v if ref is None else ref
+        assert abs(v - ref) < 1e-9 * max(1.0, abs(ref)), (m, v, ref)
+    # dimensions left alone
+    keep = np.ones(d, dtype=bool)
+    for i in rot:
+        keep[2 * i:2 * i + 2] = False
+    qr = O.hope_rotate(q[None], [123], base, win)[0]
+    assert np.array_equal(qr[keep], q[keep])
+
+
+def pin_hope_window_split():
+    """Base 16, d = 8: wavelengths 2 pi, 4 pi, 8 pi and 16 pi tokens.  A 13-token window rotates
+    pairs 0 and 1 only, a 6-token window none (identity), a 51-token window all four; position 0
+    is the identity; every pair keeps its length."""
+    g = _rng(43)
+    x = g.standard_normal((4, 8))
+    pos = [1, 2, 3, 9]
+    assert list(O.hope_rotated_pairs(8, 16.0, 13)) == [0, 1]
+    assert list(O.hope_rotated_pairs(8, 16.0, 6)) == []
+    assert list(O.hope_rotated_pairs(8, 16.0, 51)) == [0, 1, 2, 3]
+    y = O.hope_rotate(x, pos, 16.0, 13)
+    assert np.array_equal(y[:, 4:], x[:, 4:]) and not np.allclose(y[:, :4], x[:, :4])
+    assert np.array_equal(O.hope_rotate(x, pos, 16.0, 6), x)
+    assert np.allclose(O.hope_rotate(x, [0, 0, 0, 0], 16.0, 51), x, atol=0, rtol=0)
+    z = O.hope_rotate(x, pos, 16.0, 51)
+    for i in range(4):
+        assert np.allclose(np.hypot(z[:, 2 * i], z[:, 2 * i + 1]), np.hypot(x[:, 2 * i], x[:, 2 * i + 1]), atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

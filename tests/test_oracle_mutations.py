@@ -107,7 +107,42 @@ def _local_drops_wrong_one(sigma, k):
     return out
 
 
+def _hope_half_split(x, positions, rope_base, train_len):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    pos = np.broadcast_to(np.asarray(positions, dtype=np.float64), x.shape[-2:-1])
+    out = x.copy()
+    for i in O.hope_rotated_pairs(d, rope_base, train_len):
+        ang = pos * float(rope_base) ** (-2.0 * i / d)
+        a, b = x[..., i], x[..., i + d // 2]
+        out[..., i] = a * np.cos(ang) - b * np.sin(ang)
+        out[..., i + d // 2] = a * np.sin(ang) + b * np.cos(ang)
+    return out
+
+
+def _hope_theta_exponent(x, positions, rope_base, train_len):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    pos = np.broadcast_to(np.asarray(positions, dtype=np.float64), x.shape[-2:-1])
+    out = x.copy()
+    for i in O.hope_rotated_pairs(d, rope_base, train_len):
+        ang = pos * float(rope_base) ** (-1.0 * i / d)
+        a, b = x[..., 2 * i], x[..., 2 * i + 1]
+        out[..., 2 * i] = a * np.cos(ang) - b * np.sin(ang)
+        out[..., 2 * i + 1] = a * np.sin(ang) + b * np.cos(ang)
+    return out
+
+
+def _hope_window_reversed(d, rope_base, train_len, _o=O.hope_rotated_pairs):
+    inside = set(int(i) for i in _o(d, rope_base, train_len))
+    return np.asarray([i for i in range(d // 2) if i not in inside], dtype=np.int64)
+
+
 MUTATIONS = {
+    "hope_rotation_reversed": ("hope_rotate", lambda x, p, b, t, _o=O.hope_rotate: _o(x, -np.asarray(p), b, t)),
+    "hope_half_split_pairs": ("hope_rotate", _hope_half_split),
+    "hope_theta_exponent": ("hope_rotate", _hope_theta_exponent),
+    "hope_window_reversed": ("hope_rotated_pairs", _hope_window_reversed),
     "forced_local_ignored": ("select_with_local", _local_not_forced),
     "forced_local_drops_wrong_chunk": ("select_with_local", _local_drops_wrong_one),
     "bwd_dsigma_not_centred": ("inter_chunk_backward", lambda w, dw, s: s * np.asarray(w) * np.asarray(dw)),

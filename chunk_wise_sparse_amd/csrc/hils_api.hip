@@ -11,6 +11,7 @@
 
 #include "hils.h"
 #include "hils_launch.h"
+#include "hope.h"
 
 namespace {
 
@@ -793,6 +794,42 @@ int hils_dense_prefill_fwd(const hils_dense_params* p, const void* q, const void
   else
     err = d == 64 ? hils::launch_dense_prefill<float, 64>(a, s) : hils::launch_dense_prefill<float, 128>(a, s);
   if (err != hipSuccess) return hip_fail(err, "hils_dense_prefill_fwd");
+  return HILS_OK;
+}
+
+int hils_hope_rotate(const hils_hope_params* p, void* x, const int32_t* positions, void* stream) {
+  g_last_error.clear();
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "params is NULL");
+  if (!x) return fail(HILS_ERR_INVALID_ARG, "x is NULL");
+  if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
+    return fail(HILS_ERR_INVALID_ARG, "batch, heads and seq_len must be positive");
+  if (p->dtype != HILS_DTYPE_BF16 && p->dtype != HILS_DTYPE_FP32)
+    return fail(HILS_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp32", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (!(p->rope_base > 1.f)) return fail(HILS_ERR_INVALID_ARG, "rope_base must be above 1");
+  if (p->train_len < 1) return fail(HILS_ERR_INVALID_ARG, "train_len must be positive");
+  if (!aligned16(x)) return fail(HILS_ERR_ALIGNMENT, "x is not 16-byte aligned");
+  hils::HopeArgs a;
+  a.x = x;
+  a.positions = positions;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.L = p->seq_len;
+  a.pos0 = p->pos0;
+  a.rotated = 0ull;
+  const int d = p->head_dim;
+  for (int i = 0; i < 64; ++i) {
+    a.theta[i] = i < d / 2 ? pow((double)p->rope_base, -2.0 * i / d) : 0.0;
+    if (i < d / 2 && 6.283185307179586476925286766559 / a.theta[i] <= (double)p->train_len) a.rotated |= 1ull << i;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (p->dtype == HILS_DTYPE_BF16)
+    err = d == 64 ? hils::launch_hope_rotate<hils::bf16, 64>(a, s) : hils::launch_hope_rotate<hils::bf16, 128>(a, s);
+  else
+    err = d == 64 ? hils::launch_hope_rotate<float, 64>(a, s) : hils::launch_hope_rotate<float, 128>(a, s);
+  if (err != hipSuccess) return hip_fail(err, "hils_hope_rotate");
   return HILS_OK;
 }
 

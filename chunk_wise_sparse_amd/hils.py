@@ -26,7 +26,8 @@ STATUS = {0: "HILS_OK", -1: "HILS_ERR_INVALID_ARG", -2: "HILS_ERR_UNSUPPORTED", 
 EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_workspace_size",
             "hils_prefill_fwd", "hils_decode_fwd", "hils_decode_fwd_noalloc", "hils_status_string",
             "hils_last_hip_error", "hils_dense_prefill_fwd", "hils_dense_decode_workspace_size",
-            "hils_dense_decode_fwd", "hils_prefill_bwd_workspace_size", "hils_prefill_bwd"]
+            "hils_dense_decode_fwd", "hils_prefill_bwd_workspace_size", "hils_prefill_bwd",
+            "hils_hope_rotate"]
 STATIC_SCRATCH_BYTES = 64 << 20   # HILS_STATIC_SCRATCH_BYTES
 
 
@@ -56,6 +57,12 @@ class DenseParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32)]
+
+
+class HopeParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_base", ctypes.c_float), ("train_len", ctypes.c_int32),
+                ("pos0", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,6 +99,8 @@ def load(path: str = LIB_PATH):
     lib.hils_dense_decode_workspace_size.restype = sz
     lib.hils_dense_decode_fwd.argtypes = [ctypes.POINTER(DenseParams)] + [vp] * 6 + [sz, vp]
     lib.hils_dense_decode_fwd.restype = i32
+    lib.hils_hope_rotate.argtypes = [ctypes.POINTER(HopeParams), vp, vp, vp]
+    lib.hils_hope_rotate.restype = i32
     lib.hils_prefill_bwd_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     lib.hils_prefill_bwd_workspace_size.restype = sz
     lib.hils_prefill_bwd.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17 + [vp, sz, vp]
@@ -346,3 +355,28 @@ def prefill_bwd(q, k, v, lmk, h, w_down, w_up, sel_idx, sel_w, dout, *, topk: in
                               _ptr(g.get("dw_up")), workspace.data_ptr(), need, _stream_handle(q.device))
     check(st, "hils_prefill_bwd")
     return g
+
+
+def hope_rotate(x, *, rope_base: float, train_len: int, pos0: int = 0, positions=None):
+    """HoPE in place on x [B, H, L, d] (q, or k with its key/value heads): pair (2i, 2i+1) of row i
+    of sequence b turned by (positions[b] or pos0, plus i) * rope_base^(-2i/d) when its wavelength
+    fits train_len tokens.  positions: int32 [B] on x's device, or None.  Returns x."""
+    import torch
+    lib = load()
+    if x.dim() == 3:                          # [B, H, d]: one row per (sequence, head)
+        x4 = x.unsqueeze(2)
+    else:
+        x4 = x
+    B, H, L, d = x4.shape
+    _require([("x", x)], x.device, x.dtype)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous: it is rotated in place")
+    if positions is not None and (positions.dtype != torch.int32 or positions.device != x.device
+                                  or not positions.is_contiguous() or positions.numel() != B):
+        raise ValueError("positions must be a contiguous int32 tensor of batch entries on x's device")
+    p = HopeParams(B, H, L, d, float(rope_base), int(train_len), int(pos0), _dtype_code(x))
+    st = lib.hils_hope_rotate(ctypes.byref(p), _ptr(x), None if positions is None else positions.data_ptr(),
+                              _stream_handle(x.device))
+    check(st, "hils_hope_rotate")
+    return x
+

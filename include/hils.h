@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 8
+#define HILS_ABI_VERSION 9
 
 typedef enum {
   HILS_OK = 0,
@@ -230,6 +230,28 @@ size_t hils_dense_decode_workspace_size(const hils_dense_params* p);
  * o [B, H, d]. */
 int hils_dense_decode_fwd(const hils_dense_params* p, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* kv_len, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* HoPE [HiLS explainer (molayo1419.me), "Engineering details", hierarchical positional encoding]:
+ * the rotary position encoding on the dimensions inside the pre-training window, none on the
+ * others.  Rotates x in place: dimension pair (2i, 2i+1) of a row at position p is turned by the
+ * angle p * theta_i, theta_i = rope_base^(-2i / head_dim), when its wavelength 2 pi / theta_i is at
+ * most train_len tokens; the other pairs are left as they are.  The caller applies it to q and to
+ * k before the attention calls (landmarks and the Q-Cal offset see no position), for decode to
+ * the new query and to each key as it enters the cache.
+ * x [batch, heads, seq_len, head_dim] on the device, 16-byte aligned (q, or k with heads = the
+ * key/value heads).  Row i of sequence b sits at position positions[b] + i when positions (int32
+ * [batch], on the device) is given, else at pos0 + i; a decode query takes seq_len = 1 and
+ * positions = kv_len - 1.  Angles are reduced modulo 2 pi in fp64, the rotation runs in fp32 and
+ * each element is rounded once to the dtype.  Supported: head_dim in {64, 128}; rope_base > 1;
+ * train_len >= 1.  Errors as for the other calls; nothing is enqueued on an error. */
+typedef struct hils_hope_params {
+  int32_t batch, heads, seq_len, head_dim;
+  float rope_base;             /* base of the rotary frequencies (for example 10000) */
+  int32_t train_len;           /* pre-training window in tokens */
+  int32_t pos0;                /* position of row 0 when positions is NULL */
+  int32_t dtype;               /* hils_dtype */
+} hils_hope_params;
+int hils_hope_rotate(const hils_hope_params* p, void* x, const int32_t* positions, void* stream);
 
 /* hils_decode_fwd for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops and harnesses that forbid hipMalloc.  The arguments are those of

@@ -52,12 +52,12 @@ Readings taken where the pages are silent:
 
 HoPE ([P3] "Engineering details", hierarchical positional encoding item: rotary position
 encoding on the dimensions inside the pre-training window, no position encoding beyond it):
-  R10 the rotary encoding rotates dimension pairs (2i, 2i+1) by the angle pos * theta_i with
-      theta_i = base^(-2i/d) (its original, interleaved form);
-  R11 a pair is inside the pre-training window when its wavelength 2 pi / theta_i is at most the
-      window's length in tokens; the other pairs are left as they are;
-  R12 the caller applies it to q and k before the attention (prefill rows at positions pos0 + i,
-      a decode query at kv_len - 1); landmarks and the Q-Cal offset see no position.
+  H1 the rotary encoding rotates dimension pairs (2i, 2i+1) by the angle pos * theta_i with
+     theta_i = base^(-2i/d) (its original, interleaved form);
+  H2 a pair is inside the pre-training window when its wavelength 2 pi / theta_i is at most the
+     window's length in tokens; the other pairs are left as they are;
+  H3 the caller applies it to q and k before the attention (prefill rows at positions pos0 + i,
+     a decode query at kv_len - 1); landmarks and the Q-Cal offset see no position.
 """
 from __future__ import annotations
 
@@ -491,12 +491,12 @@ def prefill_backward(inp: Dict[str, np.ndarray], dout: np.ndarray, chunk: int, t
 
 
 # ------------------------------------------------------------------------------------------
-# HoPE ([P3] "Engineering details", hierarchical positional encoding item; R10-R12)
+# HoPE ([P3] "Engineering details", hierarchical positional encoding item; H1-H3)
 # ------------------------------------------------------------------------------------------
 
 def hope_rotated_pairs(d: int, rope_base: float, train_len: int) -> np.ndarray:
     """Indices i of the dimension pairs (2i, 2i+1) that carry the rotary encoding: those whose
-    wavelength 2 pi / theta_i, theta_i = base^(-2i/d), fits in the pre-training window (R10, R11)."""
+    wavelength 2 pi / theta_i, theta_i = base^(-2i/d), fits in the pre-training window (H1, H2)."""
     out = []
     for i in range(d // 2):
         theta = float(rope_base) ** (-2.0 * i / d)

@@ -573,7 +573,7 @@ def pin_forced_local_rows():
     assert np.array_equal(dec["idx"], f["idx"]) and np.array_equal(dec["o"], f["o"])
 
 
-# HoPE ([P3] "Engineering details", hierarchical positional encoding item; R10-R12)
+# HoPE ([P3] "Engineering details", hierarchical positional encoding item; H1-H3)
 
 def pin_hope_complex_rotation():
     """With base 16 and d = 8 the pair frequencies are 1, 1/2, 1/4, 1/8 exactly; with a window

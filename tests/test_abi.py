@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 8
+    assert lib.hils_abi_version() == 9
 
 
 def _pp(**kw):
@@ -190,3 +190,23 @@ def test_prefill_paged_rejects_bad_tables():
     assert _prefill(lib, _pp(seq_len=2000, block_table=bt, block_table_stride=32, num_pages=100)) == -2
     assert lib.hils_prefill_bwd_workspace_size(ctypes.byref(_pp(block_table=bt, block_table_stride=32,
                                                                  num_pages=100))) == 0
+
+
+def test_hope_rejects_bad_arguments():
+    lib = hils.load()
+
+    def call(p, x=FAKE):
+        return lib.hils_hope_rotate(ctypes.byref(p) if p is not None else None, x, None, None)
+
+    good = dict(batch=1, heads=2, seq_len=64, head_dim=128, rope_base=10000.0, train_len=4096, pos0=0,
+                dtype=hils.DTYPE_BF16)
+    mk = lambda **o: hils.HopeParams(**dict(good, **o))
+    assert call(None) == -1
+    assert call(mk(), x=None) == -1
+    assert call(mk(batch=0)) == -1
+    assert call(mk(head_dim=96)) == -2
+    assert call(mk(dtype=7)) == -2
+    assert call(mk(rope_base=1.0)) == -1
+    assert call(mk(train_len=0)) == -1
+    assert call(mk(), x=FAKE + 4) == -3
+

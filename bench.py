@@ -611,6 +611,18 @@ def main():
                 dense_over_hils=dd_ms / (dec_ms / K),
                 note="this library's dense attention of the same 8 x 32 queries over the whole 512K caches")
         extras["backward_128k"] = bench_backward(P, pcfg, o, dev)
+        # HoPE rotation of the 128K workload's q and k (a copy, rotated in place): bytes read and
+        # written once each.
+        qk = torch.cat([P["q"], P["k"]], dim=1).contiguous()
+        hope = lambda: hils.hope_rotate(qk, rope_base=10000.0, train_len=4096)
+        hope()
+        hope_ms = event_ms(hope, 5)
+        hb = 2 * qk.numel() * qk.element_size()
+        extras["hope_128k"] = dict(ms=hope_ms, GBps=hb / (hope_ms * 1e-3) / 1e9,
+                                   frac_hbm=hb / (hope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                   note="HoPE (base 10000, 4096-token window) on q and k of prefill_128k, "
+                                        "rotated in place: 2 x 2 GiB moved")
+        del qk
         print("[bench] extras: prefill_32k", file=sys.stderr, flush=True)
         scfg = synth.CONFIGS["prefill_32k"]
         P32 = synth.make_prefill_inputs_torch(scfg, dev)

@@ -1,0 +1,28 @@
+// Chunk sizes other than 64 (gchunk.hip), called by the C ABI in hils_api.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+constexpr int kGcMaxChunks = 8192;             // chunks per sequence (scores kept in LDS)
+
+struct GcArgs {
+  const void* q;             // prefill [B, H, Lq, d]; decode [B, H, d] (Lq = 1)
+  const void* key;           // [B, Hk, Lkv, d]
+  const void* val;           // [B, Hk, Lkv, d]
+  const void* lmk;           // [B, Hk, N, d], N = ceil(Lkv / C)
+  const void* w_up;          // [H * d, r] (r > 0)
+  const float* tcode;        // Q-Cal code rows, tstride floats apart (r > 0)
+  void* o;                   // like q
+  int32_t* idx;              // [B, H, Lq, k]
+  float* w;                  // [B, H, Lq, k]
+  const int32_t* kv_len;     // decode: [B], the query at kv_len - 1 (clamped to [1, Lkv]); prefill: NULL
+  int B, H, G, Lq, Lkv, N, C, k, r, tstride, force_local;
+  float scale;
+};
+
+template <typename T, int D>
+hipError_t launch_gchunk(const GcArgs& a, hipStream_t st);
+
+}  // namespace hils

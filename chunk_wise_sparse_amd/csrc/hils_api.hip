@@ -11,6 +11,7 @@
 
 #include "hils.h"
 #include "hils_launch.h"
+#include "gchunk.h"
 #include "hope.h"
 
 namespace {
@@ -65,11 +66,17 @@ int check_prefill_params(const hils_prefill_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "dtype %d is not supported", p->dtype);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(HILS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
-  if (p->chunk != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (64)", p->chunk);
+  if (p->chunk != 64 && p->chunk != 32 && p->chunk != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (32, 64 or 128)", p->chunk);
   if (p->topk < 1 || p->topk > 64)
     return fail(HILS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", p->topk);
   if ((p->seq_len + 63) / 64 > 65535)
     return fail(HILS_ERR_UNSUPPORTED, "more than 65535 chunks per sequence");
+  if (p->chunk != 64) {
+    if ((p->seq_len + p->chunk - 1) / p->chunk > hils::kGcMaxChunks)
+      return fail(HILS_ERR_UNSUPPORTED, "chunk %d: at most %d chunks per sequence", p->chunk, hils::kGcMaxChunks);
+    if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need chunk 64 (one page per chunk)");
+  }
   if (p->q_tile != 0 && p->q_tile != 16 && p->q_tile != 32 && p->q_tile != 64 && p->q_tile != 128)
     return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (16, 32, 64 or 128)", p->q_tile);
   if (p->qcal_rank < 0 || p->qcal_rank > 64)
@@ -192,8 +199,59 @@ PadLayout pad_layout(const hils_prefill_params* p) {
   return P;
 }
 
+// Chunk sizes other than 64: the Q-Cal code and the selection (when not returned) only.
+PrefillLayout gchunk_layout(const hils_prefill_params* p, bool with_sel) {
+  hils_prefill_params pp = *p;
+  pp.attn_mode = HILS_ATTN_UNION;
+  return prefill_layout(&pp, with_sel);
+}
+
 size_t prefill_workspace_bytes(const hils_prefill_params* p, bool with_sel) {
+  if (p->chunk != 64) return gchunk_layout(p, with_sel).total;
   return p->seq_len % 64 == 0 ? prefill_layout(p, with_sel).total : pad_layout(p).total;
+}
+
+template <typename T>
+hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const void* k, const void* v,
+                              const void* lmk, const void* h, const void* w_down, const void* w_up, void* o,
+                              int32_t* idx, float* w, float* tcode, hipStream_t st) {
+  hipError_t e;
+  hipEvent_t* ev = p->n_stage_events >= 4 ? (hipEvent_t*)p->stage_events : nullptr;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if (p->qcal_rank > 0) {
+    e = hils::launch_prefill_qcal_code<T>(static_cast<const T*>(h), static_cast<const T*>(w_down), tcode,
+                                          p->batch * p->seq_len, p->hidden, p->qcal_rank, st);
+    if (e != hipSuccess) return e;
+  }
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  hils::GcArgs a;
+  a.q = q;
+  a.key = k;
+  a.val = v;
+  a.lmk = lmk;
+  a.w_up = w_up;
+  a.tcode = tcode;
+  a.o = o;
+  a.idx = idx;
+  a.w = w;
+  a.kv_len = nullptr;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.Lq = a.Lkv = p->seq_len;
+  a.C = p->chunk;
+  a.N = (p->seq_len + p->chunk - 1) / p->chunk;
+  a.k = p->topk;
+  a.r = p->qcal_rank;
+  a.tstride = p->qcal_rank;
+  a.force_local = p->force_local;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
+  if (e != hipSuccess) return e;
+  // selection and attention run in one kernel: their two stage marks coincide
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 template <typename T, int D>
@@ -339,7 +397,13 @@ int check_decode_params(const hils_decode_params* p) {
     return fail(HILS_ERR_UNSUPPORTED, "dtype %d is not supported", p->dtype);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(HILS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
-  if (p->chunk != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (64)", p->chunk);
+  if (p->chunk != 64 && p->chunk != 32 && p->chunk != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (32, 64 or 128)", p->chunk);
+  if (p->chunk != 64) {
+    if ((p->max_kv_len + p->chunk - 1) / p->chunk > hils::kGcMaxChunks)
+      return fail(HILS_ERR_UNSUPPORTED, "chunk %d: at most %d chunks per sequence", p->chunk, hils::kGcMaxChunks);
+    if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "a paged cache needs chunk 64 (one page per chunk)");
+  }
   if (p->topk < 1 || p->topk > 64)
     return fail(HILS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", p->topk);
   if ((p->max_kv_len + 63) / 64 > 65535)
@@ -370,6 +434,15 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   size_t off = 0;
   L.tcode = off;
   off += align_up(B * (size_t)(p->qcal_rank > 0 ? hils::kTcodeStride : 0) * sizeof(float));
+  if (p->chunk != 64) {                        // chunk sizes 32 and 128: the code and the selection
+    L.scores = L.cand = L.partial = off;
+    L.idx = off;
+    if (!with_sel) off += align_up(B * H * k * sizeof(int32_t));
+    L.w = off;
+    if (!with_sel) off += align_up(B * H * k * sizeof(float));
+    L.total = off;
+    return L;
+  }
   const int qb = hils::decode_score_qb((int)(B * H), (int)N);
   const size_t stride = hils::decode_score_stride((int)N, qb);   // landmarks per pair, padded
   L.scores = L.cand = off;
@@ -388,6 +461,52 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   off += align_up(B * H * k * d * sizeof(float));
   L.total = off;
   return L;
+}
+
+template <typename T>
+hipError_t run_decode_gchunk(const hils_decode_params* p, const void* q, const void* kc, const void* vc,
+                             const void* lmk, const int32_t* kv_len, const void* h, const void* w_down,
+                             const void* w_up, void* o, int32_t* idx, float* w, char* ws,
+                             const DecodeLayout& L, hipStream_t st) {
+  hipError_t e;
+  hipEvent_t* ev = p->n_stage_events >= 5 ? (hipEvent_t*)p->stage_events : nullptr;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  float* tcode = reinterpret_cast<float*>(ws + L.tcode);
+  if (p->qcal_rank > 0) {
+    e = hils::launch_decode_tcode<T>(static_cast<const T*>(h), static_cast<const T*>(w_down), tcode, p->batch,
+                                     p->hidden, p->qcal_rank, st);
+    if (e != hipSuccess) return e;
+  }
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  hils::GcArgs a;
+  a.q = q;
+  a.key = kc;
+  a.val = vc;
+  a.lmk = lmk;
+  a.w_up = w_up;
+  a.tcode = tcode;
+  a.o = o;
+  a.idx = idx;
+  a.w = w;
+  a.kv_len = kv_len;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  a.Lq = 1;
+  a.Lkv = p->max_kv_len;
+  a.C = p->chunk;
+  a.N = (p->max_kv_len + p->chunk - 1) / p->chunk;
+  a.k = p->topk;
+  a.r = p->qcal_rank;
+  a.tstride = hils::kTcodeStride;
+  a.force_local = p->force_local;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
+  if (e != hipSuccess) return e;
+  // scan, selection and attention run in one kernel: their stage marks coincide
+  for (int i = 2; ev && i < 5; ++i)
+    if ((e = hipEventRecord(ev[i], st)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 template <typename T, int D>
@@ -515,7 +634,7 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
   const size_t kvb = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * S * d * e;
   const Range in[] = {{q, B * H * S * d * e, "q"},   {k, kvb, "k"},
-                      {v, kvb, "v"},  {lmk, B * Hk * ((S + 63) / 64) * d * e, "lmk"},
+                      {v, kvb, "v"},  {lmk, B * Hk * ((S + p->chunk - 1) / p->chunk) * d * e, "lmk"},
                       {p->block_table, p->block_table ? B * (size_t)p->block_table_stride * 4 : 0, "block_table"},
                       {h, qcal ? B * S * D * e : 0, "h"}, {w_down, qcal ? r * D * e : 0, "w_down"},
                       {w_up, qcal ? H * d * r * e : 0, "w_up"}};
@@ -530,7 +649,7 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
       if (&a != &b && overlap(a, b)) return fail(HILS_ERR_INVALID_ARG, "%s overlaps %s", a.name, b.name);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->attn_mode == HILS_ATTN_AUTO) {
+  if (p->attn_mode == HILS_ATTN_AUTO && p->chunk == 64) {   // (other chunk sizes take no mode)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     const hipError_t ce = hipStreamIsCapturing(s, &cs);
     if (ce != hipSuccess) return hip_fail(ce, "hils_prefill_fwd: hipStreamIsCapturing");
@@ -539,6 +658,17 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   }
   char* ws = static_cast<char*>(workspace);
   hipError_t err = hipSuccess;
+  if (p->chunk != 64) {                        // any seq_len: partial last chunks need no padding
+    const PrefillLayout G = gchunk_layout(p, with_sel);
+    int32_t* gidx = with_sel ? sel_idx : reinterpret_cast<int32_t*>(ws + G.idx);
+    float* gw = with_sel ? sel_w : reinterpret_cast<float*>(ws + G.w);
+    float* gt = qcal ? reinterpret_cast<float*>(ws + G.tcode) : nullptr;
+    err = p->dtype == HILS_DTYPE_BF16
+              ? run_prefill_gchunk<hils::bf16>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, s)
+              : run_prefill_gchunk<float>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, s);
+    if (err != hipSuccess) return hip_fail(err, "hils_prefill_fwd");
+    return HILS_OK;
+  }
   const bool padded = p->seq_len % 64 != 0;
   hils_prefill_params pp = *p;
   PrefillLayout L;
@@ -622,7 +752,7 @@ int decode_entry(const hils_decode_params* p, const void* q, const void* k_cache
     return fail(HILS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
   const size_t e = elem_bytes(p->dtype);
   const size_t B = p->batch, H = p->heads, Lm = p->max_kv_len, d = p->head_dim, kk = p->topk;
-  const size_t N = (Lm + 63) / 64, r = p->qcal_rank, D = p->hidden;
+  const size_t N = (Lm + p->chunk - 1) / p->chunk, r = p->qcal_rank, D = p->hidden;
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
   const size_t cache = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * Lm * d * e;
   if (p->block_table && ((uintptr_t)p->block_table & 3))
@@ -647,7 +777,11 @@ int decode_entry(const hils_decode_params* p, const void* q, const void* k_cache
   float* w = with_sel ? sel_w : reinterpret_cast<float*>(ws + L.w);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (p->dtype == HILS_DTYPE_BF16) {
+  if (p->chunk != 64) {
+    err = p->dtype == HILS_DTYPE_BF16
+              ? run_decode_gchunk<hils::bf16>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
+              : run_decode_gchunk<float>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
+  } else if (p->dtype == HILS_DTYPE_BF16) {
     err = p->head_dim == 64
               ? run_decode<hils::bf16, 64>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
               : run_decode<hils::bf16, 128>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
@@ -920,6 +1054,7 @@ BwdLayout bwd_layout(const hils_prefill_params* p) {
 int check_bwd_params(const hils_prefill_params* p) {
   int st = check_prefill_params(p);
   if (st != HILS_OK) return st;
+  if (p->chunk != 64) return fail(HILS_ERR_UNSUPPORTED, "the backward pass needs chunk 64");
   if (p->seq_len % 64 != 0)
     return fail(HILS_ERR_UNSUPPORTED, "the backward pass needs seq_len a multiple of the chunk (64)");
   if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "the backward pass takes contiguous keys and values");

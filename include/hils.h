@@ -54,10 +54,15 @@ typedef enum {
 
 typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
 
-/* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk == 64;
+/* Prefill over a whole sequence.  Supported: head_dim in {64, 128}; chunk in {32, 64, 128};
  * 1 <= topk <= 64; 1 <= seq_len with ceil(seq_len / chunk) <= 65535; 0 <= qcal_rank <= 64;
  * hidden a positive multiple of 128 when qcal_rank > 0.
  * scale <= 0 selects 1/sqrt(head_dim).
+ * Chunk sizes 32 and 128 take a generic path (one kernel after the Q-Cal code, no MFMA; the
+ * MFMA kernels below are built around 64-key chunks): at most 8192 chunks, contiguous keys and
+ * values only (no block_table), any seq_len without padding, and attn_mode and q_tile ignored;
+ * stage events 2 and 3 are then recorded together after that kernel.  The backward pass takes
+ * chunk == 64 only.
  * A partial last chunk (seq_len % chunk != 0) is allowed: lmk then holds ceil(seq_len / chunk)
  * landmarks, the last one for the partial chunk, and the call stages q, k, v, h and o padded to
  * whole chunks in the workspace (the padded rows are zero and come after every real row, so no
@@ -120,9 +125,11 @@ typedef struct hils_prefill_params {
 
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a
  * key/value cache of capacity max_kv_len (the new token's key and value are already stored).
- * Supported: head_dim in {64, 128}; chunk == 64; 1 <= topk <= 64;
+ * Supported: head_dim in {64, 128}; chunk in {32, 64, 128}; 1 <= topk <= 64;
  * 1 <= max_kv_len <= 65535 * chunk; 0 <= qcal_rank <= 64; hidden a positive multiple of 128
- * when qcal_rank > 0.  A partial last chunk is allowed.  With at least 5 stage events, event 0 is
+ * when qcal_rank > 0.  A partial last chunk is allowed.  Chunk sizes 32 and 128 take the generic
+ * path described for prefill (at most 8192 chunks, no block_table; stage events 2..4 recorded
+ * together after its one kernel).  With at least 5 stage events, event 0 is
  * recorded first and events 1..4 after the Q-Cal, landmark-scoring, selection and
  * chunk-attention stages; for bf16 with batch*heads >= 256 and at most 8192 chunks these three
  * stages run as one kernel, and events 2..4 are recorded together after it. */

@@ -53,7 +53,8 @@ def _prefill(lib, p, ptrs=None, ws=FAKE, wsb=1 << 40, **over):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=96), -2), (dict(chunk=32), -2), (dict(topk=0), -2), (dict(topk=65), -2),
+    (dict(head_dim=96), -2), (dict(chunk=48), -2), (dict(chunk=256), -2), (dict(topk=0), -2), (dict(topk=65), -2),
+    (dict(chunk=32, seq_len=32 * 8192 + 1), -2),              # other chunk sizes: at most 8192 chunks
     (dict(seq_len=64 * 65535 + 1), -2), (dict(q_tile=48), -2), (dict(q_tile=256), -2), (dict(qcal_rank=65), -2), (dict(hidden=100), -2),
     (dict(dtype=7), -2), (dict(batch=0), -1), (dict(heads=-1), -1), (dict(scale=float("nan")), -1),
     (dict(seq_len=64 * 65536), -2), (dict(n_stage_events=3), -1), (dict(attn_mode=3), -2),
@@ -209,4 +210,23 @@ def test_hope_rejects_bad_arguments():
     assert call(mk(rope_base=1.0)) == -1
     assert call(mk(train_len=0)) == -1
     assert call(mk(), x=FAKE + 4) == -3
+
+
+def test_other_chunk_sizes_accepted():
+    """Chunk sizes 32 and 128 (any sequence length, up to 8192 chunks): the workspace holds the
+    Q-Cal code and, when not returned, the selection; no paged keys/values and no backward."""
+    lib = hils.load()
+    a256 = lambda x: (x + 255) // 256 * 256
+    for C in (32, 128):
+        p = _pp(chunk=C, seq_len=1000)
+        t = a256(1 * 1000 * 8 * 4)
+        sel = a256(1 * 2 * 1000 * 4 * 4)
+        assert lib.hils_prefill_workspace_size(ctypes.byref(p), 0) == t + 2 * sel
+        assert lib.hils_prefill_workspace_size(ctypes.byref(p), 1) == t
+        assert lib.hils_prefill_bwd_workspace_size(ctypes.byref(p)) == 0       # the backward needs chunk 64
+        assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C)), 1) > 0
+        pb = _pp(chunk=C, block_table=FAKE, block_table_stride=64, num_pages=64)
+        assert lib.hils_prefill_workspace_size(ctypes.byref(pb), 1) == 0       # paged needs chunk 64
+        assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C, block_table=FAKE, block_table_stride=64,
+                                                               num_pages=64)), 1) == 0
 

@@ -1,0 +1,116 @@
+"""Chunk sizes 32 and 128 (the generic one-wave-per-row path) in prefill and decode, through the
+C ABI, against the oracle: every row of small prefills (ragged last chunk, GQA, forced local
+chunk), and ragged decode batches."""
+import math
+
+import numpy as np
+import pytest
+
+from chunk_wise_sparse_amd import synth
+from oracle import hils_oracle as O
+from parity import assert_within, check_rows, sample_rows
+import test_gpu_decode as TD
+import test_gpu_prefill as TP
+from test_gpu_gqa import _split
+
+pytestmark = pytest.mark.gpu
+
+
+def _ranked(res, own):
+    for key, r in res.items():
+        rs = np.array(r["sigma"], dtype=np.float64)
+        rs[own(key)] = np.inf
+        r["rank_sigma"] = rs
+    return res
+
+
+PREFILL = [
+    # (config, kv-head group size G, forced local chunk)
+    (synth.PrefillConfig("c32_bf16_d128_L1000", 1, 2, 1000, 128, 32, 8, "bf16", 16, 256), 1, False),
+    (synth.PrefillConfig("c32_bf16_d64_k64", 1, 2, 4096, 64, 32, 64, "bf16", 8, 128), 1, False),
+    (synth.PrefillConfig("c32_fp32_d64_noqcal", 2, 2, 333, 64, 32, 3, "fp32", 0, 0), 1, False),
+    (synth.PrefillConfig("c128_fp32_d64_L777", 1, 2, 777, 64, 128, 4, "fp32", 8, 128), 1, False),
+    (synth.PrefillConfig("c128_bf16_d128_walk", 1, 2, 4096, 128, 128, 8, "bf16", 32, 512, q_mode="walk"),
+     1, False),
+    (synth.PrefillConfig("c128_bf16_d128_g4", 1, 8, 2048, 128, 128, 4, "bf16", 16, 256), 4, False),
+    (synth.PrefillConfig("c32_bf16_d128_local", 1, 2, 2048, 128, 32, 8, "bf16", 16, 256), 1, True),
+    (synth.PrefillConfig("c128_fp32_d64_local", 1, 2, 1500, 64, 128, 3, "fp32", 8, 128), 1, True),
+]
+
+
+@pytest.mark.parametrize("cfg,G,local", PREFILL, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_prefill_chunk_size(lib, cfg, G, local):
+    import oracle_pool
+    print(f"[case] prefill chunk={cfg.chunk} G={G} local={local} {cfg}", flush=True)
+    inp = synth.make_prefill_inputs_np(cfg)
+    sub, full = _split(inp, G, ("k", "v", "lmk")) if G > 1 else (inp, inp)
+    o, idx, w = TP._run(lib, TP._to_dev(sub, cfg.dtype), cfg, chunk=cfg.chunk, force_local=local)
+    TP._torch().cuda.synchronize()
+    C = cfg.chunk
+    idx_np = idx.cpu().numpy()
+    for i in range(cfg.seq_len):
+        sel = idx_np[:, :, i]
+        nsel = min(cfg.topk, i // C + 1)
+        assert np.all((sel[..., :nsel] >= 0) & (sel[..., :nsel] <= i // C)), i
+        assert np.all(sel[..., nsel:] == -1), i
+        if local:
+            assert np.all(np.any(sel == i // C, axis=-1)), i
+    rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.seq_len)]
+    if len(rows) > 6000:
+        rows = sample_rows(cfg.batch, cfg.heads, cfg.seq_len, 1024, seed=41)
+    if not local:
+        TP._compare(full, cfg, o, idx, w, rows)
+        return
+    res = _ranked(oracle_pool.prefill_rows(full, rows, C, cfg.topk, cfg.dtype, force_local=True),
+                  lambda key: key[2] // C)
+    o_np, w_np = o.float().cpu().numpy(), w.cpu().numpy()
+    stats = check_rows(res, {r: o_np[r] for r in res}, {r: idx_np[r] for r in res}, {r: w_np[r] for r in res},
+                       cfg.dtype, lambda key: (full["q"][key], full["k"][key[0], key[1]], full["v"][key[0], key[1]]),
+                       C, 1.0 / math.sqrt(cfg.head_dim))
+    print(f"[parity] {cfg.name}: {stats}", flush=True)
+    assert_within(stats, cfg.dtype)
+
+
+DECODE = [
+    (synth.DecodeConfig("c32_dec_fp32_ragged", 3, 2, 3000, 64, 32, 4, "fp32", 8, 128, kv_len=(3000, 1500, 1)),
+     1, False),
+    (synth.DecodeConfig("c32_dec_bf16_d128_k64", 2, 4, 8000, 128, 32, 64, "bf16", 32, 512, kv_len=(8000, 2049)),
+     1, False),
+    (synth.DecodeConfig("c128_dec_bf16_needles", 2, 4, 30000, 64, 128, 16, "bf16", 16, 256,
+                        kv_len=(30000, 29937), needles=4), 1, False),
+    (synth.DecodeConfig("c128_dec_bf16_g4", 2, 8, 5000, 128, 128, 8, "bf16", 16, 256, kv_len=(5000, 129)), 4, False),
+    (synth.DecodeConfig("c32_dec_bf16_local", 3, 2, 4000, 128, 32, 8, "bf16", 16, 256, kv_len=(4000, 31, 33)),
+     1, True),
+    (synth.DecodeConfig("c128_dec_fp32_local", 2, 2, 3000, 64, 128, 4, "fp32", 0, 0, kv_len=(3000, 700)), 1, True),
+]
+
+
+@pytest.mark.parametrize("cfg,G,local", DECODE, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_decode_chunk_size(lib, cfg, G, local):
+    from chunk_wise_sparse_amd import hils
+    print(f"[case] decode chunk={cfg.chunk} G={G} local={local} {cfg}", flush=True)
+    inp = synth.make_decode_inputs_np(cfg)
+    sub, full = _split(inp, G, ("k_cache", "v_cache", "lmk")) if G > 1 else (inp, inp)
+    dev = TD._to_dev(sub, cfg.dtype)
+    o, idx, w = hils.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["lmk"], dev["kv_len"], dev.get("h"),
+                            dev.get("w_down"), dev.get("w_up"), topk=cfg.topk, chunk=cfg.chunk,
+                            return_selection=True, force_local=local)
+    TD._torch().cuda.synchronize()
+    C = cfg.chunk
+    pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    res = O.decode(full, C, cfg.topk, cfg.dtype, pairs=pairs, force_local=local)
+    if local:
+        res = _ranked(res, lambda key: (int(inp["kv_len"][key[0]]) - 1) // C)
+    o_np, idx_np, w_np = o.float().cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    for (b, h) in pairs:
+        own = (int(inp["kv_len"][b]) - 1) // C
+        nsel = min(cfg.topk, own + 1)
+        assert np.all(idx_np[b, h, nsel:] == -1), (b, h)
+        if local:
+            assert own in set(idx_np[b, h]), (b, h)
+    stats = check_rows(res, {p: o_np[p] for p in res}, {p: idx_np[p] for p in res}, {p: w_np[p] for p in res},
+                       cfg.dtype, lambda p: (full["q"][p], full["k_cache"][p], full["v_cache"][p]), C,
+                       1.0 / math.sqrt(cfg.head_dim), row_pos=lambda p: int(inp["kv_len"][p[0]]) - 1)
+    print(f"[parity] {cfg.name}: {stats['n_rows']} (b,h), max|do| {stats['max_abs']:.3g}, "
+          f"max|dw| {stats['max_w']:.3g}, near-tie swaps {stats['n_diff_sel']}", flush=True)
+    assert_within(stats, cfg.dtype)

@@ -11,6 +11,7 @@ Inputs are resident in HBM before timing starts.  `value` is the prefill's algor
 Printed: one JSON line (rank 0).  python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -340,7 +341,6 @@ def bench_512k(dev):
 def length_sweep_from(P512, lengths=(32768, 65536, 131072, 262144, 524288)):
     """HiLS prefill (k = 32, the 128K workload's shape) and this library's dense causal attention
     on the first L tokens of the 512K random-walk workload, L = 32K..512K."""
-    import dataclasses
     import torch
     from chunk_wise_sparse_amd import hils, synth
     base = synth.CONFIGS["prefill_128k"]
@@ -633,6 +633,16 @@ def main():
                                      attn_mode="auto")
         time_prefill(P32, scfg, 1)
         extras["prefill_32k"]["union_walk"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
+        # the same workload at chunk sizes 32 and 128 (the generic one-kernel path; its selection
+        # and attention run in one kernel, so the whole time sits in one stage)
+        for C in (32, 128):
+            ccfg = dataclasses.replace(scfg, chunk=C, name=f"prefill_32k_chunk{C}")
+            PC = synth.make_prefill_inputs_torch(ccfg, dev)
+            time_prefill(PC, ccfg, 1, chunk=C)
+            st = time_prefill(PC, ccfg, 3, chunk=C)
+            extras[f"prefill_32k_chunk{C}"] = dict(
+                prefill_ms=sum(st), qcal_code_ms=st[0], tflops=prefill_work(ccfg)["total"] / (sum(st) * 1e-3) / 1e12)
+            del PC
         extras["prefill_512k"], P512 = bench_512k(dev)
         print("[bench] extras: length sweep 32K..512K", file=sys.stderr, flush=True)
         extras["length_sweep"] = length_sweep_from(P512)

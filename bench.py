@@ -633,15 +633,16 @@ def main():
                                      attn_mode="auto")
         time_prefill(P32, scfg, 1)
         extras["prefill_32k"]["union_walk"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
-        # the same workload at chunk sizes 32 and 128 (the generic one-kernel path; its selection
-        # and attention run in one kernel, so the whole time sits in one stage)
+        # the same workload at chunk sizes 32 and 128 (selection in the generic kernel, attention
+        # in the chunk-major MFMA kernels)
         for C in (32, 128):
             ccfg = dataclasses.replace(scfg, chunk=C, name=f"prefill_32k_chunk{C}")
             PC = synth.make_prefill_inputs_torch(ccfg, dev)
             time_prefill(PC, ccfg, 1, chunk=C)
             st = time_prefill(PC, ccfg, 3, chunk=C)
             extras[f"prefill_32k_chunk{C}"] = dict(
-                prefill_ms=sum(st), qcal_code_ms=st[0], tflops=prefill_work(ccfg)["total"] / (sum(st) * 1e-3) / 1e12)
+                prefill_ms=sum(st), qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
+                tflops=prefill_work(ccfg)["total"] / (sum(st) * 1e-3) / 1e12)
             del PC
         extras["prefill_512k"], P512 = bench_512k(dev)
         print("[bench] extras: length sweep 32K..512K", file=sys.stderr, flush=True)

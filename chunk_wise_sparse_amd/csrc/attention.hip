@@ -993,15 +993,27 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
 // pair (I items, G workgroups per pair); item i belongs to the chunk j with toff[j] <= i <
 // toff[j + 1] and covers list entries off[j] + 128 (i - toff[j]) onward.  Consecutive items
 // mostly belong to one chunk, whose K/V is then staged once for the whole run of them.
-template <int D>
-__global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
+//
+// C keys per chunk (64, or 32 / 128 behind the generic selection kernel): S^T takes C / 16 key
+// blocks, PV C / 32 steps; K rows keep the 64-key kernels' layout and V's d-blocks hold C rows.
+// For C != 64 the keys and values are contiguous and a partial last chunk is read with its rows
+// clamped to the sequence: only rows of that chunk select it, as their own chunk, and the keys
+// past each such row are masked.
+template <int D, int C>
+__global__ __launch_bounds__(512, C == 128 ? 2 : 4) void cm_attn_kernel(const CmArgs a) {
   constexpr int NT = 512;
   typedef AttnLayout<bf16, D> Lay;
-  constexpr int NF = D / 32, NP = 2, VE = 8;
-  constexpr int NV = 64 * Lay::VPR / NT;
-  static_assert(NV >= 1 && (64 * Lay::VPR) % NT == 0, "chunk tile does not split over the threads");
-  __shared__ __attribute__((aligned(16))) char sk[AttnLayout<bf16, D>::KBYTES];
-  __shared__ __attribute__((aligned(16))) char sv_[AttnLayout<bf16, D>::VBYTES];
+  constexpr int NF = D / 32, NP = C / 32, NKB = C / 16, VE = 8;
+  constexpr int NVT = C * Lay::VPR;            // 16-byte vectors per tensor per chunk
+  constexpr int NV = (NVT + NT - 1) / NT;
+  static_assert(NVT % NT == 0 || NT % NVT == 0, "chunk tile does not split over the threads");
+  constexpr int VDB = C * 32 + 32;             // V d-block stride (C rows of 16 elements, padded)
+  constexpr int kLogC = C == 32 ? 5 : C == 64 ? 6 : 7;
+  static_assert(C == 32 || C == 64 || C == 128, "chunk of 32, 64 or 128 keys");
+  // (64 keys: the padded-row tile size this kernel was tuned with; a smaller one changes its
+  // register allocation and spills)
+  __shared__ __attribute__((aligned(16))) char sk[C == 64 ? Lay::KBYTES : C * BlockKLayout<D>::LD];
+  __shared__ __attribute__((aligned(16))) char sv_[(D / 16) * VDB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int N = a.N, k = a.k;
@@ -1029,14 +1041,28 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
     return *reinterpret_cast<const u32x2*>(cl.ent + 2 * (size_t)(dsc[0] + min(t, n - 1u)));
   };
   u32x4 kr[NV], vr[NV];
+  // Thread -> vector v of the chunk (row v / VPR); with fewer vectors than threads the spare
+  // threads repeat the last one (same bytes to the same LDS address).
+  auto vec_of = [&](int u) { return NVT >= NT ? tid + NT * u : min(tid, NVT - 1); };
   auto load_kv = [&](int j) {
-    const bf16* kc = kv_chunk<bf16, D>(Kb, Kb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
-    const bf16* vc = kv_chunk<bf16, D>(Vb, Vb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
+    if constexpr (C == 64) {
+      const bf16* kc = kv_chunk<bf16, D>(Kb, Kb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
+      const bf16* vc = kv_chunk<bf16, D>(Vb, Vb, cp.bt, a.num_pages, cp.Hk, cp.kvh, j);
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int v = tid + NT * u;
-      kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
-      vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+      for (int u = 0; u < NV; ++u) {
+        const int v = vec_of(u);
+        kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
+        vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int v = vec_of(u);
+        const size_t row = (size_t)min(j * C + v / Lay::VPR, a.L - 1);
+        const size_t e = row * D + (v % Lay::VPR) * VE;
+        kr[u] = *reinterpret_cast<const u32x4*>(Kb + e);
+        vr[u] = *reinterpret_cast<const u32x4*>(Vb + e);
+      }
     }
   };
   auto load_q = [&](const u32x2& pw, bf16x8 (&qf_)[NF]) {
@@ -1047,11 +1073,11 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
   auto put_kv = [&]() {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int v = tid + NT * u;
+      const int v = vec_of(u);
       const int row = v / Lay::VPR, p = v % Lay::VPR;
       *reinterpret_cast<u32x4*>(sk + BlockKLayout<D>::off(row, p)) = kr[u];
       const int e = p * VE;
-      *reinterpret_cast<u32x4*>(sv_ + (e >> 4) * Lay::VDB + row * 32 + (e & 15) * 2) = vr[u];
+      *reinterpret_cast<u32x4*>(sv_ + (e >> 4) * VDB + row * 32 + (e & 15) * 2) = vr[u];
     }
   };
   u32x2 dsc_c = ld_desc(item), dsc_n = ld_desc(item + 1), dsc_nn = ld_desc(item + 2), dsc_3;
@@ -1079,9 +1105,9 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
     const int j = (int)(dsc_c[1] >> 8);
     {
       const int r = (int)(pw_c[0] >> 6), es = (int)(pw_c[0] & 63u);
-      float sc[16];
+      float sc[4 * NKB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int st = 0; st < NF; ++st)
@@ -1089,21 +1115,21 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) sc[kb * 4 + rr] = acc[rr];
       }
-      if ((r >> 6) == j) {                     // the row's own chunk: keys after it are masked
-        const int ql = r & 63;
+      if ((r >> kLogC) == j) {                 // the row's own chunk: keys after it are masked
+        const int ql = r & (C - 1);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
             if (kb * 16 + 4 * g + rr > ql) sc[kb * 4 + rr] = -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      for (int i = 1; i < 4 * NKB; ++i) mx = fmaxf(mx, sc[i]);
       mx = col_max(mx) * zs;
       float l = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 4 * NKB; ++i) {
         // v_exp_f32 directly: arguments are <= 0, results below 2^-126 may flush to zero.
         sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], zs, -mx));
         l += sc[i];
@@ -1122,7 +1148,7 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int st = 0; st < NP; ++st)
-          acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<Lay::VDB>(sv_, m, g, db, st), pf[st], acc_o[db]);
+          acc_o[db] = Mfma<bf16>::mma(v_frag_bf16<VDB>(sv_, m, g, db, st), pf[st], acc_o[db]);
       bf16* op = P + ((size_t)r * k + es) * D;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
@@ -1155,7 +1181,7 @@ __global__ __launch_bounds__(512, 4) void cm_attn_kernel(const CmArgs a) {
 }
 
 // o[r] = sum over the row's slots, in slot order, of its partials (fp32), rounded once.  The
-// selection holds min(k, c + 1) chunks at the front of row r's list (c = r / 64, the row's
+// selection holds min(k, c + 1) chunks at the front of row r's list (c = r / C, the row's
 // chunk), so those are the valid slots.  Eight elements per thread, D / 8 threads per row.
 template <int D>
 __global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
@@ -1164,7 +1190,7 @@ __global__ __launch_bounds__(256) void cm_reduce_kernel(const CmArgs a) {
   const int t = threadIdx.x % TPR;
   if (r >= a.L) return;
   const CmPair cp = cm_pair<D>(a, blockIdx.y);
-  const int nv = min(a.k, (r >> 6) + 1);
+  const int nv = min(a.k, r / a.C + 1);
   const bf16* P = cp.partial + (size_t)r * a.k * D + t * 8;
   float acc[8] = {};
   int e = 0;
@@ -1200,7 +1226,9 @@ hipError_t launch_chunk_attention_cm(const CmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(cm_fill_kernel, dim3(gb, np), dim3(256), lds ? (size_t)a.N * 8 : 0, st, a);
   // 512 persistent workgroups in all (at least 64 per pair), each pair's own taking its items.
   const int wpp = max(64, 512 / np);
-  hipLaunchKernelGGL((cm_attn_kernel<D>), dim3(wpp, np), dim3(512), 0, st, a);
+  if (a.C == 32) hipLaunchKernelGGL((cm_attn_kernel<D, 32>), dim3(wpp, np), dim3(512), 0, st, a);
+  else if (a.C == 128) hipLaunchKernelGGL((cm_attn_kernel<D, 128>), dim3(wpp, np), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((cm_attn_kernel<D, 64>), dim3(wpp, np), dim3(512), 0, st, a);
   constexpr int RPB = 256 / (D / 8);           // rows per reduce workgroup
   hipLaunchKernelGGL((cm_reduce_kernel<D>), dim3((a.L + RPB - 1) / RPB, np), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -14,7 +14,7 @@ struct GcArgs {
   const void* lmk;           // [B, Hk, N, d], N = ceil(Lkv / C)
   const void* w_up;          // [H * d, r] (r > 0)
   const float* tcode;        // Q-Cal code rows, tstride floats apart (r > 0)
-  void* o;                   // like q
+  void* o;                   // like q; NULL: selection only (idx / w written, no attention)
   int32_t* idx;              // [B, H, Lq, k]
   float* w;                  // [B, H, Lq, k]
   const int32_t* kv_len;     // decode: [B], the query at kv_len - 1 (clamped to [1, Lkv]); prefill: NULL

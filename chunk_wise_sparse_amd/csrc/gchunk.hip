@@ -188,6 +188,9 @@ __global__ __launch_bounds__(W == 1 ? 64 * kGcRows : 64 * W) void gchunk_kernel(
     wls[slot][lane] = wl;
     if (lane == 0) scnt[slot] = cnt;
   }
+  // Selection only (no output tensor): the chunk-major MFMA kernels attend afterwards.  Uniform
+  // over the workgroup, so no wave is left waiting at a barrier.
+  if (a.o == nullptr) return;
   rsync();
 
   // The row's selected chunks, split over its waves: softmax over each chunk's visible keys,

@@ -124,7 +124,7 @@ int effective_q_tile(const hils_prefill_params* p) {
 constexpr size_t kCmBatchBytes = (size_t)8 << 30;
 constexpr size_t kCmCacheBytes = (size_t)160 << 20;
 size_t cm_pair_bytes(const hils_prefill_params* p) {
-  const size_t S = p->seq_len, k = p->topk, N = S / 64, d = p->head_dim;
+  const size_t S = p->seq_len, k = p->topk, N = (S + p->chunk - 1) / p->chunk, d = p->head_dim;
   return (4 * N + 2) * 4 + S * k * 8 + hils::cm_max_items(S * k, N) * 8 + S * k * d * 2;
 }
 int cm_batch_pairs(const hils_prefill_params* p) {
@@ -148,7 +148,7 @@ PrefillLayout prefill_layout(const hils_prefill_params* p, bool with_sel) {
   if (p->attn_mode != HILS_ATTN_UNION) {       // chunk-major: a batch of (batch, head) pairs
     L.probe = off;                             // union probe counter (auto mode)
     off += align_up(4);
-    const size_t N = S / 64, d = p->head_dim, P = cm_batch_pairs(p);
+    const size_t N = (S + p->chunk - 1) / p->chunk, d = p->head_dim, P = cm_batch_pairs(p);
     L.cm_cnt = off;
     off += align_up(P * N * 4);
     L.cm_off = off;
@@ -199,11 +199,52 @@ PadLayout pad_layout(const hils_prefill_params* p) {
   return P;
 }
 
-// Chunk sizes other than 64: the Q-Cal code and the selection (when not returned) only.
+// Chunk sizes other than 64: the Q-Cal code, the selection (when not returned) and, for bf16,
+// the chunk-major lists and partials.
 PrefillLayout gchunk_layout(const hils_prefill_params* p, bool with_sel) {
   hils_prefill_params pp = *p;
-  pp.attn_mode = HILS_ATTN_UNION;
+  pp.attn_mode = p->dtype == HILS_DTYPE_BF16 ? HILS_ATTN_CHUNK_MAJOR : HILS_ATTN_UNION;
   return prefill_layout(&pp, with_sel);
+}
+
+// Chunk-major attention (bf16) over the selection in idx / w: the (batch, head) pairs in batches,
+// one launch per stage and batch.
+template <int D>
+hipError_t run_chunk_major(const hils_prefill_params* p, const void* q, const void* k, const void* v, void* o,
+                           const int32_t* idx, const float* w, char* ws, const PrefillLayout& L, float scale,
+                           hipStream_t st) {
+  hils::CmArgs ca;
+  ca.q = q;
+  ca.key = k;
+  ca.val = v;
+  ca.o = o;
+  ca.idx = idx;
+  ca.w = w;
+  ca.cnt = reinterpret_cast<uint32_t*>(ws + L.cm_cnt);
+  ca.off = reinterpret_cast<uint32_t*>(ws + L.cm_off);
+  ca.cur = reinterpret_cast<uint32_t*>(ws + L.cm_cur);
+  ca.toff = reinterpret_cast<uint32_t*>(ws + L.cm_toff);
+  ca.ent = reinterpret_cast<uint32_t*>(ws + L.cm_ent);
+  ca.desc = reinterpret_cast<uint32_t*>(ws + L.cm_desc);
+  ca.partial = ws + L.cm_partial;
+  ca.L = p->seq_len;
+  ca.C = p->chunk;
+  ca.N = (p->seq_len + p->chunk - 1) / p->chunk;
+  ca.k = p->topk;
+  ca.scale = scale;
+  ca.H = p->heads;
+  ca.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
+  ca.bt = p->block_table;
+  ca.bt_stride = p->block_table_stride;
+  ca.num_pages = p->num_pages;
+  const int BH = p->batch * p->heads, P = cm_batch_pairs(p);
+  for (int pair0 = 0; pair0 < BH; pair0 += P) {
+    ca.pair0 = pair0;
+    ca.npairs = std::min(P, BH - pair0);
+    const hipError_t e = hils::launch_chunk_attention_cm<D>(ca, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 size_t prefill_workspace_bytes(const hils_prefill_params* p, bool with_sel) {
@@ -214,7 +255,9 @@ size_t prefill_workspace_bytes(const hils_prefill_params* p, bool with_sel) {
 template <typename T>
 hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const void* k, const void* v,
                               const void* lmk, const void* h, const void* w_down, const void* w_up, void* o,
-                              int32_t* idx, float* w, float* tcode, hipStream_t st) {
+                              int32_t* idx, float* w, float* tcode, char* ws, const PrefillLayout& L,
+                              hipStream_t st) {
+  constexpr bool cm = sizeof(T) == 2;          // bf16: selection here, attention chunk-major
   hipError_t e;
   hipEvent_t* ev = p->n_stage_events >= 4 ? (hipEvent_t*)p->stage_events : nullptr;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
@@ -231,7 +274,7 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
   a.lmk = lmk;
   a.w_up = w_up;
   a.tcode = tcode;
-  a.o = o;
+  a.o = cm ? nullptr : o;
   a.idx = idx;
   a.w = w;
   a.kv_len = nullptr;
@@ -248,8 +291,13 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
   if (e != hipSuccess) return e;
-  // selection and attention run in one kernel: their two stage marks coincide
+  // fp32: selection and attention run in one kernel, so their two stage marks coincide
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if constexpr (cm) {
+    e = p->head_dim == 64 ? run_chunk_major<64>(p, q, k, v, o, idx, w, ws, L, a.scale, st)
+                          : run_chunk_major<128>(p, q, k, v, o, idx, w, ws, L, a.scale, st);
+    if (e != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -340,35 +388,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
       chunk_major = groups > 0 && (double)total / groups > 8.0 * p->topk;
     }
     if (chunk_major) {
-      hils::CmArgs ca;
-      ca.q = q;
-      ca.key = k;
-      ca.val = v;
-      ca.o = o;
-      ca.idx = idx;
-      ca.w = w;
-      ca.cnt = reinterpret_cast<uint32_t*>(ws + L.cm_cnt);
-      ca.off = reinterpret_cast<uint32_t*>(ws + L.cm_off);
-      ca.cur = reinterpret_cast<uint32_t*>(ws + L.cm_cur);
-      ca.toff = reinterpret_cast<uint32_t*>(ws + L.cm_toff);
-      ca.ent = reinterpret_cast<uint32_t*>(ws + L.cm_ent);
-      ca.desc = reinterpret_cast<uint32_t*>(ws + L.cm_desc);
-      ca.partial = ws + L.cm_partial;
-      ca.L = p->seq_len;
-      ca.N = p->seq_len / 64;
-      ca.k = p->topk;
-      ca.scale = scale;
-      ca.H = p->heads;
-      ca.G = aa.G;
-      ca.bt = p->block_table;
-      ca.bt_stride = p->block_table_stride;
-      ca.num_pages = p->num_pages;
-      const int BH = p->batch * p->heads, P = cm_batch_pairs(p);
-      for (int pair0 = 0; pair0 < BH; pair0 += P) {
-        ca.pair0 = pair0;
-        ca.npairs = std::min(P, BH - pair0);
-        if ((e = hils::launch_chunk_attention_cm<D>(ca, st)) != hipSuccess) return e;
-      }
+      if ((e = run_chunk_major<D>(p, q, k, v, o, idx, w, ws, L, scale, st)) != hipSuccess) return e;
       if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
       return hipSuccess;
     }
@@ -664,8 +684,8 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
     float* gw = with_sel ? sel_w : reinterpret_cast<float*>(ws + G.w);
     float* gt = qcal ? reinterpret_cast<float*>(ws + G.tcode) : nullptr;
     err = p->dtype == HILS_DTYPE_BF16
-              ? run_prefill_gchunk<hils::bf16>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, s)
-              : run_prefill_gchunk<float>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, s);
+              ? run_prefill_gchunk<hils::bf16>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, ws, G, s)
+              : run_prefill_gchunk<float>(p, q, k, v, lmk, h, w_down, w_up, o, gidx, gw, gt, ws, G, s);
     if (err != hipSuccess) return hip_fail(err, "hils_prefill_fwd");
     return HILS_OK;
   }

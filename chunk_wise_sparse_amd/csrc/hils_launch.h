@@ -62,6 +62,7 @@ struct CmArgs {
                         // entries), in item order
   void* partial;        // [npairs][L,k,d] bf16: w_j * o_j of slot j of each row
   int L, N, k;
+  int C;                // keys per chunk: 64, or 32 / 128 (contiguous keys/values only)
   float scale;
   int H, G, pair0, npairs;   // query heads, query heads per key/value head, the batch of pairs
   // Paged keys/values: key / val are the pools, bt the block table ([B, bt_stride]); NULL: key /

@@ -1,6 +1,8 @@
-"""Chunk sizes 32 and 128 (the generic one-wave-per-row path) in prefill and decode, through the
-C ABI, against the oracle: every row of small prefills (ragged last chunk, GQA, forced local
-chunk), and ragged decode batches."""
+"""Chunk sizes 32 and 128 in prefill and decode, through the C ABI, against the oracle: every row
+of small prefills (ragged last chunk, GQA, forced local chunk), and ragged decode batches.  bf16
+prefills select in the generic kernel and attend in the chunk-major MFMA kernels (several work
+items per chunk, partial last chunks read with clamped rows); fp32 prefills and decode run the
+generic kernel throughout."""
 import math
 
 import numpy as np
@@ -35,6 +37,11 @@ PREFILL = [
     (synth.PrefillConfig("c128_bf16_d128_g4", 1, 8, 2048, 128, 128, 4, "bf16", 16, 256), 4, False),
     (synth.PrefillConfig("c32_bf16_d128_local", 1, 2, 2048, 128, 32, 8, "bf16", 16, 256), 1, True),
     (synth.PrefillConfig("c128_fp32_d64_local", 1, 2, 1500, 64, 128, 3, "fp32", 8, 128), 1, True),
+    # the 32K workload's shape (d = 64, k = 16, r = 16) at a ragged length: chunks chosen by
+    # hundreds of rows (several chunk-major work items each)
+    (synth.PrefillConfig("c32_bf16_d64_k16_L3333", 1, 4, 3333, 64, 32, 16, "bf16", 16, 256), 1, False),
+    (synth.PrefillConfig("c128_bf16_d64_k16_L5000", 2, 2, 5000, 64, 128, 16, "bf16", 16, 256), 1, False),
+    (synth.PrefillConfig("c128_bf16_d128_k64_L9000", 1, 1, 9000, 128, 128, 64, "bf16", 0, 0), 1, False),
 ]
 
 

@@ -289,7 +289,29 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
   a.tstride = p->qcal_rank;
   a.force_local = p->force_local;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
-  e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
+  if (cm && p->seq_len % 64 == 0 && !p->force_local) {
+    // whole 64-query tiles: the MFMA selection (each tile scored against its last row's
+    // candidates, later landmarks masked per query)
+    hils::SelectArgs sa;
+    sa.q = q;
+    sa.lmk = lmk;
+    sa.tcode = tcode;
+    sa.w_up = w_up;
+    sa.idx = idx;
+    sa.w = w;
+    sa.B = p->batch;
+    sa.G = a.G;
+    sa.H = p->heads;
+    sa.L = p->seq_len;
+    sa.N = a.N;
+    sa.C = p->chunk;
+    sa.k = p->topk;
+    sa.r = p->qcal_rank;
+    sa.scale = a.scale;
+    e = p->head_dim == 64 ? hils::launch_select<T, 64>(sa, st) : hils::launch_select<T, 128>(sa, st);
+  } else {
+    e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
+  }
   if (e != hipSuccess) return e;
   // fp32: selection and attention run in one kernel, so their two stage marks coincide
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
@@ -329,6 +351,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
   sa.H = p->heads;
   sa.L = p->seq_len;
   sa.N = p->seq_len / 64;
+  sa.C = 64;
   sa.k = p->topk;
   sa.r = p->qcal_rank;
   sa.scale = scale;

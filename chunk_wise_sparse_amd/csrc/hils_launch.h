@@ -18,6 +18,8 @@ struct SelectArgs {
   float* w;             // [B,H,L,k]
   int B, H, L, N, k, r;
   int G;                // query heads per key/value (and landmark) head
+  int C;                // keys per chunk: 64 (every selection kernel), or 32 / 128 (bf16: the
+                        // MFMA selection, L a multiple of 64); N = ceil(L / C)
   float scale;
 };
 

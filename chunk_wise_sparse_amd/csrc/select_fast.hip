@@ -107,8 +107,11 @@ __device__ __forceinline__ float pick(const float (&x)[N], int kk) {
   return r;
 }
 
-// Wave w takes the 64-query tile of chunk c_top - w, so the tiles of a workgroup are consecutive
-// chunks of one (batch, head) and need the same landmark blocks.
+// Wave w takes 64-query tile t_top - w, so the tiles of a workgroup are consecutive tiles of one
+// (batch, head) and need the same landmark blocks.  Chunks of C = 32 or 128 keys: a tile's rows
+// have the candidates 0 .. (row / C), the same for the whole tile at C = 128 (two tiles per
+// chunk) and one more for its second half at C = 32; the tile is scored against the candidates
+// of its last row and each query masks the landmarks past its own chunk.
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -143,20 +146,26 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
-  const int G = (a.N + kTiles - 1) / kTiles;   // tile groups per (batch, head)
+  const int lc = 31 - __builtin_clz((unsigned)a.C);   // log2 of the chunk size
+  const int T = a.L >> 6;                      // 64-query tiles per (batch, head)
+  const int G = (T + kTiles - 1) / kTiles;     // tile groups per (batch, head)
   const uint32_t total = (uint32_t)a.B * a.H * G;
   const uint32_t grp = xcd_remap(blockIdx.x, total);
   const int bh = grp / G;
-  const int c_top = a.N - 1 - kTiles * (int)(grp % G);   // longest groups first
-  // A wave past chunk 0 (N not a multiple of kTiles) runs tile 0 again and writes nothing.
-  const bool active = c_top - wave >= 0;
-  const int c = max(c_top - wave, 0);
+  const int t_top = T - 1 - kTiles * (int)(grp % G);     // longest groups first
+  // A wave past tile 0 (T not a multiple of kTiles) runs tile 0 again and writes nothing.
+  const bool active = t_top - wave >= 0;
+  const int q0 = max(t_top - wave, 0) * 64;
+  const int c_top = (64 * t_top + 63) >> lc;   // the group's last candidate chunk
   const int b = bh / a.H, hd = bh % a.H;
-  const int n_cand = c + 1;
+  const int n_cand = ((q0 + 63) >> lc) + 1;    // candidates of the tile's last row
+  // Candidates of query col and col + 32 (MFMA output columns), and of query `lane` (after the
+  // lane swap each lane owns one query); equal to n_cand at C >= 64.
+  const int nc0 = ((q0 + col) >> lc) + 1, nc1 = ((q0 + 32 + col) >> lc) + 1;
+  const int nql = ((q0 + lane) >> lc) + 1;
   const int nb = (n_cand + 31) >> 5;           // this tile's 32-landmark blocks
   const int nbg = (c_top + 1 + 31) >> 5;       // blocks the group sweeps
-  const int kq = min(a.k, n_cand);
-  const int q0 = c * 64;
+  const int kq = min(a.k, nql);
   const bf16* Q = static_cast<const bf16*>(a.q) + (size_t)bh * a.L * D;
   const bf16* LM = static_cast<const bf16*>(a.lmk) + (size_t)kv_pair(bh, a.H, a.G) * a.N * D;
   // This lane's list: row i at ls[64 i], lj[64 i].
@@ -375,7 +384,7 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
   // and lanes 32-63 both row halves of column block 1.
   auto for_scores = [&](auto last_block, int jb, const f32x16& acc0, const f32x16& acc1, auto&& f) {
     constexpr bool last = decltype(last_block)::value;
-    const int lim = n_cand - 32 * jb;
+    const int lim = nql - 32 * jb;
 #pragma unroll
     for (int grp4 = 0; grp4 < 4; ++grp4) {
       float x[4], y[4];
@@ -414,12 +423,12 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
         m1[P][i] = fmaxf(m1[P][i], v);
       };
       if (jb == nb - 1) {
-        const int lim = n_cand - 32 * jb;
+        const int lim0 = nc0 - 32 * jb, lim1 = nc1 - 32 * jb;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const bool out = 8 * (e / 4) + 4 * half + e % 4 >= lim;
-          top2(e, out ? -INFINITY : acc0[e]);
-          top2(16 + e, out ? -INFINITY : acc1[e]);
+          const int row = 8 * (e / 4) + 4 * half + e % 4;
+          top2(e, row >= lim0 ? -INFINITY : acc0[e]);
+          top2(16 + e, row >= lim1 ? -INFINITY : acc1[e]);
         }
       } else {
 #pragma unroll
@@ -662,7 +671,7 @@ __global__ __launch_bounds__(64 * SelCfg<KQ>::kTiles) void select_fast_kernel(co
 template <int D, int KQ>
 void launch_select_fast_k(const SelectArgs& a, hipStream_t st) {
   constexpr int T = SelCfg<KQ>::kTiles;
-  const uint32_t groups = (uint32_t)a.B * a.H * ((a.N + T - 1) / T);
+  const uint32_t groups = (uint32_t)a.B * a.H * ((a.L / 64 + T - 1) / T);
   if (a.r > 0 && a.r % 8 == 0 && a.r <= 32)
     hipLaunchKernelGGL((select_fast_kernel<D, KQ, 1>), dim3(groups), dim3(64 * T), 0, st, a);
   else

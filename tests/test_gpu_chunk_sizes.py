@@ -1,8 +1,9 @@
 """Chunk sizes 32 and 128 in prefill and decode, through the C ABI, against the oracle: every row
 of small prefills (ragged last chunk, GQA, forced local chunk), and ragged decode batches.  bf16
-prefills select in the generic kernel and attend in the chunk-major MFMA kernels (several work
-items per chunk, partial last chunks read with clamped rows); fp32 prefills and decode run the
-generic kernel throughout."""
+prefills select with the MFMA kernel when the sequence is whole 64-query tiles (else, and with
+the forced local chunk, in the generic kernel) and attend in the chunk-major MFMA kernels (several
+work items per chunk, partial last chunks read with clamped rows); fp32 prefills and decode run
+the generic kernel throughout."""
 import math
 
 import numpy as np
@@ -42,6 +43,15 @@ PREFILL = [
     (synth.PrefillConfig("c32_bf16_d64_k16_L3333", 1, 4, 3333, 64, 32, 16, "bf16", 16, 256), 1, False),
     (synth.PrefillConfig("c128_bf16_d64_k16_L5000", 2, 2, 5000, 64, 128, 16, "bf16", 16, 256), 1, False),
     (synth.PrefillConfig("c128_bf16_d128_k64_L9000", 1, 1, 9000, 128, 128, 64, "bf16", 0, 0), 1, False),
+    # whole 64-query tiles: the MFMA selection (tiles scored against their last row's candidates,
+    # the first half of a C = 32 tile masking one more landmark), with and without its bound pass
+    (synth.PrefillConfig("c32_bf16_d64_k16_L8192", 1, 2, 8192, 64, 32, 16, "bf16", 16, 256), 1, False),
+    (synth.PrefillConfig("c32_bf16_d128_k32_walk", 1, 2, 4096, 128, 32, 32, "bf16", 32, 512, q_mode="walk"),
+     1, False),
+    (synth.PrefillConfig("c128_bf16_d128_k16_r12_L16384", 1, 1, 16384, 128, 128, 16, "bf16", 12, 256), 1, False),
+    (synth.PrefillConfig("c128_bf16_d64_L2368", 1, 2, 2368, 64, 128, 8, "bf16", 8, 128), 1, False),
+    (synth.PrefillConfig("c32_bf16_d64_k40_L2368", 1, 2, 2368, 64, 32, 40, "bf16", 8, 128), 1, False),
+    (synth.PrefillConfig("c32_bf16_d128_g2_L3072", 1, 4, 3072, 128, 32, 8, "bf16", 16, 256), 2, False),
 ]
 
 

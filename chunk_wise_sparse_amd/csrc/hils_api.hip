@@ -289,9 +289,9 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
   a.tstride = p->qcal_rank;
   a.force_local = p->force_local;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
-  if (cm && p->seq_len % 64 == 0 && !p->force_local) {
+  if (cm && p->seq_len % 64 == 0) {
     // whole 64-query tiles: the MFMA selection (each tile scored against its last row's
-    // candidates, later landmarks masked per query)
+    // candidates, later landmarks masked per query), amended for the forced local chunk
     hils::SelectArgs sa;
     sa.q = q;
     sa.lmk = lmk;
@@ -309,6 +309,28 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
     sa.r = p->qcal_rank;
     sa.scale = a.scale;
     e = p->head_dim == 64 ? hils::launch_select<T, 64>(sa, st) : hils::launch_select<T, 128>(sa, st);
+    if (e == hipSuccess && p->force_local) {
+      hils::LocalArgs la;
+      la.q = q;
+      la.lmk = lmk;
+      la.w_up = w_up;
+      la.tcode = tcode;
+      la.kv_len = nullptr;
+      la.idx = idx;
+      la.w = w;
+      la.B = p->batch;
+      la.H = p->heads;
+      la.L = p->seq_len;
+      la.N = a.N;
+      la.G = a.G;
+      la.k = p->topk;
+      la.r = p->qcal_rank;
+      la.tstride = p->qcal_rank;
+      la.lc = p->chunk == 32 ? 5 : 7;
+      la.scale = a.scale;
+      e = p->head_dim == 64 ? hils::launch_force_local<T, 64>(la, false, st)
+                            : hils::launch_force_local<T, 128>(la, false, st);
+    }
   } else {
     e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
   }
@@ -373,6 +395,7 @@ hipError_t run_prefill(const hils_prefill_params* p, const void* q, const void* 
     la.k = p->topk;
     la.r = p->qcal_rank;
     la.tstride = p->qcal_rank;
+    la.lc = 6;
     la.scale = scale;
     if ((e = hils::launch_force_local<T, D>(la, false, st)) != hipSuccess) return e;
   }
@@ -621,6 +644,7 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
     la.k = p->topk;
     la.r = p->qcal_rank;
     la.tstride = hils::kTcodeStride;
+    la.lc = 6;
     la.scale = a.scale;
     if ((e = hils::launch_force_local<T, D>(la, true, st)) != hipSuccess) return e;
   }

@@ -197,6 +197,7 @@ struct LocalArgs {
   int32_t* idx;         // [rows, k], updated in place
   float* w;             // [rows, k]
   int B, H, L, N, G, k, r, tstride;
+  int lc;               // log2 of the chunk size (6: 64 keys)
   float scale;
 };
 template <typename T, int D>

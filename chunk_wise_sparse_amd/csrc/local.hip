@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void force_local_kernel(const LocalArgs a) {
     i = (int)(row % a.L);
     t = a.tcode + ((size_t)(bh / a.H) * a.L + i) * a.tstride;
   }
-  const int c = i >> 6, k = a.k, h = bh % a.H;
+  const int c = i >> a.lc, k = a.k, h = bh % a.H;
   if (c + 1 <= k) return;                      // every candidate selected
   int32_t* ip = a.idx + row * k;
   float* wp = a.w + row * k;

@@ -58,9 +58,10 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  * 1 <= topk <= 64; 1 <= seq_len with ceil(seq_len / chunk) <= 65535; 0 <= qcal_rank <= 64;
  * hidden a positive multiple of 128 when qcal_rank > 0.
  * scale <= 0 selects 1/sqrt(head_dim).
- * Chunk sizes 32 and 128, bf16: when seq_len is a multiple of 64 and force_local is 0, the MFMA
- * selection (64-query tiles scored against their last row's candidates, later landmarks masked
- * per query), else a generic kernel (one query row per wave or per workgroup, scores in LDS); the
+ * Chunk sizes 32 and 128, bf16: when seq_len is a multiple of 64, the MFMA selection (64-query
+ * tiles scored against their last row's candidates, later landmarks masked per query; the forced
+ * local chunk amends it as at chunk 64), else a generic kernel (one query row per wave or per
+ * workgroup, scores in LDS); the
  * attention is always the chunk-major MFMA mode (attn_mode and q_tile are ignored, and the
  * workspace is that mode's).  fp32 selects and attends in the generic kernel, whose stage events
  * 2 and 3 are recorded together after it.  Limits: at most 8192 chunks, contiguous keys and

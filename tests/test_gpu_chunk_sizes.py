@@ -1,7 +1,8 @@
 """Chunk sizes 32 and 128 in prefill and decode, through the C ABI, against the oracle: every row
 of small prefills (ragged last chunk, GQA, forced local chunk), and ragged decode batches.  bf16
-prefills select with the MFMA kernel when the sequence is whole 64-query tiles (else, and with
-the forced local chunk, in the generic kernel) and attend in the chunk-major MFMA kernels (several
+prefills select with the MFMA kernel when the sequence is whole 64-query tiles (else in the
+generic kernel; the forced local chunk amends the MFMA selection in a post-pass, and the generic
+selection takes it directly) and attend in the chunk-major MFMA kernels (several
 work items per chunk, partial last chunks read with clamped rows); fp32 prefills and decode run
 the generic kernel throughout."""
 import math
@@ -52,6 +53,9 @@ PREFILL = [
     (synth.PrefillConfig("c128_bf16_d64_L2368", 1, 2, 2368, 64, 128, 8, "bf16", 8, 128), 1, False),
     (synth.PrefillConfig("c32_bf16_d64_k40_L2368", 1, 2, 2368, 64, 32, 40, "bf16", 8, 128), 1, False),
     (synth.PrefillConfig("c32_bf16_d128_g2_L3072", 1, 4, 3072, 128, 32, 8, "bf16", 16, 256), 2, False),
+    # forced local chunk: the MFMA selection amended by the post-pass, and (ragged) the generic one
+    (synth.PrefillConfig("c128_bf16_d64_local_L4096", 1, 2, 4096, 64, 128, 4, "bf16", 8, 128), 1, True),
+    (synth.PrefillConfig("c32_bf16_d64_local_L999", 1, 2, 999, 64, 32, 6, "bf16", 8, 128), 1, True),
 ]
 
 

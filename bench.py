@@ -367,6 +367,33 @@ def length_sweep_from(P512, lengths=(32768, 65536, 131072, 262144, 524288)):
     return out
 
 
+def bench_decode_chunk_sizes(D, dcfg, dev):
+    """The 512K decode step at chunk 128 and its first 256K tokens at chunk 32 (the generic
+    selection's limit is 8192 chunks): the same q, caches and Q-Cal inputs, landmarks made for the
+    chunk size by the workload's recipe (chunk means plus noise, no needles)."""
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+    out = {}
+    for C, L in ((128, dcfg.max_kv_len), (32, dcfg.max_kv_len // 2)):
+        kc = D["k_cache"] if L == dcfg.max_kv_len else D["k_cache"][:, :, :L].contiguous()
+        vc = D["v_cache"] if L == dcfg.max_kv_len else D["v_cache"][:, :, :L].contiguous()
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.subseed(dcfg.seed, "lmk_noise"))
+        lmk = synth._landmarks_dev(gen, kc, C, kc.dtype)
+        kvl = torch.full_like(D["kv_len"], L)
+        run = lambda: hils.decode(D["q"], kc, vc, lmk, kvl, D["h"], D["w_down"], D["w_up"], topk=dcfg.topk,
+                                  chunk=C)
+        run()
+        ms = event_ms(run, 5)
+        nb = dcfg.batch * dcfg.heads * ((L // C) * dcfg.head_dim * 2 + 2 * dcfg.topk * C * dcfg.head_dim * 2)
+        out[f"chunk{C}"] = dict(kv_len=L, us_per_step=ms * 1e3, GBps=nb / (ms * 1e-3) / 1e9,
+                                frac_hbm=nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                note="landmarks + selected keys/values read once per step")
+        del kc, vc, lmk
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_backward(P, cfg, o, dev):
     """Backward pass of the 128K prefill for a random dout: ms and algorithmic TFLOP/s.  Work per
     selected (row, chunk): S, dP, dq, dk and dv products, 10 C d FLOP; Q-Cal: four rank-r products."""
@@ -610,6 +637,7 @@ def main():
                 us_per_step=dd_ms * 1e3, GBps=kvb / (dd_ms * 1e-3) / 1e9, frac_hbm=kvb / (dd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 dense_over_hils=dd_ms / (dec_ms / K),
                 note="this library's dense attention of the same 8 x 32 queries over the whole 512K caches")
+            extras["decode_chunk_sizes"] = bench_decode_chunk_sizes(D, dcfg, dev)
         extras["backward_128k"] = bench_backward(P, pcfg, o, dev)
         # HoPE rotation of the 128K workload's q and k (a copy, rotated in place): bytes read and
         # written once each.

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  const int n_b = (kvl + kChunk - 1) / kChunk;
+  const int n_b = (kvl + a.C - 1) / a.C;
   const int nblk = (n_b + kScoreChunksPerBlock - 1) / kScoreChunksPerBlock;
   const int qb = a.score_qb;
   const int blk0 = blockIdx.y * qb;            // this workgroup's blocks: blk0 .. blk0 + nq - 1
@@ -465,7 +465,7 @@ __device__ __forceinline__ void select_candidates(const DecodeArgs& a, int bh, C
   if ((threadIdx.x >> 6) != 0) return;
   const int b = bh / a.H;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  const int n = (kvl + kChunk - 1) / kChunk;
+  const int n = (kvl + a.C - 1) / a.C;
   const int kk = min(a.k, n);
   const int yb = ((n + kScoreBlock - 1) / kScoreBlock + a.score_qb - 1) / a.score_qb;   // scan workgroups, <= 32
   if (yb <= 8) select_candidates_wave<8>(a, bh, kk, yb, sm);
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_select_kernel(const DecodeArgs a) 
   __shared__ uint32_t kmax_w[4];
   const int bh = blockIdx.x, b = bh / a.H, tid = threadIdx.x, wave = tid >> 6;
   const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
-  const int n = (kvl + kChunk - 1) / kChunk;
+  const int n = (kvl + a.C - 1) / a.C;
   const int kk = min(a.k, n);
   const float* G = a.scores + (size_t)bh * a.score_stride;
   auto S = [&](int x) -> float { return G[decode_score_pos(x, a.score_qb)]; };
@@ -1083,6 +1083,89 @@ __global__ __launch_bounds__(256) void decode_attend_split_kernel(const DecodeAr
   }
 }
 
+// Chunks of C = 32 or 128 keys (selected by the generic chunk-size kernel): one wave per slot,
+// the chunk taken in 64-row pieces (one for C = 32, two for C = 128).  The keys of every piece
+// give the chunk's scores, one softmax runs over all of them, then the values of every piece are
+// weighted; w_j * o_j goes to the slot's partial as above.  Rows past the chunk's visible ones
+// come back as zeros from the buffer loads and score -inf.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(256) void decode_attend_gc_kernel(const DecodeArgs a) {
+  typedef ChunkGather<T, D> CG;
+  constexpr int NPC = (C + 63) / 64;           // 64-row pieces of a chunk
+  __shared__ float sp[4][NPC * 64];
+  const int bh = blockIdx.x, b = bh / a.H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.y * 4 + wave;
+  const int kvl = min(max(a.kv_len[b], 1), a.Lmax);
+  const int j = u < a.k ? a.idx[(size_t)bh * a.k + u] : -1;
+  const bool live = j >= 0 && j * C < kvl;
+  const int n_vis = live ? min(C, kvl - j * C) : 0;
+  const float wj = live ? a.w[(size_t)bh * a.k + u] : 0.f;
+  const size_t row0 = (size_t)kv_pair(bh, a.H, a.G) * a.Lmax + (size_t)max(j, 0) * C;
+  auto piece = [&](const void* cache, int pc) {
+    const int nv = min(max(n_vis - 64 * pc, 0), 64);
+    return buffer_rsrc(static_cast<const T*>(cache) + (row0 + 64 * pc) * D, nv * D * (int)sizeof(T));
+  };
+  float qf[CG::VE];
+  load_query<T, D>(a, bh, lane, qf);
+  float* spw = sp[wave];
+  CG cg;
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) {
+    CG::load(piece(a.k_cache, pc), cg.kr, lane);
+    cg.scores(qf, min(max(n_vis - 64 * pc, 0), 64), spw + 64 * pc, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's scores are in LDS
+  __builtin_amdgcn_wave_barrier();
+  const float zs = a.scale * 1.4426950408889634f;
+  float sv[NPC];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) {
+    sv[pc] = spw[64 * pc + lane];
+    mx = fmaxf(mx, sv[pc]);
+  }
+  mx = live ? wave_max(mx) : 0.f;
+  float l = 0.f;
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) {
+    sv[pc] = live ? exp2f((sv[pc] - mx) * zs) : 0.f;
+    l += sv[pc];
+  }
+  l = wave_sum(l);
+  const float f = live ? wj / l : 0.f;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) spw[64 * pc + lane] = sv[pc] * f;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const int sub = lane / CG::LPR;
+  float part[CG::VE];
+#pragma unroll
+  for (int e = 0; e < CG::VE; ++e) part[e] = 0.f;
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) {
+    CG::load(piece(a.v_cache, pc), cg.vr, lane);
+#pragma unroll
+    for (int it = 0; it < CG::NIT; ++it) {
+      const float pr = spw[64 * pc + it * CG::RPI + sub];
+#pragma unroll
+      for (int e = 0; e < CG::VE; ++e) part[e] = fmaf(pr, to_f32(cg.vr[it][e]), part[e]);
+    }
+  }
+#pragma unroll
+  for (int mk = CG::LPR; mk < 64; mk <<= 1) {
+#pragma unroll
+    for (int e = 0; e < CG::VE; ++e) part[e] += shfl_xor_f(part[e], mk);
+  }
+  if (u < a.k && lane < CG::LPR) {
+    float* pt = a.partial + ((size_t)bh * a.k + u) * D;
+#pragma unroll
+    for (int e = 0; e < CG::VE; ++e) pt[lane * CG::VE + e] = part[e];
+  }
+}
+
 // o[d] = sum over slots u of partial[u][d] in a fixed order: 8 slot groups (group gq takes
 // slots gq, gq + 8, ...), then the groups in order.
 template <typename T, int D>
@@ -1174,6 +1257,17 @@ hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Chunks of 32 or 128 keys: the split attention over the selection in idx / w, then the reduce.
+template <typename T, int D>
+hipError_t launch_decode_attend_gc(const DecodeArgs& a, int C, hipStream_t st) {
+  const dim3 grid(a.B * a.H, (a.k + 3) / 4);
+  if (C == 32) hipLaunchKernelGGL((decode_attend_gc_kernel<T, D, 32>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((decode_attend_gc_kernel<T, D, 128>), grid, dim3(256), 0, st, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.B * a.H), dim3(2 * D), 0, st, a);
+  return hipGetLastError();
+}
+
 template bool decode_fused_ok<bf16>(const DecodeArgs&);
 template bool decode_fused_ok<float>(const DecodeArgs&);
 template bool decode_select_fused<bf16>(const DecodeArgs&);
@@ -1183,7 +1277,8 @@ template hipError_t launch_decode_tcode<float>(const float*, const float*, float
 #define HILS_DECODE_INST(T, D)                                                      \
   template hipError_t launch_decode_scores<T, D>(const DecodeArgs&, hipStream_t); \
   template hipError_t launch_decode_fused<T, D>(const DecodeArgs&, hipStream_t); \
-  template hipError_t launch_decode_attend<T, D>(const DecodeArgs&, hipStream_t);
+  template hipError_t launch_decode_attend<T, D>(const DecodeArgs&, hipStream_t); \
+  template hipError_t launch_decode_attend_gc<T, D>(const DecodeArgs&, int, hipStream_t);
 HILS_DECODE_INST(bf16, 64)
 HILS_DECODE_INST(bf16, 128)
 HILS_DECODE_INST(float, 64)

@@ -466,8 +466,8 @@ int check_decode_params(const hils_decode_params* p) {
   if (p->chunk != 64 && p->chunk != 32 && p->chunk != 128)
     return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (32, 64 or 128)", p->chunk);
   if (p->chunk != 64) {
-    if ((p->max_kv_len + p->chunk - 1) / p->chunk > hils::kGcMaxChunks)
-      return fail(HILS_ERR_UNSUPPORTED, "chunk %d: at most %d chunks per sequence", p->chunk, hils::kGcMaxChunks);
+    if ((p->max_kv_len + p->chunk - 1) / p->chunk > 65535)
+      return fail(HILS_ERR_UNSUPPORTED, "chunk %d: more than 65535 chunks per sequence", p->chunk);
     if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "a paged cache needs chunk 64 (one page per chunk)");
   }
   if (p->topk < 1 || p->topk > 64)
@@ -496,19 +496,10 @@ int check_decode_params(const hils_decode_params* p) {
 DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   DecodeLayout L{};
   const size_t B = p->batch, H = p->heads, d = p->head_dim, k = p->topk;
-  const size_t N = (p->max_kv_len + 63) / 64;
+  const size_t N = (p->max_kv_len + p->chunk - 1) / p->chunk;
   size_t off = 0;
   L.tcode = off;
   off += align_up(B * (size_t)(p->qcal_rank > 0 ? hils::kTcodeStride : 0) * sizeof(float));
-  if (p->chunk != 64) {                        // chunk sizes 32 and 128: the code and the selection
-    L.scores = L.cand = L.partial = off;
-    L.idx = off;
-    if (!with_sel) off += align_up(B * H * k * sizeof(int32_t));
-    L.w = off;
-    if (!with_sel) off += align_up(B * H * k * sizeof(float));
-    L.total = off;
-    return L;
-  }
   const int qb = hils::decode_score_qb((int)(B * H), (int)N);
   const size_t stride = hils::decode_score_stride((int)N, qb);   // landmarks per pair, padded
   L.scores = L.cand = off;
@@ -529,49 +520,76 @@ DecodeLayout decode_layout(const hils_decode_params* p, bool with_sel) {
   return L;
 }
 
-template <typename T>
-hipError_t run_decode_gchunk(const hils_decode_params* p, const void* q, const void* kc, const void* vc,
-                             const void* lmk, const int32_t* kv_len, const void* h, const void* w_down,
-                             const void* w_up, void* o, int32_t* idx, float* w, char* ws,
-                             const DecodeLayout& L, hipStream_t st) {
+// Chunk sizes 32 and 128: the scan and the selection of the 64-key path (chunk counts from
+// kv_len and C), the forced local chunk's post-pass, then the split attention of
+// launch_decode_attend_gc.
+template <typename T, int D>
+hipError_t run_decode_gc(const hils_decode_params* p, const void* q, const void* kc, const void* vc,
+                         const void* lmk, const int32_t* kv_len, const void* h, const void* w_down,
+                         const void* w_up, void* o, int32_t* idx, float* w, char* ws, const DecodeLayout& L,
+                         hipStream_t st) {
   hipError_t e;
   hipEvent_t* ev = p->n_stage_events >= 5 ? (hipEvent_t*)p->stage_events : nullptr;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   float* tcode = reinterpret_cast<float*>(ws + L.tcode);
-  if (p->qcal_rank > 0) {
-    e = hils::launch_decode_tcode<T>(static_cast<const T*>(h), static_cast<const T*>(w_down), tcode, p->batch,
-                                     p->hidden, p->qcal_rank, st);
-    if (e != hipSuccess) return e;
-  }
+  e = hils::launch_decode_tcode<T>(static_cast<const T*>(h), static_cast<const T*>(w_down), tcode, p->batch,
+                                   p->hidden, p->qcal_rank, st);
+  if (e != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  hils::GcArgs a;
+  hils::DecodeArgs a{};
   a.q = q;
-  a.key = kc;
-  a.val = vc;
-  a.lmk = lmk;
   a.w_up = w_up;
   a.tcode = tcode;
-  a.o = o;
+  a.k_cache = kc;
+  a.v_cache = vc;
+  a.lmk = lmk;
+  a.kv_len = kv_len;
+  a.scores = reinterpret_cast<float*>(ws + L.scores);
   a.idx = idx;
   a.w = w;
-  a.kv_len = kv_len;
+  a.partial = reinterpret_cast<float*>(ws + L.partial);
+  a.o = o;
   a.B = p->batch;
-  a.H = p->heads;
   a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
-  a.Lq = 1;
-  a.Lkv = p->max_kv_len;
+  a.H = p->heads;
+  a.Lmax = p->max_kv_len;
   a.C = p->chunk;
-  a.N = (p->max_kv_len + p->chunk - 1) / p->chunk;
+  a.Nmax = (p->max_kv_len + p->chunk - 1) / p->chunk;
   a.k = p->topk;
   a.r = p->qcal_rank;
-  a.tstride = hils::kTcodeStride;
+  a.score_qb = hils::decode_score_qb(a.B * a.H, a.Nmax);
+  a.score_stride = hils::decode_score_stride(a.Nmax, a.score_qb);
+  a.score_ymax = (int)(a.score_stride / (a.score_qb * hils::kScoreBlock));
+  a.cand = a.Nmax <= kDecodeCandMaxChunks ? static_cast<void*>(ws + L.cand) : nullptr;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
   a.force_local = p->force_local;
-  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
-  e = p->head_dim == 64 ? hils::launch_gchunk<T, 64>(a, st) : hils::launch_gchunk<T, 128>(a, st);
-  if (e != hipSuccess) return e;
-  // scan, selection and attention run in one kernel: their stage marks coincide
-  for (int i = 2; ev && i < 5; ++i)
-    if ((e = hipEventRecord(ev[i], st)) != hipSuccess) return e;
+  if ((e = hils::launch_decode_scores<T, D>(a, st)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if ((e = hils::launch_decode_select(a, st)) != hipSuccess) return e;
+  if (p->force_local) {
+    hils::LocalArgs la;
+    la.q = q;
+    la.lmk = lmk;
+    la.w_up = w_up;
+    la.tcode = tcode;
+    la.kv_len = kv_len;
+    la.idx = idx;
+    la.w = w;
+    la.B = p->batch;
+    la.H = p->heads;
+    la.L = p->max_kv_len;
+    la.N = a.Nmax;
+    la.G = a.G;
+    la.k = p->topk;
+    la.r = p->qcal_rank;
+    la.tstride = hils::kTcodeStride;
+    la.lc = p->chunk == 32 ? 5 : 7;
+    la.scale = a.scale;
+    if ((e = hils::launch_force_local<T, D>(la, true, st)) != hipSuccess) return e;
+  }
+  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  if ((e = hils::launch_decode_attend_gc<T, D>(a, p->chunk, st)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -618,6 +636,7 @@ hipError_t run_decode(const hils_decode_params* p, const void* q, const void* kc
   a.cand = cand ? static_cast<void*>(ws + L.cand) : nullptr;
   a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)D);
   a.force_local = p->force_local;
+  a.C = 64;
   if (hils::decode_fused_ok<T>(a)) {           // scan, selection and attention in one kernel
     if ((e = hils::launch_decode_fused<T, D>(a, st)) != hipSuccess) return e;
     for (int s = 2; s <= 4; ++s)
@@ -845,9 +864,14 @@ int decode_entry(const hils_decode_params* p, const void* q, const void* k_cache
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (p->chunk != 64) {
-    err = p->dtype == HILS_DTYPE_BF16
-              ? run_decode_gchunk<hils::bf16>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
-              : run_decode_gchunk<float>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
+    if (p->dtype == HILS_DTYPE_BF16)
+      err = p->head_dim == 64
+                ? run_decode_gc<hils::bf16, 64>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
+                : run_decode_gc<hils::bf16, 128>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
+    else
+      err = p->head_dim == 64
+                ? run_decode_gc<float, 64>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)
+                : run_decode_gc<float, 128>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s);
   } else if (p->dtype == HILS_DTYPE_BF16) {
     err = p->head_dim == 64
               ? run_decode<hils::bf16, 64>(p, q, k_cache, v_cache, lmk, kv_len, h, w_down, w_up, o, idx, w, ws, L, s)

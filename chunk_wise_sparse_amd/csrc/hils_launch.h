@@ -131,6 +131,8 @@ struct DecodeArgs {
   int score_ymax;       // scan workgroups per pair: ceil(ceil(Nmax / 256) / score_qb)
   float scale;
   int force_local;      // the selection is written out and amended before the attention
+  int C;                // keys per chunk: 64; 32 or 128 for the scan, the selection and
+                        // launch_decode_attend_gc (contiguous caches)
 };
 
 // Dense causal attention (the full-attention baseline): prefill over [B,H,L,d] (L % 64 == 0) and
@@ -243,5 +245,9 @@ template <typename T>
 bool decode_select_fused(const DecodeArgs& a);
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st);
+// Chunks of C = 32 or 128 keys (contiguous caches, the selection in idx / w): split attention into
+// `partial`, then the fixed-order reduce into o.
+template <typename T, int D>
+hipError_t launch_decode_attend_gc(const DecodeArgs& a, int C, hipStream_t st);
 
 }  // namespace hils

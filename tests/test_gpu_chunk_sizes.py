@@ -3,8 +3,9 @@ of small prefills (ragged last chunk, GQA, forced local chunk), and ragged decod
 prefills select with the MFMA kernel when the sequence is whole 64-query tiles (else in the
 generic kernel; the forced local chunk amends the MFMA selection in a post-pass, and the generic
 selection takes it directly) and attend in the chunk-major MFMA kernels (several
-work items per chunk, partial last chunks read with clamped rows); fp32 prefills and decode run
-the generic kernel throughout."""
+work items per chunk, partial last chunks read with clamped rows); fp32 prefills run the
+generic kernel.  Decode steps at these sizes take the 64-key path's landmark scan and selection
+and a split attention over C-key chunks."""
 import math
 
 import numpy as np
@@ -103,6 +104,12 @@ DECODE = [
     (synth.DecodeConfig("c32_dec_bf16_local", 3, 2, 4000, 128, 32, 8, "bf16", 16, 256, kv_len=(4000, 31, 33)),
      1, True),
     (synth.DecodeConfig("c128_dec_fp32_local", 2, 2, 3000, 64, 128, 4, "fp32", 0, 0, kv_len=(3000, 700)), 1, True),
+    # more than 8192 chunks: dense scores and the radix selection instead of candidate lists
+    (synth.DecodeConfig("c32_dec_bf16_dense_scores", 2, 2, 300000, 64, 32, 16, "bf16", 8, 128,
+                        kv_len=(300000, 262177)), 1, False),
+    # one key in the last chunk, a cache of exactly one chunk, and k above the candidates
+    (synth.DecodeConfig("c128_dec_bf16_short", 3, 2, 1000, 128, 128, 12, "bf16", 16, 256, kv_len=(897, 128, 1)),
+     1, False),
 ]
 
 

@@ -1,4 +1,7 @@
-// HiLS for chunk sizes C other than 64 (32 and 128): prefill rows and decode steps.  The steps
+// HiLS for chunk sizes C other than 64 (32 and 128): the selection and attention of prefill rows
+// that the MFMA kernels do not take (fp32; bf16 selection of sequences that are not whole
+// 64-query tiles, with attention left to the chunk-major kernels), and of decode-shaped launches
+// (kv_len given; the library's decode steps use the landmark scan instead).  The steps
 // are the method's [HiLS-Attention model page, "Model Description"; HiLS Attention explainer
 // (molayo1419.me), "Core idea" and "Engineering details"]: q~ = q + W_up t (Q-Cal), a score per
 // causal chunk against its landmark key, the top-k chunks (ties to the smaller index; with the

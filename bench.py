@@ -367,6 +367,36 @@ def length_sweep_from(P512, lengths=(32768, 65536, 131072, 262144, 524288)):
     return out
 
 
+def prefill_chunk_sizes(scfg, dev):
+    """The 32K prefill workload at chunk sizes 32 and 128 (MFMA selection, chunk-major MFMA
+    attention): stage times of three calls after one untimed call."""
+    from chunk_wise_sparse_amd import synth
+    out = {}
+    for C in (32, 128):
+        ccfg = dataclasses.replace(scfg, chunk=C, name=f"prefill_32k_chunk{C}")
+        PC = synth.make_prefill_inputs_torch(ccfg, dev)
+        time_prefill(PC, ccfg, 1, chunk=C)
+        st = time_prefill(PC, ccfg, 3, chunk=C)
+        out[f"prefill_32k_chunk{C}"] = dict(
+            prefill_ms=sum(st), qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
+            tflops=prefill_work(ccfg)["total"] / (sum(st) * 1e-3) / 1e12)
+        del PC
+    return out
+
+
+def chunk_sizes_only():
+    """bench.py --chunk-sizes: the chunk-size extras alone, one JSON line."""
+    import torch
+    from chunk_wise_sparse_amd import hils, synth
+    hils.load()
+    dev = torch.device("cuda:0")
+    res = prefill_chunk_sizes(synth.CONFIGS["prefill_32k"], dev)
+    dcfg = synth.CONFIGS["decode_512k"]
+    D = synth.make_decode_inputs_torch(dcfg, dev)
+    res["decode_chunk_sizes"] = bench_decode_chunk_sizes(D, dcfg, dev)
+    print(json.dumps(res), flush=True)
+
+
 def bench_decode_chunk_sizes(D, dcfg, dev):
     """The 512K decode step at chunk 128 and its first 256K tokens at chunk 32 (the generic
     selection's limit is 8192 chunks): the same q, caches and Q-Cal inputs, landmarks made for the
@@ -445,6 +475,9 @@ def main():
                          "the dense comparators")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--chunk-sizes", action="store_true",
+                    help="only time the 32K prefill workload at chunk sizes 32 and 128 and the 512K decode step "
+                         "at chunk 128 (256K at chunk 32), one JSON line, and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the prefill of the 128K workload's shape at 32K..512K tokens "
                          "(one JSON line per length, beside this library's dense causal prefill of "
@@ -460,6 +493,9 @@ def main():
         return
     if args.sweep:
         length_sweep()
+        return
+    if args.chunk_sizes:
+        chunk_sizes_only()
         return
 
     import torch
@@ -661,17 +697,7 @@ def main():
                                      attn_mode="auto")
         time_prefill(P32, scfg, 1)
         extras["prefill_32k"]["union_walk"] = stage_dict(scfg, time_prefill(P32, scfg, 5))
-        # the same workload at chunk sizes 32 and 128 (selection in the generic kernel, attention
-        # in the chunk-major MFMA kernels)
-        for C in (32, 128):
-            ccfg = dataclasses.replace(scfg, chunk=C, name=f"prefill_32k_chunk{C}")
-            PC = synth.make_prefill_inputs_torch(ccfg, dev)
-            time_prefill(PC, ccfg, 1, chunk=C)
-            st = time_prefill(PC, ccfg, 3, chunk=C)
-            extras[f"prefill_32k_chunk{C}"] = dict(
-                prefill_ms=sum(st), qcal_code_ms=st[0], select_ms=st[1], attention_ms=st[2],
-                tflops=prefill_work(ccfg)["total"] / (sum(st) * 1e-3) / 1e12)
-            del PC
+        extras.update(prefill_chunk_sizes(scfg, dev))
         extras["prefill_512k"], P512 = bench_512k(dev)
         print("[bench] extras: length sweep 32K..512K", file=sys.stderr, flush=True)
         extras["length_sweep"] = length_sweep_from(P512)

@@ -407,9 +407,7 @@ def bench_decode_chunk_sizes(D, dcfg, dev):
     for C, L in ((128, dcfg.max_kv_len), (32, dcfg.max_kv_len // 2)):
         kc = D["k_cache"] if L == dcfg.max_kv_len else D["k_cache"][:, :, :L].contiguous()
         vc = D["v_cache"] if L == dcfg.max_kv_len else D["v_cache"][:, :, :L].contiguous()
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(synth.subseed(dcfg.seed, "lmk_noise"))
-        lmk = synth._landmarks_dev(gen, kc, C, kc.dtype)
+        lmk = synth.chunk_landmarks_dev(kc, C, dcfg.seed)
         kvl = torch.full_like(D["kv_len"], L)
         run = lambda: hils.decode(D["q"], kc, vc, lmk, kvl, D["h"], D["w_down"], D["w_up"], topk=dcfg.topk,
                                   chunk=C)

@@ -255,6 +255,15 @@ def _landmarks_dev(gen, k, chunk: int, dtype):
     return lmk
 
 
+def chunk_landmarks_dev(k, chunk: int, seed: int = 0):
+    """Landmarks of a device key cache [B,H,L,d] (L a multiple of chunk) for another chunk size, by
+    the workloads' recipe (chunk means plus noise, no needles), in k's dtype."""
+    import torch
+    gen = torch.Generator(device=k.device)
+    gen.manual_seed(subseed(seed, "lmk_noise"))
+    return _landmarks_dev(gen, k, chunk, k.dtype)
+
+
 def make_prefill_inputs_torch(cfg: PrefillConfig, device="cuda", q_mode: Optional[str] = None,
                               h_mode: Optional[str] = None):
     """Device inputs for a prefill config (torch tensors in the run dtype)."""

@@ -8,17 +8,16 @@ namespace hils {
 constexpr int kGcMaxChunks = 8192;             // chunks per sequence (scores kept in LDS)
 
 struct GcArgs {
-  const void* q;             // prefill [B, H, Lq, d]; decode [B, H, d] (Lq = 1)
-  const void* key;           // [B, Hk, Lkv, d]
-  const void* val;           // [B, Hk, Lkv, d]
-  const void* lmk;           // [B, Hk, N, d], N = ceil(Lkv / C)
+  const void* q;             // [B, H, L, d]
+  const void* key;           // [B, Hk, L, d]
+  const void* val;           // [B, Hk, L, d]
+  const void* lmk;           // [B, Hk, N, d], N = ceil(L / C)
   const void* w_up;          // [H * d, r] (r > 0)
   const float* tcode;        // Q-Cal code rows, tstride floats apart (r > 0)
   void* o;                   // like q; NULL: selection only (idx / w written, no attention)
-  int32_t* idx;              // [B, H, Lq, k]
-  float* w;                  // [B, H, Lq, k]
-  const int32_t* kv_len;     // decode: [B], the query at kv_len - 1 (clamped to [1, Lkv]); prefill: NULL
-  int B, H, G, Lq, Lkv, N, C, k, r, tstride, force_local;
+  int32_t* idx;              // [B, H, L, k]
+  float* w;                  // [B, H, L, k]
+  int B, H, G, L, N, C, k, r, tstride, force_local;
   float scale;
 };
 

@@ -1,7 +1,6 @@
-// HiLS for chunk sizes C other than 64 (32 and 128): the selection and attention of prefill rows
-// that the MFMA kernels do not take (fp32; bf16 selection of sequences that are not whole
-// 64-query tiles, with attention left to the chunk-major kernels), and of decode-shaped launches
-// (kv_len given; the library's decode steps use the landmark scan instead).  The steps
+// HiLS prefill for chunk sizes C other than 64 (32 and 128), for the rows the MFMA kernels do not
+// take: selection and attention for fp32, and for bf16 the selection of sequences that are not
+// whole 64-query tiles (the chunk-major kernels attend afterwards).  The steps
 // are the method's [HiLS-Attention model page, "Model Description"; HiLS Attention explainer
 // (molayo1419.me), "Core idea" and "Engineering details"]: q~ = q + W_up t (Q-Cal), a score per
 // causal chunk against its landmark key, the top-k chunks (ties to the smaller index; with the
@@ -11,7 +10,7 @@
 // The 64-key kernels tie their tiles to one 64-key chunk (a 64-query tile shares one candidate
 // set, a chunk is one MFMA tile); this path has no such tie and no MFMA.  W waves own one query
 // row (W = 1: each wave its own row, kGcRows rows per workgroup, for prefills with many rows;
-// W = 4 for prefill rows with more than 2048 chunks; W = 16 for decode and other launches of few
+// W = 4 for rows with more than 2048 chunks; W = 16 for launches of few
 // rows).  The row's scores sit in LDS (up to 8192 chunks, sized to the launch's chunk count);
 // the k-th largest is found by bisection over the order-preserving 32-bit keys with row-wide
 // counts; the first wave then takes the keys above it and the earliest equal ones in chunk
@@ -54,7 +53,7 @@ __global__ __launch_bounds__(W == 1 ? 64 * kGcRows : 64 * W) void gchunk_kernel(
   const size_t row = (size_t)blockIdx.x * SL + slot;
   // W == 1: a wave past the last row leaves (its row-mates never wait for it).  W > 1: the grid
   // holds exactly one workgroup per row.
-  if (W == 1 && row >= (size_t)a.B * a.H * a.Lq) return;
+  if (W == 1 && row >= (size_t)a.B * a.H * a.L) return;
   float* sc = gc_sc + (size_t)slot * a.N;
   // A wave's own LDS writes, visible to its other lanes.
   auto wsync = [] {
@@ -80,12 +79,11 @@ __global__ __launch_bounds__(W == 1 ? 64 * kGcRows : 64 * W) void gchunk_kernel(
     }
     return s;
   };
-  const int bh = (int)(row / a.Lq), i0 = (int)(row % a.Lq);
+  const int bh = (int)(row / a.L), i0 = (int)(row % a.L);
   const int b = bh / a.H, h = bh % a.H;
   const size_t kvp = (size_t)b * (a.H / a.G) + h / a.G;
-  const int pos = a.kv_len ? min(max(a.kv_len[b], 1), a.Lkv) - 1 : i0;
   const int C = a.C;
-  const int nc = pos / C + 1;                  // causal chunks; the last one holds the query
+  const int nc = i0 / C + 1;                   // causal chunks; the last one holds the query
   const float scale = a.scale;
 
   // q and q~ = round(q + W_up t): the offset and the sum in fp32, one rounding to the dtype.
@@ -97,7 +95,7 @@ __global__ __launch_bounds__(W == 1 ? 64 * kGcRows : 64 * W) void gchunk_kernel(
       const float qv = to_f32(qrow[e]);
       float qt = qv;
       if (a.r > 0) {
-        const float* t = a.tcode + (size_t)(a.kv_len ? b : b * a.Lq + i0) * a.tstride;
+        const float* t = a.tcode + ((size_t)b * a.L + i0) * a.tstride;
         const T* wu = static_cast<const T*>(a.w_up) + (size_t)(h * D + e) * a.r;
         float dq = 0.f;
         if (a.r % VE == 0) {
@@ -203,12 +201,12 @@ __global__ __launch_bounds__(W == 1 ? 64 * kGcRows : 64 * W) void gchunk_kernel(
   float acc[VE];
 #pragma unroll
   for (int z = 0; z < VE; ++z) acc[z] = 0.f;
-  const T* kbase = static_cast<const T*>(a.key) + kvp * a.Lkv * D;
-  const T* vbase = static_cast<const T*>(a.val) + kvp * a.Lkv * D + dv * VE;
+  const T* kbase = static_cast<const T*>(a.key) + kvp * a.L * D;
+  const T* vbase = static_cast<const T*>(a.val) + kvp * a.L * D + dv * VE;
   for (int s = part; s < cnt; s += W) {
     const int j = il[slot][s];
     const float wj = wls[slot][s];
-    const int lo = j * C, nk = min(lo + C, pos + 1) - lo;
+    const int lo = j * C, nk = min(lo + C, i0 + 1) - lo;
     float lmax = -INFINITY;
     for (int t = lane; t < nk; t += 64) {
       const vecT* kr = reinterpret_cast<const vecT*>(kbase + (size_t)(lo + t) * D);
@@ -280,7 +278,7 @@ hipError_t launch_gchunk_w(const GcArgs& a, size_t rows, hipStream_t st) {
 
 template <typename T, int D>
 hipError_t launch_gchunk(const GcArgs& a, hipStream_t st) {
-  const size_t rows = (size_t)a.B * a.H * a.Lq;
+  const size_t rows = (size_t)a.B * a.H * a.L;
   if (rows == 0) return hipSuccess;
   if (rows <= (size_t)kGcFewRows) return launch_gchunk_w<T, D, 16>(a, rows, st);
   if (a.N > kGcWideChunks) return launch_gchunk_w<T, D, 4>(a, rows, st);

@@ -277,11 +277,10 @@ hipError_t run_prefill_gchunk(const hils_prefill_params* p, const void* q, const
   a.o = cm ? nullptr : o;
   a.idx = idx;
   a.w = w;
-  a.kv_len = nullptr;
   a.B = p->batch;
   a.H = p->heads;
   a.G = p->kv_heads > 0 ? p->heads / p->kv_heads : 1;
-  a.Lq = a.Lkv = p->seq_len;
+  a.L = p->seq_len;
   a.C = p->chunk;
   a.N = (p->seq_len + p->chunk - 1) / p->chunk;
   a.k = p->topk;

@@ -252,6 +252,51 @@ def pin_exact_chunk_mass_identity():
         assert np.allclose(r["o"], dense[i], rtol=0, atol=2e-5), (i, np.abs(r["o"] - dense[i]).max())
 
 
+def pin_exact_chunk_mass_other_chunk_sizes():
+    """The exact-chunk-mass identity at chunk sizes 32 and 128, with a partial last chunk (the
+    sequence is not a multiple of the chunk): the factorisation with every chunk kept and each
+    landmark score equal to its chunk's log attention mass is dense causal attention."""
+    g = _rng(21)
+    L, d = 300, 16
+    s = 0.25
+    q = g.standard_normal((L, d)).astype(np.float32)
+    k = g.standard_normal((L, d)).astype(np.float32)
+    v = g.standard_normal((L, d)).astype(np.float32)
+    dense = _dense_causal(q, k, v, s)
+    for C in (32, 128):
+        N = -(-L // C)
+        for i in (0, C - 1, C, 150, 255, 256, L - 1):
+            c = i // C
+            a = s * (k[: i + 1].astype(np.float64) @ q[i].astype(np.float64))
+            lse = np.array([scipy.special.logsumexp(a[j * C:min((j + 1) * C, i + 1)]) for j in range(c + 1)])
+            qq = q[i].astype(np.float64)
+            lmk = np.zeros((N, d), dtype=np.float32)
+            lmk[: c + 1] = (np.outer(lse / s, qq) / qq.dot(qq)).astype(np.float32)
+            inp = dict(q=q[None, None], k=k[None, None], v=v[None, None], lmk=lmk[None, None])
+            r = O.prefill_rows(inp, [(0, 0, i)], C, c + 1, "fp32", scale=s)[(0, 0, i)]
+            assert np.allclose(r["o"], dense[i], rtol=0, atol=2e-5), (C, i, np.abs(r["o"] - dense[i]).max())
+
+
+def pin_decode_matches_prefill_row_other_chunk_sizes():
+    """decode(kv_len = i + 1) equals prefill row i at chunk sizes 32 and 128, the cache ending
+    inside a chunk."""
+    for C, L in ((32, 200), (128, 300)):
+        inp = _small_inputs(22, L=L, C=C, dtype="bf16")
+        N = -(-L // C)
+        import torch
+        lmk = (_rng(23).standard_normal((1, 2, N, 16)) * 0.5).astype(np.float32)
+        inp["lmk"] = torch.from_numpy(lmk).to(torch.bfloat16).float().numpy()
+        rows = [(0, 0, 0), (0, 1, C - 1), (0, 0, C), (0, 1, L // 2), (0, 0, L - 1)]
+        pre = O.prefill_rows(inp, rows, C, 3, "bf16")
+        for (b, h, i) in rows:
+            dec_in = dict(q=inp["q"][:, :, i], k_cache=inp["k"], v_cache=inp["v"], lmk=inp["lmk"],
+                          kv_len=np.array([i + 1], np.int32), h=inp["h"][:, i], w_down=inp["w_down"],
+                          w_up=inp["w_up"])
+            dec = O.decode(dec_in, C, 3, "bf16", pairs=[(b, h)])[(b, h)]
+            assert np.array_equal(dec["idx"], pre[(b, h, i)]["idx"]), (C, i)
+            assert np.array_equal(dec["o"], pre[(b, h, i)]["o"]), (C, i)
+
+
 def pin_causality():
     """Row i ignores keys, values and landmarks after it."""
     inp = _small_inputs(14, L=256, C=64)

@@ -57,6 +57,9 @@ PREFILL = [
     # forced local chunk: the MFMA selection amended by the post-pass, and (ragged) the generic one
     (synth.PrefillConfig("c128_bf16_d64_local_L4096", 1, 2, 4096, 64, 128, 4, "bf16", 8, 128), 1, True),
     (synth.PrefillConfig("c32_bf16_d64_local_L999", 1, 2, 999, 64, 32, 6, "bf16", 8, 128), 1, True),
+    # one 64-query tile: a single partial 128-key chunk, and two 32-key chunks with k = 1
+    (synth.PrefillConfig("c128_bf16_d128_L64", 2, 2, 64, 128, 128, 4, "bf16", 8, 128), 1, False),
+    (synth.PrefillConfig("c32_bf16_d64_L64_k1", 1, 3, 64, 64, 32, 1, "bf16", 8, 128), 1, False),
 ]
 
 
@@ -107,6 +110,9 @@ DECODE = [
     # more than 8192 chunks: dense scores and the radix selection instead of candidate lists
     (synth.DecodeConfig("c32_dec_bf16_dense_scores", 2, 2, 300000, 64, 32, 16, "bf16", 8, 128,
                         kv_len=(300000, 262177)), 1, False),
+    # fp32 past 8192 chunks (dense scores, radix selection)
+    (synth.DecodeConfig("c32_dec_fp32_dense_scores", 1, 2, 290000, 64, 32, 8, "fp32", 8, 128,
+                        kv_len=(289999,)), 1, False),
     # one key in the last chunk, a cache of exactly one chunk, and k above the candidates
     (synth.DecodeConfig("c128_dec_bf16_short", 3, 2, 1000, 128, 128, 12, "bf16", 16, 256, kv_len=(897, 128, 1)),
      1, False),
@@ -142,3 +148,18 @@ def test_decode_chunk_size(lib, cfg, G, local):
     print(f"[parity] {cfg.name}: {stats['n_rows']} (b,h), max|do| {stats['max_abs']:.3g}, "
           f"max|dw| {stats['max_w']:.3g}, near-tie swaps {stats['n_diff_sel']}", flush=True)
     assert_within(stats, cfg.dtype)
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_prefill_chunk_size_ignores_mode_and_q_tile(lib, C):
+    """attn_mode and q_tile leave chunk sizes 32 and 128 on their one path: bitwise equal results."""
+    from chunk_wise_sparse_amd import hils
+    cfg = synth.PrefillConfig(f"c{C}_modes", 1, 2, 2048, 128, C, 8, "bf16", 16, 256)
+    print(f"[case] modes chunk={C} {cfg}", flush=True)
+    dev = TP._to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)
+    ref = TP._run(lib, dev, cfg, chunk=C)
+    for kw in (dict(attn_mode=hils.ATTN_UNION), dict(attn_mode=hils.ATTN_AUTO), dict(q_tile=16)):
+        got = TP._run(lib, dev, cfg, chunk=C, **kw)
+        TP._torch().cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert TP._torch().equal(a, b), kw

@@ -1178,7 +1178,15 @@ __global__ __launch_bounds__(D * 2) void decode_reduce_kernel(const DecodeArgs a
 #pragma unroll
   for (int gq = g0; gq < NG; gq += 2) {
     float s = 0.f;
-    for (int u = gq; u < a.k; u += NG) s += P[(size_t)u * D];
+    // the group's (at most 8) slots loaded together, then added in slot order
+    float pv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int u = gq + NG * t;
+      pv[t] = u < a.k ? P[(size_t)u * D] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s += pv[t];
     part[gq][d] = s;
   }
   __syncthreads();

@@ -196,11 +196,13 @@ def prefill(q, k, v, lmk, h=None, w_down=None, w_up=None, *, topk: int, chunk: i
             q_tile: int = 0, scale: Optional[float] = None, return_selection: bool = False,
             out=None, workspace=None, events: Optional[StageEvents] = None, attn_mode: int = 0,
             block_table=None, force_local: bool = False):
-    """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,L/C,d]; h [B,L,D]; w_down [r,D];
-    w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
+    """HiLS prefill.  q [B,H,L,d]; k, v [B,Hkv,L,d]; lmk [B,Hkv,ceil(L/C),d]; h [B,L,D];
+    w_down [r,D]; w_up [H*d,r].  Hkv divides H (grouped-query attention when Hkv < H).
+    chunk: 32, 64 or 128 keys per chunk.
     attn_mode: ATTN_UNION (0), ATTN_CHUNK_MAJOR (1, bf16; for selections with little overlap
     between neighbouring rows) or ATTN_AUTO (2, bf16; measures the overlap and picks one; waits
-    on the stream once).
+    on the stream once).  Chunks of 32 and 128 keys always attend chunk-major (bf16) and ignore
+    attn_mode and q_tile.
 
     Paged keys/values: block_table [B, S] int32 (device) and k, v pools [pages, Hkv, C, d]; chunk j
     of sequence b is page block_table[b, j].

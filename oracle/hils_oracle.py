@@ -58,6 +58,13 @@ encoding on the dimensions inside the pre-training window, no position encoding 
      window's length in tokens; the other pairs are left as they are;
   H3 the caller applies it to q and k before the attention (prefill rows at positions pos0 + i,
      a decode query at kv_len - 1); landmarks and the Q-Cal offset see no position.
+
+Landmark of the chunk still being filled during decode ([P3] "Core idea": a landmark token is
+appended at the end of each chunk, so a chunk that has not reached C tokens has none yet):
+  P1 its stand-in is the mean of the chunk's keys so far, rows jC .. kv_len-1 of the cache with
+     j = floor((kv_len - 1) / C), rounded once to the run dtype; it is recomputed from the cache
+     at every step (no running state), and the caller replaces it with the model's landmark once
+     the chunk is complete.
 """
 from __future__ import annotations
 
@@ -71,7 +78,7 @@ __all__ = [
     "select_top_k", "select_with_local", "inter_chunk_weights", "intra_chunk_attention", "fuse", "prefill_rows",
     "prefill", "decode", "attend_given_selection", "dense_attention_row", "dense_causal_rows",
     "dense_decode", "chunk_backward", "inter_chunk_backward", "prefill_backward",
-    "hope_rotated_pairs", "hope_rotate",
+    "hope_rotated_pairs", "hope_rotate", "partial_landmark",
 ]
 
 
@@ -521,3 +528,21 @@ def hope_rotate(x: np.ndarray, positions, rope_base: float, train_len: int) -> n
         out[..., 2 * i + 1] = a * s_ + b * c
     return out
 
+
+# ------------------------------------------------------------------------------------------
+# Landmark of the chunk still being filled (P1)
+# ------------------------------------------------------------------------------------------
+def partial_landmark(k_cache: np.ndarray, kv_len, chunk: int, dtype: str) -> Dict[tuple, tuple]:
+    """k_cache [B, Hk, Lmax, d], kv_len [B].  For every (sequence b, key/value head g): the chunk
+    j = floor((kv_len[b] - 1) / C) that holds the newest key, and the mean of its keys so far
+    (rows jC .. kv_len[b] - 1, float64), rounded once to the run dtype (P1).  kv_len is clamped to
+    [1, Lmax].  Returns {(b, g): (j, landmark [d])}."""
+    B, Hk, Lmax, _ = k_cache.shape
+    out = {}
+    for b in range(B):
+        n_keys = min(max(int(kv_len[b]), 1), Lmax)
+        j = (n_keys - 1) // chunk
+        for g in range(Hk):
+            rows = np.asarray(k_cache[b, g, j * chunk:n_keys], dtype=np.float64)
+            out[(b, g)] = (j, round_to_run_dtype(rows.sum(axis=0) / rows.shape[0], dtype))
+    return out

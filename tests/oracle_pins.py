@@ -679,4 +679,53 @@ def pin_hope_window_split():
         assert np.allclose(np.hypot(z[:, 2 * i], z[:, 2 * i + 1]), np.hypot(x[:, 2 * i], x[:, 2 * i + 1]), atol=1e-12)
 
 
+def pin_partial_landmark_arithmetic_keys():
+    """Keys in arithmetic progression (row t holds c + t u, small integers, exact in fp32): the
+    landmark of the chunk holding the newest key is c + u (first + last) / 2 over that chunk's
+    rows so far; one key gives the key itself, a full chunk its own mean, and kv_len is clamped."""
+    B, Hk, Lmax, d = 6, 2, 300, 4
+    u = np.array([1.0, -2.0, 0.5, 4.0])
+    c = np.array([3.0, 0.0, -1.0, 2.0])
+    t = np.arange(Lmax, dtype=np.float64)[:, None]
+    k = np.broadcast_to((c + t * u)[None, None], (B, Hk, Lmax, d)).astype(np.float32).copy()
+    k[:, 1] *= -1.0                                    # the second key/value head differs
+    for C in (32, 64, 128):
+        kv_len = np.array([1, C, C + 1, 2 * C + 7, Lmax, Lmax + 50], np.int32)
+        res = O.partial_landmark(k, kv_len, C, "fp32")
+        for b in range(B):
+            n_keys = min(int(kv_len[b]), Lmax)
+            j = (n_keys - 1) // C
+            first, last = j * C, n_keys - 1
+            for g in range(Hk):
+                want = (c + u * (first + last) / 2.0) * (1.0 if g == 0 else -1.0)
+                got_j, got = res[(b, g)]
+                assert got_j == j, (C, b, got_j, j)
+                assert np.array_equal(got, want.astype(np.float32)), (C, b, g, got, want)
+
+
+def pin_partial_landmark_only_its_rows():
+    """The landmark depends on rows jC .. kv_len-1 only, not on their order, and equal keys give
+    that key exactly (bf16)."""
+    g = _rng(31)
+    B, Hk, Lmax, d, C = 3, 2, 200, 8, 64
+    k = g.standard_normal((B, Hk, Lmax, d)).astype(np.float32)
+    kv_len = np.array([70, 128, 200], np.int32)
+    base = O.partial_landmark(k, kv_len, C, "fp32")
+    pert = k.copy()
+    for b in range(B):
+        j = (int(kv_len[b]) - 1) // C
+        pert[b, :, : j * C] += 3.0                     # earlier chunks
+        pert[b, :, int(kv_len[b]):] -= 5.0             # rows past the newest key
+        rows = np.arange(j * C, int(kv_len[b]))
+        pert[b, :, rows] = k[b, :, rows[::-1]]        # the chunk's rows reversed
+    got = O.partial_landmark(pert, kv_len, C, "fp32")
+    for key in base:
+        assert got[key][0] == base[key][0]
+        assert np.allclose(got[key][1], base[key][1], rtol=0, atol=1e-6), key
+    same = np.broadcast_to(np.array([1.5, -0.25, 3.0, 0.0078125, -7.0, 2.0, 0.5, 1.0], np.float32),
+                           (B, Hk, Lmax, d)).copy()
+    for (b, gh), (j, lm) in O.partial_landmark(same, kv_len, C, "bf16").items():
+        assert np.array_equal(lm, same[0, 0, 0]), (b, gh)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -138,7 +138,25 @@ def _hope_window_reversed(d, rope_base, train_len, _o=O.hope_rotated_pairs):
     return np.asarray([i for i in range(d // 2) if i not in inside], dtype=np.int64)
 
 
+def _partial_landmark_over_chunk(k_cache, kv_len, chunk, dtype):
+    # divides the chunk's key sum by C instead of by the keys present
+    out = {}
+    for (b, g), (j, lm) in O.__dict__["_orig_partial_landmark"](k_cache, kv_len, chunk, dtype).items():
+        n = min(max(int(kv_len[b]), 1), k_cache.shape[2]) - j * chunk
+        out[(b, g)] = (j, O.round_to_run_dtype(np.asarray(lm, np.float64) * n / chunk, dtype))
+    return out
+
+
+def _partial_landmark_wrong_chunk(k_cache, kv_len, chunk, dtype):
+    # takes the chunk of position kv_len rather than of the newest key kv_len - 1
+    return O.__dict__["_orig_partial_landmark"](k_cache, np.asarray(kv_len) + 1, chunk, dtype)
+
+
+O._orig_partial_landmark = O.partial_landmark
+
 MUTATIONS = {
+    "partial_landmark_over_chunk": ("partial_landmark", _partial_landmark_over_chunk),
+    "partial_landmark_wrong_chunk": ("partial_landmark", _partial_landmark_wrong_chunk),
     "hope_rotation_reversed": ("hope_rotate", lambda x, p, b, t, _o=O.hope_rotate: _o(x, -np.asarray(p), b, t)),
     "hope_half_split_pairs": ("hope_rotate", _hope_half_split),
     "hope_theta_exponent": ("hope_rotate", _hope_theta_exponent),

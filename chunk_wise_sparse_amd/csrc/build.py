@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 SOURCES = ["hils_api.hip", "qcal.hip", "select.hip", "select_fast.hip", "attention.hip", "decode.hip",
-           "dense.hip", "backward.hip", "pad.hip", "local.hip", "hope.hip", "gchunk.hip"]
+           "dense.hip", "backward.hip", "pad.hip", "local.hip", "hope.hip", "gchunk.hip", "landmark.hip"]
 LIB = os.path.join(PKG, "libhils.so")
 # Per-file flags.  Selection and attention take finite scores only, so NaN handling is dropped
 # there (max/min then need no NaN quieting of their operands).

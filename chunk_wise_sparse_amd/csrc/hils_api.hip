@@ -12,6 +12,7 @@
 #include "hils.h"
 #include "hils_launch.h"
 #include "gchunk.h"
+#include "landmark.h"
 #include "hope.h"
 
 namespace {
@@ -1054,6 +1055,49 @@ int hils_hope_rotate(const hils_hope_params* p, void* x, const int32_t* position
   else
     err = d == 64 ? hils::launch_hope_rotate<float, 64>(a, s) : hils::launch_hope_rotate<float, 128>(a, s);
   if (err != hipSuccess) return hip_fail(err, "hils_hope_rotate");
+  return HILS_OK;
+}
+
+int hils_partial_landmark(const hils_landmark_params* p, const void* k_cache, void* lmk, const int32_t* kv_len,
+                          void* stream) {
+  g_last_error.clear();
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "params is NULL");
+  if (!k_cache || !lmk || !kv_len) return fail(HILS_ERR_INVALID_ARG, "a required tensor is NULL");
+  if (p->batch < 1 || p->kv_heads < 1 || p->max_kv_len < 1)
+    return fail(HILS_ERR_INVALID_ARG, "batch, kv_heads and max_kv_len must be positive");
+  if (p->dtype != HILS_DTYPE_BF16 && p->dtype != HILS_DTYPE_FP32)
+    return fail(HILS_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp32", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (p->chunk != 32 && p->chunk != 64 && p->chunk != 128)
+    return fail(HILS_ERR_UNSUPPORTED, "chunk %d is not supported (32, 64 or 128)", p->chunk);
+  if ((double)p->batch * p->kv_heads * p->max_kv_len * p->head_dim > 4e18 / 8 ||
+      (double)p->batch * p->kv_heads > 2147483647.0)
+    return fail(HILS_ERR_UNSUPPORTED, "problem too large");
+  if (!aligned16(k_cache) || !aligned16(lmk)) return fail(HILS_ERR_ALIGNMENT, "a tensor is not 16-byte aligned");
+  if ((uintptr_t)kv_len & 3u) return fail(HILS_ERR_ALIGNMENT, "kv_len is not 4-byte aligned");
+  const size_t e = elem_bytes(p->dtype), B = p->batch, Hk = p->kv_heads, d = p->head_dim;
+  const size_t N = ((size_t)p->max_kv_len + p->chunk - 1) / p->chunk;
+  const Range kr{k_cache, B * Hk * (size_t)p->max_kv_len * d * e, "k_cache"}, lr{lmk, B * Hk * N * d * e, "lmk"},
+      vr{kv_len, B * 4, "kv_len"};
+  if (overlap(lr, kr) || overlap(lr, vr)) return fail(HILS_ERR_INVALID_ARG, "lmk overlaps an input");
+  hils::PartialLmkArgs a;
+  a.k_cache = k_cache;
+  a.lmk = lmk;
+  a.kv_len = kv_len;
+  a.B = p->batch;
+  a.Hk = p->kv_heads;
+  a.Lmax = p->max_kv_len;
+  a.N = (int)N;
+  a.C = p->chunk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (p->dtype == HILS_DTYPE_BF16)
+    err = d == 64 ? hils::launch_partial_landmark<hils::bf16, 64>(a, s)
+                  : hils::launch_partial_landmark<hils::bf16, 128>(a, s);
+  else
+    err = d == 64 ? hils::launch_partial_landmark<float, 64>(a, s) : hils::launch_partial_landmark<float, 128>(a, s);
+  if (err != hipSuccess) return hip_fail(err, "hils_partial_landmark");
   return HILS_OK;
 }
 

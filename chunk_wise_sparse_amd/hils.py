@@ -27,7 +27,7 @@ EXPORTED = ["hils_abi_version", "hils_prefill_workspace_size", "hils_decode_work
             "hils_prefill_fwd", "hils_decode_fwd", "hils_decode_fwd_noalloc", "hils_status_string",
             "hils_last_hip_error", "hils_dense_prefill_fwd", "hils_dense_decode_workspace_size",
             "hils_dense_decode_fwd", "hils_prefill_bwd_workspace_size", "hils_prefill_bwd",
-            "hils_hope_rotate"]
+            "hils_hope_rotate", "hils_partial_landmark"]
 STATIC_SCRATCH_BYTES = 64 << 20   # HILS_STATIC_SCRATCH_BYTES
 
 
@@ -63,6 +63,11 @@ class HopeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("rope_base", ctypes.c_float), ("train_len", ctypes.c_int32),
                 ("pos0", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class LandmarkParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -101,6 +106,8 @@ def load(path: str = LIB_PATH):
     lib.hils_dense_decode_fwd.restype = i32
     lib.hils_hope_rotate.argtypes = [ctypes.POINTER(HopeParams), vp, vp, vp]
     lib.hils_hope_rotate.restype = i32
+    lib.hils_partial_landmark.argtypes = [ctypes.POINTER(LandmarkParams), vp, vp, vp, vp]
+    lib.hils_partial_landmark.restype = i32
     lib.hils_prefill_bwd_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     lib.hils_prefill_bwd_workspace_size.restype = sz
     lib.hils_prefill_bwd.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17 + [vp, sz, vp]
@@ -382,3 +389,24 @@ def hope_rotate(x, *, rope_base: float, train_len: int, pos0: int = 0, positions
     check(st, "hils_hope_rotate")
     return x
 
+
+def partial_landmark(k_cache, lmk, kv_len, *, chunk: int = 64):
+    """The landmark of the chunk holding each sequence's newest key, in place: lmk[b, g, j] = the
+    mean of k_cache[b, g, j*chunk : n] with n = kv_len[b] and j = (n - 1) // chunk.  k_cache
+    [B, Hkv, Lmax, d]; lmk [B, Hkv, ceil(Lmax/chunk), d]; kv_len [B] int32 (device).  Returns lmk."""
+    import torch
+    lib = load()
+    B, Hk, Lmax, d = k_cache.shape
+    _require([("k_cache", k_cache), ("lmk", lmk)], k_cache.device, k_cache.dtype)
+    if not lmk.is_contiguous():
+        raise ValueError("lmk must be contiguous: it is updated in place")
+    if tuple(lmk.shape) != (B, Hk, -(-Lmax // chunk), d):
+        raise ValueError(f"lmk must be [{B}, {Hk}, {-(-Lmax // chunk)}, {d}]")
+    if (kv_len.dtype != torch.int32 or kv_len.device != k_cache.device or kv_len.numel() != B
+            or not kv_len.is_contiguous()):
+        raise ValueError("kv_len must be a contiguous int32 tensor of batch entries on the cache's device")
+    p = LandmarkParams(B, Hk, Lmax, d, int(chunk), _dtype_code(k_cache))
+    st = lib.hils_partial_landmark(ctypes.byref(p), _ptr(k_cache), _ptr(lmk), _ptr(kv_len),
+                                   _stream_handle(k_cache.device))
+    check(st, "hils_partial_landmark")
+    return lmk

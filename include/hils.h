@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 9
+#define HILS_ABI_VERSION 10
 
 typedef enum {
   HILS_OK = 0,
@@ -263,6 +263,25 @@ typedef struct hils_hope_params {
   int32_t dtype;               /* hils_dtype */
 } hils_hope_params;
 int hils_hope_rotate(const hils_hope_params* p, void* x, const int32_t* positions, void* stream);
+
+/* Landmark of the chunk still being filled during decode.  [HiLS Attention explainer
+ * (molayo1419.me), "Core idea: landmark tokens and hierarchical factorisation": a landmark token
+ * closes each chunk, so the chunk holding the newest key has none until it has C keys.]  For each
+ * sequence b and key/value head g, with n = kv_len[b] clamped to [1, max_kv_len] and
+ * j = (n - 1) / chunk, writes lmk[b][g][j] = the mean of k_cache[b][g][j*chunk .. n-1] (fp32 sums
+ * in a fixed order, one rounding to the dtype); every other landmark row is left as it is.  The
+ * mean is this library's stand-in until the chunk is complete and the model's landmark replaces
+ * it; call it after the new key is stored and before hils_decode_fwd.
+ * k_cache: [batch, kv_heads, max_kv_len, head_dim], device, read only.  lmk: [batch, kv_heads,
+ * ceil(max_kv_len / chunk), head_dim], device, updated in place.  kv_len: [batch] int32, device.
+ * Supported: head_dim in {64, 128}; chunk in {32, 64, 128}; dtype bf16 or fp32; contiguous
+ * caches (no block table).  Errors as for the other calls; nothing is enqueued on an error. */
+typedef struct hils_landmark_params {
+  int32_t batch, kv_heads, max_kv_len, head_dim, chunk;
+  int32_t dtype;               /* hils_dtype */
+} hils_landmark_params;
+int hils_partial_landmark(const hils_landmark_params* p, const void* k_cache, void* lmk,
+                          const int32_t* kv_len, void* stream);
 
 /* hils_decode_fwd for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops and harnesses that forbid hipMalloc.  The arguments are those of

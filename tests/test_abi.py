@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(hils.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.hils_abi_version() == 9
+    assert lib.hils_abi_version() == 10
 
 
 def _pp(**kw):
@@ -230,3 +230,24 @@ def test_other_chunk_sizes_accepted():
         assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C, block_table=FAKE, block_table_stride=64,
                                                                num_pages=64)), 1) == 0
 
+
+
+def test_partial_landmark_rejects_bad_arguments():
+    lib = hils.load()
+
+    def call(p, k=FAKE, lm=FAKE + (1 << 30), kv=FAKE + (2 << 30)):
+        return lib.hils_partial_landmark(ctypes.byref(p) if p is not None else None, k, lm, kv, None)
+
+    good = dict(batch=2, kv_heads=4, max_kv_len=1000, head_dim=128, chunk=64, dtype=hils.DTYPE_BF16)
+    mk = lambda **o: hils.LandmarkParams(**dict(good, **o))
+    assert call(None) == -1
+    assert call(mk(), k=None) == -1
+    assert call(mk(), kv=None) == -1
+    assert call(mk(batch=0)) == -1
+    assert call(mk(max_kv_len=0)) == -1
+    assert call(mk(head_dim=96)) == -2
+    assert call(mk(chunk=16)) == -2
+    assert call(mk(dtype=7)) == -2
+    assert call(mk(), lm=FAKE + 8) == -3
+    assert call(mk(), kv=FAKE + (2 << 30) + 2) == -3
+    assert call(mk(), lm=FAKE + 4096) == -1           # lmk inside k_cache

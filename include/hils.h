@@ -22,7 +22,8 @@
  *     unless stated.  The caller owns every buffer; the library keeps no pointer after the call.
  *   - Inputs are read-only.  Every output element is written (idx padding -1, w padding 0).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and nothing is
- *     synchronised; results are valid once the caller synchronises that stream.
+ *     synchronised (the one exception: prefill with attn_mode HILS_ATTN_AUTO waits on the stream
+ *     once, see there); results are valid once the caller synchronises that stream.
  *   - All checks a host can make run before any launch; on failure nothing is enqueued and a
  *     negative status is returned.  Launch failures return HILS_ERR_HIP; hils_last_hip_error()
  *     gives the message (per thread).

@@ -1083,7 +1083,7 @@ __global__ __launch_bounds__(256) void decode_attend_split_kernel(const DecodeAr
   }
 }
 
-// Chunks of C = 32 or 128 keys (selected by the generic chunk-size kernel): one wave per slot,
+// Chunks of C = 32 or 128 keys (contiguous or paged caches): one wave per slot,
 // the chunk taken in 64-row pieces (one for C = 32, two for C = 128).  The keys of every piece
 // give the chunk's scores, one softmax runs over all of them, then the values of every piece are
 // weighted; w_j * o_j goes to the slot's partial as above.  Rows past the chunk's visible ones
@@ -1102,7 +1102,16 @@ __global__ __launch_bounds__(256) void decode_attend_gc_kernel(const DecodeArgs 
   const bool live = j >= 0 && j * C < kvl;
   const int n_vis = live ? min(C, kvl - j * C) : 0;
   const float wj = live ? a.w[(size_t)bh * a.k + u] : 0.f;
-  const size_t row0 = (size_t)kv_pair(bh, a.H, a.G) * a.Lmax + (size_t)max(j, 0) * C;
+  // First row of the chunk: in the (sequence, key/value head) cache, or in the chunk's page of a
+  // paged pool [pages, H/G, C, d].
+  const int kvp = kv_pair(bh, a.H, a.G);
+  size_t row0;
+  if (a.block_table) {
+    const int hk = a.H / a.G;
+    row0 = ((size_t)page_of(a, b, j) * hk + kvp % hk) * C;
+  } else {
+    row0 = (size_t)kvp * a.Lmax + (size_t)max(j, 0) * C;
+  }
   auto piece = [&](const void* cache, int pc) {
     const int nv = min(max(n_vis - 64 * pc, 0), 64);
     return buffer_rsrc(static_cast<const T*>(cache) + (row0 + 64 * pc) * D, nv * D * (int)sizeof(T));

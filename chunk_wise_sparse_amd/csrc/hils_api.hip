@@ -468,7 +468,6 @@ int check_decode_params(const hils_decode_params* p) {
   if (p->chunk != 64) {
     if ((p->max_kv_len + p->chunk - 1) / p->chunk > 65535)
       return fail(HILS_ERR_UNSUPPORTED, "chunk %d: more than 65535 chunks per sequence", p->chunk);
-    if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "a paged cache needs chunk 64 (one page per chunk)");
   }
   if (p->topk < 1 || p->topk > 64)
     return fail(HILS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", p->topk);
@@ -485,9 +484,9 @@ int check_decode_params(const hils_decode_params* p) {
     return fail(HILS_ERR_INVALID_ARG, "kv_heads %d must divide heads %d", p->kv_heads, p->heads);
   if (p->force_local != 0 && p->force_local != 1)
     return fail(HILS_ERR_INVALID_ARG, "force_local must be 0 or 1");
-  if (p->block_table && (p->num_pages < 1 || p->block_table_stride < (p->max_kv_len + 63) / 64))
+  if (p->block_table && (p->num_pages < 1 || p->block_table_stride < (p->max_kv_len + p->chunk - 1) / p->chunk))
     return fail(HILS_ERR_INVALID_ARG, "paged cache: num_pages >= 1 and block_table_stride >= %d needed",
-                (p->max_kv_len + 63) / 64);
+                (p->max_kv_len + p->chunk - 1) / p->chunk);
   if ((double)p->batch * p->heads > 2147483647.0)
     return fail(HILS_ERR_UNSUPPORTED, "problem too large");
   return HILS_OK;
@@ -555,6 +554,9 @@ hipError_t run_decode_gc(const hils_decode_params* p, const void* q, const void*
   a.Lmax = p->max_kv_len;
   a.C = p->chunk;
   a.Nmax = (p->max_kv_len + p->chunk - 1) / p->chunk;
+  a.block_table = p->block_table;
+  a.bt_stride = p->block_table_stride;
+  a.num_pages = p->num_pages;
   a.k = p->topk;
   a.r = p->qcal_rank;
   a.score_qb = hils::decode_score_qb(a.B * a.H, a.Nmax);
@@ -840,7 +842,7 @@ int decode_entry(const hils_decode_params* p, const void* q, const void* k_cache
   const size_t B = p->batch, H = p->heads, Lm = p->max_kv_len, d = p->head_dim, kk = p->topk;
   const size_t N = (Lm + p->chunk - 1) / p->chunk, r = p->qcal_rank, D = p->hidden;
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
-  const size_t cache = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * Lm * d * e;
+  const size_t cache = p->block_table ? (size_t)p->num_pages * Hk * p->chunk * d * e : B * Hk * Lm * d * e;
   if (p->block_table && ((uintptr_t)p->block_table & 3))
     return fail(HILS_ERR_ALIGNMENT, "block_table is not 4-byte aligned");
   const Range in[] = {{q, B * H * d * e, "q"},           {k_cache, cache, "k_cache"},

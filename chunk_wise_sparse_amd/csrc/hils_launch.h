@@ -132,7 +132,7 @@ struct DecodeArgs {
   float scale;
   int force_local;      // the selection is written out and amended before the attention
   int C;                // keys per chunk: 64; 32 or 128 for the scan, the selection and
-                        // launch_decode_attend_gc (contiguous caches)
+                        // launch_decode_attend_gc (pages, if any, hold C rows)
 };
 
 // Dense causal attention (the full-attention baseline): prefill over [B,H,L,d] (L % 64 == 0) and
@@ -245,8 +245,8 @@ template <typename T>
 bool decode_select_fused(const DecodeArgs& a);
 template <typename T, int D>
 hipError_t launch_decode_attend(const DecodeArgs& a, hipStream_t st);
-// Chunks of C = 32 or 128 keys (contiguous caches, the selection in idx / w): split attention into
-// `partial`, then the fixed-order reduce into o.
+// Chunks of C = 32 or 128 keys (contiguous caches, or pages of C rows; the selection in idx / w):
+// split attention into `partial`, then the fixed-order reduce into o.
 template <typename T, int D>
 hipError_t launch_decode_attend_gc(const DecodeArgs& a, int C, hipStream_t st);
 

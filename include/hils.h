@@ -133,8 +133,8 @@ typedef struct hils_prefill_params {
  * Supported: head_dim in {64, 128}; chunk in {32, 64, 128}; 1 <= topk <= 64;
  * 1 <= max_kv_len <= 65535 * chunk; 0 <= qcal_rank <= 64; hidden a positive multiple of 128
  * when qcal_rank > 0.  A partial last chunk is allowed.  Chunk sizes 32 and 128 take the same
- * landmark scan and selection as 64 and a split attention over C-key chunks (no block_table;
- * never the one-kernel step below).  With at least 5 stage events, event 0 is
+ * landmark scan and selection as 64 and a split attention over C-key chunks (paged caches hold
+ * C rows per page; never the one-kernel step below).  With at least 5 stage events, event 0 is
  * recorded first and events 1..4 after the Q-Cal, landmark-scoring, selection and
  * chunk-attention stages; for chunk 64, bf16, batch*heads >= 256 and at most 8192 chunks these
  * three stages run as one kernel, and events 2..4 are recorded together after it. */

@@ -213,8 +213,10 @@ def test_hope_rejects_bad_arguments():
 
 
 def test_other_chunk_sizes_accepted():
-    """Chunk sizes 32 and 128 (any sequence length, up to 8192 chunks): the workspace holds the
-    Q-Cal code and, when not returned, the selection; no paged keys/values and no backward."""
+    """Chunk sizes 32 and 128 (any sequence length, up to 8192 chunks): the fp32 prefill workspace
+    holds the Q-Cal code and, when not returned, the selection; no paged prefill and no backward;
+    paged decode caches of C-row pages, with a block table of at least ceil(max_kv_len / C)
+    entries per sequence."""
     lib = hils.load()
     a256 = lambda x: (x + 255) // 256 * 256
     for C in (32, 128):
@@ -227,7 +229,10 @@ def test_other_chunk_sizes_accepted():
         assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C)), 1) > 0
         pb = _pp(chunk=C, block_table=FAKE, block_table_stride=64, num_pages=64)
         assert lib.hils_prefill_workspace_size(ctypes.byref(pb), 1) == 0       # paged needs chunk 64
-        assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C, block_table=FAKE, block_table_stride=64,
+        n = -(-1000 // C)
+        assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C, block_table=FAKE, block_table_stride=n,
+                                                               num_pages=64)), 1) > 0
+        assert lib.hils_decode_workspace_size(ctypes.byref(_dp(chunk=C, block_table=FAKE, block_table_stride=n - 1,
                                                                num_pages=64)), 1) == 0
 
 

@@ -994,11 +994,11 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const CmArgs a) {
 // toff[j + 1] and covers list entries off[j] + 128 (i - toff[j]) onward.  Consecutive items
 // mostly belong to one chunk, whose K/V is then staged once for the whole run of them.
 //
-// C keys per chunk (64, or 32 / 128 behind the generic selection kernel): S^T takes C / 16 key
-// blocks, PV C / 32 steps; K rows keep the 64-key kernels' layout and V's d-blocks hold C rows.
-// For C != 64 the keys and values are contiguous and a partial last chunk is read with its rows
-// clamped to the sequence: only rows of that chunk select it, as their own chunk, and the keys
-// past each such row are masked.
+// C keys per chunk (64, or 32 / 128): S^T takes C / 16 key blocks, PV C / 32 steps; K rows keep
+// the 64-key kernels' layout and V's d-blocks hold C rows.  For C != 64 the keys and values are
+// either pages of C rows (whole chunks) or contiguous, where a partial last chunk is read with
+// its rows clamped to the sequence: only rows of that chunk select it, as their own chunk, and the
+// keys past each such row are masked.
 template <int D, int C>
 __global__ __launch_bounds__(512, C == 128 ? 2 : 4) void cm_attn_kernel(const CmArgs a) {
   constexpr int NT = 512;
@@ -1053,6 +1053,16 @@ __global__ __launch_bounds__(512, C == 128 ? 2 : 4) void cm_attn_kernel(const Cm
         const int v = vec_of(u);
         kr[u] = *reinterpret_cast<const u32x4*>(kc + (size_t)v * VE);
         vr[u] = *reinterpret_cast<const u32x4*>(vc + (size_t)v * VE);
+      }
+    } else if (cp.bt != nullptr) {             // pages of C rows (whole chunks only)
+      const int pg = min(max(cp.bt[j], 0), a.num_pages - 1);
+      const size_t base = ((size_t)pg * cp.Hk + cp.kvh) * C * D;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int v = vec_of(u);
+        const size_t e = base + (size_t)v * VE;
+        kr[u] = *reinterpret_cast<const u32x4*>(Kb + e);
+        vr[u] = *reinterpret_cast<const u32x4*>(Vb + e);
       }
     } else {
 #pragma unroll

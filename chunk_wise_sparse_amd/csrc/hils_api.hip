@@ -76,7 +76,9 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (p->chunk != 64) {
     if ((p->seq_len + p->chunk - 1) / p->chunk > hils::kGcMaxChunks)
       return fail(HILS_ERR_UNSUPPORTED, "chunk %d: at most %d chunks per sequence", p->chunk, hils::kGcMaxChunks);
-    if (p->block_table) return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need chunk 64 (one page per chunk)");
+    if (p->block_table && (p->dtype != HILS_DTYPE_BF16 || p->seq_len % 64 != 0))
+      return fail(HILS_ERR_UNSUPPORTED, "chunk %d: paged keys/values need bf16 and seq_len a multiple of 64",
+                  p->chunk);
   }
   if (p->q_tile != 0 && p->q_tile != 16 && p->q_tile != 32 && p->q_tile != 64 && p->q_tile != 128)
     return fail(HILS_ERR_UNSUPPORTED, "q_tile %d is not supported (16, 32, 64 or 128)", p->q_tile);
@@ -96,11 +98,11 @@ int check_prefill_params(const hils_prefill_params* p) {
   if (p->force_local != 0 && p->force_local != 1)
     return fail(HILS_ERR_INVALID_ARG, "force_local must be 0 or 1");
   if (p->block_table) {
-    if (p->seq_len % 64 != 0)
-      return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need seq_len a multiple of the chunk (64)");
-    if (p->num_pages < 1 || p->block_table_stride < p->seq_len / 64)
+    if (p->seq_len % p->chunk != 0)
+      return fail(HILS_ERR_UNSUPPORTED, "paged keys/values need seq_len a multiple of the chunk (%d)", p->chunk);
+    if (p->num_pages < 1 || p->block_table_stride < p->seq_len / p->chunk)
       return fail(HILS_ERR_INVALID_ARG, "paged keys/values: num_pages >= 1 and block_table_stride >= %d needed",
-                  p->seq_len / 64);
+                  p->seq_len / p->chunk);
     if ((uintptr_t)p->block_table & 3) return fail(HILS_ERR_ALIGNMENT, "block_table is not 4-byte aligned");
   }
   const double bhld = (double)p->batch * p->heads * (p->seq_len + 63.0) * p->head_dim;
@@ -720,7 +722,7 @@ int hils_prefill_fwd(const hils_prefill_params* p, const void* q, const void* k,
   const size_t B = p->batch, H = p->heads, S = p->seq_len, d = p->head_dim, kk = p->topk;
   const size_t r = p->qcal_rank, D = p->hidden;
   const size_t Hk = p->kv_heads > 0 ? (size_t)p->kv_heads : H;   // key/value heads
-  const size_t kvb = p->block_table ? (size_t)p->num_pages * Hk * 64 * d * e : B * Hk * S * d * e;
+  const size_t kvb = p->block_table ? (size_t)p->num_pages * Hk * p->chunk * d * e : B * Hk * S * d * e;
   const Range in[] = {{q, B * H * S * d * e, "q"},   {k, kvb, "k"},
                       {v, kvb, "v"},  {lmk, B * Hk * ((S + p->chunk - 1) / p->chunk) * d * e, "lmk"},
                       {p->block_table, p->block_table ? B * (size_t)p->block_table_stride * 4 : 0, "block_table"},

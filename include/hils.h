@@ -65,9 +65,9 @@ typedef enum { HILS_DTYPE_BF16 = 0, HILS_DTYPE_FP32 = 1 } hils_dtype;
  * workgroup, scores in LDS); the
  * attention is always the chunk-major MFMA mode (attn_mode and q_tile are ignored, and the
  * workspace is that mode's).  fp32 selects and attends in the generic kernel, whose stage events
- * 2 and 3 are recorded together after it.  Limits: at most 8192 chunks, contiguous keys and
- * values only (no block_table), any seq_len without padding.  The backward pass takes
- * chunk == 64 only.
+ * 2 and 3 are recorded together after it.  Limits: at most 8192 chunks; any seq_len without
+ * padding; paged keys/values (pages of chunk rows) for bf16 with seq_len a multiple of the chunk
+ * and of 64.  The backward pass takes chunk == 64 only.
  * A partial last chunk (seq_len % chunk != 0) is allowed: lmk then holds ceil(seq_len / chunk)
  * landmarks, the last one for the partial chunk, and the call stages q, k, v, h and o padded to
  * whole chunks in the workspace (the padded rows are zero and come after every real row, so no
@@ -126,7 +126,8 @@ typedef struct hils_prefill_params {
  * non-NULL, k and v are pools of num_pages pages of one chunk each, [num_pages, kv heads, chunk,
  * head_dim], and chunk j of sequence b is page block_table[b * block_table_stride + j] (entries
  * outside [0, num_pages) are clamped).  q, lmk, h and the outputs keep their layouts.  Needs
- * seq_len a multiple of the chunk; the backward pass takes contiguous keys and values only. */
+ * seq_len a multiple of the chunk (chunks of 32 and 128: bf16 and seq_len also a multiple of
+ * 64); the backward pass takes contiguous keys and values only. */
 
 /* One decode step for `batch` sequences, one new token each, at position kv_len[b] - 1 of a
  * key/value cache of capacity max_kv_len (the new token's key and value are already stored).

@@ -1,6 +1,7 @@
 """hils_decode_fwd_noalloc (the library's static scratch, no workspace argument) against
-hils_decode_fwd with a caller workspace: two calls in a row on one GPU, the second smaller, each
-bitwise equal to the workspace entry point (same kernels), and the first also against the oracle."""
+hils_decode_fwd with a caller workspace: calls in a row on one GPU, the second smaller than the
+first, the third at chunks of 128 keys, each bitwise equal to the workspace entry point (same
+kernels), and the first also against the oracle."""
 import numpy as np
 import pytest
 
@@ -31,8 +32,8 @@ def _both(cfg):
     inp = synth.make_decode_inputs_np(cfg)
     d = _dev(inp, cfg.dtype)
     args = (d["q"], d["k_cache"], d["v_cache"], d["lmk"], d["kv_len"], d.get("h"), d.get("w_down"), d.get("w_up"))
-    ref = hils.decode(*args, topk=cfg.topk, return_selection=True)
-    got = hils.decode(*args, topk=cfg.topk, return_selection=True, no_alloc=True)
+    ref = hils.decode(*args, topk=cfg.topk, chunk=cfg.chunk, return_selection=True)
+    got = hils.decode(*args, topk=cfg.topk, chunk=cfg.chunk, return_selection=True, no_alloc=True)
     torch.cuda.synchronize()
     return inp, ref, got
 
@@ -42,6 +43,8 @@ CASES = [
     synth.DecodeConfig("noalloc_fused", 4, 64, 3000, 128, 64, 64, "bf16", 32, 512, kv_len=(3000, 1, 65, 2047)),
     # a smaller second call: fp32, four pairs, the multi-kernel path
     synth.DecodeConfig("noalloc_small", 2, 2, 1500, 64, 64, 8, "fp32", 8, 128, kv_len=(1500, 700)),
+    # a third call at chunks of 128 keys: the scan, the selection and the split attention
+    synth.DecodeConfig("noalloc_c128", 2, 4, 5000, 128, 128, 16, "bf16", 16, 256, kv_len=(5000, 333)),
 ]
 
 

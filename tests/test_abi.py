@@ -256,3 +256,21 @@ def test_partial_landmark_rejects_bad_arguments():
     assert call(mk(), lm=FAKE + 8) == -3
     assert call(mk(), kv=FAKE + (2 << 30) + 2) == -3
     assert call(mk(), lm=FAKE + 4096) == -1           # lmk inside k_cache
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """include/hils.h is a plain C header: it compiles alone as C99 (pedantic) and as C++17."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "hils.h"\n'
+                   'int main(void) { hils_landmark_params p = {1, 1, 64, 64, 64, 0}; (void)p;\n'
+                   '  return hils_abi_version() == HILS_ABI_VERSION ? 0 : 1; }\n')
+    inc = os.path.join(ROOT, "include")
+    for cc, flags in (("gcc", ["-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror"]),
+                      ("g++", ["-std=c++17", "-Wall", "-Werror", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        r = subprocess.run([cc, *flags, "-I", inc, "-c", str(src), "-o", str(tmp_path / "use.o")],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr

@@ -163,3 +163,25 @@ def test_prefill_chunk_size_ignores_mode_and_q_tile(lib, C):
         TP._torch().cuda.synchronize()
         for a, b in zip(ref, got):
             assert TP._torch().equal(a, b), kw
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_chunk_size_selection_in_workspace(lib, C):
+    """With the selection kept in the workspace (no idx / w outputs) prefill and decode give
+    bitwise the same output as with the selection returned."""
+    from chunk_wise_sparse_amd import hils
+    torch = TP._torch()
+    cfg = synth.PrefillConfig(f"c{C}_ws", 1, 2, 2048, 64, C, 8, "bf16", 16, 256)
+    print(f"[case] selection in workspace, chunk={C}", flush=True)
+    dev = TP._to_dev(synth.make_prefill_inputs_np(cfg), cfg.dtype)
+    o_sel, _, _ = TP._run(lib, dev, cfg, chunk=C)
+    o_ws = hils.prefill(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["h"], dev["w_down"], dev["w_up"],
+                        topk=cfg.topk, chunk=C)
+    dcfg = synth.DecodeConfig(f"c{C}_dec_ws", 2, 4, 3000, 128, C, 8, "bf16", 16, 256, kv_len=(3000, 777))
+    dd = TD._to_dev(synth.make_decode_inputs_np(dcfg), dcfg.dtype)
+    args = (dd["q"], dd["k_cache"], dd["v_cache"], dd["lmk"], dd["kv_len"], dd["h"], dd["w_down"], dd["w_up"])
+    od_sel, _, _ = hils.decode(*args, topk=dcfg.topk, chunk=C, return_selection=True)
+    od_ws = hils.decode(*args, topk=dcfg.topk, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o_sel, o_ws)
+    assert torch.equal(od_sel, od_ws)
